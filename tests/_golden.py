@@ -1,0 +1,56 @@
+"""Readers for the text fixtures under tests/golden/ (shared by CPU and GPU tests)."""
+
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                yield line.split()
+
+
+def partition_counts():
+    return [(int(a), int(b)) for a, b in _rows("partition_counts.txt")]
+
+
+def e4m3fn_codes():
+    return [(int(a, 16), float(b)) for a, b in _rows("e4m3fn_codes.txt")]
+
+
+def worked_example(alibi=False):
+    """Inputs (pages' layouts, fp32, x = 4) and the closed-form output of the
+    hand-derived example in worked_example.txt."""
+    kv = {k: v for k, v in _rows("worked_example.txt")}
+    n, d, scale, phys = int(kv["seq_len"]), int(kv["head_size"]), float(kv["scale"]), int(kv["table"])
+    bs, x, pool = 16, 4, 8
+    k_pool = np.zeros((pool, 1, d // x, bs, x), np.float32)
+    v_pool = np.zeros((pool, 1, d, bs), np.float32)
+    v_rows = [(1.0, 0.0, 2.0), (0.0, 1.0, 2.0), (0.0, 0.0, 2.0)]
+    for t in range(n):
+        k_pool[phys, 0, 0, t, 0] = float(t)           # K[t] = t * e0
+        for dd, val in enumerate(v_rows[t]):
+            v_pool[phys, 0, dd, t] = val
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = 8.0
+    e = math.e
+    expect = np.zeros((1, 1, d))
+    if alibi:
+        w = np.array([e ** -2, 1.0, e ** 2]) / (e ** -2 + 1.0 + e ** 2)
+    else:
+        w = np.array([1.0, e, e * e]) / (1.0 + e + e * e)
+    expect[0, 0, 0] = w[0]
+    expect[0, 0, 1] = w[1]
+    expect[0, 0, 2] = 2.0
+    slopes = np.ones(1, np.float32) if alibi else None
+    return {
+        "query": q, "key_cache": k_pool, "value_cache": v_pool,
+        "block_tables": np.array([[phys]], np.int32), "seq_lens": np.array([n], np.int32),
+        "scale": scale, "alibi_slopes": slopes, "expect": expect,
+    }

@@ -1,0 +1,14 @@
+"""Seeded synthetic decode workloads (no attention arithmetic lives here)."""
+
+from .configs import CONFIGS, FP8, GQA, LONG, MHA, TINY, DecodeConfig  # noqa: F401
+from .generate import (  # noqa: F401
+    Case,
+    Metadata,
+    alibi_slopes,
+    default_x,
+    draw_seq_lens,
+    host_arrays,
+    kv_elem,
+    make_case,
+    make_metadata,
+)

@@ -1,0 +1,56 @@
+"""The five decode workloads, as plain data.
+
+Shapes follow the pages' workloads: head sizes 64/128 and 256-token partitions
+(PR #47361 report, test and benchmark snippets), a pool of 128*1024 physical
+blocks (same benchmark), block_size 16, and physical blocks scattered through a
+per-sequence table (10100.com article, §1).
+
+Readings where the workload text is silent:
+  * lognormal lengths: sigma = 1.0 in natural-log units around ln(4096),
+    rounded to the nearest integer, clipped to [1, 16384];
+  * the long-context pool is 131072 blocks, like the other large configs;
+  * one amax over all generated K and V values gives k_scale = v_scale =
+    amax / 448 for the fp8 cache.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_size: int
+    block_size: int
+    pool_blocks: int
+    q_dtype: str          # "f32" or "bf16"; out has the same dtype
+    kv_dtype: str         # "auto" (= q dtype) or "fp8_e4m3"
+    seq_lens: tuple       # recipe: ("fixed", (..)), ("const", n), ("uniform", lo, hi),
+                          #         ("lognormal", median, sigma, cap)
+    alibi: bool
+    seed: int
+
+    @property
+    def group(self) -> int:
+        return self.num_heads // self.num_kv_heads
+
+    def with_(self, **kw) -> "DecodeConfig":
+        return replace(self, **kw)
+
+
+TINY = DecodeConfig("tiny", 2, 4, 4, 64, 16, 16, "f32", "auto",
+                    ("fixed", (17, 40)), False, 0)
+MHA = DecodeConfig("mha", 64, 32, 32, 128, 16, 32768, "bf16", "auto",
+                   ("const", 4096), False, 1)
+GQA = DecodeConfig("gqa", 128, 64, 8, 128, 16, 128 * 1024, "bf16", "auto",
+                   ("uniform", 1, 8192), False, 2)
+LONG = DecodeConfig("long", 8, 32, 8, 128, 16, 128 * 1024, "bf16", "auto",
+                    ("const", 32768), True, 3)
+FP8 = DecodeConfig("fp8", 256, 64, 8, 128, 16, 128 * 1024, "bf16", "fp8_e4m3",
+                   ("lognormal", 4096, 1.0, 16384), False, 4)
+
+CONFIGS = {c.name: c for c in (TINY, MHA, GQA, LONG, FP8)}
