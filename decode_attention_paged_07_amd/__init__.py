@@ -1,0 +1,293 @@
+"""Paged decode attention for AMD MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libpa_decode.so`` (C ABI declared in
+``include/pa_decode.h``). The ``pa_*`` functions mirror the C entry points one
+to one (plain integers and device addresses); ``paged_attention_decode`` takes
+torch tensors and only marshals their metadata, device addresses and the
+current HIP stream. Every step of the computation runs in the library's
+kernels; there is no fallback path. Importing this package fails with
+ImportError when the library has not been built.
+
+The call follows the ROCm decode call kept in the PR #47361 report
+(prhub.com.cn, "关键源码片段"): out, query, key_cache, value_cache,
+num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
+alibi_slopes, kv_cache_dtype, k_scale, v_scale; its three partial-result
+buffers are replaced by one workspace the binding keeps per device.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+__all__ = [
+    "PA_OK", "PA_ERR_NULL", "PA_ERR_SHAPE", "PA_ERR_DTYPE", "PA_ERR_WORKSPACE", "PA_ERR_ALIGN",
+    "PA_ERR_HIP", "PA_DTYPE_F32", "PA_DTYPE_BF16", "PA_KV_AUTO", "PA_KV_FP8_E4M3",
+    "PA_BLOCK_SIZE", "PA_PARTITION_SIZE", "PA_MAX_GROUP",
+    "pa_paged_attention_decode", "pa_paged_attention_decode_split", "pa_decode_plan",
+    "pa_workspace_bytes", "pa_kv_layout", "pa_last_error", "pa_version", "pa_timing_enable",
+    "pa_timing_read", "paged_attention_decode", "kv_cache_shapes", "LIB_PATH", "PagedAttentionError",
+]
+
+PA_OK = 0
+PA_ERR_NULL = -1
+PA_ERR_SHAPE = -2
+PA_ERR_DTYPE = -3
+PA_ERR_WORKSPACE = -4
+PA_ERR_ALIGN = -5
+PA_ERR_HIP = -6
+PA_DTYPE_F32 = 0
+PA_DTYPE_BF16 = 1
+PA_KV_AUTO = 0
+PA_KV_FP8_E4M3 = 1
+PA_BLOCK_SIZE = 16
+PA_PARTITION_SIZE = 256
+PA_MAX_GROUP = 16
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
+        "or python decode_attention_paged_07_amd/build.py). There is no non-HIP fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_c_int, _c_float, _c_size, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+
+class _LayoutDesc(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_int), ("elem_bytes", ctypes.c_int),
+                ("k_block_stride", ctypes.c_int64), ("k_head_stride", ctypes.c_int64),
+                ("v_block_stride", ctypes.c_int64), ("v_head_stride", ctypes.c_int64)]
+
+
+_DECODE_ARGS = [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _c_int,
+                _vp, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp, _c_size, _vp]
+
+_lib.pa_paged_attention_decode.argtypes = _DECODE_ARGS
+_lib.pa_paged_attention_decode.restype = _c_int
+_lib.pa_paged_attention_decode_split.argtypes = _DECODE_ARGS + [_c_int]
+_lib.pa_paged_attention_decode_split.restype = _c_int
+_lib.pa_decode_plan.argtypes = [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                ctypes.POINTER(_c_int), ctypes.POINTER(_c_int), ctypes.POINTER(_c_size)]
+_lib.pa_decode_plan.restype = _c_int
+_lib.pa_workspace_bytes.argtypes = [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_size)]
+_lib.pa_workspace_bytes.restype = _c_int
+_lib.pa_kv_layout.argtypes = [_c_int, _c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_LayoutDesc)]
+_lib.pa_kv_layout.restype = _c_int
+_lib.pa_last_error.argtypes = []
+_lib.pa_last_error.restype = ctypes.c_char_p
+_lib.pa_version.argtypes = []
+_lib.pa_version.restype = _c_int
+_lib.pa_timing_enable.argtypes = [_c_int]
+_lib.pa_timing_enable.restype = _c_int
+_lib.pa_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_int),
+                                ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_int)]
+_lib.pa_timing_read.restype = _c_int
+
+
+class PagedAttentionError(RuntimeError):
+    """A PA_ERR_HIP failure reported by the library."""
+
+
+def _raise_for(code: int, what: str):
+    if code == PA_OK:
+        return
+    msg = f"{what}: {pa_last_error()} (code {code})"
+    if code == PA_ERR_DTYPE:
+        raise TypeError(msg)
+    if code == PA_ERR_HIP:
+        raise PagedAttentionError(msg)
+    raise ValueError(msg)
+
+
+# ---------------------------------------------------------------------------
+# One-to-one wrappers of the C entry points (integers and device addresses).
+# ---------------------------------------------------------------------------
+
+def pa_paged_attention_decode(out, query, key_cache, value_cache, num_seqs, num_heads,
+                              num_kv_heads, head_size, num_blocks, scale, block_tables,
+                              max_blocks_per_seq, seq_lens, block_size, max_seq_len,
+                              alibi_slopes, q_dtype, kv_cache_dtype, k_scale, v_scale,
+                              workspace, workspace_bytes, stream) -> int:
+    return _lib.pa_paged_attention_decode(out, query, key_cache, value_cache, num_seqs, num_heads,
+                                          num_kv_heads, head_size, num_blocks, scale, block_tables,
+                                          max_blocks_per_seq, seq_lens, block_size, max_seq_len,
+                                          alibi_slopes, q_dtype, kv_cache_dtype, k_scale, v_scale,
+                                          workspace, workspace_bytes, stream)
+
+
+def pa_paged_attention_decode_split(out, query, key_cache, value_cache, num_seqs, num_heads,
+                                    num_kv_heads, head_size, num_blocks, scale, block_tables,
+                                    max_blocks_per_seq, seq_lens, block_size, max_seq_len,
+                                    alibi_slopes, q_dtype, kv_cache_dtype, k_scale, v_scale,
+                                    workspace, workspace_bytes, stream, split_tokens) -> int:
+    return _lib.pa_paged_attention_decode_split(out, query, key_cache, value_cache, num_seqs,
+                                                num_heads, num_kv_heads, head_size, num_blocks,
+                                                scale, block_tables, max_blocks_per_seq, seq_lens,
+                                                block_size, max_seq_len, alibi_slopes, q_dtype,
+                                                kv_cache_dtype, k_scale, v_scale, workspace,
+                                                workspace_bytes, stream, split_tokens)
+
+
+def pa_decode_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len,
+                   requested_split_tokens=0):
+    """-> (split_tokens, num_splits, workspace_bytes); raises on invalid sizes."""
+    st, ns, wb = _c_int(), _c_int(), _c_size()
+    rc = _lib.pa_decode_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len,
+                             requested_split_tokens, ctypes.byref(st), ctypes.byref(ns),
+                             ctypes.byref(wb))
+    _raise_for(rc, "pa_decode_plan")
+    return st.value, ns.value, wb.value
+
+
+def pa_workspace_bytes(num_seqs, num_heads, head_size, max_seq_len) -> int:
+    out = _c_size()
+    rc = _lib.pa_workspace_bytes(num_seqs, num_heads, head_size, max_seq_len, ctypes.byref(out))
+    _raise_for(rc, "pa_workspace_bytes")
+    return out.value
+
+
+def pa_kv_layout(num_kv_heads, head_size, block_size, q_dtype, kv_cache_dtype) -> dict:
+    d = _LayoutDesc()
+    rc = _lib.pa_kv_layout(num_kv_heads, head_size, block_size, q_dtype, kv_cache_dtype,
+                           ctypes.byref(d))
+    _raise_for(rc, "pa_kv_layout")
+    return {f: getattr(d, f) for f, _ in _LayoutDesc._fields_}
+
+
+def pa_last_error() -> str:
+    return _lib.pa_last_error().decode()
+
+
+def pa_version() -> int:
+    return _lib.pa_version()
+
+
+def pa_timing_enable(on: bool) -> None:
+    _raise_for(_lib.pa_timing_enable(1 if on else 0), "pa_timing_enable")
+
+
+def pa_timing_read():
+    """-> (partition_ms, partition_launches, reduce_ms, reduce_launches) since the last read."""
+    pm, pn, rm, rn = ctypes.c_double(), _c_int(), ctypes.c_double(), _c_int()
+    rc = _lib.pa_timing_read(ctypes.byref(pm), ctypes.byref(pn), ctypes.byref(rm), ctypes.byref(rn))
+    _raise_for(rc, "pa_timing_read")
+    return pm.value, pn.value, rm.value, rn.value
+
+
+# ---------------------------------------------------------------------------
+# Tensor-level call.
+# ---------------------------------------------------------------------------
+
+_Q_DTYPES = {torch.float32: PA_DTYPE_F32, torch.bfloat16: PA_DTYPE_BF16}
+_KV_NAMES = {"auto": PA_KV_AUTO, "fp8": PA_KV_FP8_E4M3, "fp8_e4m3": PA_KV_FP8_E4M3}
+_workspaces: dict = {}
+_scalars: dict = {}
+
+
+def kv_cache_shapes(num_blocks, num_kv_heads, head_size, q_dtype=torch.bfloat16,
+                    kv_cache_dtype="auto", block_size=PA_BLOCK_SIZE):
+    """Shapes of (key_cache, value_cache) in the library's layout."""
+    lay = pa_kv_layout(num_kv_heads, head_size, block_size, _Q_DTYPES[q_dtype],
+                       _KV_NAMES[kv_cache_dtype])
+    x = lay["x"]
+    return ((num_blocks, num_kv_heads, head_size // x, block_size, x),
+            (num_blocks, num_kv_heads, head_size, block_size))
+
+
+def _device_scalar(v, device):
+    if isinstance(v, torch.Tensor):
+        if v.dtype != torch.float32 or v.numel() != 1 or v.device != device:
+            raise ValueError("k_scale/v_scale tensors must be one float32 element on the query's device")
+        return v
+    key = (device, float(v))
+    t = _scalars.get(key)
+    if t is None:
+        t = torch.tensor([float(v)], dtype=torch.float32, device=device)
+        _scalars[key] = t
+    return t
+
+
+def _workspace_for(device, nbytes):
+    if nbytes == 0:
+        return None
+    t = _workspaces.get(device)
+    if t is None or t.numel() < nbytes:
+        t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[device] = t
+    return t
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def paged_attention_decode(out, query, key_cache, value_cache, num_kv_heads, scale, block_tables,
+                           seq_lens, block_size, max_seq_len, alibi_slopes=None,
+                           kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0, *, workspace=None,
+                           split_tokens=0) -> None:
+    """Write softmax(scale*q.K^T + alibi).V for every (sequence, query head) into ``out``.
+
+    out, query: [num_seqs, num_heads, head_size], float32 or bfloat16, contiguous, on one GPU.
+    key_cache, value_cache: the library's layout (``kv_cache_shapes``); same dtype as query for
+    kv_cache_dtype "auto", uint8 / float8_e4m3fn codes for "fp8" / "fp8_e4m3".
+    block_tables int32 [num_seqs, max_blocks]; seq_lens int32 [num_seqs].
+    alibi_slopes: float32 [num_heads] or None. k_scale / v_scale: float or one-element float32
+    tensor (used for the fp8 cache only). Runs asynchronously on the current stream.
+    """
+    if kv_cache_dtype not in _KV_NAMES:
+        raise TypeError(f"kv_cache_dtype {kv_cache_dtype!r} is not one of {sorted(_KV_NAMES)}")
+    kvd = _KV_NAMES[kv_cache_dtype]
+    if query.dtype not in _Q_DTYPES:
+        raise TypeError(f"query dtype {query.dtype} is not float32 or bfloat16")
+    qd = _Q_DTYPES[query.dtype]
+    dev = query.device
+    _need(dev.type == "cuda", "query must be on a GPU")
+    for name, t in (("out", out), ("key_cache", key_cache), ("value_cache", value_cache),
+                    ("block_tables", block_tables), ("seq_lens", seq_lens)):
+        _need(t.device == dev, f"{name} is not on the query's device")
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+    _need(query.is_contiguous(), "query must be contiguous")
+    _need(out.dtype == query.dtype and out.shape == query.shape, "out must match query in shape and dtype")
+    _need(query.dim() == 3, "query must be [num_seqs, num_heads, head_size]")
+    num_seqs, num_heads, head_size = query.shape
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == num_seqs, "block_tables must be int32 [num_seqs, max_blocks]")
+    _need(seq_lens.dtype == torch.int32 and seq_lens.shape == (num_seqs,), "seq_lens must be int32 [num_seqs]")
+    if kvd == PA_KV_AUTO:
+        if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
+            raise TypeError("with kv_cache_dtype 'auto' the caches must have the query's dtype")
+    elif key_cache.dtype not in (torch.uint8, torch.float8_e4m3fn) or value_cache.dtype != key_cache.dtype:
+        raise TypeError("the fp8 cache must be uint8 or float8_e4m3fn codes")
+    num_blocks = key_cache.shape[0]
+    k_shape, v_shape = kv_cache_shapes(num_blocks, num_kv_heads, head_size, query.dtype,
+                                       kv_cache_dtype, block_size)
+    _need(tuple(key_cache.shape) == k_shape, f"key_cache shape {tuple(key_cache.shape)} != {k_shape}")
+    _need(tuple(value_cache.shape) == v_shape, f"value_cache shape {tuple(value_cache.shape)} != {v_shape}")
+    slopes_ptr = None
+    if alibi_slopes is not None:
+        _need(alibi_slopes.dtype == torch.float32 and alibi_slopes.shape == (num_heads,)
+              and alibi_slopes.device == dev and alibi_slopes.is_contiguous(),
+              "alibi_slopes must be contiguous float32 [num_heads] on the query's device")
+        slopes_ptr = alibi_slopes.data_ptr()
+    ks = _device_scalar(k_scale, dev) if kvd == PA_KV_FP8_E4M3 else None
+    vs = _device_scalar(v_scale, dev) if kvd == PA_KV_FP8_E4M3 else None
+    if workspace is None:
+        _, _, need = pa_decode_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len,
+                                    split_tokens)
+        workspace = _workspace_for(dev, need)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = _lib.pa_paged_attention_decode_split(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), num_seqs,
+        num_heads, num_kv_heads, head_size, num_blocks, float(scale), block_tables.data_ptr(),
+        block_tables.shape[1], seq_lens.data_ptr(), block_size, int(max_seq_len), slopes_ptr, qd,
+        kvd, ks.data_ptr() if ks is not None else None, vs.data_ptr() if vs is not None else None,
+        ws_ptr, ws_bytes, stream, int(split_tokens))
+    _raise_for(rc, "paged_attention_decode")

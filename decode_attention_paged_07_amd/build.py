@@ -1,0 +1,56 @@
+"""Compile the HIP sources into the in-tree shared library libpa_decode.so.
+
+One hipcc invocation for gfx950; the result is written next to this file and
+replaced atomically so a running process never loads a half-written library.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+LIB_NAME = "libpa_decode.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+SOURCES = [os.path.join(PKG_DIR, "csrc", f) for f in ("pa_kernels.hip", "pa_api.cpp")]
+INCLUDE = os.path.join(ROOT, "include")
+
+# Packed-fp32 VALU instructions stay disabled in device code: plain float
+# arithmetic is emitted as scalar-per-lane VALU ops.
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wall", "-Wno-unused-function"]
+
+
+def hipcc() -> str:
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libpa_decode.so")
+    return exe
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    tmp = LIB_PATH + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", os.path.join(PKG_DIR, "csrc"),
+           "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 target feature; drop that notice.
+    noise = "is not a recognized feature for this target"
+    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+    if res.returncode != 0:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
+    if verbose and msgs.strip():
+        print(msgs, file=sys.stderr)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

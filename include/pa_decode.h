@@ -1,0 +1,195 @@
+/*
+ * pa_decode.h — C ABI of the paged decode-attention library (libpa_decode.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes. One decode step of PagedAttention: for every sequence s
+ * and query head h, the single query row q[s,h,:] attends over the sequence's
+ * first seq_lens[s] cached tokens,
+ *
+ *     out[s,h,:] = sum_t softmax_t( scale * q[s,h,:].K[t,:] + alibi ) * V[t,:]
+ *
+ * where token t of sequence s lives in physical block
+ * block_tables[s, t / block_size] at slot t % block_size (the block-table
+ * indirection of the 10100.com retirement article, §1, and of the vLLM 0.25.0
+ * notes on jokeuncle.github.io, §1). The attention formula itself was lost in
+ * the extraction of that article (§2); this is the standard decode-attention
+ * definition the rest of the pages support. The argument list follows the
+ * ROCm call kept in the PR #47361 report (prhub.com.cn, "关键源码片段",
+ * benchmark and _custom_ops.py snippets), with its three partial-result
+ * buffers folded into one caller-provided workspace.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named "device" are HIP device addresses; all others are host.
+ *    The caller owns every buffer; the library allocates nothing, keeps no
+ *    per-call state, writes only `out` and `workspace`, and never blocks the
+ *    host: kernels are queued on `stream` (a hipStream_t; NULL = the null
+ *    stream). No host synchronisation and no allocation happen inside a call,
+ *    so it can be captured into a HIP graph.
+ *  - Every argument is validated on the host before any HIP call; on failure
+ *    nothing is launched, a negative PA_ERR_* code is returned and
+ *    pa_last_error() describes the problem (thread-local text).
+ *  - Values that live in device memory (seq_lens, block-table entries) are the
+ *    caller's contract: seq_lens[s] in [0, max_seq_len], entries for the
+ *    blocks a sequence uses in [0, num_blocks). The kernels clamp both into
+ *    range, so a violation gives unspecified output values but never an
+ *    out-of-bounds access.
+ *  - Results are deterministic for given inputs and launch plan (no atomics).
+ */
+#ifndef PA_DECODE_H
+#define PA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define PA_OK             0
+#define PA_ERR_NULL      (-1)  /* a required pointer is NULL                     */
+#define PA_ERR_SHAPE     (-2)  /* sizes out of the supported set / inconsistent  */
+#define PA_ERR_DTYPE     (-3)  /* unsupported dtype combination                   */
+#define PA_ERR_WORKSPACE (-4)  /* workspace missing or smaller than required      */
+#define PA_ERR_ALIGN     (-5)  /* pointer not aligned as documented               */
+#define PA_ERR_HIP       (-6)  /* the HIP runtime reported an error on launch     */
+
+/* Element types of query/out (q_dtype). */
+#define PA_DTYPE_F32   0
+#define PA_DTYPE_BF16  1
+
+/* Cache element type (kv_cache_dtype). AUTO = same as q_dtype. FP8_E4M3 =
+ * OCP E4M3FN codes (uint8; max 448, no infinities), each decoded value
+ * multiplied by *k_scale (K) or *v_scale (V), the scaled conversion of the
+ * 10100.com retirement article, §4. FP8 requires q_dtype = BF16. */
+#define PA_KV_AUTO      0
+#define PA_KV_FP8_E4M3  1
+
+/* Fixed sizes: tokens per cache block, and the partition granularity of the
+ * split-KV path (the 256-token partitions of the PR #47361 report). */
+#define PA_BLOCK_SIZE      16
+#define PA_PARTITION_SIZE  256
+#define PA_MAX_GROUP       16   /* num_heads / num_kv_heads */
+
+/*
+ * Cache layouts (the pages' layouts, 10100.com retirement article, §2), with
+ * x = 16 bytes / element size (4 for f32, 8 for bf16, 16 for fp8):
+ *   key_cache   [num_blocks][num_kv_heads][head_size/x][block_size][x]
+ *   value_cache [num_blocks][num_kv_heads][head_size][block_size]
+ * so one (block, kv head) K tile and V tile are each one contiguous run of
+ * head_size*block_size elements. All strides below are in elements.
+ */
+typedef struct pa_layout_desc {
+  int x;                    /* innermost K width                                 */
+  int elem_bytes;           /* bytes per cache element                           */
+  int64_t k_block_stride;   /* elements between consecutive physical K blocks    */
+  int64_t k_head_stride;    /* elements between kv heads inside a K block        */
+  int64_t v_block_stride;
+  int64_t v_head_stride;
+} pa_layout_desc;
+
+/* Describe the cache layout for (num_kv_heads, head_size, block_size, dtypes).
+ * Host only; no HIP call. Returns PA_OK or PA_ERR_SHAPE / PA_ERR_DTYPE / PA_ERR_NULL. */
+int pa_kv_layout(int num_kv_heads, int head_size, int block_size, int q_dtype,
+                 int kv_cache_dtype, pa_layout_desc* desc);
+
+/*
+ * Launch plan. The split-KV path divides each sequence into splits of
+ * split_tokens tokens (a multiple of PA_PARTITION_SIZE); one workgroup handles
+ * one (sequence, kv head, split) and the query heads that share that kv head.
+ * Sequences longer than one split write per-split partial results into the
+ * workspace and a reduce kernel merges them (log-sum-exp merge).
+ *
+ * requested_split_tokens: 0 = library's choice; otherwise a positive multiple
+ * of PA_PARTITION_SIZE. Outputs (any may be NULL): chosen split_tokens,
+ * num_splits = ceil(max_seq_len / split_tokens) (>= 1), and the workspace
+ * bytes this plan needs (0 when num_splits == 1). Host only; no HIP call.
+ *
+ * Workspace layout for num_splits = P > 1, all fp32, each array starting at a
+ * 256-byte-aligned offset from the workspace base, in this order:
+ *   tmp_out    [num_seqs][num_heads][P][head_size]  normalised partial outputs
+ *                                                   (already multiplied by *v_scale)
+ *   max_logits [num_seqs][num_heads][P]             max of scale*q.k + alibi (natural units)
+ *   exp_sums   [num_seqs][num_heads][P]             sum of exp(logit - max_logit)
+ * Entries of splits that start at or after a sequence's length are not written.
+ */
+int pa_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                   int max_seq_len, int requested_split_tokens,
+                   int* split_tokens, int* num_splits, size_t* workspace_bytes);
+
+/* Workspace bytes sufficient for every plan of this problem (the 256-token
+ * plan needs the most). Host only. */
+int pa_workspace_bytes(int num_seqs, int num_heads, int head_size, int max_seq_len,
+                       size_t* bytes);
+
+/*
+ * The decode step. Arguments:
+ *   out          device, [num_seqs][num_heads][head_size], q_dtype, contiguous,
+ *                16-byte aligned, must not overlap `query`.
+ *   query        device, [num_seqs][num_heads][head_size], q_dtype, contiguous, 16-B aligned.
+ *   key_cache    device, layout above, 16-B aligned.  value_cache  likewise.
+ *   num_seqs     >= 0 (0 is a no-op).        num_heads, num_kv_heads: > 0,
+ *                num_heads % num_kv_heads == 0, group <= PA_MAX_GROUP; query
+ *                head h uses kv head h / (num_heads / num_kv_heads).
+ *   head_size    64 or 128 (the head sizes of the PR #47361 report's test).
+ *   num_blocks   physical blocks in each cache (> 0).
+ *   scale        finite; multiplies q.k (not the ALiBi term).
+ *   block_tables device int32 [num_seqs][max_blocks_per_seq], 4-B aligned.
+ *   seq_lens     device int32 [num_seqs].
+ *   block_size   must be PA_BLOCK_SIZE.
+ *   max_seq_len  >= every seq_lens[s], <= max_blocks_per_seq * block_size.
+ *   alibi_slopes device fp32 [num_heads] or NULL; adds
+ *                slope[h] * (t - (seq_len - 1)) to the logit of token t.
+ *   q_dtype, kv_cache_dtype: see above.
+ *   k_scale, v_scale: device fp32 scalars or NULL (= 1.0); used only when
+ *                kv_cache_dtype is PA_KV_FP8_E4M3.
+ *   workspace    device, >= the plan's workspace bytes (may be NULL when the
+ *                plan needs none), 16-B aligned.
+ *   stream       hipStream_t or NULL.
+ * A sequence with seq_lens[s] == 0 gets an all-zero output row.
+ */
+int pa_paged_attention_decode(void* out, const void* query, const void* key_cache,
+                              const void* value_cache, int num_seqs, int num_heads,
+                              int num_kv_heads, int head_size, int num_blocks, float scale,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* seq_lens, int block_size, int max_seq_len,
+                              const float* alibi_slopes, int q_dtype, int kv_cache_dtype,
+                              const float* k_scale, const float* v_scale, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Same as pa_paged_attention_decode with an explicit split size (see
+ * pa_decode_plan; 0 = library's choice). */
+int pa_paged_attention_decode_split(void* out, const void* query, const void* key_cache,
+                                    const void* value_cache, int num_seqs, int num_heads,
+                                    int num_kv_heads, int head_size, int num_blocks,
+                                    float scale, const int32_t* block_tables,
+                                    int max_blocks_per_seq, const int32_t* seq_lens,
+                                    int block_size, int max_seq_len,
+                                    const float* alibi_slopes, int q_dtype,
+                                    int kv_cache_dtype, const float* k_scale,
+                                    const float* v_scale, void* workspace,
+                                    size_t workspace_bytes, void* stream,
+                                    int split_tokens);
+
+/* Text describing the last error returned on the calling thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int pa_version(void);
+
+/*
+ * Kernel timing. While enabled, each decode call records HIP events on its
+ * stream around the partition kernel and around the reduce kernel (creating
+ * events on first use, outside any graph capture). pa_timing_read waits for
+ * the recorded events, returns the summed milliseconds and launch counts since
+ * the last read, and clears them. Meant for benchmarks; off by default.
+ */
+int pa_timing_enable(int on);
+int pa_timing_read(double* partition_ms, int* partition_launches, double* reduce_ms,
+                   int* reduce_launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_DECODE_H */

@@ -1,0 +1,168 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call.
+
+Fake device addresses (aligned integers) are safe here: every call below fails
+validation, or is the num_seqs == 0 no-op, so nothing is dereferenced or launched.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa_decode.h")
+
+
+@pytest.fixture(scope="module")
+def pa():
+    from decode_attention_paged_07_amd import build as b
+    if not os.path.exists(b.LIB_PATH):
+        b.build()
+    import decode_attention_paged_07_amd as mod
+    return mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("pa_paged_attention_decode", "pa_paged_attention_decode_split", "pa_decode_plan",
+                     "pa_workspace_bytes", "pa_kv_layout", "pa_last_error", "pa_version",
+                     "pa_timing_enable", "pa_timing_read"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(pa):
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(ctypes.CDLL(pa.LIB_PATH), name)
+
+
+def test_binding_names_match_c_entry_points(pa):
+    for name in declared_functions():
+        assert callable(getattr(pa, name)), name
+
+
+FAKE = dict(out=0x10000, query=0x20000, key_cache=0x30000, value_cache=0x40000, num_seqs=2,
+            num_heads=8, num_kv_heads=2, head_size=128, num_blocks=16, scale=0.1,
+            block_tables=0x50000, max_blocks_per_seq=4, seq_lens=0x60000, block_size=16,
+            max_seq_len=40, alibi_slopes=None, q_dtype=1, kv_cache_dtype=0, k_scale=None,
+            v_scale=None, workspace=None, workspace_bytes=0, stream=None)
+ORDER = list(FAKE)
+
+
+def call(pa, **over):
+    a = dict(FAKE)
+    a.update(over)
+    return pa.pa_paged_attention_decode(*[a[k] for k in ORDER])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(out=None), -1), (dict(query=None), -1), (dict(key_cache=None), -1),
+    (dict(value_cache=None), -1), (dict(block_tables=None), -1), (dict(seq_lens=None), -1),
+    (dict(head_size=96), -2), (dict(head_size=256), -2), (dict(block_size=32), -2),
+    (dict(num_heads=6, num_kv_heads=4), -2), (dict(num_heads=64, num_kv_heads=2), -2),
+    (dict(num_kv_heads=0), -2), (dict(num_seqs=-1), -2), (dict(num_blocks=0), -2),
+    (dict(max_blocks_per_seq=0), -2), (dict(max_seq_len=65), -2), (dict(max_seq_len=-1), -2),
+    (dict(scale=float("inf")), -2), (dict(scale=float("nan")), -2),
+    (dict(q_dtype=7), -3), (dict(kv_cache_dtype=5), -3), (dict(q_dtype=0, kv_cache_dtype=1), -3),
+    (dict(out=0x10008), -5), (dict(query=0x20004), -5), (dict(key_cache=0x30002), -5),
+    (dict(block_tables=0x50002), -5), (dict(alibi_slopes=0x70001), -5),
+    (dict(out=0x20000 + 64), -2),                                  # overlaps query
+    (dict(max_seq_len=300, max_blocks_per_seq=32), -4),            # needs a workspace
+    (dict(max_seq_len=300, max_blocks_per_seq=32, workspace=0x80000, workspace_bytes=16), -4),
+    (dict(max_seq_len=300, max_blocks_per_seq=32, workspace=0x80008, workspace_bytes=1 << 20), -5),
+])
+def test_validation_rejects(pa, over, code):
+    rc = call(pa, **over)
+    assert rc == code, (rc, pa.pa_last_error())
+    assert pa.pa_last_error() != ""
+
+
+def test_zero_sequences_is_a_noop(pa):
+    assert call(pa, num_seqs=0, out=None, query=None) == 0
+    assert pa.pa_last_error() == ""
+
+
+def test_split_size_must_be_partition_multiple(pa):
+    a = dict(FAKE)
+    rc = pa.pa_paged_attention_decode_split(*[a[k] for k in ORDER], 300)
+    assert rc == -2
+    with pytest.raises(ValueError):
+        pa.pa_decode_plan(2, 8, 2, 128, 4096, 100)
+
+
+def test_plan_partition_counts_follow_the_pages(pa):
+    from tests import _golden
+    for max_len, parts in _golden.partition_counts():
+        st, ns, wb = pa.pa_decode_plan(3, 8, 2, 128, max_len, 256)
+        assert (st, ns) == (256, parts)
+        rows = 3 * 8 * parts
+        if parts == 1:
+            assert wb == 0
+        else:
+            def up(v):
+                return (v + 255) // 256 * 256
+            assert wb == up(rows * 128 * 4) + 2 * up(rows * 4)
+        assert pa.pa_workspace_bytes(3, 8, 128, max_len) == wb
+
+
+def test_auto_plan_never_needs_more_than_workspace_bytes(pa):
+    for s, h, hkv, L in [(128, 64, 8, 8192), (8, 32, 8, 32768), (256, 64, 8, 16384), (64, 32, 32, 4096),
+                         (2, 4, 4, 40), (1, 16, 1, 1 << 20)]:
+        st, ns, wb = pa.pa_decode_plan(s, h, hkv, 128, L)
+        assert st % 256 == 0 and ns == max(1, -(-L // st))
+        assert wb <= pa.pa_workspace_bytes(s, h, 128, L)
+
+
+def test_kv_layout_matches_generator(pa):
+    import workloads
+    for name in ("tiny", "mha", "gqa", "long", "fp8"):
+        cfg = workloads.CONFIGS[name]
+        q = 0 if cfg.q_dtype == "f32" else 1
+        kv = 1 if cfg.kv_dtype == "fp8_e4m3" else 0
+        lay = pa.pa_kv_layout(cfg.num_kv_heads, cfg.head_size, 16, q, kv)
+        assert lay["x"] == workloads.default_x(cfg)
+        assert lay["k_head_stride"] == cfg.head_size * 16
+        assert lay["k_block_stride"] == cfg.head_size * 16 * cfg.num_kv_heads
+        k_shape, v_shape = pa.kv_cache_shapes(cfg.pool_blocks, cfg.num_kv_heads, cfg.head_size,
+                                              torch.float32 if q == 0 else torch.bfloat16, cfg.kv_dtype)
+        c = workloads.make_case(cfg.with_(pool_blocks=16, num_seqs=1, seq_lens=("fixed", (5,))))
+        assert k_shape[1:] == tuple(c.key_cache.shape[1:])
+        assert v_shape[1:] == tuple(c.value_cache.shape[1:])
+
+
+def test_tensor_call_refuses_cpu_tensors(pa):
+    """No CPU fallback: host tensors are rejected before anything runs."""
+    import workloads
+    c = workloads.make_case(workloads.TINY)
+    out = torch.empty_like(c.query)
+    with pytest.raises(ValueError, match="GPU"):
+        pa.paged_attention_decode(out, c.query, c.key_cache, c.value_cache, 4, c.scale,
+                                  c.block_tables, c.seq_lens, 16, c.max_seq_len)
+
+
+def test_tensor_call_rejects_bad_kv_dtype_name(pa):
+    import workloads
+    c = workloads.make_case(workloads.TINY)
+    with pytest.raises(TypeError):
+        pa.paged_attention_decode(torch.empty_like(c.query), c.query, c.key_cache, c.value_cache, 4,
+                                  c.scale, c.block_tables, c.seq_lens, 16, c.max_seq_len,
+                                  kv_cache_dtype="int8")
+
+
+def test_timing_read_without_launches(pa):
+    pa.pa_timing_enable(True)
+    assert pa.pa_timing_read() == (0.0, 0, 0.0, 0)
+    pa.pa_timing_enable(False)
