@@ -52,40 +52,59 @@ int check_dtypes(int q_dtype, int kv_cache_dtype) {
   return PA_OK;
 }
 
-// Split size chosen by the library: the largest split (a power-of-two
-// multiple of the 256-token partition, up to 8) that still leaves at least
-// kTargetItems (sequence, kv head, split) work items, so that every one of the
-// 256 compute units gets several workgroups.
-constexpr int64_t kTargetItems = 2048;
-
-int choose_split_tokens(int num_seqs, int num_kv_heads, int max_seq_len) {
-  const int64_t parts = std::max<int64_t>(1, (max_seq_len + PA_PARTITION_SIZE - 1) / PA_PARTITION_SIZE);
-  for (int k = 8; k > 1; k >>= 1) {
-    const int64_t splits = (parts + k - 1) / k;
-    if ((int64_t)num_seqs * num_kv_heads * splits >= kTargetItems) return k * PA_PARTITION_SIZE;
-  }
-  return PA_PARTITION_SIZE;
-}
-
+// Two schedulers (see pa_kernels.hip): an explicit split size selects the
+// split grid, whose multi-split sequences keep per-split partials in the
+// pages' partition format; split_tokens == 0 selects stream-K, where every
+// wave gets an equal share of all (block, kv head) tiles. Workspace carving:
+//   split:    tmp_out [S][H][P][D] | max_logits [S][H][P] | exp_sums [S][H][P]
+//   stream-K: seg_out [slots][G][D] | seg_max [slots][G] | seg_sum [slots][G] | seg_meta [S*Hkv][2]
+// with slots = S*Hkv + PA_SK_MAX_WAVES; each array 256-byte aligned.
 struct Plan {
+  bool streamk;
   int split_tokens;
   int num_splits;
-  size_t tmp_off, ml_off, es_off, bytes;
+  size_t off[4];
+  size_t bytes;
 };
 
 Plan make_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_seq_len,
                int split_tokens) {
   Plan p{};
-  p.split_tokens = split_tokens > 0 ? split_tokens : choose_split_tokens(num_seqs, num_kv_heads, max_seq_len);
-  p.num_splits = std::max(1, (max_seq_len + p.split_tokens - 1) / p.split_tokens);
-  if (p.num_splits > 1) {
-    const size_t rows = (size_t)num_seqs * num_heads * p.num_splits;
-    p.tmp_off = 0;
-    p.ml_off = round_up(rows * head_size * sizeof(float), 256);
-    p.es_off = p.ml_off + round_up(rows * sizeof(float), 256);
-    p.bytes = p.es_off + round_up(rows * sizeof(float), 256);
+  if (split_tokens > 0) {
+    p.split_tokens = split_tokens;
+    p.num_splits = std::max(1, (max_seq_len + split_tokens - 1) / split_tokens);
+    if (p.num_splits > 1) {
+      const size_t rows = (size_t)num_seqs * num_heads * p.num_splits;
+      p.off[0] = 0;
+      p.off[1] = round_up(rows * head_size * sizeof(float), 256);
+      p.off[2] = p.off[1] + round_up(rows * sizeof(float), 256);
+      p.bytes = p.off[2] + round_up(rows * sizeof(float), 256);
+    }
+    return p;
   }
+  p.streamk = true;
+  const size_t group = (size_t)(num_heads / num_kv_heads);
+  const size_t pairs = (size_t)num_seqs * num_kv_heads;
+  const size_t slots = pairs + PA_SK_MAX_WAVES;
+  p.off[0] = 0;
+  p.off[1] = round_up(slots * group * head_size * sizeof(float), 256);
+  p.off[2] = p.off[1] + round_up(slots * group * sizeof(float), 256);
+  p.off[3] = p.off[2] + round_up(slots * group * sizeof(float), 256);
+  p.bytes = p.off[3] + round_up(pairs * 2 * sizeof(int32_t), 256);
   return p;
+}
+
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 int check_plan_args(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_seq_len,
@@ -196,9 +215,17 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
   a.k_scale = fp8 ? k_scale : nullptr;
   a.v_scale = fp8 ? v_scale : nullptr;
   char* ws = static_cast<char*>(workspace);
-  a.tmp_out = plan.bytes ? reinterpret_cast<float*>(ws + plan.tmp_off) : nullptr;
-  a.max_logits = plan.bytes ? reinterpret_cast<float*>(ws + plan.ml_off) : nullptr;
-  a.exp_sums = plan.bytes ? reinterpret_cast<float*>(ws + plan.es_off) : nullptr;
+  if (plan.bytes && !plan.streamk) {
+    a.tmp_out = reinterpret_cast<float*>(ws + plan.off[0]);
+    a.max_logits = reinterpret_cast<float*>(ws + plan.off[1]);
+    a.exp_sums = reinterpret_cast<float*>(ws + plan.off[2]);
+  }
+  if (plan.streamk) {
+    a.seg_out = reinterpret_cast<float*>(ws + plan.off[0]);
+    a.seg_max = reinterpret_cast<float*>(ws + plan.off[1]);
+    a.seg_sum = reinterpret_cast<float*>(ws + plan.off[2]);
+    a.seg_meta = reinterpret_cast<int32_t*>(ws + plan.off[3]);
+  }
   a.k_block_stride_bytes = tile * num_kv_heads;
   a.k_head_stride_bytes = tile;
   a.v_block_stride_bytes = tile * num_kv_heads;
@@ -215,7 +242,15 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
   a.split_tokens = plan.split_tokens;
   a.num_splits = plan.num_splits;
   const int kind = fp8 ? pa::KIND_FP8 : (q_dtype == PA_DTYPE_F32 ? pa::KIND_F32 : pa::KIND_BF16);
-
+  if (plan.streamk) {
+    // Persistent waves per compute unit, measured per cache type: the bf16
+    // path streams best with one wave per SIMD, the fp8 path needs more waves
+    // to overlap its in-register dequantisation with loads.
+    const int per_cu = kind == pa::KIND_FP8 ? PA_SK_WAVES_PER_CU_FP8
+                       : kind == pa::KIND_F32 ? PA_SK_WAVES_PER_CU_F32 : PA_SK_WAVES_PER_CU_BF16;
+    const int waves = std::min(PA_SK_MAX_WAVES, device_cus() * per_cu);
+    a.streamk_workgroups = std::max(1, waves / PA_WAVES);
+  }
   pa::LaunchHooks hooks;
   std::unique_lock<std::mutex> lock(g_timing.mu, std::defer_lock);
   bool timed = false;
@@ -264,18 +299,23 @@ int pa_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size,
   int rc = check_plan_args(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, requested_split_tokens);
   if (rc) return rc;
   const Plan p = make_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, requested_split_tokens);
-  if (split_tokens) *split_tokens = p.split_tokens;
-  if (num_splits) *num_splits = p.num_splits;
+  if (split_tokens) *split_tokens = p.split_tokens;   // 0 for the stream-K plan
+  if (num_splits) *num_splits = p.num_splits;         // 0 for the stream-K plan
   if (workspace_bytes) *workspace_bytes = p.bytes;
   return ok();
 }
 
 int pa_workspace_bytes(int num_seqs, int num_heads, int head_size, int max_seq_len, size_t* bytes) {
   if (!bytes) return fail(PA_ERR_NULL, "bytes is NULL");
-  // The 256-token plan needs the most workspace; its size does not depend on num_kv_heads.
+  // The larger of the 256-token split plan and the stream-K plan over every
+  // valid num_kv_heads (stream-K grows with the group size G = H / Hkv).
   int rc = check_plan_args(num_seqs, num_heads, num_heads, head_size, max_seq_len, PA_PARTITION_SIZE);
   if (rc) return rc;
-  *bytes = make_plan(num_seqs, num_heads, num_heads, head_size, max_seq_len, PA_PARTITION_SIZE).bytes;
+  size_t best = make_plan(num_seqs, num_heads, num_heads, head_size, max_seq_len, PA_PARTITION_SIZE).bytes;
+  for (int g = 1; g <= PA_MAX_GROUP && g <= num_heads; ++g)
+    if (num_heads % g == 0)
+      best = std::max(best, make_plan(num_seqs, num_heads, num_heads / g, head_size, max_seq_len, 0).bytes);
+  *bytes = best;
   return ok();
 }
 

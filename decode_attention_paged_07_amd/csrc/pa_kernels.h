@@ -4,7 +4,34 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#define PA_MAX_GROUP_DEV 16
+// Tuning knobs (compile-time): waves per workgroup, blocks per wave
+// iteration for each cache type, stream-K waves per compute unit.
+#ifndef PA_WAVES
+#define PA_WAVES 4
+#endif
+#ifndef PA_NB_BF16
+#define PA_NB_BF16 1
+#endif
+#ifndef PA_NB_FP8
+#define PA_NB_FP8 1
+#endif
+#ifndef PA_NB_F32
+#define PA_NB_F32 1
+#endif
+#ifndef PA_SK_WAVES_PER_CU_BF16
+#define PA_SK_WAVES_PER_CU_BF16 4
+#endif
+#ifndef PA_SK_WAVES_PER_CU_FP8
+#define PA_SK_WAVES_PER_CU_FP8 8
+#endif
+#ifndef PA_SK_WAVES_PER_CU_F32
+#define PA_SK_WAVES_PER_CU_F32 4
+#endif
+#ifndef PA_PIPE
+#define PA_PIPE 1
+#endif
+// Upper bound on stream-K waves; sizes the segment workspace.
+#define PA_SK_MAX_WAVES 4096
 
 namespace pa {
 
@@ -21,9 +48,15 @@ struct DecodeArgs {
   const float* alibi_slopes;   // nullable
   const float* k_scale;        // nullable (1.0)
   const float* v_scale;        // nullable (1.0)
-  float* tmp_out;              // [S][H][num_splits][D]   (num_splits > 1 only)
+  // split grid (streamk_workgroups == 0), num_splits > 1 only:
+  float* tmp_out;              // [S][H][num_splits][D]
   float* max_logits;           // [S][H][num_splits]
   float* exp_sums;             // [S][H][num_splits]
+  // stream-K (streamk_workgroups > 0); slots = S*Hkv + PA_SK_MAX_WAVES:
+  float* seg_out;              // [slots][G][D]  normalised segment output (times v_scale)
+  float* seg_max;              // [slots][G]     segment running max (log2 units)
+  float* seg_sum;              // [slots][G]     segment exp2-sum relative to seg_max
+  int32_t* seg_meta;           // [S*Hkv][2]     first and last wave of each (kv head, sequence) pair
   int64_t k_block_stride_bytes;
   int64_t k_head_stride_bytes;
   int64_t v_block_stride_bytes;
@@ -39,6 +72,7 @@ struct DecodeArgs {
   int max_seq_len;
   int split_tokens;
   int num_splits;
+  int streamk_workgroups;      // > 0 selects the stream-K scheduler
 };
 
 // Optional callbacks around each launch (used for event timing).

@@ -80,9 +80,9 @@ def call(pa, **over):
     (dict(out=0x10008), -5), (dict(query=0x20004), -5), (dict(key_cache=0x30002), -5),
     (dict(block_tables=0x50002), -5), (dict(alibi_slopes=0x70001), -5),
     (dict(out=0x20000 + 64), -2),                                  # overlaps query
-    (dict(max_seq_len=300, max_blocks_per_seq=32), -4),            # needs a workspace
-    (dict(max_seq_len=300, max_blocks_per_seq=32, workspace=0x80000, workspace_bytes=16), -4),
-    (dict(max_seq_len=300, max_blocks_per_seq=32, workspace=0x80008, workspace_bytes=1 << 20), -5),
+    (dict(), -4),                                                  # stream-K needs a workspace
+    (dict(workspace=0x80000, workspace_bytes=16), -4),
+    (dict(workspace=0x80008, workspace_bytes=64 << 20), -5),
 ])
 def test_validation_rejects(pa, over, code):
     rc = call(pa, **over)
@@ -115,15 +115,23 @@ def test_plan_partition_counts_follow_the_pages(pa):
             def up(v):
                 return (v + 255) // 256 * 256
             assert wb == up(rows * 128 * 4) + 2 * up(rows * 4)
-        assert pa.pa_workspace_bytes(3, 8, 128, max_len) == wb
+        assert pa.pa_workspace_bytes(3, 8, 128, max_len) >= wb
 
 
-def test_auto_plan_never_needs_more_than_workspace_bytes(pa):
+def test_auto_plan_is_streamk_and_fits_workspace_bytes(pa):
     for s, h, hkv, L in [(128, 64, 8, 8192), (8, 32, 8, 32768), (256, 64, 8, 16384), (64, 32, 32, 4096),
-                         (2, 4, 4, 40), (1, 16, 1, 1 << 20)]:
+                         (2, 4, 4, 40), (1, 16, 1, 1 << 20), (3, 48, 3, 100)]:
         st, ns, wb = pa.pa_decode_plan(s, h, hkv, 128, L)
-        assert st % 256 == 0 and ns == max(1, -(-L // st))
+        assert (st, ns) == (0, 0)                      # stream-K scheduler
+        g = h // hkv
+        slots = s * hkv + 4096
+
+        def up(v):
+            return (v + 255) // 256 * 256
+        assert wb == up(slots * g * 128 * 4) + 2 * up(slots * g * 4) + up(s * hkv * 8)
         assert wb <= pa.pa_workspace_bytes(s, h, 128, L)
+        for split in (256, 1024):
+            assert pa.pa_decode_plan(s, h, hkv, 128, L, split)[2] <= pa.pa_workspace_bytes(s, h, 128, L)
 
 
 def test_kv_layout_matches_generator(pa):
