@@ -19,7 +19,8 @@ HEADER = os.path.join(ROOT, "include", "pa_decode.h")
 
 @pytest.fixture(scope="module")
 def pa():
-    from decode_attention_paged_07_amd import build as b
+    import __graft_entry__
+    b = __graft_entry__._build_module()
     if not os.path.exists(b.LIB_PATH):
         b.build()
     import decode_attention_paged_07_amd as mod
