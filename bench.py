@@ -50,10 +50,10 @@ def kv_bytes(case) -> int:
     return tokens * cfg.num_kv_heads * cfg.head_size * 2 * e
 
 
-def traffic_from_profiles(config: str):
-    """HBM bytes per partition launch from committed rocprofv3 counter runs,
-    only while the kernel source is unchanged since they were taken."""
-    path = os.path.join(ROOT, "profiles", f"pa_partition_{config}_traffic.json")
+def traffic_from_profiles(kernel: str, config: str):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter
+    summary, only while the kernel source is unchanged since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -61,6 +61,129 @@ def traffic_from_profiles(config: str):
     if t.get("kernel_sha") != kernel_sha():
         return None
     return t.get("bytes_per_launch")
+
+
+def _last_json(log_path):
+    with open(log_path) as f:
+        for line in reversed(f.read().splitlines()):
+            if line.startswith("{"):
+                return json.loads(line)
+    raise ValueError(f"no JSON line in {log_path}")
+
+
+def _counter_per_dispatch(run_dir, kernel):
+    import csv
+    import statistics
+    with open(os.path.join(run_dir, "run_counter_collection.csv")) as f:
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(f) if kernel in r["Kernel_Name"]]
+    if not vals:
+        raise ValueError(f"{kernel} not found in {run_dir}")
+    return statistics.median(vals), len(vals)
+
+
+def summarise_profiles(config, stats_dir, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
+    """Write the committed summaries of one workload's rocprofv3 runs.
+
+    stats_dir: --kernel-trace --stats --output-format csv run of this bench;
+    fetch_dir / write_dir: --pmc FETCH_SIZE / --pmc WRITE_SIZE runs of it;
+    cal_*_dir: the same counters over --copy-calibration, where the probe
+    reads and torch's fill writes exactly 1 GiB per launch. Each counter is
+    scaled by (1 GiB / its calibration reading), both in KiB per dispatch.
+    The run logs (<dir>.log, holding the bench's JSON line) must sit beside
+    the directories.
+    """
+    import csv
+    with open(os.path.join(stats_dir, "run_kernel_stats.csv")) as f:
+        stats = [r for r in csv.DictReader(f) if "pa::" in r["Name"] or "pa2" in r["Name"]]
+    stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    top = stats[0]
+    kernel = "pa_" + top["Name"].split("pa_", 1)[1].split("<", 1)[0].split("I", 1)[0]
+    with open(os.path.join(stats_dir, "run_kernel_trace.csv")) as f:
+        tr = next(r for r in csv.DictReader(f) if kernel in r["Kernel_Name"])
+    rec = _last_json(stats_dir.rstrip("/") + ".log")
+    fetch, n_f = _counter_per_dispatch(fetch_dir, kernel)
+    write, n_w = _counter_per_dispatch(write_dir, kernel)
+    cal_f, _ = _counter_per_dispatch(cal_fetch_dir, "pa_read_probe_kernel")
+    cal_w, _ = _counter_per_dispatch(cal_write_dir, "FillFunctor<unsigned char>")
+    f_fac, w_fac = (1 << 20) / cal_f, (1 << 20) / cal_w
+    nbytes = int(round((fetch * f_fac + write * w_fac) * 1024))
+    algo = rec["roofline"]["algorithmic_bytes_per_launch"]
+    sha = _last_json(fetch_dir.rstrip("/") + ".log")["kernel_sha"]
+    if _last_json(write_dir.rstrip("/") + ".log")["kernel_sha"] != sha or rec["kernel_sha"] != sha:
+        raise ValueError("the runs were taken from different kernel sources")
+    rel = lambda d: os.path.relpath(os.path.abspath(d), ROOT)  # noqa: E731
+    cmds = {
+        "stats": f"rocprofv3 --kernel-trace --stats --output-format csv -d {rel(stats_dir)} -o run -- "
+                 f"python3 bench.py --config {config} --steps 20 --warmup 5 --no-cpu-baseline --no-ceiling",
+        "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {rel(fetch_dir)} -o run -- "
+                 f"python3 bench.py --config {config} --steps 3 --warmup 1 --no-cpu-baseline --no-ceiling",
+        "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {rel(write_dir)} -o run -- "
+                 f"python3 bench.py --config {config} --steps 3 --warmup 1 --no-cpu-baseline --no-ceiling",
+        "calibration": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run -- "
+                       "python3 bench.py --copy-calibration --steps 3",
+    }
+    traffic = {
+        "kernel": kernel, "workload": WORKLOAD_TEXT[config], "kernel_sha": sha,
+        "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write, "dispatches": [n_f, n_w],
+        "calibration": {"probe_read_kib": 1 << 20, "fetch_reading_kib": cal_f, "fetch_factor": round(f_fac, 4),
+                        "fill_write_kib": 1 << 20, "write_reading_kib": cal_w, "write_factor": round(w_fac, 4)},
+        "bytes_per_launch": nbytes, "algorithmic_bytes_per_launch": algo,
+        "traffic_over_algorithmic": round(nbytes / algo, 4), "commands": cmds,
+    }
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+        f.write("\n")
+    lines = [f"# rocprofv3 summary: {kernel}, {WORKLOAD_TEXT[config]}", "",
+             f"kernel source sha256[:16]: {sha}", "", "Commands (run from /tmp with the repository at /root/repo):"]
+    lines += [f"  {k}: {v}" for k, v in cmds.items()]
+    lines += ["", "Kernel stats (rocprofv3 --stats, ns):",
+              "  name | calls | average | min | max"]
+    for r in stats:
+        lines.append(f"  {r['Name'][:80]} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']}")
+    lines += ["", f"Dominant kernel resources: grid {tr['Grid_Size_X']} threads, workgroup {tr['Workgroup_Size_X']}, "
+              f"VGPR {tr['VGPR_Count']}, AGPR {tr['Accum_VGPR_Count']}, SGPR {tr['SGPR_Count']}, "
+              f"LDS {tr['LDS_Block_Size']} B, scratch {tr['Scratch_Size']} B", "",
+              f"Counters per dispatch of {kernel} (median over {n_f} / {n_w} dispatches):",
+              f"  FETCH_SIZE {fetch:.0f} KiB x {f_fac:.4f} (1 GiB probe read read as {cal_f:.0f} KiB)",
+              f"  WRITE_SIZE {write:.0f} KiB x {w_fac:.4f} (1 GiB fill read as {cal_w:.0f} KiB)",
+              f"  HBM traffic {nbytes} B per launch; algorithmic K+V bytes {algo} B; ratio {nbytes / algo:.4f}", "",
+              "Bench line of the --stats run:",
+              f"  avg launch {rec['roofline']['avg_launch_ms']} ms, achieved {rec['roofline']['achieved']} GB/s "
+              f"({rec['roofline']['frac']:.1%} of 8 TB/s), ms/step {rec['ms_per_step']}"]
+    with open(os.path.join(ROOT, "profiles", f"{kernel}_{config}_rocprof.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_ceiling(dev, nbytes=4 << 30, reps=10):
+    """Best read bandwidth of the library's streaming probe over a few launch
+    sizes (GB/s), with the probe launches timed by HIP events on one stream."""
+    import torch
+
+    import decode_attention_paged_07_amd as pa
+
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    best = (0.0, 0)
+    for wg in (1024, 2048, 4096, 8192, 16384):
+        for _ in range(2):
+            rc = pa.pa_hbm_read_probe(buf.data_ptr(), nbytes, wg, sink.data_ptr(), stream.cuda_stream)
+            if rc:
+                raise RuntimeError(f"pa_hbm_read_probe: {pa.pa_last_error()}")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            pa.pa_hbm_read_probe(buf.data_ptr(), nbytes, wg, sink.data_ptr(), stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbps = nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+        best = max(best, (gbps, wg))
+    del buf
+    torch.cuda.empty_cache()
+    return {"gbps": round(best[0], 1), "workgroups": best[1], "bytes": nbytes,
+            "kernel": "pa_read_probe_kernel (16-B non-temporal loads, 256 threads/workgroup)"}
 
 
 def cpu_baseline(case, budget_s: float):
@@ -115,9 +238,16 @@ def main():
     ap.add_argument("--split", type=int, default=0, help="split tokens (0 = library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
+    ap.add_argument("--summarise", nargs=5, metavar=("STATS", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="write profiles/ summaries from rocprofv3 csv run directories (no GPU)")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device copy (for counter calibration)")
+                    help="only run 1 GiB probe reads and 1 GiB fills (counter calibration)")
     args = ap.parse_args()
+
+    if args.summarise:
+        summarise_profiles(args.config, *args.summarise)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -128,12 +258,19 @@ def main():
 
     dev = torch.device("cuda:0")
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
+        # Counter calibration: the probe reads exactly 1 GiB per launch and
+        # torch's fill writes exactly 1 GiB per launch.
+        import decode_attention_paged_07_amd as pa
+        buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
         for _ in range(args.steps):
-            dst.copy_(src)
+            if pa.pa_hbm_read_probe(buf.data_ptr(), 1 << 30, 4096, sink.data_ptr(), stream):
+                raise RuntimeError(pa.pa_last_error())
+            buf.fill_(1)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": args.steps}))
+        print(json.dumps({"calibration_bytes_read_by_probe": 1 << 30,
+                          "calibration_bytes_written_by_fill": 1 << 30, "launches": args.steps}))
         return
 
     import decode_attention_paged_07_amd as pa
@@ -179,6 +316,7 @@ def main():
     ms_with_events = e0.elapsed_time(e1) / args.steps
 
     nbytes = kv_bytes(case)
+    kernel_name = "pa_streamk_kernel" if split_tokens == 0 else "pa_split_kernel"
     seqs_per_s = cfg.num_seqs / (ms_per_step / 1e3)
     gbps = nbytes / (ms_per_step / 1e3) / 1e9
     part_avg = part_ms / max(part_n, 1)
@@ -212,12 +350,12 @@ def main():
         "frac_of_peak_hbm": round(gbps / PEAK_HBM_GBPS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_streamk_kernel" if split_tokens == 0 else "pa_split_kernel",
+            "kernel": kernel_name,
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": traffic_from_profiles(args.config),
+            "traffic": traffic_from_profiles(kernel_name, args.config),
             "avg_launch_ms": round(part_avg, 5),
             "algorithmic_bytes_per_launch": nbytes,
         },
@@ -226,6 +364,10 @@ def main():
         "kernel_sha": kernel_sha(),
         "cpu_baseline": None,
     }
+    if not args.no_ceiling:
+        ceil = read_ceiling(dev)
+        ceil["decode_frac_of_ceiling"] = round(achieved / ceil["gbps"], 4)
+        rec["read_ceiling"] = ceil
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         step()

@@ -30,7 +30,8 @@ __all__ = [
     "PA_BLOCK_SIZE", "PA_PARTITION_SIZE", "PA_MAX_GROUP",
     "pa_paged_attention_decode", "pa_paged_attention_decode_split", "pa_decode_plan",
     "pa_workspace_bytes", "pa_kv_layout", "pa_last_error", "pa_version", "pa_timing_enable",
-    "pa_timing_read", "paged_attention_decode", "kv_cache_shapes", "LIB_PATH", "PagedAttentionError",
+    "pa_timing_read", "pa_hbm_read_probe", "paged_attention_decode", "kv_cache_shapes", "LIB_PATH",
+    "PagedAttentionError",
 ]
 
 PA_OK = 0
@@ -87,6 +88,8 @@ _lib.pa_timing_enable.restype = _c_int
 _lib.pa_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_int),
                                 ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_int)]
 _lib.pa_timing_read.restype = _c_int
+_lib.pa_hbm_read_probe.argtypes = [_vp, _c_size, _c_int, _vp, _vp]
+_lib.pa_hbm_read_probe.restype = _c_int
 
 
 class PagedAttentionError(RuntimeError):
@@ -177,6 +180,10 @@ def pa_timing_read():
     rc = _lib.pa_timing_read(ctypes.byref(pm), ctypes.byref(pn), ctypes.byref(rm), ctypes.byref(rn))
     _raise_for(rc, "pa_timing_read")
     return pm.value, pn.value, rm.value, rn.value
+
+
+def pa_hbm_read_probe(buf, nbytes, workgroups, sink, stream) -> int:
+    return _lib.pa_hbm_read_probe(buf, nbytes, workgroups, sink, stream)
 
 
 # ---------------------------------------------------------------------------

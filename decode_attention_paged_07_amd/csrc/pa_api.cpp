@@ -345,6 +345,17 @@ int pa_paged_attention_decode_split(void* out, const void* query, const void* ke
                      stream, split_tokens);
 }
 
+int pa_hbm_read_probe(const void* buf, size_t bytes, int workgroups, unsigned* sink, void* stream) {
+  if (!buf || !sink) return fail(PA_ERR_NULL, "buf and sink must be non-NULL");
+  if (bytes == 0 || bytes % 16) return fail(PA_ERR_SHAPE, "bytes %zu is not a positive multiple of 16", bytes);
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(PA_ERR_SHAPE, "workgroups %d is outside [1, 1<<20]", workgroups);
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(PA_ERR_ALIGN, "buf must be 16-B and sink 4-B aligned");
+  hipError_t err = pa::launch_read_probe(buf, bytes, workgroups, sink, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "probe launch failed: %s", hipGetErrorString(err));
+  return ok();
+}
+
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
 int pa_version(void) { return 100; }

@@ -85,4 +85,8 @@ struct LaunchHooks {
 
 hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream, const LaunchHooks& hooks);
 
+// Streaming read of `bytes` (a multiple of 16) from `buf` by `workgroups`
+// workgroups of 256 threads (pa_probe.hip).
+hipError_t launch_read_probe(const void* buf, uint64_t bytes, int workgroups, unsigned* sink, hipStream_t stream);
+
 }  // namespace pa

@@ -171,6 +171,19 @@ int pa_paged_attention_decode_split(void* out, const void* query, const void* ke
                                     size_t workspace_bytes, void* stream,
                                     int split_tokens);
 
+/*
+ * HBM read-bandwidth probe (measurement aid, not part of the decode path):
+ * reads every byte of `buf` once with the decode kernels' load form
+ * (16-byte non-temporal loads, 1 KiB contiguous per wave instruction) using
+ * `workgroups` workgroups of 256 threads, on `stream`. Timing the call gives
+ * the read bandwidth a pure streaming kernel reaches on the device, the
+ * practical ceiling for the decode kernels. buf: device, 16-B aligned,
+ * bytes a positive multiple of 16. sink: device, 4 bytes, written only in the
+ * (practically impossible) case that the XOR of all words read equals
+ * 0x9E3779B9. workgroups in [1, 1<<20]. Errors as for the decode call.
+ */
+int pa_hbm_read_probe(const void* buf, size_t bytes, int workgroups, unsigned* sink, void* stream);
+
 /* Text describing the last error returned on the calling thread ("" if none). */
 const char* pa_last_error(void);
 

@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("pa_paged_attention_decode", "pa_paged_attention_decode_split", "pa_decode_plan",
                      "pa_workspace_bytes", "pa_kv_layout", "pa_last_error", "pa_version",
-                     "pa_timing_enable", "pa_timing_read"):
+                     "pa_timing_enable", "pa_timing_read", "pa_hbm_read_probe"):
         assert required in names
 
 
@@ -169,6 +169,17 @@ def test_tensor_call_rejects_bad_kv_dtype_name(pa):
         pa.paged_attention_decode(torch.empty_like(c.query), c.query, c.key_cache, c.value_cache, 4,
                                   c.scale, c.block_tables, c.seq_lens, 16, c.max_seq_len,
                                   kv_cache_dtype="int8")
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 1 << 20, 1024, 0x1000, None), -1), ((0x10000, 1 << 20, 1024, None, None), -1),
+    ((0x10000, 0, 1024, 0x1000, None), -2), ((0x10000, 100, 1024, 0x1000, None), -2),
+    ((0x10000, 1 << 20, 0, 0x1000, None), -2), ((0x10000, 1 << 20, (1 << 20) + 1, 0x1000, None), -2),
+    ((0x10008, 1 << 20, 1024, 0x1000, None), -5), ((0x10000, 1 << 20, 1024, 0x1002, None), -5),
+])
+def test_read_probe_validation(pa, args, code):
+    assert pa.pa_hbm_read_probe(*args) == code
+    assert pa.pa_last_error() != ""
 
 
 def test_timing_read_without_launches(pa):
