@@ -186,6 +186,54 @@ def read_ceiling(dev, nbytes=4 << 30, reps=10):
             "kernel": "pa_read_probe_kernel (16-B non-temporal loads, 256 threads/workgroup)"}
 
 
+def gather_ceilings(dev, pool_bytes=8 << 30, read_bytes=2 << 30, reps=10):
+    """Markdown table of the library's gather probe: whole tiles of 2, 4 and
+    8 KiB read from an 8 GiB pool in pool order or in a seeded random order
+    (as a block table scatters them), over waves per CU and tiles in flight."""
+    import numpy as np
+    import torch
+
+    import decode_attention_paged_07_amd as pa
+
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    rng = np.random.default_rng(11)
+    lines = ["| tile bytes | order | waves/CU | tiles in flight per wave | GB/s |", "|---|---|---|---|---|"]
+    best = {}
+    for tile in (2048, 4096, 8192):
+        n = read_bytes // tile
+        for order in ("pool", "random"):
+            ids = np.arange(n) if order == "pool" else rng.permutation(pool_bytes // tile)[:n]
+            ids_t = torch.from_numpy(ids.astype(np.int32)).to(dev)
+            for wpc in (4, 8, 16, 32):
+                for depth in (1, 2):
+                    wg = cus * wpc // 4
+
+                    def call():
+                        rc = pa.pa_hbm_gather_probe(pool.data_ptr(), pool_bytes, tile, ids_t.data_ptr(), n,
+                                                    depth, wg, sink.data_ptr(), stream.cuda_stream)
+                        if rc:
+                            raise RuntimeError(f"pa_hbm_gather_probe: {pa.pa_last_error()}")
+                    call()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for _ in range(reps):
+                        call()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    gbps = read_bytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+                    lines.append(f"| {tile} | {order} | {wpc} | {depth} | {gbps:.0f} |")
+                    best[(tile, order)] = max(best.get((tile, order), 0.0), gbps)
+            print(f"[ceilings] tile {tile} {order}: best {best[(tile, order)]:.0f} GB/s", file=sys.stderr, flush=True)
+    summary = ["| tile bytes | order | best GB/s |", "|---|---|---|"]
+    summary += [f"| {t} | {o} | {v:.0f} |" for (t, o), v in sorted(best.items())]
+    del pool
+    torch.cuda.empty_cache()
+    return "\n".join(summary + ["", "All runs:", ""] + lines)
+
+
 def cpu_baseline(case, budget_s: float):
     """Time the fp64 oracle on the host over the first sequences of the batch
     until about budget_s seconds of work, and check the GPU output on them."""
@@ -241,6 +289,8 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--summarise", nargs=5, metavar=("STATS", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="write profiles/ summaries from rocprofv3 csv run directories (no GPU)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only print the gather-probe read ceilings (markdown table)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 1 GiB probe reads and 1 GiB fills (counter calibration)")
     args = ap.parse_args()
@@ -257,6 +307,9 @@ def main():
     import torch
 
     dev = torch.device("cuda:0")
+    if args.ceilings:
+        print(gather_ceilings(dev), flush=True)
+        return
     if args.copy_calibration:
         # Counter calibration: the probe reads exactly 1 GiB per launch and
         # torch's fill writes exactly 1 GiB per launch.

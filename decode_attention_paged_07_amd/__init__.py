@@ -30,7 +30,7 @@ __all__ = [
     "PA_BLOCK_SIZE", "PA_PARTITION_SIZE", "PA_MAX_GROUP",
     "pa_paged_attention_decode", "pa_paged_attention_decode_split", "pa_decode_plan",
     "pa_workspace_bytes", "pa_kv_layout", "pa_last_error", "pa_version", "pa_timing_enable",
-    "pa_timing_read", "pa_hbm_read_probe", "paged_attention_decode", "kv_cache_shapes", "LIB_PATH",
+    "pa_timing_read", "pa_hbm_read_probe", "pa_hbm_gather_probe", "paged_attention_decode", "kv_cache_shapes", "LIB_PATH",
     "PagedAttentionError",
 ]
 
@@ -90,6 +90,8 @@ _lib.pa_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(
 _lib.pa_timing_read.restype = _c_int
 _lib.pa_hbm_read_probe.argtypes = [_vp, _c_size, _c_int, _vp, _vp]
 _lib.pa_hbm_read_probe.restype = _c_int
+_lib.pa_hbm_gather_probe.argtypes = [_vp, _c_size, _c_int, _vp, _c_int, _c_int, _c_int, _vp, _vp]
+_lib.pa_hbm_gather_probe.restype = _c_int
 
 
 class PagedAttentionError(RuntimeError):
@@ -184,6 +186,12 @@ def pa_timing_read():
 
 def pa_hbm_read_probe(buf, nbytes, workgroups, sink, stream) -> int:
     return _lib.pa_hbm_read_probe(buf, nbytes, workgroups, sink, stream)
+
+
+def pa_hbm_gather_probe(pool, pool_bytes, tile_bytes, ids, num_tiles, depth, workgroups, sink,
+                        stream) -> int:
+    return _lib.pa_hbm_gather_probe(pool, pool_bytes, tile_bytes, ids, num_tiles, depth, workgroups,
+                                    sink, stream)
 
 
 # ---------------------------------------------------------------------------

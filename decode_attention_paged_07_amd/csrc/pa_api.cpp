@@ -356,6 +356,25 @@ int pa_hbm_read_probe(const void* buf, size_t bytes, int workgroups, unsigned* s
   return ok();
 }
 
+int pa_hbm_gather_probe(const void* pool, size_t pool_bytes, int tile_bytes, const int32_t* ids, int num_tiles,
+                        int depth, int workgroups, unsigned* sink, void* stream) {
+  if (!pool || !ids || !sink) return fail(PA_ERR_NULL, "pool, ids and sink must be non-NULL");
+  if (tile_bytes != 1024 && tile_bytes != 2048 && tile_bytes != 4096 && tile_bytes != 8192)
+    return fail(PA_ERR_SHAPE, "tile_bytes %d is not 1024, 2048, 4096 or 8192", tile_bytes);
+  if (pool_bytes < (size_t)tile_bytes) return fail(PA_ERR_SHAPE, "pool of %zu bytes holds no tile", pool_bytes);
+  if (num_tiles < 1 || num_tiles > (1 << 28))
+    return fail(PA_ERR_SHAPE, "num_tiles %d is outside [1, 1<<28]", num_tiles);
+  if (depth != 1 && depth != 2) return fail(PA_ERR_SHAPE, "depth %d is not 1 or 2", depth);
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(PA_ERR_SHAPE, "workgroups %d is outside [1, 1<<20]", workgroups);
+  if (!aligned(pool, 16) || !aligned(ids, 4) || !aligned(sink, 4))
+    return fail(PA_ERR_ALIGN, "pool must be 16-B aligned, ids and sink 4-B aligned");
+  hipError_t err = pa::launch_gather_probe(pool, pool_bytes, tile_bytes, ids, num_tiles, depth, workgroups, sink,
+                                           static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "probe launch failed: %s", hipGetErrorString(err));
+  return ok();
+}
+
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
 int pa_version(void) { return 100; }

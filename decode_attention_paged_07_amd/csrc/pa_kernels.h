@@ -89,4 +89,8 @@ hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream, cons
 // workgroups of 256 threads (pa_probe.hip).
 hipError_t launch_read_probe(const void* buf, uint64_t bytes, int workgroups, unsigned* sink, hipStream_t stream);
 
+// Whole-tile gathers of `tile_bytes` tiles listed in `ids` (pa_probe.hip).
+hipError_t launch_gather_probe(const void* pool, uint64_t pool_bytes, int tile_bytes, const int32_t* ids,
+                               int num_tiles, int depth, int workgroups, unsigned* sink, hipStream_t stream);
+
 }  // namespace pa

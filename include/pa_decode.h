@@ -184,6 +184,21 @@ int pa_paged_attention_decode_split(void* out, const void* query, const void* ke
  */
 int pa_hbm_read_probe(const void* buf, size_t bytes, int workgroups, unsigned* sink, void* stream);
 
+/*
+ * HBM gather probe (measurement aid, not part of the decode path): reads the
+ * whole tiles ids[0..num_tiles) of `pool`, tile t being bytes
+ * [t*tile_bytes, (t+1)*tile_bytes), the way the decode kernels read one
+ * (block, kv head) K or V tile. Wave w of the grid reads tiles w, w+W, ...
+ * (W = 4*workgroups waves of 64 lanes), `depth` tiles in flight before any
+ * is consumed. pool: device, 16-B aligned, pool_bytes >= tile_bytes.
+ * tile_bytes: 1024, 2048, 4096 or 8192. ids: device int32 [num_tiles];
+ * entries outside the pool are clamped into it; num_tiles in [1, 1<<28].
+ * depth: 1 or 2.
+ * workgroups in [1, 1<<20]; sink as for pa_hbm_read_probe.
+ */
+int pa_hbm_gather_probe(const void* pool, size_t pool_bytes, int tile_bytes, const int32_t* ids,
+                        int num_tiles, int depth, int workgroups, unsigned* sink, void* stream);
+
 /* Text describing the last error returned on the calling thread ("" if none). */
 const char* pa_last_error(void);
 

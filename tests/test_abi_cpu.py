@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("pa_paged_attention_decode", "pa_paged_attention_decode_split", "pa_decode_plan",
                      "pa_workspace_bytes", "pa_kv_layout", "pa_last_error", "pa_version",
-                     "pa_timing_enable", "pa_timing_read", "pa_hbm_read_probe"):
+                     "pa_timing_enable", "pa_timing_read", "pa_hbm_read_probe",
+                     "pa_hbm_gather_probe"):
         assert required in names
 
 
@@ -179,6 +180,19 @@ def test_tensor_call_rejects_bad_kv_dtype_name(pa):
 ])
 def test_read_probe_validation(pa, args, code):
     assert pa.pa_hbm_read_probe(*args) == code
+    assert pa.pa_last_error() != ""
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(pool=None), -1), (dict(ids=None), -1), (dict(sink=None), -1), (dict(tile_bytes=3000), -2),
+    (dict(pool_bytes=1000), -2), (dict(num_tiles=0), -2), (dict(depth=3), -2), (dict(workgroups=0), -2),
+    (dict(pool=0x10008), -5), (dict(ids=0x20002), -5),
+])
+def test_gather_probe_validation(pa, over, code):
+    a = dict(pool=0x10000, pool_bytes=1 << 20, tile_bytes=4096, ids=0x20000, num_tiles=16, depth=1,
+             workgroups=64, sink=0x30000, stream=None)
+    a.update(over)
+    assert pa.pa_hbm_gather_probe(*a.values()) == code
     assert pa.pa_last_error() != ""
 
 
