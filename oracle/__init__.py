@@ -17,7 +17,8 @@ Sources (cited by page title and section):
     to non-contiguous physical blocks through a per-sequence table; shared
     blocks).
 
-Parity status of each function is listed in ``decode_fp64.PINS``.
+Parity status of each function is listed in ``decode_fp64.PINS`` and
+``kv_append.PINS``.
 """
 
 from .decode_fp64 import (  # noqa: F401
@@ -33,3 +34,5 @@ from .decode_fp64 import (  # noqa: F401
     paged_decode,
     paged_decode_partitioned,
 )
+from .kv_append import PINS as APPEND_PINS  # noqa: F401,E402
+from .kv_append import append_tokens, quantise_e4m3fn  # noqa: F401,E402
