@@ -25,7 +25,9 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "paged decode attn: seqs/s + effective KV-read HBM GB/s (% of MI355X peak)"
-KERNEL_SRC = os.path.join(ROOT, "decode_attention_paged_07_amd", "csrc", "pa_kernels.hip")
+CSRC = os.path.join(ROOT, "decode_attention_paged_07_amd", "csrc")
+KERNEL_SRC = {"pa_streamk_kernel": "pa_kernels.hip", "pa_split_kernel": "pa_kernels.hip",
+              "pa_append_kernel": "pa_append.hip"}
 WORKLOAD_TEXT = {
     "tiny": "tiny fp32 paged decode: 2 seqs {17,40}, 4/4 heads, D=64, bs=16, 16-block pool",
     "mha": "bf16 MHA decode: 64 seqs x 4096, 32/32 heads, D=128, bs=16, 32768-block pool",
@@ -38,8 +40,9 @@ WORKLOAD_TEXT = {
 }
 
 
-def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_sha(kernel: str = "pa_streamk_kernel") -> str:
+    """sha256 prefix of the source file that holds ``kernel``."""
+    with open(os.path.join(CSRC, KERNEL_SRC[kernel]), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -58,7 +61,7 @@ def traffic_from_profiles(kernel: str, config: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_sha") != kernel_sha():
+    if t.get("kernel_sha") != kernel_sha(kernel):
         return None
     return t.get("bytes_per_launch")
 
@@ -81,7 +84,7 @@ def _counter_per_dispatch(run_dir, kernel):
     return statistics.median(vals), len(vals)
 
 
-def summarise_profiles(config, stats_dir, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
+def summarise_profiles(config, stats_dir, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, append=0):
     """Write the committed summaries of one workload's rocprofv3 runs.
 
     stats_dir: --kernel-trace --stats --output-format csv run of this bench;
@@ -90,12 +93,16 @@ def summarise_profiles(config, stats_dir, fetch_dir, write_dir, cal_fetch_dir, c
     reads and torch's fill writes exactly 1 GiB per launch. Each counter is
     scaled by (1 GiB / its calibration reading), both in KiB per dispatch.
     The run logs (<dir>.log, holding the bench's JSON line) must sit beside
-    the directories.
+    the directories. append > 0: the runs timed the KV-append kernel with that
+    many new tokens per sequence (bench.py --append).
     """
     import csv
     with open(os.path.join(stats_dir, "run_kernel_stats.csv")) as f:
         stats = [r for r in csv.DictReader(f) if "pa::" in r["Name"] or "pa2" in r["Name"]]
     stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    if append:
+        stats = [r for r in stats if "pa_append_kernel" in r["Name"]] + \
+                [r for r in stats if "pa_append_kernel" not in r["Name"]]
     top = stats[0]
     kernel = "pa_" + top["Name"].split("pa_", 1)[1].split("<", 1)[0].split("I", 1)[0]
     with open(os.path.join(stats_dir, "run_kernel_trace.csv")) as f:
@@ -107,23 +114,26 @@ def summarise_profiles(config, stats_dir, fetch_dir, write_dir, cal_fetch_dir, c
     cal_w, _ = _counter_per_dispatch(cal_write_dir, "FillFunctor<unsigned char>")
     f_fac, w_fac = (1 << 20) / cal_f, (1 << 20) / cal_w
     nbytes = int(round((fetch * f_fac + write * w_fac) * 1024))
-    algo = rec["roofline"]["algorithmic_bytes_per_launch"]
+    algo = rec["algorithmic_bytes"] if append else rec["roofline"]["algorithmic_bytes_per_launch"]
     sha = _last_json(fetch_dir.rstrip("/") + ".log")["kernel_sha"]
     if _last_json(write_dir.rstrip("/") + ".log")["kernel_sha"] != sha or rec["kernel_sha"] != sha:
         raise ValueError("the runs were taken from different kernel sources")
     rel = lambda d: os.path.relpath(os.path.abspath(d), ROOT)  # noqa: E731
+    mode = f"--append {append}" if append else "--no-cpu-baseline --no-ceiling"
+    label = f"{config}_append{append}" if append else config
     cmds = {
         "stats": f"rocprofv3 --kernel-trace --stats --output-format csv -d {rel(stats_dir)} -o run -- "
-                 f"python3 bench.py --config {config} --steps 20 --warmup 5 --no-cpu-baseline --no-ceiling",
+                 f"python3 bench.py --config {config} --steps 20 --warmup 5 {mode}",
         "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {rel(fetch_dir)} -o run -- "
-                 f"python3 bench.py --config {config} --steps 3 --warmup 1 --no-cpu-baseline --no-ceiling",
+                 f"python3 bench.py --config {config} --steps 3 --warmup 1 {mode}",
         "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {rel(write_dir)} -o run -- "
-                 f"python3 bench.py --config {config} --steps 3 --warmup 1 --no-cpu-baseline --no-ceiling",
+                 f"python3 bench.py --config {config} --steps 3 --warmup 1 {mode}",
         "calibration": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run -- "
                        "python3 bench.py --copy-calibration --steps 3",
     }
     traffic = {
-        "kernel": kernel, "workload": WORKLOAD_TEXT[config], "kernel_sha": sha,
+        "kernel": kernel, "workload": WORKLOAD_TEXT[config] + (f"; {append} new tokens per sequence" if append else ""),
+        "kernel_sha": sha,
         "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write, "dispatches": [n_f, n_w],
         "calibration": {"probe_read_kib": 1 << 20, "fetch_reading_kib": cal_f, "fetch_factor": round(f_fac, 4),
                         "fill_write_kib": 1 << 20, "write_reading_kib": cal_w, "write_factor": round(w_fac, 4)},
@@ -131,10 +141,10 @@ def summarise_profiles(config, stats_dir, fetch_dir, write_dir, cal_fetch_dir, c
         "traffic_over_algorithmic": round(nbytes / algo, 4), "commands": cmds,
     }
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.json"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", f"{kernel}_{label}_traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
         f.write("\n")
-    lines = [f"# rocprofv3 summary: {kernel}, {WORKLOAD_TEXT[config]}", "",
+    lines = [f"# rocprofv3 summary: {kernel}, {traffic['workload']}", "",
              f"kernel source sha256[:16]: {sha}", "", "Commands (run from /tmp with the repository at /root/repo):"]
     lines += [f"  {k}: {v}" for k, v in cmds.items()]
     lines += ["", "Kernel stats (rocprofv3 --stats, ns):",
@@ -147,11 +157,15 @@ def summarise_profiles(config, stats_dir, fetch_dir, write_dir, cal_fetch_dir, c
               f"Counters per dispatch of {kernel} (median over {n_f} / {n_w} dispatches):",
               f"  FETCH_SIZE {fetch:.0f} KiB x {f_fac:.4f} (1 GiB probe read read as {cal_f:.0f} KiB)",
               f"  WRITE_SIZE {write:.0f} KiB x {w_fac:.4f} (1 GiB fill read as {cal_w:.0f} KiB)",
-              f"  HBM traffic {nbytes} B per launch; algorithmic K+V bytes {algo} B; ratio {nbytes / algo:.4f}", "",
-              "Bench line of the --stats run:",
-              f"  avg launch {rec['roofline']['avg_launch_ms']} ms, achieved {rec['roofline']['achieved']} GB/s "
-              f"({rec['roofline']['frac']:.1%} of 8 TB/s), ms/step {rec['ms_per_step']}"]
-    with open(os.path.join(ROOT, "profiles", f"{kernel}_{config}_rocprof.txt"), "w") as f:
+              f"  HBM traffic {nbytes} B per launch; algorithmic bytes {algo} B; ratio {nbytes / algo:.4f}", "",
+              "Bench line of the --stats run:"]
+    if append:
+        lines.append(f"  kernel avg {rec['kernel_avg_ms']} ms (HIP events), {rec['kernel_gbps']} GB/s algorithmic, "
+                     f"ms/step {rec['ms_per_step']}")
+    else:
+        lines.append(f"  avg launch {rec['roofline']['avg_launch_ms']} ms, achieved {rec['roofline']['achieved']} GB/s "
+                     f"({rec['roofline']['frac']:.1%} of 8 TB/s), ms/step {rec['ms_per_step']}")
+    with open(os.path.join(ROOT, "profiles", f"{kernel}_{label}_rocprof.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -234,6 +248,66 @@ def gather_ceilings(dev, pool_bytes=8 << 30, read_bytes=2 << 30, reps=10):
     return "\n".join(summary + ["", "All runs:", ""] + lines)
 
 
+def bench_append(case, tokens, steps, warmup):
+    """Time the KV-append kernel on the workload's shapes: `tokens` new tokens
+    per sequence written over each sequence's last `tokens` positions (the
+    slots exist in the table), inputs resident in HBM."""
+    import numpy as np
+    import torch
+
+    import decode_attention_paged_07_amd as pa
+
+    cfg = case.cfg
+    dev = case.query.device
+    S, hkv, d = cfg.num_seqs, cfg.num_kv_heads, cfg.head_size
+    in_dtype = case.query.dtype
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed + 100)
+    key = torch.randn((S, tokens, hkv, d), generator=g, device=dev).to(in_dtype)
+    value = torch.randn((S, tokens, hkv, d), generator=g, device=dev).to(in_dtype)
+    pos = torch.from_numpy(np.maximum(case.meta.seq_lens.astype(np.int64) - tokens, 0).astype(np.int32)).to(dev)
+
+    def step():
+        pa.kv_cache_append(case.key_cache, case.value_cache, key, value, case.block_tables, pos,
+                           kv_cache_dtype=cfg.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale)
+    for _ in range(warmup):
+        step()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    pa.pa_timing_read_append()
+    pa.pa_timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    pa.pa_timing_enable(False)
+    k_ms, k_n = pa.pa_timing_read_append()
+    kernel_ms = k_ms / max(k_n, 1)
+    e_in = key.element_size()
+    e_kv = 1 if cfg.kv_dtype == "fp8_e4m3" else e_in
+    nbytes = S * tokens * hkv * d * 2 * (e_in + e_kv)
+    return {
+        "metric": "paged KV-cache append: tokens/s + algorithmic GB/s (inputs read + cache slots written)",
+        "value": round(S * tokens / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "dtype": f"{cfg.q_dtype} in -> {'fp8 e4m3' if e_kv == 1 else cfg.q_dtype} cache",
+        "data": "synthetic", "config": {"workload": WORKLOAD_TEXT[cfg.name] + f"; {tokens} new token(s) per sequence",
+                                        "num_seqs": S, "tokens_per_seq": tokens, "num_kv_heads": hkv,
+                                        "head_size": d},
+        "algorithmic_bytes": nbytes, "kernel": "pa_append_kernel",
+        "kernel_avg_ms": round(kernel_ms, 5), "kernel_gbps": round(nbytes / (kernel_ms / 1e3) / 1e9, 1),
+        "note": "ms_per_step is host-launch bound for a few-microsecond kernel; kernel_avg_ms is the "
+                "HIP-event time of the kernel on its stream",
+        "kernel_sha": kernel_sha("pa_append_kernel"),
+    }
+
+
 def cpu_baseline(case, budget_s: float):
     """Time the fp64 oracle on the host over the first sequences of the batch
     until about budget_s seconds of work, and check the GPU output on them."""
@@ -289,6 +363,8 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--summarise", nargs=5, metavar=("STATS", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="write profiles/ summaries from rocprofv3 csv run directories (no GPU)")
+    ap.add_argument("--append", type=int, default=0, metavar="T",
+                    help="time the KV-append kernel with T new tokens per sequence instead of decode")
     ap.add_argument("--ceilings", action="store_true",
                     help="only print the gather-probe read ceilings (markdown table)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -296,7 +372,7 @@ def main():
     args = ap.parse_args()
 
     if args.summarise:
-        summarise_profiles(args.config, *args.summarise)
+        summarise_profiles(args.config, *args.summarise, append=args.append)
         return
 
     if args.gpus != 1:
@@ -333,6 +409,9 @@ def main():
     cfg = workloads.CONFIGS[args.config]
     print(f"[bench] building {args.config} inputs", file=sys.stderr, flush=True)
     case = workloads.make_case(cfg, device=dev)
+    if args.append:
+        print(json.dumps(bench_append(case, args.append, args.steps, args.warmup)), flush=True)
+        return
     out = torch.empty_like(case.query)
     split_tokens, num_splits, _ = pa.pa_decode_plan(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads,
                                                     cfg.head_size, case.max_seq_len, args.split)
@@ -414,7 +493,7 @@ def main():
         },
         "reduce_avg_ms": round(red_ms / red_n, 5) if red_n else 0.0,
         "ms_per_step_with_kernel_events": round(ms_with_events, 5),
-        "kernel_sha": kernel_sha(),
+        "kernel_sha": kernel_sha(kernel_name),
         "cpu_baseline": None,
     }
     if not args.no_ceiling:

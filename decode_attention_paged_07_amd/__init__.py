@@ -30,7 +30,8 @@ __all__ = [
     "PA_BLOCK_SIZE", "PA_PARTITION_SIZE", "PA_MAX_GROUP",
     "pa_paged_attention_decode", "pa_paged_attention_decode_split", "pa_decode_plan",
     "pa_workspace_bytes", "pa_kv_layout", "pa_last_error", "pa_version", "pa_timing_enable",
-    "pa_timing_read", "pa_hbm_read_probe", "pa_hbm_gather_probe", "paged_attention_decode", "kv_cache_shapes", "LIB_PATH",
+    "pa_timing_read", "pa_timing_read_append", "pa_hbm_read_probe", "pa_hbm_gather_probe", "pa_kv_cache_append",
+    "paged_attention_decode", "kv_cache_append", "kv_cache_shapes", "LIB_PATH",
     "PagedAttentionError",
 ]
 
@@ -88,10 +89,15 @@ _lib.pa_timing_enable.restype = _c_int
 _lib.pa_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_int),
                                 ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_int)]
 _lib.pa_timing_read.restype = _c_int
+_lib.pa_timing_read_append.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_int)]
+_lib.pa_timing_read_append.restype = _c_int
 _lib.pa_hbm_read_probe.argtypes = [_vp, _c_size, _c_int, _vp, _vp]
 _lib.pa_hbm_read_probe.restype = _c_int
 _lib.pa_hbm_gather_probe.argtypes = [_vp, _c_size, _c_int, _vp, _c_int, _c_int, _c_int, _vp, _vp]
 _lib.pa_hbm_gather_probe.restype = _c_int
+_lib.pa_kv_cache_append.argtypes = [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp,
+                                    _c_int, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp]
+_lib.pa_kv_cache_append.restype = _c_int
 
 
 class PagedAttentionError(RuntimeError):
@@ -184,6 +190,13 @@ def pa_timing_read():
     return pm.value, pn.value, rm.value, rn.value
 
 
+def pa_timing_read_append():
+    """-> (append_ms, append_launches) since the last read."""
+    ms, n = ctypes.c_double(), _c_int()
+    _raise_for(_lib.pa_timing_read_append(ctypes.byref(ms), ctypes.byref(n)), "pa_timing_read_append")
+    return ms.value, n.value
+
+
 def pa_hbm_read_probe(buf, nbytes, workgroups, sink, stream) -> int:
     return _lib.pa_hbm_read_probe(buf, nbytes, workgroups, sink, stream)
 
@@ -192,6 +205,15 @@ def pa_hbm_gather_probe(pool, pool_bytes, tile_bytes, ids, num_tiles, depth, wor
                         stream) -> int:
     return _lib.pa_hbm_gather_probe(pool, pool_bytes, tile_bytes, ids, num_tiles, depth, workgroups,
                                     sink, stream)
+
+
+def pa_kv_cache_append(key_cache, value_cache, key, value, num_seqs, tokens_per_seq, num_kv_heads,
+                       head_size, num_blocks, block_tables, max_blocks_per_seq, positions, block_size,
+                       in_dtype, kv_cache_dtype, k_scale, v_scale, stream) -> int:
+    return _lib.pa_kv_cache_append(key_cache, value_cache, key, value, num_seqs, tokens_per_seq,
+                                   num_kv_heads, head_size, num_blocks, block_tables,
+                                   max_blocks_per_seq, positions, block_size, in_dtype,
+                                   kv_cache_dtype, k_scale, v_scale, stream)
 
 
 # ---------------------------------------------------------------------------
@@ -306,3 +328,57 @@ def paged_attention_decode(out, query, key_cache, value_cache, num_kv_heads, sca
         kvd, ks.data_ptr() if ks is not None else None, vs.data_ptr() if vs is not None else None,
         ws_ptr, ws_bytes, stream, int(split_tokens))
     _raise_for(rc, "paged_attention_decode")
+
+
+def kv_cache_append(key_cache, value_cache, key, value, block_tables, positions,
+                    kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0) -> None:
+    """Store new tokens' K/V rows in the paged cache (in place, current stream).
+
+    key, value: [num_seqs, num_kv_heads, head_size] (one token per sequence) or
+    [num_seqs, T, num_kv_heads, head_size], float32 or bfloat16, contiguous.
+    Token j of sequence s is written at logical position positions[s] + j
+    through block_tables (int32 [num_seqs, max_blocks]); positions int32
+    [num_seqs], negative = skip. Caches in the library's layout
+    (``kv_cache_shapes``): the input dtype for "auto", uint8 / float8_e4m3fn
+    codes for "fp8" / "fp8_e4m3" (value / scale rounded to the nearest code).
+    """
+    if kv_cache_dtype not in _KV_NAMES:
+        raise TypeError(f"kv_cache_dtype {kv_cache_dtype!r} is not one of {sorted(_KV_NAMES)}")
+    kvd = _KV_NAMES[kv_cache_dtype]
+    if key.dtype not in _Q_DTYPES or value.dtype != key.dtype:
+        raise TypeError("key/value must both be float32 or bfloat16")
+    dev = key.device
+    _need(dev.type == "cuda", "key must be on a GPU")
+    for name, t in (("key_cache", key_cache), ("value_cache", value_cache), ("value", value),
+                    ("block_tables", block_tables), ("positions", positions)):
+        _need(t.device == dev, f"{name} is not on the key's device")
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+    _need(key.is_contiguous(), "key must be contiguous")
+    _need(key.shape == value.shape and key.dim() in (3, 4), "key/value must be [S, Hkv, D] or [S, T, Hkv, D]")
+    num_seqs = key.shape[0]
+    tokens = 1 if key.dim() == 3 else key.shape[1]
+    num_kv_heads, head_size = key.shape[-2], key.shape[-1]
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == num_seqs, "block_tables must be int32 [num_seqs, max_blocks]")
+    _need(positions.dtype == torch.int32 and positions.shape == (num_seqs,),
+          "positions must be int32 [num_seqs]")
+    if kvd == PA_KV_AUTO:
+        if key_cache.dtype != key.dtype or value_cache.dtype != key.dtype:
+            raise TypeError("with kv_cache_dtype 'auto' the caches must have the key's dtype")
+    elif key_cache.dtype not in (torch.uint8, torch.float8_e4m3fn) or value_cache.dtype != key_cache.dtype:
+        raise TypeError("the fp8 cache must be uint8 or float8_e4m3fn codes")
+    num_blocks = key_cache.shape[0]
+    # the layout depends only on the cache element type (fp8 codes for any input type)
+    layout_dtype = key.dtype if kvd == PA_KV_AUTO else torch.bfloat16
+    k_shape, v_shape = kv_cache_shapes(num_blocks, num_kv_heads, head_size, layout_dtype, kv_cache_dtype)
+    _need(tuple(key_cache.shape) == k_shape, f"key_cache shape {tuple(key_cache.shape)} != {k_shape}")
+    _need(tuple(value_cache.shape) == v_shape, f"value_cache shape {tuple(value_cache.shape)} != {v_shape}")
+    ks = _device_scalar(k_scale, dev) if kvd == PA_KV_FP8_E4M3 else None
+    vs = _device_scalar(v_scale, dev) if kvd == PA_KV_FP8_E4M3 else None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = _lib.pa_kv_cache_append(
+        key_cache.data_ptr(), value_cache.data_ptr(), key.data_ptr(), value.data_ptr(), num_seqs,
+        tokens, num_kv_heads, head_size, num_blocks, block_tables.data_ptr(), block_tables.shape[1],
+        positions.data_ptr(), PA_BLOCK_SIZE, _Q_DTYPES[key.dtype], kvd,
+        ks.data_ptr() if ks is not None else None, vs.data_ptr() if vs is not None else None, stream)
+    _raise_for(rc, "kv_cache_append")

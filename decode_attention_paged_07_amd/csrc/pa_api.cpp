@@ -132,7 +132,7 @@ struct Timing {
   std::mutex mu;
   bool on = false;
   std::vector<hipEvent_t> pool;                 // free events
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> part, red;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> part, red, app;
   hipEvent_t pending = nullptr;
 };
 Timing g_timing;
@@ -161,6 +161,24 @@ void record_end_into(std::vector<std::pair<hipEvent_t, hipEvent_t>>& v, hipStrea
 }
 void hook_part_end(hipStream_t s) { record_end_into(g_timing.part, s); }
 void hook_red_end(hipStream_t s) { record_end_into(g_timing.red, s); }
+
+// Drains recorded (begin, end) event pairs into a total and a count; the
+// caller holds g_timing.mu.
+hipError_t drain_events(std::vector<std::pair<hipEvent_t, hipEvent_t>>& v, double& t, int& n) {
+  hipError_t first_err = hipSuccess;
+  for (auto& pr : v) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(pr.second);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess && first_err == hipSuccess) first_err = e;
+    t += ms;
+    ++n;
+    g_timing.pool.push_back(pr.first);
+    g_timing.pool.push_back(pr.second);
+  }
+  v.clear();
+  return first_err;
+}
 
 int decode_impl(void* out, const void* query, const void* key_cache, const void* value_cache,
                 int num_seqs, int num_heads, int num_kv_heads, int head_size, int num_blocks,
@@ -375,6 +393,61 @@ int pa_hbm_gather_probe(const void* pool, size_t pool_bytes, int tile_bytes, con
   return ok();
 }
 
+int pa_kv_cache_append(void* key_cache, void* value_cache, const void* key, const void* value, int num_seqs,
+                       int tokens_per_seq, int num_kv_heads, int head_size, int num_blocks,
+                       const int32_t* block_tables, int max_blocks_per_seq, const int32_t* positions,
+                       int block_size, int in_dtype, int kv_cache_dtype, const float* k_scale,
+                       const float* v_scale, void* stream) {
+  if (in_dtype != PA_DTYPE_F32 && in_dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_DTYPE, "in_dtype %d is not PA_DTYPE_F32 or PA_DTYPE_BF16", in_dtype);
+  if (kv_cache_dtype != PA_KV_AUTO && kv_cache_dtype != PA_KV_FP8_E4M3)
+    return fail(PA_ERR_DTYPE, "kv_cache_dtype %d is not PA_KV_AUTO or PA_KV_FP8_E4M3", kv_cache_dtype);
+  if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
+  if (tokens_per_seq < 1) return fail(PA_ERR_SHAPE, "tokens_per_seq %d must be positive", tokens_per_seq);
+  if (num_kv_heads <= 0) return fail(PA_ERR_SHAPE, "num_kv_heads %d must be positive", num_kv_heads);
+  if (head_size != 64 && head_size != 128) return fail(PA_ERR_SHAPE, "head_size %d is not 64 or 128", head_size);
+  if (block_size != PA_BLOCK_SIZE) return fail(PA_ERR_SHAPE, "block_size %d is not %d", block_size, PA_BLOCK_SIZE);
+  if (num_blocks <= 0) return fail(PA_ERR_SHAPE, "num_blocks %d must be positive", num_blocks);
+  if (max_blocks_per_seq <= 0) return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d must be positive", max_blocks_per_seq);
+  if ((int64_t)num_seqs * tokens_per_seq * num_kv_heads >= ((int64_t)1 << 31))
+    return fail(PA_ERR_SHAPE, "num_seqs * tokens_per_seq * num_kv_heads must be below 2^31");
+  if (num_seqs == 0) return ok();
+  if (!key_cache || !value_cache || !key || !value || !block_tables || !positions)
+    return fail(PA_ERR_NULL, "key_cache, value_cache, key, value, block_tables and positions must be non-NULL");
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(key, 16) || !aligned(value, 16))
+    return fail(PA_ERR_ALIGN, "key_cache, value_cache, key and value must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(positions, 4) || (k_scale && !aligned(k_scale, 4)) ||
+      (v_scale && !aligned(v_scale, 4)))
+    return fail(PA_ERR_ALIGN, "block_tables, positions and scales must be 4-byte aligned");
+  pa::AppendArgs a{};
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.key = key;
+  a.value = value;
+  a.block_tables = block_tables;
+  a.positions = positions;
+  const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
+  a.k_scale = fp8 ? k_scale : nullptr;
+  a.v_scale = fp8 ? v_scale : nullptr;
+  a.num_seqs = num_seqs;
+  a.tokens_per_seq = tokens_per_seq;
+  a.num_kv_heads = num_kv_heads;
+  a.head_size = head_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  const int in_kind = in_dtype == PA_DTYPE_F32 ? pa::KIND_F32 : pa::KIND_BF16;
+  const int cache_kind = fp8 ? pa::KIND_FP8 : in_kind;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::unique_lock<std::mutex> lock(g_timing.mu);
+  const bool timed = g_timing.on;
+  if (!timed) lock.unlock();
+  if (timed) record_begin(st);
+  hipError_t err = pa::launch_append(a, in_kind, cache_kind, st);
+  if (timed) record_end_into(g_timing.app, st);
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "append launch failed: %s", hipGetErrorString(err));
+  return ok();
+}
+
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
 int pa_version(void) { return 100; }
@@ -389,27 +462,25 @@ int pa_timing_read(double* partition_ms, int* partition_launches, double* reduce
   std::lock_guard<std::mutex> g(g_timing.mu);
   double tp = 0, tr = 0;
   int np = 0, nr = 0;
-  hipError_t first_err = hipSuccess;
-  auto drain = [&](std::vector<std::pair<hipEvent_t, hipEvent_t>>& v, double& t, int& n) {
-    for (auto& pr : v) {
-      float ms = 0.f;
-      hipError_t e = hipEventSynchronize(pr.second);
-      if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
-      if (e != hipSuccess && first_err == hipSuccess) first_err = e;
-      t += ms;
-      ++n;
-      g_timing.pool.push_back(pr.first);
-      g_timing.pool.push_back(pr.second);
-    }
-    v.clear();
-  };
-  drain(g_timing.part, tp, np);
-  drain(g_timing.red, tr, nr);
+  hipError_t e1 = drain_events(g_timing.part, tp, np);
+  hipError_t e2 = drain_events(g_timing.red, tr, nr);
   if (partition_ms) *partition_ms = tp;
   if (partition_launches) *partition_launches = np;
   if (reduce_ms) *reduce_ms = tr;
   if (reduce_launches) *reduce_launches = nr;
-  if (first_err != hipSuccess) return fail(PA_ERR_HIP, "event timing failed: %s", hipGetErrorString(first_err));
+  const hipError_t err = e1 != hipSuccess ? e1 : e2;
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "event timing failed: %s", hipGetErrorString(err));
+  return ok();
+}
+
+int pa_timing_read_append(double* append_ms, int* append_launches) {
+  std::lock_guard<std::mutex> g(g_timing.mu);
+  double t = 0;
+  int n = 0;
+  hipError_t err = drain_events(g_timing.app, t, n);
+  if (append_ms) *append_ms = t;
+  if (append_launches) *append_launches = n;
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "event timing failed: %s", hipGetErrorString(err));
   return ok();
 }
 

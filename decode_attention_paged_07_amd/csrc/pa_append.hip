@@ -1,0 +1,173 @@
+// KV-cache append for gfx950: store the new tokens' K and V rows in the
+// paged cache, the step that precedes attention in every decode iteration
+// (the cache grows one token per step; vLLM 0.25.0 解读 §1). Token j of
+// sequence s goes to logical position p = positions[s] + j, i.e. physical
+// block block_tables[s, p / 16], slot p % 16 (10100.com retirement article,
+// §1), in the pages' layouts (same article, §2):
+//   K [num_blocks][num_kv_heads][D/x][16][x],  V [num_blocks][num_kv_heads][D][16].
+// With an fp8 cache each element is stored as the E4M3FN code nearest to
+// x / scale (ties to even, saturating at 448; same article, §4, for the
+// scaled fp8 storage).
+//
+// One wave per (sequence, kv head, physical block touched): the wave stores
+// the run of new tokens that falls in that block. Lanes walk the run with the
+// token index fastest, so each store instruction covers consecutive slots:
+// for K, 16-byte rows of one chunk (contiguous 16*run bytes); for V, elements
+// of one dim row (contiguous run*elem bytes). A single token per block (the
+// decode step) can only write 16-byte K pieces and single V elements.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_kernels.h"
+
+namespace pa {
+
+namespace {
+
+typedef unsigned u32x4a __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
+
+// E4M3FN code of v / scale: IEEE float32 quotient, nearest code with ties to
+// even (the hardware conversion rounds to nearest even), magnitude saturated
+// at 448, NaN -> 0x7F, sign bit taken from the quotient.
+__device__ __forceinline__ unsigned quant_e4m3(float v, float scale) {
+  const float y = v / scale;
+  if (__builtin_isnan(y)) return 0x7Fu;
+  const float mag = fminf(__builtin_fabsf(y), 448.0f);
+  const unsigned c = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(mag, 0.0f, 0, false) & 0x7Fu;
+  return c | ((__float_as_uint(y) >> 24) & 0x80u);
+}
+
+template <int KIND, int D>
+struct AppendPolicy;
+
+// f32 input, f32 cache (x = 4) and bf16 input, bf16 cache (x = 8): copies.
+template <int D>
+struct AppendPolicy<KIND_F32, D> {
+  using In = float;
+  static constexpr int kX = 4;
+  static constexpr int kElem = 4;
+  __device__ static void k_chunk(const In* src, char* dst, float) {
+    *reinterpret_cast<u32x4a*>(dst) = *reinterpret_cast<const u32x4a*>(src);
+  }
+  __device__ static void v_elem(const In* src, char* dst, float) { *reinterpret_cast<float*>(dst) = *src; }
+};
+
+template <int D>
+struct AppendPolicy<KIND_BF16, D> {
+  using In = unsigned short;
+  static constexpr int kX = 8;
+  static constexpr int kElem = 2;
+  __device__ static void k_chunk(const In* src, char* dst, float) {
+    *reinterpret_cast<u32x4a*>(dst) = *reinterpret_cast<const u32x4a*>(src);
+  }
+  __device__ static void v_elem(const In* src, char* dst, float) {
+    *reinterpret_cast<unsigned short*>(dst) = *src;
+  }
+};
+
+// fp8 cache (x = 16) from bf16 or f32 input.
+template <typename InT>
+struct QuantPolicy {
+  using In = InT;
+  static constexpr int kX = 16;
+  static constexpr int kElem = 1;
+  __device__ static float val(In v) {
+    if constexpr (sizeof(In) == 4) return v;
+    else return bf16_to_f32(v);
+  }
+  // src is 16-byte aligned: token rows are multiples of 128 bytes apart and
+  // chunks 16 elements apart.
+  __device__ static void k_chunk(const In* src, char* dst, float scale) {
+    constexpr int kVec = 16 / sizeof(In);                 // elements per 16-byte load
+    In v[16];
+#pragma unroll
+    for (int q = 0; q < 16 / kVec; ++q)
+      *reinterpret_cast<u32x4a*>(v + q * kVec) = *reinterpret_cast<const u32x4a*>(src + q * kVec);
+    u32x4a w = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) w[e >> 2] |= quant_e4m3(val(v[e]), scale) << (8 * (e & 3));
+    *reinterpret_cast<u32x4a*>(dst) = w;
+  }
+  __device__ static void v_elem(const In* src, char* dst, float scale) {
+    *reinterpret_cast<unsigned char*>(dst) = (unsigned char)quant_e4m3(val(*src), scale);
+  }
+};
+
+template <typename Pol, int D>
+__global__ void __launch_bounds__(256) pa_append_kernel(const AppendArgs a, int runs_per_pair) {
+  using In = typename Pol::In;
+  constexpr int kChunks = D / Pol::kX;
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * runs_per_pair;
+  if (item >= items) return;
+  const int r = (int)(item % runs_per_pair);
+  const int64_t sh = item / runs_per_pair;                // s * Hkv + h
+  const int h = (int)(sh % a.num_kv_heads);
+  const int s = (int)(sh / a.num_kv_heads);
+  const int p0 = a.positions[s];
+  if (p0 < 0) return;
+  const int64_t blk = (int64_t)(p0 >> 4) + r;             // logical block of this run
+  const int64_t t_lo = blk * 16 > p0 ? blk * 16 : (int64_t)p0;
+  const int64_t p_end = (int64_t)p0 + a.tokens_per_seq;
+  const int64_t t_hi = (blk + 1) * 16 < p_end ? (blk + 1) * 16 : p_end;
+  if (t_lo >= t_hi || blk >= a.max_blocks_per_seq) return;
+  const int b = a.block_tables[(int64_t)s * a.max_blocks_per_seq + blk];
+  if (b < 0 || b >= a.num_blocks) return;
+  const int o0 = (int)(t_lo & 15);                        // first slot
+  const int n = (int)(t_hi - t_lo);                       // tokens in this run, 1..16
+  const int j0 = (int)(t_lo - p0);                        // their first index among the new tokens
+  const int64_t tile = (int64_t)D * 16 * Pol::kElem;
+  const int64_t base = ((int64_t)b * a.num_kv_heads + h) * tile;
+  const int64_t row_stride = (int64_t)a.num_kv_heads * D;  // elements between consecutive tokens
+  const int64_t row0 = ((int64_t)s * a.tokens_per_seq + j0) * row_stride + (int64_t)h * D;
+  const In* krow = reinterpret_cast<const In*>(a.key) + row0;
+  const In* vrow = reinterpret_cast<const In*>(a.value) + row0;
+  const float ks = a.k_scale ? *a.k_scale : 1.f;
+  const float vs = a.v_scale ? *a.v_scale : 1.f;
+  char* kc = reinterpret_cast<char*>(a.key_cache) + base;
+  char* vc = reinterpret_cast<char*>(a.value_cache) + base;
+  // K: item i = c * n + t -> chunk c of token t, 16 bytes at row o0 + t.
+  for (int i = lane; i < kChunks * n; i += 64) {
+    const int c = i / n, t = i - c * n;
+    Pol::k_chunk(krow + t * row_stride + c * Pol::kX, kc + ((int64_t)c * 16 + o0 + t) * 16, ks);
+  }
+  // V: item i = d * n + t -> element d of token t at row d, slot o0 + t.
+  for (int i = lane; i < D * n; i += 64) {
+    const int d = i / n, t = i - d * n;
+    Pol::v_elem(vrow + t * row_stride + d, vc + ((int64_t)d * 16 + o0 + t) * Pol::kElem, vs);
+  }
+}
+
+template <typename Pol, int D>
+hipError_t launch_append_t(const AppendArgs& a, hipStream_t stream) {
+  // A run of T tokens starting anywhere in a block touches at most
+  // floor((15 + T - 1) / 16) + 1 blocks.
+  const int runs = (15 + a.tokens_per_seq - 1) / 16 + 1;
+  const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * runs;
+  const int64_t wgs = (items + 3) / 4;
+  hipLaunchKernelGGL((pa_append_kernel<Pol, D>), dim3((unsigned)wgs), dim3(256), 0, stream, a, runs);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, int in_kind, int cache_kind, hipStream_t stream) {
+  const int key = (in_kind * 10 + cache_kind) * 1000 + a.head_size;
+  switch (key) {
+    case (KIND_F32 * 10 + KIND_F32) * 1000 + 64: return launch_append_t<AppendPolicy<KIND_F32, 64>, 64>(a, stream);
+    case (KIND_F32 * 10 + KIND_F32) * 1000 + 128: return launch_append_t<AppendPolicy<KIND_F32, 128>, 128>(a, stream);
+    case (KIND_BF16 * 10 + KIND_BF16) * 1000 + 64: return launch_append_t<AppendPolicy<KIND_BF16, 64>, 64>(a, stream);
+    case (KIND_BF16 * 10 + KIND_BF16) * 1000 + 128: return launch_append_t<AppendPolicy<KIND_BF16, 128>, 128>(a, stream);
+    case (KIND_BF16 * 10 + KIND_FP8) * 1000 + 64: return launch_append_t<QuantPolicy<unsigned short>, 64>(a, stream);
+    case (KIND_BF16 * 10 + KIND_FP8) * 1000 + 128: return launch_append_t<QuantPolicy<unsigned short>, 128>(a, stream);
+    case (KIND_F32 * 10 + KIND_FP8) * 1000 + 64: return launch_append_t<QuantPolicy<float>, 64>(a, stream);
+    case (KIND_F32 * 10 + KIND_FP8) * 1000 + 128: return launch_append_t<QuantPolicy<float>, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

@@ -75,6 +75,26 @@ struct DecodeArgs {
   int streamk_workgroups;      // > 0 selects the stream-K scheduler
 };
 
+// Arguments of the KV-cache append kernel (pa_append.hip).
+struct AppendArgs {
+  void* key_cache;
+  void* value_cache;
+  const void* key;             // [num_seqs][tokens_per_seq][num_kv_heads][head_size]
+  const void* value;
+  const int32_t* block_tables; // [num_seqs][max_blocks_per_seq]
+  const int32_t* positions;    // [num_seqs]
+  const float* k_scale;        // nullable (1.0), fp8 cache only
+  const float* v_scale;
+  int num_seqs;
+  int tokens_per_seq;
+  int num_kv_heads;
+  int head_size;
+  int num_blocks;
+  int max_blocks_per_seq;
+};
+
+hipError_t launch_append(const AppendArgs& a, int in_kind, int cache_kind, hipStream_t stream);
+
 // Optional callbacks around each launch (used for event timing).
 struct LaunchHooks {
   void (*before_partition)(hipStream_t) = nullptr;

@@ -199,6 +199,42 @@ int pa_hbm_read_probe(const void* buf, size_t bytes, int workgroups, unsigned* s
 int pa_hbm_gather_probe(const void* pool, size_t pool_bytes, int tile_bytes, const int32_t* ids,
                         int num_tiles, int depth, int workgroups, unsigned* sink, void* stream);
 
+/*
+ * KV-cache append: store the K and V rows of new tokens in the paged cache,
+ * the step before attention in every decode iteration (the cache grows one
+ * token per step; "vLLM 0.25.0 解读" §1). Token j (0 <= j < tokens_per_seq)
+ * of sequence s goes to logical position p = positions[s] + j, i.e. physical
+ * block block_tables[s, p / 16], slot p % 16 (10100.com retirement article,
+ * §1), written in the cache layouts described by pa_kv_layout.
+ *   key_cache, value_cache  device, the caches (16-B aligned); written only at
+ *                the slots named by the positions.
+ *   key, value   device, [num_seqs][tokens_per_seq][num_kv_heads][head_size],
+ *                element type in_dtype, contiguous, 16-B aligned.
+ *   num_seqs >= 0 (0 is a no-op); tokens_per_seq >= 1; num_kv_heads > 0;
+ *   head_size 64 or 128; num_blocks > 0; max_blocks_per_seq > 0 (table
+ *   stride); block_size must be PA_BLOCK_SIZE;
+ *   num_seqs * tokens_per_seq * num_kv_heads < 2^31.
+ *   block_tables device int32 [num_seqs][max_blocks_per_seq]; positions device
+ *   int32 [num_seqs]. A negative position skips the sequence; positions past
+ *   max_blocks_per_seq*16 and table entries outside [0, num_blocks) are not
+ *   written.
+ *   in_dtype: PA_DTYPE_F32 or PA_DTYPE_BF16. kv_cache_dtype: PA_KV_AUTO (the
+ *   cache holds in_dtype and the rows are copied unchanged) or
+ *   PA_KV_FP8_E4M3: each element is stored as the E4M3FN code nearest to
+ *   value / scale (float32 quotient, ties to even, magnitude saturated at
+ *   448, NaN -> 0x7F, sign kept), scale = *k_scale for K and *v_scale for V
+ *   (device fp32 scalars; NULL = 1.0), the inverse of the decode call's
+ *   dequantisation (10100.com article, §4).
+ * Two tokens naming the same slot leave either one. Asynchronous on `stream`;
+ * no allocation; host-side validation as for the decode call.
+ */
+int pa_kv_cache_append(void* key_cache, void* value_cache, const void* key, const void* value,
+                       int num_seqs, int tokens_per_seq, int num_kv_heads, int head_size,
+                       int num_blocks, const int32_t* block_tables, int max_blocks_per_seq,
+                       const int32_t* positions, int block_size, int in_dtype,
+                       int kv_cache_dtype, const float* k_scale, const float* v_scale,
+                       void* stream);
+
 /* Text describing the last error returned on the calling thread ("" if none). */
 const char* pa_last_error(void);
 
@@ -207,14 +243,17 @@ int pa_version(void);
 
 /*
  * Kernel timing. While enabled, each decode call records HIP events on its
- * stream around the partition kernel and around the reduce kernel (creating
- * events on first use, outside any graph capture). pa_timing_read waits for
+ * stream around the partition kernel and around the reduce kernel, and each
+ * append call around its kernel (creating events on first use, outside any
+ * graph capture). pa_timing_read waits for
  * the recorded events, returns the summed milliseconds and launch counts since
  * the last read, and clears them. Meant for benchmarks; off by default.
  */
 int pa_timing_enable(int on);
 int pa_timing_read(double* partition_ms, int* partition_launches, double* reduce_ms,
                    int* reduce_launches);
+/* The same for the KV-append kernel launched by pa_kv_cache_append. */
+int pa_timing_read_append(double* append_ms, int* append_launches);
 
 #ifdef __cplusplus
 }

@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
     for required in ("pa_paged_attention_decode", "pa_paged_attention_decode_split", "pa_decode_plan",
                      "pa_workspace_bytes", "pa_kv_layout", "pa_last_error", "pa_version",
                      "pa_timing_enable", "pa_timing_read", "pa_hbm_read_probe",
-                     "pa_hbm_gather_probe"):
+                     "pa_hbm_gather_probe", "pa_kv_cache_append", "pa_timing_read_append"):
         assert required in names
 
 
@@ -196,7 +196,44 @@ def test_gather_probe_validation(pa, over, code):
     assert pa.pa_last_error() != ""
 
 
+APPEND = dict(key_cache=0x10000, value_cache=0x20000, key=0x30000, value=0x40000, num_seqs=2,
+              tokens_per_seq=1, num_kv_heads=2, head_size=128, num_blocks=16, block_tables=0x50000,
+              max_blocks_per_seq=4, positions=0x60000, block_size=16, in_dtype=1, kv_cache_dtype=0,
+              k_scale=None, v_scale=None, stream=None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(key_cache=None), -1), (dict(value=None), -1), (dict(positions=None), -1),
+    (dict(block_tables=None), -1), (dict(head_size=96), -2), (dict(block_size=32), -2),
+    (dict(tokens_per_seq=0), -2), (dict(num_kv_heads=0), -2), (dict(num_blocks=0), -2),
+    (dict(max_blocks_per_seq=0), -2), (dict(num_seqs=-1), -2),
+    (dict(num_seqs=1 << 20, tokens_per_seq=1 << 10, num_kv_heads=8), -2),
+    (dict(in_dtype=5), -3), (dict(kv_cache_dtype=2), -3),
+    (dict(key=0x30008), -5), (dict(value_cache=0x20004), -5), (dict(positions=0x60002), -5),
+])
+def test_append_validation_rejects(pa, over, code):
+    a = dict(APPEND)
+    a.update(over)
+    assert pa.pa_kv_cache_append(*a.values()) == code, pa.pa_last_error()
+    assert pa.pa_last_error() != ""
+
+
+def test_append_zero_sequences_is_a_noop(pa):
+    a = dict(APPEND, num_seqs=0, key=None, value=None)
+    assert pa.pa_kv_cache_append(*a.values()) == 0
+
+
+def test_tensor_append_refuses_cpu_tensors(pa):
+    kc = torch.zeros((4, 2, 16, 16, 8), dtype=torch.bfloat16)
+    vc = torch.zeros((4, 2, 128, 16), dtype=torch.bfloat16)
+    k = torch.zeros((1, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        pa.kv_cache_append(kc, vc, k, k.clone(), torch.zeros((1, 4), dtype=torch.int32),
+                           torch.zeros(1, dtype=torch.int32))
+
+
 def test_timing_read_without_launches(pa):
     pa.pa_timing_enable(True)
     assert pa.pa_timing_read() == (0.0, 0, 0.0, 0)
+    assert pa.pa_timing_read_append() == (0.0, 0)
     pa.pa_timing_enable(False)
