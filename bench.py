@@ -316,7 +316,6 @@ def cpu_baseline(case, budget_s: float):
 
     import oracle
     import workloads
-    from tests import _run
 
     cores = min(len(os.sched_getaffinity(0)), 16)
     done, wall, cpu = [], 0.0, 0.0
@@ -404,7 +403,6 @@ def main():
 
     import decode_attention_paged_07_amd as pa
     import workloads
-    from tests import _run
 
     cfg = workloads.CONFIGS[args.config]
     print(f"[bench] building {args.config} inputs", file=sys.stderr, flush=True)
@@ -417,7 +415,11 @@ def main():
                                                     cfg.head_size, case.max_seq_len, args.split)
 
     def step():
-        _run.run_hip(case, split_tokens=args.split, out=out)
+        pa.paged_attention_decode(out, case.query, case.key_cache, case.value_cache, cfg.num_kv_heads,
+                                  case.scale, case.block_tables, case.seq_lens, cfg.block_size,
+                                  case.max_seq_len, alibi_slopes=case.alibi_slopes,
+                                  kv_cache_dtype=cfg.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale,
+                                  split_tokens=args.split)
 
     for _ in range(args.warmup):
         step()
@@ -504,6 +506,7 @@ def main():
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         step()
         torch.cuda.synchronize()
+        from tests import _run
         base, done = cpu_baseline(case, args.cpu_seconds)
         worst = (0.0, 0.0)
         for seqs, ref in done:
