@@ -31,7 +31,9 @@ __all__ = [
     "pa_paged_attention_decode", "pa_paged_attention_decode_split", "pa_decode_plan",
     "pa_workspace_bytes", "pa_kv_layout", "pa_last_error", "pa_version", "pa_timing_enable",
     "pa_timing_read", "pa_timing_read_append", "pa_hbm_read_probe", "pa_hbm_gather_probe", "pa_kv_cache_append",
-    "paged_attention_decode", "kv_cache_append", "kv_cache_shapes", "LIB_PATH",
+    "paged_attention_decode", "kv_cache_append", "PA_ERR_NOMEM", "pa_pool_create", "pa_pool_destroy",
+    "pa_pool_num_free", "pa_pool_refcount", "pa_pool_append", "pa_pool_fork", "pa_pool_release",
+    "pa_copy_blocks", "BlockPool", "copy_blocks", "kv_cache_shapes", "LIB_PATH",
     "PagedAttentionError",
 ]
 
@@ -42,6 +44,7 @@ PA_ERR_DTYPE = -3
 PA_ERR_WORKSPACE = -4
 PA_ERR_ALIGN = -5
 PA_ERR_HIP = -6
+PA_ERR_NOMEM = -7
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
 PA_KV_AUTO = 0
@@ -100,8 +103,31 @@ _lib.pa_kv_cache_append.argtypes = [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, 
 _lib.pa_kv_cache_append.restype = _c_int
 
 
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_lib.pa_pool_create.argtypes = [_c_int, _c_int, ctypes.POINTER(_vp)]
+_lib.pa_pool_create.restype = _c_int
+_lib.pa_pool_destroy.argtypes = [_vp]
+_lib.pa_pool_destroy.restype = None
+_lib.pa_pool_num_free.argtypes = [_vp, ctypes.POINTER(_c_int)]
+_lib.pa_pool_num_free.restype = _c_int
+_lib.pa_pool_refcount.argtypes = [_vp, ctypes.c_int32, ctypes.POINTER(_c_int)]
+_lib.pa_pool_refcount.restype = _c_int
+_lib.pa_pool_append.argtypes = [_vp, _i32p, _c_int, _c_int, _c_int, _i32p, _i32p, ctypes.POINTER(_c_int)]
+_lib.pa_pool_append.restype = _c_int
+_lib.pa_pool_fork.argtypes = [_vp, _i32p, _c_int, _i32p, _c_int]
+_lib.pa_pool_fork.restype = _c_int
+_lib.pa_pool_release.argtypes = [_vp, _i32p, _c_int]
+_lib.pa_pool_release.restype = _c_int
+_lib.pa_copy_blocks.argtypes = [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_size, _vp]
+_lib.pa_copy_blocks.restype = _c_int
+
+
 class PagedAttentionError(RuntimeError):
     """A PA_ERR_HIP failure reported by the library."""
+
+
+class PoolExhausted(MemoryError):
+    """PA_ERR_NOMEM: the block pool has too few free blocks."""
 
 
 def _raise_for(code: int, what: str):
@@ -112,6 +138,8 @@ def _raise_for(code: int, what: str):
         raise TypeError(msg)
     if code == PA_ERR_HIP:
         raise PagedAttentionError(msg)
+    if code == PA_ERR_NOMEM:
+        raise PoolExhausted(msg)
     raise ValueError(msg)
 
 
@@ -214,6 +242,115 @@ def pa_kv_cache_append(key_cache, value_cache, key, value, num_seqs, tokens_per_
                                    num_kv_heads, head_size, num_blocks, block_tables,
                                    max_blocks_per_seq, positions, block_size, in_dtype,
                                    kv_cache_dtype, k_scale, v_scale, stream)
+
+
+def pa_pool_create(num_blocks, block_size, pool_out) -> int:
+    return _lib.pa_pool_create(num_blocks, block_size, pool_out)
+
+
+def pa_pool_destroy(pool) -> None:
+    _lib.pa_pool_destroy(pool)
+
+
+def pa_pool_num_free(pool, num_free) -> int:
+    return _lib.pa_pool_num_free(pool, num_free)
+
+
+def pa_pool_refcount(pool, block, refcount) -> int:
+    return _lib.pa_pool_refcount(pool, block, refcount)
+
+
+def pa_pool_append(pool, table_row, max_blocks, seq_len, num_new, cow_src, cow_dst, num_cow) -> int:
+    return _lib.pa_pool_append(pool, table_row, max_blocks, seq_len, num_new, cow_src, cow_dst, num_cow)
+
+
+def pa_pool_fork(pool, src_row, seq_len, dst_row, max_blocks) -> int:
+    return _lib.pa_pool_fork(pool, src_row, seq_len, dst_row, max_blocks)
+
+
+def pa_pool_release(pool, table_row, seq_len) -> int:
+    return _lib.pa_pool_release(pool, table_row, seq_len)
+
+
+def pa_copy_blocks(key_cache, value_cache, src, dst, num_pairs, num_blocks, block_bytes, stream) -> int:
+    return _lib.pa_copy_blocks(key_cache, value_cache, src, dst, num_pairs, num_blocks, block_bytes, stream)
+
+
+class BlockPool:
+    """Host block pool (include/pa_blocks.h): reference-counted physical
+    blocks, on-demand growth, sharing by fork, copy-on-write of a shared
+    partially filled block. Table rows are host int32 numpy arrays, updated in
+    place; the caller mirrors them to the device table."""
+
+    def __init__(self, num_blocks: int, block_size: int = PA_BLOCK_SIZE):
+        h = _vp()
+        _raise_for(_lib.pa_pool_create(num_blocks, block_size, ctypes.byref(h)), "pa_pool_create")
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            _lib.pa_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass
+
+    @staticmethod
+    def _row(row):
+        import numpy as np
+        if not (isinstance(row, np.ndarray) and row.dtype == np.int32 and row.ndim == 1
+                and row.flags["C_CONTIGUOUS"]):
+            raise TypeError("table rows must be contiguous 1-D int32 numpy arrays")
+        return row.ctypes.data_as(_i32p)
+
+    @property
+    def num_free(self) -> int:
+        n = _c_int()
+        _raise_for(_lib.pa_pool_num_free(self._h, ctypes.byref(n)), "pa_pool_num_free")
+        return n.value
+
+    def refcount(self, block: int) -> int:
+        n = _c_int()
+        _raise_for(_lib.pa_pool_refcount(self._h, int(block), ctypes.byref(n)), "pa_pool_refcount")
+        return n.value
+
+    def append(self, row, seq_len: int, num_new: int):
+        """Room for num_new tokens after seq_len; -> (src, dst) copy-on-write pair or None."""
+        src, dst, n = ctypes.c_int32(), ctypes.c_int32(), _c_int()
+        _raise_for(_lib.pa_pool_append(self._h, self._row(row), row.shape[0], int(seq_len), int(num_new),
+                                       ctypes.byref(src), ctypes.byref(dst), ctypes.byref(n)), "pa_pool_append")
+        return (src.value, dst.value) if n.value else None
+
+    def fork(self, src_row, seq_len: int, dst_row) -> None:
+        _raise_for(_lib.pa_pool_fork(self._h, self._row(src_row), int(seq_len), self._row(dst_row),
+                                     dst_row.shape[0]), "pa_pool_fork")
+
+    def release(self, row, seq_len: int) -> None:
+        _raise_for(_lib.pa_pool_release(self._h, self._row(row), int(seq_len)), "pa_pool_release")
+
+
+def copy_blocks(key_cache, value_cache, src, dst) -> None:
+    """Copy physical blocks src[i] -> dst[i] in both caches (device int32
+    tensors), on the current stream."""
+    dev = key_cache.device
+    _need(dev.type == "cuda", "caches must be on a GPU")
+    for name, t in (("value_cache", value_cache), ("src", src), ("dst", dst)):
+        _need(t.device == dev, f"{name} is not on the caches' device")
+    _need(src.dtype == torch.int32 and dst.dtype == torch.int32 and src.shape == dst.shape and src.dim() == 1,
+          "src and dst must be int32 vectors of one length")
+    _need(key_cache.is_contiguous() and value_cache.is_contiguous() and key_cache.shape[0] == value_cache.shape[0],
+          "caches must be contiguous with one block count")
+    block_bytes = key_cache[0].numel() * key_cache.element_size()
+    _need(value_cache[0].numel() * value_cache.element_size() == block_bytes, "K and V blocks differ in size")
+    rc = _lib.pa_copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(), src.data_ptr(), dst.data_ptr(),
+                             src.shape[0], key_cache.shape[0], block_bytes,
+                             torch.cuda.current_stream(dev).cuda_stream)
+    _raise_for(rc, "copy_blocks")
 
 
 # ---------------------------------------------------------------------------

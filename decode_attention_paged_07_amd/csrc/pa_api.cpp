@@ -290,6 +290,18 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
 
 }  // namespace
 
+// Error helpers for the other host translation units (pa_blocks.cpp).
+__attribute__((visibility("hidden"))) int pa_internal_fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+__attribute__((visibility("hidden"))) int pa_internal_ok() { return ok(); }
+
 extern "C" {
 
 int pa_kv_layout(int num_kv_heads, int head_size, int block_size, int q_dtype, int kv_cache_dtype,

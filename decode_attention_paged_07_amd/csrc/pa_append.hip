@@ -153,7 +153,33 @@ hipError_t launch_append_t(const AppendArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Copy-on-write support: pair blockIdx.x copies physical block src -> dst in
+// both caches, 16 bytes per lane, workgroups along y splitting the block.
+__global__ void __launch_bounds__(256) pa_copy_blocks_kernel(char* key_cache, char* value_cache,
+                                                             const int32_t* src, const int32_t* dst,
+                                                             int num_blocks, int64_t block_bytes) {
+  const int32_t s = src[blockIdx.x], d = dst[blockIdx.x];
+  if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) return;
+  const int64_t so = (int64_t)s * block_bytes, dof = (int64_t)d * block_bytes;
+  for (int64_t off = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 16; off < block_bytes;
+       off += (int64_t)gridDim.y * 256 * 16) {
+    *reinterpret_cast<u32x4a*>(key_cache + dof + off) = *reinterpret_cast<const u32x4a*>(key_cache + so + off);
+    *reinterpret_cast<u32x4a*>(value_cache + dof + off) = *reinterpret_cast<const u32x4a*>(value_cache + so + off);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* src, const int32_t* dst,
+                              int num_pairs, int num_blocks, size_t block_bytes, hipStream_t stream) {
+  const int64_t per_wg = 256 * 16 * 4;                    // bytes per workgroup pass
+  const int64_t gy64 = ((int64_t)block_bytes + per_wg - 1) / per_wg;
+  const unsigned gy = (unsigned)(gy64 < 1024 ? gy64 : 1024);
+  hipLaunchKernelGGL(pa_copy_blocks_kernel, dim3(num_pairs, gy), dim3(256), 0, stream,
+                     static_cast<char*>(key_cache), static_cast<char*>(value_cache), src, dst, num_blocks,
+                     (int64_t)block_bytes);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendArgs& a, int in_kind, int cache_kind, hipStream_t stream) {
   const int key = (in_kind * 10 + cache_kind) * 1000 + a.head_size;

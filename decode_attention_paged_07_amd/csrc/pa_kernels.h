@@ -95,6 +95,10 @@ struct AppendArgs {
 
 hipError_t launch_append(const AppendArgs& a, int in_kind, int cache_kind, hipStream_t stream);
 
+// Whole-block copies src[i] -> dst[i] in both caches (pa_append.hip).
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* src, const int32_t* dst,
+                              int num_pairs, int num_blocks, size_t block_bytes, hipStream_t stream);
+
 // Optional callbacks around each launch (used for event timing).
 struct LaunchHooks {
   void (*before_partition)(hipStream_t) = nullptr;

@@ -14,7 +14,8 @@ import pytest
 import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pa_decode.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -28,7 +29,7 @@ def pa():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pa_\w+)\s*\(", text, flags=re.M)))
 
@@ -38,7 +39,9 @@ def test_header_declares_the_boundary():
     for required in ("pa_paged_attention_decode", "pa_paged_attention_decode_split", "pa_decode_plan",
                      "pa_workspace_bytes", "pa_kv_layout", "pa_last_error", "pa_version",
                      "pa_timing_enable", "pa_timing_read", "pa_hbm_read_probe",
-                     "pa_hbm_gather_probe", "pa_kv_cache_append", "pa_timing_read_append"):
+                     "pa_hbm_gather_probe", "pa_kv_cache_append", "pa_timing_read_append",
+                     "pa_pool_create", "pa_pool_destroy", "pa_pool_num_free", "pa_pool_refcount",
+                     "pa_pool_append", "pa_pool_fork", "pa_pool_release", "pa_copy_blocks"):
         assert required in names
 
 

@@ -1,0 +1,151 @@
+"""GPU: block copies for copy-on-write, and a parallel-sampling run in which
+sequences share a prompt's physical blocks (host block pool + device copies +
+append kernel + decode kernel), checked against dense attention over each
+sequence's own token list."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+
+
+def host(t):
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+@pytest.mark.parametrize("dtype,x", [(torch.bfloat16, 8), (torch.uint8, 16), (torch.float32, 4)])
+def test_copy_blocks_bit_exact(dtype, x):
+    import decode_attention_paged_07_amd as pa
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3)
+    nb, hkv, d = 40, 4, 128
+    if dtype == torch.uint8:
+        kc = torch.randint(0, 256, (nb, hkv, d // x, 16, x), generator=g, device=DEV, dtype=torch.int32).to(dtype)
+        vc = torch.randint(0, 256, (nb, hkv, d, 16), generator=g, device=DEV, dtype=torch.int32).to(dtype)
+    else:
+        kc = torch.randn((nb, hkv, d // x, 16, x), generator=g, device=DEV).to(dtype)
+        vc = torch.randn((nb, hkv, d, 16), generator=g, device=DEV).to(dtype)
+    src = np.array([3, 7, 7, 39, 0, 12], np.int32)
+    dst = np.array([20, 21, 22, 5, 38, 100], np.int32)          # 100 is outside the pool: skipped
+    k0, v0 = host(kc), host(vc)
+    print(f"[case] copy_blocks {dtype}", flush=True)
+    pa.copy_blocks(kc, vc, torch.from_numpy(src).to(DEV), torch.from_numpy(dst).to(DEV))
+    torch.cuda.synchronize()
+    ek, ev = k0.copy(), v0.copy()
+    for s_, d_ in zip(src, dst):
+        if d_ < nb:
+            ek[d_] = k0[s_]
+            ev[d_] = v0[s_]
+    assert np.array_equal(host(kc).view(np.uint8), ek.view(np.uint8))
+    assert np.array_equal(host(vc).view(np.uint8), ev.view(np.uint8))
+
+
+def dense_reference(q, ks, vs, scale, kv_kind, k_scale=1.0, v_scale=1.0):
+    """softmax(scale q K^T) V per sequence from its own token list (float64).
+    q [S,H,D] bf16 bits; ks[s], vs[s]: stored rows [L, Hkv, D] (bf16 bits or fp8 codes)."""
+    qf = oracle.bf16_bits_to_f64(q)
+    out = np.zeros(qf.shape)
+    for s in range(qf.shape[0]):
+        k = oracle.decode_cache_values(ks[s], kv_kind, k_scale if kv_kind == "e4m3fn" else 1.0)
+        v = oracle.decode_cache_values(vs[s], kv_kind, v_scale if kv_kind == "e4m3fn" else 1.0)
+        h, hkv = qf.shape[1], k.shape[1]
+        for hh in range(h):
+            kv = hh // (h // hkv)
+            lg = scale * (k[:, kv, :] @ qf[s, hh])
+            w = np.exp(lg - lg.max())
+            out[s, hh] = (w / w.sum()) @ v[:, kv, :]
+    return out
+
+
+@pytest.mark.parametrize("kv", ["auto", "fp8"])
+def test_parallel_sampling_shares_the_prompt(kv):
+    """A 37-token prompt is written once; four children fork it, so all five
+    sequences map the prompt to the same physical blocks. Each then decodes
+    several tokens of its own: the first write into the shared, partially
+    filled block copies it (copy-on-write), later ones go to private blocks.
+    Every sequence must attend over exactly its own tokens."""
+    import decode_attention_paged_07_amd as pa
+    from tests import _run
+    hkv, h, d, bs, max_blocks = 2, 8, 128, 16, 8
+    pool = pa.BlockPool(48, bs)
+    fp8 = kv == "fp8"
+    ks_, vs_ = (0.011, 0.013) if fp8 else (1.0, 1.0)
+    cache_dt = torch.uint8 if fp8 else torch.bfloat16
+    x = 16 if fp8 else 8
+    kc = torch.zeros((48, hkv, d // x, bs, x), dtype=cache_dt, device=DEV)
+    vc = torch.zeros((48, hkv, d, bs), dtype=cache_dt, device=DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(21)
+    rows = {0: np.full(max_blocks, 0, np.int32)}
+    lens = {0: 0}
+    tokens = {0: ([], [])}                                     # stored K, V rows per sequence
+
+    def stored(t):
+        """What the cache will hold for bf16 rows t [n, hkv, d]: bf16 bits or fp8 codes."""
+        b = host(t)
+        if not fp8:
+            return b
+        f = oracle.bf16_bits_to_f64(b).astype(np.float32)
+        return f
+
+    def write(sid, k_rows, v_rows):
+        n = k_rows.shape[0]
+        cow = pool.append(rows[sid], lens[sid], n)
+        if cow is not None:
+            pa.copy_blocks(kc, vc, torch.tensor([cow[0]], dtype=torch.int32, device=DEV),
+                           torch.tensor([cow[1]], dtype=torch.int32, device=DEV))
+        tbl = torch.from_numpy(rows[sid][None]).to(DEV)
+        pos = torch.tensor([lens[sid]], dtype=torch.int32, device=DEV)
+        pa.kv_cache_append(kc, vc, k_rows[None], v_rows[None], tbl, pos, kv_cache_dtype=kv,
+                           k_scale=ks_, v_scale=vs_)
+        lens[sid] += n
+        if fp8:
+            kq = oracle.quantise_e4m3fn(stored(k_rows), np.float32(ks_))
+            vq = oracle.quantise_e4m3fn(stored(v_rows), np.float32(vs_))
+        else:
+            kq, vq = stored(k_rows), stored(v_rows)
+        tokens[sid][0].append(kq)
+        tokens[sid][1].append(vq)
+        return cow
+
+    def rnd(n):
+        return torch.randn((n, hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+
+    print(f"[case] parallel sampling kv={kv}", flush=True)
+    write(0, rnd(37), rnd(37))                                 # prompt: blocks 0..2, block 2 partial
+    for c in (1, 2, 3, 4):
+        rows[c] = np.zeros(max_blocks, np.int32)
+        pool.fork(rows[0], lens[0], rows[c])
+        lens[c] = lens[0]
+        tokens[c] = (list(tokens[0][0]), list(tokens[0][1]))
+    assert pool.refcount(int(rows[0][0])) == 5
+    cows = []
+    for step in range(14):                                     # decode steps, children and parent
+        for sid in (1, 2, 3, 4, 0):
+            if step < 4 + 5 * (sid % 3):                       # sequence 2 grows into a fourth block
+                cows.append(write(sid, rnd(1), rnd(1)))
+    torch.cuda.synchronize()
+    assert sum(c is not None for c in cows) == 4               # each child copied the shared tail once
+    assert pool.refcount(int(rows[0][0])) == 5                 # full prompt blocks stay shared
+    S = 5
+    table = torch.from_numpy(np.stack([rows[s] for s in range(S)])).to(DEV)
+    seq_lens = torch.tensor([lens[s] for s in range(S)], dtype=torch.int32, device=DEV)
+    q = torch.randn((S, h, d), generator=g, device=DEV).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    pa.paged_attention_decode(out, q, kc, vc, hkv, d ** -0.5, table, seq_lens, bs, max_blocks * bs,
+                              kv_cache_dtype=kv, k_scale=ks_, v_scale=vs_)
+    torch.cuda.synchronize()
+    ks = [np.concatenate(tokens[s][0]) for s in range(S)]
+    vs = [np.concatenate(tokens[s][1]) for s in range(S)]
+    ref = dense_reference(host(q), ks, vs, d ** -0.5, "e4m3fn" if fp8 else "bf16",
+                          float(np.float32(ks_)), float(np.float32(vs_)))
+    _run.compare(out, ref, "bf16", what=f"parallel sampling {kv}")
