@@ -26,8 +26,9 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0
 METRIC = "paged decode attn: seqs/s + effective KV-read HBM GB/s (% of MI355X peak)"
 CSRC = os.path.join(ROOT, "decode_attention_paged_07_amd", "csrc")
-KERNEL_SRC = {"pa_streamk_kernel": "pa_kernels.hip", "pa_split_kernel": "pa_kernels.hip",
-              "pa_append_kernel": "pa_append.hip"}
+KERNEL_SRC = {"pa_streamk_kernel": ("pa_kernels.hip", "pa_wave.h", "pa_kernels.h"),
+              "pa_split_kernel": ("pa_kernels.hip", "pa_wave.h", "pa_kernels.h"),
+              "pa_append_kernel": ("pa_append.hip", "pa_kernels.h")}
 WORKLOAD_TEXT = {
     "tiny": "tiny fp32 paged decode: 2 seqs {17,40}, 4/4 heads, D=64, bs=16, 16-block pool",
     "mha": "bf16 MHA decode: 64 seqs x 4096, 32/32 heads, D=128, bs=16, 32768-block pool",
@@ -37,13 +38,18 @@ WORKLOAD_TEXT = {
             "131072-block pool",
     "fp8": "fp8 e4m3 KV cache: 256 seqs, lognormal lens (median 4096, sigma 1, cap 16384, seed 4), "
            "64/8 heads, D=128, bs=16, bf16 q, 131072-block pool",
+    "shared": "shared-prompt decode: 16 prompts of 4096 tokens x 8 samples each (128 seqs), own lens U[1,512] "
+              "(seed 5), 64/8 heads, D=128, bs=16, bf16, 131072-block pool",
 }
 
 
 def kernel_sha(kernel: str = "pa_streamk_kernel") -> str:
-    """sha256 prefix of the source file that holds ``kernel``."""
-    with open(os.path.join(CSRC, KERNEL_SRC[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 prefix over the source files that define ``kernel``."""
+    h = hashlib.sha256()
+    for name in KERNEL_SRC[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def kv_bytes(case) -> int:
@@ -308,6 +314,64 @@ def bench_append(case, tokens, steps, warmup):
     }
 
 
+def bench_shared(case, steps, warmup):
+    """Time the shared-prefix decode and the plain decode on the same batch.
+    Logical bytes count every sequence's K/V; unique bytes count each shared
+    prompt block once per group."""
+    import numpy as np
+    import torch
+
+    import decode_attention_paged_07_amd as pa
+
+    cfg = case.cfg
+    dev = case.query.device
+    groups = pa.find_prefix_groups(case.meta.block_tables, case.meta.seq_lens)
+    g = pa.prefix_groups(groups, cfg.num_seqs, dev)
+    out = torch.empty_like(case.query)
+    stream = torch.cuda.current_stream(dev)
+
+    def shared():
+        pa.paged_attention_decode_shared(out, case.query, case.key_cache, case.value_cache, cfg.num_kv_heads,
+                                         case.scale, case.block_tables, case.seq_lens, cfg.block_size,
+                                         case.max_seq_len, g)
+
+    def plain():
+        pa.paged_attention_decode(out, case.query, case.key_cache, case.value_cache, cfg.num_kv_heads,
+                                  case.scale, case.block_tables, case.seq_lens, cfg.block_size, case.max_seq_len)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_shared = timed(shared)
+    ms_plain = timed(plain)
+    per_token = cfg.num_kv_heads * cfg.head_size * 2 * 2
+    lens = case.meta.seq_lens.astype(np.int64)
+    logical = int(lens.sum()) * per_token
+    shared_tokens = sum((len(m) - 1) * p * cfg.block_size for m, p in groups)
+    unique = logical - shared_tokens * per_token
+    return {
+        "metric": "shared-prefix paged decode: seqs/s + unique KV-read GB/s",
+        "value": round(cfg.num_seqs / (ms_shared / 1e3), 1), "unit": "seqs/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms_shared, 5), "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic", "config": {"workload": WORKLOAD_TEXT[cfg.name], "groups": len(groups),
+                                        "prefix_blocks": sorted({p for _, p in groups})},
+        "logical_kv_bytes": logical, "unique_kv_bytes": unique,
+        "unique_gbps": round(unique / (ms_shared / 1e3) / 1e9, 1),
+        "plain_decode_ms": round(ms_plain, 5),
+        "plain_decode_logical_gbps": round(logical / (ms_plain / 1e3) / 1e9, 1),
+        "speedup_vs_plain": round(ms_plain / ms_shared, 3),
+    }
+
+
 def cpu_baseline(case, budget_s: float):
     """Time the fp64 oracle on the host over the first sequences of the batch
     until about budget_s seconds of work, and check the GPU output on them."""
@@ -404,9 +468,12 @@ def main():
     import decode_attention_paged_07_amd as pa
     import workloads
 
-    cfg = workloads.CONFIGS[args.config]
+    cfg = {**workloads.CONFIGS, **workloads.EXTRA_CONFIGS}[args.config]
     print(f"[bench] building {args.config} inputs", file=sys.stderr, flush=True)
     case = workloads.make_case(cfg, device=dev)
+    if cfg.prefix_groups:
+        print(json.dumps(bench_shared(case, args.steps, args.warmup)), flush=True)
+        return
     if args.append:
         print(json.dumps(bench_append(case, args.append, args.steps, args.warmup)), flush=True)
         return

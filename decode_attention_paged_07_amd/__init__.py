@@ -33,7 +33,9 @@ __all__ = [
     "pa_timing_read", "pa_timing_read_append", "pa_hbm_read_probe", "pa_hbm_gather_probe", "pa_kv_cache_append",
     "paged_attention_decode", "kv_cache_append", "PA_ERR_NOMEM", "pa_pool_create", "pa_pool_destroy",
     "pa_pool_num_free", "pa_pool_refcount", "pa_pool_append", "pa_pool_fork", "pa_pool_release",
-    "pa_copy_blocks", "BlockPool", "copy_blocks", "kv_cache_shapes", "LIB_PATH",
+    "pa_copy_blocks", "BlockPool", "copy_blocks", "pa_shared_workspace_bytes",
+    "pa_paged_attention_decode_shared", "PrefixGroups", "prefix_groups", "find_prefix_groups",
+    "paged_attention_decode_shared", "kv_cache_shapes", "LIB_PATH",
     "PagedAttentionError",
 ]
 
@@ -118,6 +120,11 @@ _lib.pa_pool_fork.argtypes = [_vp, _i32p, _c_int, _i32p, _c_int]
 _lib.pa_pool_fork.restype = _c_int
 _lib.pa_pool_release.argtypes = [_vp, _i32p, _c_int]
 _lib.pa_pool_release.restype = _c_int
+_lib.pa_shared_workspace_bytes.argtypes = [_c_int] * 8 + [ctypes.POINTER(_c_size)]
+_lib.pa_shared_workspace_bytes.restype = _c_int
+_lib.pa_paged_attention_decode_shared.argtypes = _DECODE_ARGS[:20] + [_c_int, _vp, _vp, _c_int, _vp, _vp, _c_int,
+                                                                      _c_int, _vp, _c_size, _vp]
+_lib.pa_paged_attention_decode_shared.restype = _c_int
 _lib.pa_copy_blocks.argtypes = [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_size, _vp]
 _lib.pa_copy_blocks.restype = _c_int
 
@@ -270,6 +277,29 @@ def pa_pool_fork(pool, src_row, seq_len, dst_row, max_blocks) -> int:
 
 def pa_pool_release(pool, table_row, seq_len) -> int:
     return _lib.pa_pool_release(pool, table_row, seq_len)
+
+
+def pa_shared_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, num_groups,
+                              max_group_size, max_prefix_blocks) -> int:
+    out = _c_size()
+    rc = _lib.pa_shared_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, num_groups,
+                                        max_group_size, max_prefix_blocks, ctypes.byref(out))
+    _raise_for(rc, "pa_shared_workspace_bytes")
+    return out.value
+
+
+def pa_paged_attention_decode_shared(out, query, key_cache, value_cache, num_seqs, num_heads, num_kv_heads,
+                                     head_size, num_blocks, scale, block_tables, max_blocks_per_seq, seq_lens,
+                                     block_size, max_seq_len, alibi_slopes, q_dtype, kv_cache_dtype, k_scale,
+                                     v_scale, num_groups, group_start, group_seqs, num_members,
+                                     group_prefix_blocks, seq_prefix_blocks, max_group_size,
+                                     max_prefix_blocks, workspace, workspace_bytes, stream) -> int:
+    return _lib.pa_paged_attention_decode_shared(
+        out, query, key_cache, value_cache, num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale,
+        block_tables, max_blocks_per_seq, seq_lens, block_size, max_seq_len, alibi_slopes, q_dtype,
+        kv_cache_dtype, k_scale, v_scale, num_groups, group_start, group_seqs, num_members,
+        group_prefix_blocks, seq_prefix_blocks, max_group_size, max_prefix_blocks, workspace,
+        workspace_bytes, stream)
 
 
 def pa_copy_blocks(key_cache, value_cache, src, dst, num_pairs, num_blocks, block_bytes, stream) -> int:
@@ -519,3 +549,119 @@ def kv_cache_append(key_cache, value_cache, key, value, block_tables, positions,
         positions.data_ptr(), PA_BLOCK_SIZE, _Q_DTYPES[key.dtype], kvd,
         ks.data_ptr() if ks is not None else None, vs.data_ptr() if vs is not None else None, stream)
     _raise_for(rc, "kv_cache_append")
+
+
+class PrefixGroups:
+    """Device description of shared-prefix groups for paged_attention_decode_shared."""
+
+    def __init__(self, groups, num_seqs, device):
+        """groups: iterable of (member sequence ids, shared prefix blocks)."""
+        groups = [(list(map(int, m)), int(p)) for m, p in groups if len(m) > 0]
+        seen = set()
+        start, seqs, pref = [0], [], []
+        seq_pref = [0] * num_seqs
+        for members, p in groups:
+            if p < 0:
+                raise ValueError("prefix blocks must be >= 0")
+            for s in members:
+                if not 0 <= s < num_seqs or s in seen:
+                    raise ValueError(f"sequence {s} is out of range or in two groups")
+                seen.add(s)
+                seq_pref[s] = p
+            seqs.extend(members)
+            start.append(len(seqs))
+            pref.append(p)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.num_groups = len(groups)
+        self.group_start = torch.tensor(start, **i32)
+        self.group_seqs = torch.tensor(seqs if seqs else [0], **i32)
+        self.num_members = len(seqs)
+        self.group_prefix_blocks = torch.tensor(pref if pref else [0], **i32)
+        self.seq_prefix_blocks = torch.tensor(seq_pref, **i32)
+        self.max_group_size = max([len(m) for m, _ in groups], default=1)
+        self.max_prefix_blocks = max(pref, default=0)
+
+
+def prefix_groups(groups, num_seqs, device) -> PrefixGroups:
+    return PrefixGroups(groups, num_seqs, device)
+
+
+def find_prefix_groups(block_tables, seq_lens, block_size=PA_BLOCK_SIZE, min_prefix_blocks=1):
+    """Groups of sequences whose leading full blocks are the same physical
+    blocks, from host copies of the table and lengths: sequences are grouped
+    by their first physical block, and a group's prefix is the longest run of
+    leading table entries all members share, cut to each member's full
+    blocks. Returns [(members, prefix_blocks)] for groups of two or more."""
+    import numpy as np
+    table = np.asarray(block_tables)
+    lens = np.asarray(seq_lens)
+    by_first = {}
+    for s in range(table.shape[0]):
+        if lens[s] >= block_size:
+            by_first.setdefault(int(table[s, 0]), []).append(s)
+    out = []
+    for members in by_first.values():
+        if len(members) < 2:
+            continue
+        full = min(int(lens[s]) // block_size for s in members)
+        rows = table[members, :full]
+        same = np.all(rows == rows[0], axis=0)
+        p = int(np.argmin(same)) if not same.all() else full
+        if p >= min_prefix_blocks:
+            out.append((members, p))
+    return out
+
+
+def paged_attention_decode_shared(out, query, key_cache, value_cache, num_kv_heads, scale, block_tables,
+                                  seq_lens, block_size, max_seq_len, groups: PrefixGroups, alibi_slopes=None,
+                                  kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0, *, workspace=None) -> None:
+    """paged_attention_decode for a batch with shared-prefix groups (PrefixGroups):
+    each shared K/V block is read once per group. Same result as the plain call."""
+    if kv_cache_dtype not in _KV_NAMES:
+        raise TypeError(f"kv_cache_dtype {kv_cache_dtype!r} is not one of {sorted(_KV_NAMES)}")
+    kvd = _KV_NAMES[kv_cache_dtype]
+    if query.dtype not in _Q_DTYPES:
+        raise TypeError(f"query dtype {query.dtype} is not float32 or bfloat16")
+    dev = query.device
+    _need(dev.type == "cuda", "query must be on a GPU")
+    for name, t in (("out", out), ("key_cache", key_cache), ("value_cache", value_cache),
+                    ("block_tables", block_tables), ("seq_lens", seq_lens),
+                    ("group_start", groups.group_start), ("group_seqs", groups.group_seqs),
+                    ("group_prefix_blocks", groups.group_prefix_blocks),
+                    ("seq_prefix_blocks", groups.seq_prefix_blocks)):
+        _need(t.device == dev, f"{name} is not on the query's device")
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+    _need(query.is_contiguous() and out.dtype == query.dtype and out.shape == query.shape,
+          "out must match a contiguous query in shape and dtype")
+    num_seqs, num_heads, head_size = query.shape
+    _need(groups.seq_prefix_blocks.shape == (num_seqs,), "groups were built for another batch size")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == num_seqs,
+          "block_tables must be int32 [num_seqs, max_blocks]")
+    _need(seq_lens.dtype == torch.int32 and seq_lens.shape == (num_seqs,), "seq_lens must be int32 [num_seqs]")
+    num_blocks = key_cache.shape[0]
+    k_shape, v_shape = kv_cache_shapes(num_blocks, num_kv_heads, head_size, query.dtype, kv_cache_dtype,
+                                       block_size)
+    _need(tuple(key_cache.shape) == k_shape and tuple(value_cache.shape) == v_shape,
+          "caches are not in the library's layout")
+    slopes_ptr = None
+    if alibi_slopes is not None:
+        _need(alibi_slopes.dtype == torch.float32 and alibi_slopes.shape == (num_heads,)
+              and alibi_slopes.device == dev, "alibi_slopes must be float32 [num_heads] on the query's device")
+        slopes_ptr = alibi_slopes.data_ptr()
+    ks = _device_scalar(k_scale, dev) if kvd == PA_KV_FP8_E4M3 else None
+    vs = _device_scalar(v_scale, dev) if kvd == PA_KV_FP8_E4M3 else None
+    if workspace is None:
+        need = pa_shared_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len,
+                                         groups.num_groups, groups.max_group_size, groups.max_prefix_blocks)
+        workspace = _workspace_for(dev, need)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = _lib.pa_paged_attention_decode_shared(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), num_seqs, num_heads,
+        num_kv_heads, head_size, num_blocks, float(scale), block_tables.data_ptr(), block_tables.shape[1],
+        seq_lens.data_ptr(), block_size, int(max_seq_len), slopes_ptr, _Q_DTYPES[query.dtype], kvd,
+        ks.data_ptr() if ks is not None else None, vs.data_ptr() if vs is not None else None,
+        groups.num_groups, groups.group_start.data_ptr(), groups.group_seqs.data_ptr(), groups.num_members,
+        groups.group_prefix_blocks.data_ptr(), groups.seq_prefix_blocks.data_ptr(), groups.max_group_size,
+        groups.max_prefix_blocks, ws_ptr, ws_bytes, torch.cuda.current_stream(dev).cuda_stream)
+    _raise_for(rc, "paged_attention_decode_shared")

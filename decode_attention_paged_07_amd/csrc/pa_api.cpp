@@ -180,18 +180,19 @@ hipError_t drain_events(std::vector<std::pair<hipEvent_t, hipEvent_t>>& v, doubl
   return first_err;
 }
 
-int decode_impl(void* out, const void* query, const void* key_cache, const void* value_cache,
-                int num_seqs, int num_heads, int num_kv_heads, int head_size, int num_blocks,
-                float scale, const int32_t* block_tables, int max_blocks_per_seq,
-                const int32_t* seq_lens, int block_size, int max_seq_len,
-                const float* alibi_slopes, int q_dtype, int kv_cache_dtype, const float* k_scale,
-                const float* v_scale, void* workspace, size_t workspace_bytes, void* stream,
-                int split_tokens) {
+// Host-side checks shared by the decode entry points; everything before the
+// launch plan. Returns PA_OK, or an error code (nothing launched).
+int check_decode_args(void* out, const void* query, const void* key_cache, const void* value_cache,
+                      int num_seqs, int num_heads, int num_kv_heads, int head_size, int num_blocks,
+                      float scale, const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* seq_lens, int block_size, int max_seq_len,
+                      const float* alibi_slopes, int q_dtype, int kv_cache_dtype, const float* k_scale,
+                      const float* v_scale, int split_tokens) {
   int rc = check_plan_args(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, split_tokens);
   if (rc) return rc;
   if ((rc = check_dtypes(q_dtype, kv_cache_dtype))) return rc;
   if (block_size != PA_BLOCK_SIZE) return fail(PA_ERR_SHAPE, "block_size %d is not %d", block_size, PA_BLOCK_SIZE);
-  if (num_seqs == 0) return ok();
+  if (num_seqs == 0) return PA_OK;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens)
     return fail(PA_ERR_NULL, "out, query, key_cache, value_cache, block_tables and seq_lens must be non-NULL");
   if (num_blocks <= 0) return fail(PA_ERR_SHAPE, "num_blocks %d must be positive", num_blocks);
@@ -209,19 +210,18 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
   const size_t qo_bytes = (size_t)num_seqs * num_heads * head_size * ebq;
   const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), q0 = reinterpret_cast<uintptr_t>(query);
   if (o0 < q0 + qo_bytes && q0 < o0 + qo_bytes) return fail(PA_ERR_SHAPE, "out overlaps query");
+  return PA_OK;
+}
 
-  const Plan plan = make_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, split_tokens);
-  if (plan.bytes) {
-    if (!workspace) return fail(PA_ERR_WORKSPACE, "this plan needs a workspace of %zu bytes", plan.bytes);
-    if (workspace_bytes < plan.bytes)
-      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu this plan needs",
-                  workspace_bytes, plan.bytes);
-    if (!aligned(workspace, 16)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
-  }
-
+// The launch-independent fields of DecodeArgs; returns the kernel kind.
+int fill_decode_args(pa::DecodeArgs& a, void* out, const void* query, const void* key_cache,
+                     const void* value_cache, int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                     int num_blocks, float scale, const int32_t* block_tables, int max_blocks_per_seq,
+                     const int32_t* seq_lens, int block_size, int max_seq_len, const float* alibi_slopes,
+                     int q_dtype, int kv_cache_dtype, const float* k_scale, const float* v_scale) {
   const int eb = elem_bytes_of(q_dtype, kv_cache_dtype);
   const int64_t tile = (int64_t)head_size * block_size * eb;   // one (block, kv head) tile
-  pa::DecodeArgs a{};
+  a = pa::DecodeArgs{};
   a.out = out;
   a.query = query;
   a.key_cache = key_cache;
@@ -232,18 +232,6 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
   const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
   a.k_scale = fp8 ? k_scale : nullptr;
   a.v_scale = fp8 ? v_scale : nullptr;
-  char* ws = static_cast<char*>(workspace);
-  if (plan.bytes && !plan.streamk) {
-    a.tmp_out = reinterpret_cast<float*>(ws + plan.off[0]);
-    a.max_logits = reinterpret_cast<float*>(ws + plan.off[1]);
-    a.exp_sums = reinterpret_cast<float*>(ws + plan.off[2]);
-  }
-  if (plan.streamk) {
-    a.seg_out = reinterpret_cast<float*>(ws + plan.off[0]);
-    a.seg_max = reinterpret_cast<float*>(ws + plan.off[1]);
-    a.seg_sum = reinterpret_cast<float*>(ws + plan.off[2]);
-    a.seg_meta = reinterpret_cast<int32_t*>(ws + plan.off[3]);
-  }
   a.k_block_stride_bytes = tile * num_kv_heads;
   a.k_head_stride_bytes = tile;
   a.v_block_stride_bytes = tile * num_kv_heads;
@@ -257,9 +245,53 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_seq_len = max_seq_len;
+  return fp8 ? pa::KIND_FP8 : (q_dtype == PA_DTYPE_F32 ? pa::KIND_F32 : pa::KIND_BF16);
+}
+
+int check_workspace(const void* workspace, size_t workspace_bytes, size_t need) {
+  if (!need) return PA_OK;
+  if (!workspace) return fail(PA_ERR_WORKSPACE, "this plan needs a workspace of %zu bytes", need);
+  if (workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu this plan needs", workspace_bytes,
+                need);
+  if (!aligned(workspace, 16)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return PA_OK;
+}
+
+int decode_impl(void* out, const void* query, const void* key_cache, const void* value_cache,
+                int num_seqs, int num_heads, int num_kv_heads, int head_size, int num_blocks,
+                float scale, const int32_t* block_tables, int max_blocks_per_seq,
+                const int32_t* seq_lens, int block_size, int max_seq_len,
+                const float* alibi_slopes, int q_dtype, int kv_cache_dtype, const float* k_scale,
+                const float* v_scale, void* workspace, size_t workspace_bytes, void* stream,
+                int split_tokens) {
+  int rc = check_decode_args(out, query, key_cache, value_cache, num_seqs, num_heads, num_kv_heads, head_size,
+                             num_blocks, scale, block_tables, max_blocks_per_seq, seq_lens, block_size,
+                             max_seq_len, alibi_slopes, q_dtype, kv_cache_dtype, k_scale, v_scale, split_tokens);
+  if (rc) return rc;
+  if (num_seqs == 0) return ok();
+  const Plan plan = make_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, split_tokens);
+  if ((rc = check_workspace(workspace, workspace_bytes, plan.bytes))) return rc;
+
+  pa::DecodeArgs a;
+  const int kind = fill_decode_args(a, out, query, key_cache, value_cache, num_seqs, num_heads, num_kv_heads,
+                                    head_size, num_blocks, scale, block_tables, max_blocks_per_seq, seq_lens,
+                                    block_size, max_seq_len, alibi_slopes, q_dtype, kv_cache_dtype, k_scale,
+                                    v_scale);
+  char* ws = static_cast<char*>(workspace);
+  if (plan.bytes && !plan.streamk) {
+    a.tmp_out = reinterpret_cast<float*>(ws + plan.off[0]);
+    a.max_logits = reinterpret_cast<float*>(ws + plan.off[1]);
+    a.exp_sums = reinterpret_cast<float*>(ws + plan.off[2]);
+  }
+  if (plan.streamk) {
+    a.seg_out = reinterpret_cast<float*>(ws + plan.off[0]);
+    a.seg_max = reinterpret_cast<float*>(ws + plan.off[1]);
+    a.seg_sum = reinterpret_cast<float*>(ws + plan.off[2]);
+    a.seg_meta = reinterpret_cast<int32_t*>(ws + plan.off[3]);
+  }
   a.split_tokens = plan.split_tokens;
   a.num_splits = plan.num_splits;
-  const int kind = fp8 ? pa::KIND_FP8 : (q_dtype == PA_DTYPE_F32 ? pa::KIND_F32 : pa::KIND_BF16);
   if (plan.streamk) {
     // Persistent waves per compute unit, measured per cache type: the bf16
     // path streams best with one wave per SIMD, the fp8 path needs more waves
@@ -286,6 +318,70 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
   hipError_t err = pa::launch_decode(a, kind, static_cast<hipStream_t>(stream), hooks);
   if (err != hipSuccess) return fail(PA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return ok();
+}
+
+// ---- shared-prefix decode -------------------------------------------------------
+
+constexpr int kSharedSuffixSplit = 512;     // tokens per suffix split
+constexpr int kSharedTargetWaves = 1024;    // prefix waves the split count aims for (one per SIMD)
+constexpr int kSharedMinSplitBlocks = 32;   // fewest prefix blocks per wave
+
+struct SharedPlan {
+  int column_tiles = 1;
+  int members_per_chunk = 1;
+  int max_chunks = 0;
+  int prefix_split_blocks = 1;
+  int max_prefix_splits = 0;
+  int num_splits = 1;                       // suffix splits
+  size_t off[6] = {0, 0, 0, 0, 0, 0};
+  size_t bytes = 0;
+};
+
+int check_shared_plan_args(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_seq_len,
+                           int num_groups, int max_group_size, int max_prefix_blocks) {
+  int rc = check_plan_args(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, 0);
+  if (rc) return rc;
+  if (num_groups < 0) return fail(PA_ERR_SHAPE, "num_groups %d < 0", num_groups);
+  if (num_groups > 0 && max_group_size < 1)
+    return fail(PA_ERR_SHAPE, "max_group_size %d must be positive with groups", max_group_size);
+  if (max_prefix_blocks < 0) return fail(PA_ERR_SHAPE, "max_prefix_blocks %d < 0", max_prefix_blocks);
+  if ((int64_t)max_prefix_blocks * PA_BLOCK_SIZE > max_seq_len)
+    return fail(PA_ERR_SHAPE, "max_prefix_blocks %d exceeds max_seq_len %d / %d", max_prefix_blocks, max_seq_len,
+                PA_BLOCK_SIZE);
+  return PA_OK;
+}
+
+// max_tiles: the kernel kind's column-tile limit (pa::max_column_tiles); the
+// workspace for 4 bounds that of every smaller limit (fewer tiles, more
+// member chunks, fewer prefix splits).
+SharedPlan make_shared_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_seq_len,
+                            int num_groups, int max_group_size, int max_prefix_blocks, int max_tiles = 4) {
+  SharedPlan p;
+  const int group = num_heads / num_kv_heads;
+  const int64_t cols = (int64_t)std::max(1, max_group_size) * group;
+  p.column_tiles = std::min(max_tiles, cols <= 16 ? 1 : (cols <= 32 ? 2 : 4));
+  p.members_per_chunk = std::max(1, 16 * p.column_tiles / group);
+  p.max_chunks = num_groups > 0 ? (std::max(1, max_group_size) + p.members_per_chunk - 1) / p.members_per_chunk : 0;
+  if (num_groups > 0 && max_prefix_blocks > 0) {
+    const int64_t base = (int64_t)num_groups * p.max_chunks * num_kv_heads;
+    int64_t splits = std::max<int64_t>(1, (kSharedTargetWaves + base - 1) / base);
+    splits = std::min<int64_t>(splits, std::max(1, (max_prefix_blocks + kSharedMinSplitBlocks - 1) /
+                                                        kSharedMinSplitBlocks));
+    p.prefix_split_blocks = (int)((max_prefix_blocks + splits - 1) / splits);
+    p.max_prefix_splits = (max_prefix_blocks + p.prefix_split_blocks - 1) / p.prefix_split_blocks;
+  }
+  p.num_splits = std::max(1, (max_seq_len + kSharedSuffixSplit - 1) / kSharedSuffixSplit);
+  const size_t rows_s = (size_t)num_seqs * num_heads * p.num_splits;
+  const size_t rows_p = (size_t)num_seqs * num_heads * p.max_prefix_splits;
+  size_t o = 0;
+  p.off[0] = o; o += round_up(rows_s * head_size * sizeof(float), 256);
+  p.off[1] = o; o += round_up(rows_s * sizeof(float), 256);
+  p.off[2] = o; o += round_up(rows_s * sizeof(float), 256);
+  p.off[3] = o; o += round_up(rows_p * head_size * sizeof(float), 256);
+  p.off[4] = o; o += round_up(rows_p * sizeof(float), 256);
+  p.off[5] = o; o += round_up(rows_p * sizeof(float), 256);
+  p.bytes = o;
+  return p;
 }
 
 }  // namespace
@@ -373,6 +469,80 @@ int pa_paged_attention_decode_split(void* out, const void* query, const void* ke
                      num_blocks, scale, block_tables, max_blocks_per_seq, seq_lens, block_size, max_seq_len,
                      alibi_slopes, q_dtype, kv_cache_dtype, k_scale, v_scale, workspace, workspace_bytes,
                      stream, split_tokens);
+}
+
+int pa_shared_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_seq_len,
+                              int num_groups, int max_group_size, int max_prefix_blocks, size_t* bytes) {
+  if (!bytes) return fail(PA_ERR_NULL, "bytes is NULL");
+  int rc = check_shared_plan_args(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, num_groups,
+                                  max_group_size, max_prefix_blocks);
+  if (rc) return rc;
+  *bytes = make_shared_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, num_groups,
+                            max_group_size, max_prefix_blocks)
+               .bytes;
+  return ok();
+}
+
+int pa_paged_attention_decode_shared(void* out, const void* query, const void* key_cache,
+                                     const void* value_cache, int num_seqs, int num_heads, int num_kv_heads,
+                                     int head_size, int num_blocks, float scale, const int32_t* block_tables,
+                                     int max_blocks_per_seq, const int32_t* seq_lens, int block_size,
+                                     int max_seq_len, const float* alibi_slopes, int q_dtype,
+                                     int kv_cache_dtype, const float* k_scale, const float* v_scale,
+                                     int num_groups, const int32_t* group_start, const int32_t* group_seqs,
+                                     int num_members, const int32_t* group_prefix_blocks,
+                                     const int32_t* seq_prefix_blocks, int max_group_size,
+                                     int max_prefix_blocks, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  int rc = check_decode_args(out, query, key_cache, value_cache, num_seqs, num_heads, num_kv_heads, head_size,
+                             num_blocks, scale, block_tables, max_blocks_per_seq, seq_lens, block_size,
+                             max_seq_len, alibi_slopes, q_dtype, kv_cache_dtype, k_scale, v_scale, 0);
+  if (rc) return rc;
+  if ((rc = check_shared_plan_args(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, num_groups,
+                                   max_group_size, max_prefix_blocks)))
+    return rc;
+  if (num_seqs == 0) return ok();
+  if (!seq_prefix_blocks) return fail(PA_ERR_NULL, "seq_prefix_blocks must be non-NULL");
+  if (num_groups > 0 && (!group_start || !group_prefix_blocks || (num_members > 0 && !group_seqs)))
+    return fail(PA_ERR_NULL, "group_start, group_seqs and group_prefix_blocks must be non-NULL with groups");
+  if (num_members < 0) return fail(PA_ERR_SHAPE, "num_members %d < 0", num_members);
+  if (!aligned(seq_prefix_blocks, 4) || (group_start && !aligned(group_start, 4)) ||
+      (group_seqs && !aligned(group_seqs, 4)) || (group_prefix_blocks && !aligned(group_prefix_blocks, 4)))
+    return fail(PA_ERR_ALIGN, "group arrays must be 4-byte aligned");
+  const int max_tiles = pa::max_column_tiles(q_dtype == PA_DTYPE_F32 ? 4 : 2, head_size);
+  const SharedPlan plan = make_shared_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, num_groups,
+                                           max_group_size, max_prefix_blocks, max_tiles);
+  if (plan.max_prefix_splits > 65535) return fail(PA_ERR_SHAPE, "too many prefix splits");
+  if ((rc = check_workspace(workspace, workspace_bytes, plan.bytes))) return rc;
+
+  pa::SharedArgs sa{};
+  const int kind = fill_decode_args(sa.d, out, query, key_cache, value_cache, num_seqs, num_heads, num_kv_heads,
+                                    head_size, num_blocks, scale, block_tables, max_blocks_per_seq, seq_lens,
+                                    block_size, max_seq_len, alibi_slopes, q_dtype, kv_cache_dtype, k_scale,
+                                    v_scale);
+  char* ws = static_cast<char*>(workspace);
+  sa.d.tmp_out = reinterpret_cast<float*>(ws + plan.off[0]);
+  sa.d.max_logits = reinterpret_cast<float*>(ws + plan.off[1]);
+  sa.d.exp_sums = reinterpret_cast<float*>(ws + plan.off[2]);
+  sa.d.split_tokens = kSharedSuffixSplit;
+  sa.d.num_splits = plan.num_splits;
+  sa.d.first_block = seq_prefix_blocks;
+  sa.d.max_first_block = plan.max_prefix_splits * plan.prefix_split_blocks;
+  sa.group_start = group_start;
+  sa.group_seqs = group_seqs;
+  sa.num_members = num_members;
+  sa.group_prefix_blocks = group_prefix_blocks;
+  sa.num_groups = num_groups;
+  sa.max_chunks = plan.max_chunks;
+  sa.members_per_chunk = plan.members_per_chunk;
+  sa.prefix_split_blocks = plan.prefix_split_blocks;
+  sa.max_prefix_splits = plan.max_prefix_splits;
+  sa.pre_out = reinterpret_cast<float*>(ws + plan.off[3]);
+  sa.pre_max = reinterpret_cast<float*>(ws + plan.off[4]);
+  sa.pre_sum = reinterpret_cast<float*>(ws + plan.off[5]);
+  hipError_t err = pa::launch_shared(sa, kind, plan.column_tiles, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return ok();
 }
 
 int pa_hbm_read_probe(const void* buf, size_t bytes, int workgroups, unsigned* sink, void* stream) {

@@ -73,7 +73,41 @@ struct DecodeArgs {
   int split_tokens;
   int num_splits;
   int streamk_workgroups;      // > 0 selects the stream-K scheduler
+  // split grid only: per-sequence count of leading blocks handled elsewhere
+  // (a shared prefix), clamped to [0, min(L / 16, max_first_block)];
+  // nullable. When set, every split writes partials and no reduce runs.
+  const int32_t* first_block;
+  int max_first_block;
 };
+
+// Shared-prefix decode (pa_shared.hip): the members of a group map their
+// first prefix blocks to the same physical blocks; the prefix is read once
+// per group (all members' query heads as MFMA columns), the rest per
+// sequence through the split grid with first_block, and a merge combines the
+// partials.
+struct SharedArgs {
+  DecodeArgs d;                        // split plan over the suffixes (tmp_out, max_logits, exp_sums)
+  const int32_t* group_start;          // [num_groups + 1] offsets into group_seqs
+  const int32_t* group_seqs;           // [num_members] member sequence ids
+  int num_members;
+  const int32_t* group_prefix_blocks;  // [num_groups] shared full blocks
+  int num_groups;
+  int max_chunks;                      // chunks of members per group in the grid
+  int members_per_chunk;
+  int prefix_split_blocks;             // prefix blocks per wave
+  int max_prefix_splits;
+  float* pre_out;                      // [S][H][max_prefix_splits][D]
+  float* pre_max;                      // [S][H][max_prefix_splits] natural-log units
+  float* pre_sum;                      // [S][H][max_prefix_splits]
+};
+
+// Most 16-column query tiles a prefix wave carries: four, except with fp32
+// queries at head_size 128, whose operands would not fit in registers.
+constexpr int max_column_tiles(int q_elem_bytes, int head_size) {
+  return (q_elem_bytes == 4 && head_size == 128) ? 2 : 4;
+}
+
+hipError_t launch_shared(const SharedArgs& a, int kind, int column_tiles, hipStream_t stream);
 
 // Arguments of the KV-cache append kernel (pa_append.hip).
 struct AppendArgs {

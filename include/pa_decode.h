@@ -235,6 +235,46 @@ int pa_kv_cache_append(void* key_cache, void* value_cache, const void* key, cons
                        int kv_cache_dtype, const float* k_scale, const float* v_scale,
                        void* stream);
 
+/*
+ * Shared-prefix decode: the same result as pa_paged_attention_decode, for a
+ * batch in which groups of sequences map their first blocks to the same
+ * physical blocks (a forked prompt: parallel sampling, beam search, a shared
+ * system prompt; "vLLM 0.25.0 解读" §1 on sharing). Each shared K/V tile is
+ * read once per group: the query heads of up to 16*T/G members (T = 4 tiles
+ * of 16 MFMA columns; 2 for fp32 queries at head_size 128) are multiplied
+ * against it together. Each sequence's remaining blocks are processed on
+ * their own and a log-sum-exp merge combines the two parts.
+ * Arguments as for pa_paged_attention_decode, plus (device int32 arrays):
+ *   num_groups >= 0; group_start [num_groups + 1]: members of group g are
+ *   group_seqs[group_start[g] .. group_start[g+1]) (num_members entries in
+ *   all; each sequence in at most one group); group_prefix_blocks
+ *   [num_groups]: P_g, the number of leading logical blocks all members map
+ *   to the same physical blocks, each member holding at least P_g * 16
+ *   tokens; seq_prefix_blocks [num_seqs]: P_g of the sequence's group, 0 if
+ *   it is in none. max_group_size >= the largest group (host), and
+ *   max_prefix_blocks >= every P_g (host; P_g beyond it are cut to it).
+ *   Sequences in no group are computed as by the plain call.
+ *   workspace: >= pa_shared_workspace_bytes(...) bytes.
+ * Device values that break this contract give unspecified output but no
+ * access outside the arrays (ids and offsets are clamped).
+ */
+int pa_shared_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                              int max_seq_len, int num_groups, int max_group_size,
+                              int max_prefix_blocks, size_t* bytes);
+
+int pa_paged_attention_decode_shared(void* out, const void* query, const void* key_cache,
+                                     const void* value_cache, int num_seqs, int num_heads,
+                                     int num_kv_heads, int head_size, int num_blocks, float scale,
+                                     const int32_t* block_tables, int max_blocks_per_seq,
+                                     const int32_t* seq_lens, int block_size, int max_seq_len,
+                                     const float* alibi_slopes, int q_dtype, int kv_cache_dtype,
+                                     const float* k_scale, const float* v_scale, int num_groups,
+                                     const int32_t* group_start, const int32_t* group_seqs,
+                                     int num_members, const int32_t* group_prefix_blocks,
+                                     const int32_t* seq_prefix_blocks, int max_group_size,
+                                     int max_prefix_blocks, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
 /* Text describing the last error returned on the calling thread ("" if none). */
 const char* pa_last_error(void);
 

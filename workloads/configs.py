@@ -33,6 +33,11 @@ class DecodeConfig:
                           #         ("lognormal", median, sigma, cap)
     alibi: bool
     seed: int
+    # (group_size, prefix_tokens): consecutive sequences in groups of
+    # group_size share the physical blocks of a prefix_tokens-token prompt
+    # (a multiple of block_size); their lengths are prefix_tokens plus the
+    # drawn length. None: no sharing.
+    prefix_groups: tuple | None = None
 
     @property
     def group(self) -> int:
@@ -53,4 +58,11 @@ LONG = DecodeConfig("long", 8, 32, 8, 128, 16, 128 * 1024, "bf16", "auto",
 FP8 = DecodeConfig("fp8", 256, 64, 8, 128, 16, 128 * 1024, "bf16", "fp8_e4m3",
                    ("lognormal", 4096, 1.0, 16384), False, 4)
 
+# Shared-prompt decode (not one of the five reference workloads): parallel
+# sampling with n = 8 over 16 prompts of 4096 tokens, each sample with its
+# own U[1, 512] generated tokens; otherwise the GQA workload's shapes.
+SHARED = DecodeConfig("shared", 128, 64, 8, 128, 16, 128 * 1024, "bf16", "auto",
+                      ("uniform", 1, 512), False, 5, prefix_groups=(8, 4096))
+
 CONFIGS = {c.name: c for c in (TINY, MHA, GQA, LONG, FP8)}
+EXTRA_CONFIGS = {c.name: c for c in (SHARED,)}

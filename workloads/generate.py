@@ -9,10 +9,14 @@ Recipe (stated in full so both sides can be regenerated anywhere):
   * metadata from numpy.random.default_rng(seed), in this order:
       1. sequence lengths: "uniform" -> rng.integers(lo, hi + 1, S);
          "lognormal" -> rint(rng.lognormal(ln(median), sigma, S)) clipped to
-         [1, cap]; "const"/"fixed" draw nothing;
+         [1, cap]; "const"/"fixed" draw nothing; with prefix groups
+         (group_size, prefix_tokens) every length gets prefix_tokens added;
       2. pool = rng.permutation(pool_blocks); sequence s takes the next
          ceil(L_s / block_size) entries, in sequence order;
-      3. table entries past a sequence's last block hold ``pad_id``.
+      3. table entries past a sequence's last block hold ``pad_id``; with
+         prefix groups, members after a group's first sequence take that
+         sequence's first prefix_tokens / block_size entries instead of
+         drawing their own.
   * values from torch.Generator(device).manual_seed(seed), in this order:
     query, K pool, V pool, each torch.randn in float32, then cast with
     round-to-nearest-even to bfloat16 when the dtype is bf16. For the fp8
@@ -99,6 +103,11 @@ def make_metadata(cfg: DecodeConfig, seed: int | None = None, *,
         lens = np.asarray(seq_lens, dtype=np.int64)
         if lens.shape != (cfg.num_seqs,):
             raise ValueError("seq_lens must have num_seqs entries")
+    group_size, prefix_tokens = cfg.prefix_groups if cfg.prefix_groups else (1, 0)
+    if prefix_tokens % cfg.block_size:
+        raise ValueError("a shared prefix must be whole blocks")
+    if prefix_tokens and seq_lens is None:
+        lens = lens + prefix_tokens
     longest = int(lens.max()) if lens.size else 0
     msl = longest if max_seq_len is None else int(max_seq_len)
     if msl < longest:
@@ -109,10 +118,14 @@ def make_metadata(cfg: DecodeConfig, seed: int | None = None, *,
     perm = rng.permutation(cfg.pool_blocks).astype(np.int64)
     table = np.full((cfg.num_seqs, max_blocks), pad_id, dtype=np.int64)
     pos = 0
+    prefix_blocks = prefix_tokens // bs
     for s in range(cfg.num_seqs):
         nb = need[s]
         shared = min(share_prefix_blocks, nb, need[0]) if s > 0 else 0
-        if shared:
+        if s % group_size and prefix_blocks:                 # a later member of a prompt group
+            shared = min(prefix_blocks, nb)
+            table[s, :shared] = table[s - s % group_size, :shared]
+        elif shared:
             table[s, :shared] = table[0, :shared]
         own = nb - shared
         if pos + own > cfg.pool_blocks:
