@@ -38,6 +38,8 @@ WORKLOAD_TEXT = {
             "131072-block pool",
     "fp8": "fp8 e4m3 KV cache: 256 seqs, lognormal lens (median 4096, sigma 1, cap 16384, seed 4), "
            "64/8 heads, D=128, bs=16, bf16 q, 131072-block pool",
+    "gqa32": "bf16 GQA decode with 32-token blocks: 128 seqs, lens U[1,8192] (seed 2), 64/8 heads, D=128, "
+             "bs=32, 65536-block pool",
     "shared": "shared-prompt decode: 16 prompts of 4096 tokens x 8 samples each (128 seqs), own lens U[1,512] "
               "(seed 5), 64/8 heads, D=128, bs=16, bf16, 131072-block pool",
 }

@@ -120,7 +120,7 @@ _lib.pa_pool_fork.argtypes = [_vp, _i32p, _c_int, _i32p, _c_int]
 _lib.pa_pool_fork.restype = _c_int
 _lib.pa_pool_release.argtypes = [_vp, _i32p, _c_int]
 _lib.pa_pool_release.restype = _c_int
-_lib.pa_shared_workspace_bytes.argtypes = [_c_int] * 8 + [ctypes.POINTER(_c_size)]
+_lib.pa_shared_workspace_bytes.argtypes = [_c_int] * 9 + [ctypes.POINTER(_c_size)]
 _lib.pa_shared_workspace_bytes.restype = _c_int
 _lib.pa_paged_attention_decode_shared.argtypes = _DECODE_ARGS[:20] + [_c_int, _vp, _vp, _c_int, _vp, _vp, _c_int,
                                                                       _c_int, _vp, _c_size, _vp]
@@ -279,11 +279,11 @@ def pa_pool_release(pool, table_row, seq_len) -> int:
     return _lib.pa_pool_release(pool, table_row, seq_len)
 
 
-def pa_shared_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, num_groups,
-                              max_group_size, max_prefix_blocks) -> int:
+def pa_shared_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, block_size, max_seq_len,
+                              num_groups, max_group_size, max_prefix_blocks) -> int:
     out = _c_size()
-    rc = _lib.pa_shared_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, num_groups,
-                                        max_group_size, max_prefix_blocks, ctypes.byref(out))
+    rc = _lib.pa_shared_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, block_size, max_seq_len,
+                                        num_groups, max_group_size, max_prefix_blocks, ctypes.byref(out))
     _raise_for(rc, "pa_shared_workspace_bytes")
     return out.value
 
@@ -498,7 +498,7 @@ def paged_attention_decode(out, query, key_cache, value_cache, num_kv_heads, sca
 
 
 def kv_cache_append(key_cache, value_cache, key, value, block_tables, positions,
-                    kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0) -> None:
+                    kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0, block_size=None) -> None:
     """Store new tokens' K/V rows in the paged cache (in place, current stream).
 
     key, value: [num_seqs, num_kv_heads, head_size] (one token per sequence) or
@@ -508,6 +508,8 @@ def kv_cache_append(key_cache, value_cache, key, value, block_tables, positions,
     [num_seqs], negative = skip. Caches in the library's layout
     (``kv_cache_shapes``): the input dtype for "auto", uint8 / float8_e4m3fn
     codes for "fp8" / "fp8_e4m3" (value / scale rounded to the nearest code).
+    block_size: tokens per cache block (16 or 32); None takes it from the
+    value cache's last dimension.
     """
     if kv_cache_dtype not in _KV_NAMES:
         raise TypeError(f"kv_cache_dtype {kv_cache_dtype!r} is not one of {sorted(_KV_NAMES)}")
@@ -535,9 +537,13 @@ def kv_cache_append(key_cache, value_cache, key, value, block_tables, positions,
     elif key_cache.dtype not in (torch.uint8, torch.float8_e4m3fn) or value_cache.dtype != key_cache.dtype:
         raise TypeError("the fp8 cache must be uint8 or float8_e4m3fn codes")
     num_blocks = key_cache.shape[0]
+    if block_size is None:
+        _need(value_cache.dim() == 4, "value_cache must be [num_blocks, num_kv_heads, head_size, block_size]")
+        block_size = int(value_cache.shape[-1])
     # the layout depends only on the cache element type (fp8 codes for any input type)
     layout_dtype = key.dtype if kvd == PA_KV_AUTO else torch.bfloat16
-    k_shape, v_shape = kv_cache_shapes(num_blocks, num_kv_heads, head_size, layout_dtype, kv_cache_dtype)
+    k_shape, v_shape = kv_cache_shapes(num_blocks, num_kv_heads, head_size, layout_dtype, kv_cache_dtype,
+                                       block_size)
     _need(tuple(key_cache.shape) == k_shape, f"key_cache shape {tuple(key_cache.shape)} != {k_shape}")
     _need(tuple(value_cache.shape) == v_shape, f"value_cache shape {tuple(value_cache.shape)} != {v_shape}")
     ks = _device_scalar(k_scale, dev) if kvd == PA_KV_FP8_E4M3 else None
@@ -546,7 +552,7 @@ def kv_cache_append(key_cache, value_cache, key, value, block_tables, positions,
     rc = _lib.pa_kv_cache_append(
         key_cache.data_ptr(), value_cache.data_ptr(), key.data_ptr(), value.data_ptr(), num_seqs,
         tokens, num_kv_heads, head_size, num_blocks, block_tables.data_ptr(), block_tables.shape[1],
-        positions.data_ptr(), PA_BLOCK_SIZE, _Q_DTYPES[key.dtype], kvd,
+        positions.data_ptr(), int(block_size), _Q_DTYPES[key.dtype], kvd,
         ks.data_ptr() if ks is not None else None, vs.data_ptr() if vs is not None else None, stream)
     _raise_for(rc, "kv_cache_append")
 
@@ -651,7 +657,7 @@ def paged_attention_decode_shared(out, query, key_cache, value_cache, num_kv_hea
     ks = _device_scalar(k_scale, dev) if kvd == PA_KV_FP8_E4M3 else None
     vs = _device_scalar(v_scale, dev) if kvd == PA_KV_FP8_E4M3 else None
     if workspace is None:
-        need = pa_shared_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len,
+        need = pa_shared_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, block_size, max_seq_len,
                                          groups.num_groups, groups.max_group_size, groups.max_prefix_blocks)
         workspace = _workspace_for(dev, need)
     ws_ptr = workspace.data_ptr() if workspace is not None else None

@@ -42,6 +42,21 @@ int elem_bytes_of(int q_dtype, int kv_cache_dtype) {
   return q_dtype == PA_DTYPE_F32 ? 4 : 2;
 }
 
+// Head sizes 32, 64 and 128 (the pages' kernel instantiations list these
+// among others).
+int check_head_size(int head_size) {
+  if (head_size != 32 && head_size != 64 && head_size != 128)
+    return fail(PA_ERR_SHAPE, "head_size %d is not 32, 64 or 128", head_size);
+  return PA_OK;
+}
+
+// Cache blocks of 16 or 32 tokens; the kernels walk either as 16-token
+// sub-blocks.
+int check_block_size(int block_size) {
+  if (block_size != 16 && block_size != 32) return fail(PA_ERR_SHAPE, "block_size %d is not 16 or 32", block_size);
+  return PA_OK;
+}
+
 int check_dtypes(int q_dtype, int kv_cache_dtype) {
   if (q_dtype != PA_DTYPE_F32 && q_dtype != PA_DTYPE_BF16)
     return fail(PA_ERR_DTYPE, "q_dtype %d is not PA_DTYPE_F32 or PA_DTYPE_BF16", q_dtype);
@@ -116,7 +131,8 @@ int check_plan_args(int num_seqs, int num_heads, int num_kv_heads, int head_size
     return fail(PA_ERR_SHAPE, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
   if (num_heads / num_kv_heads > PA_MAX_GROUP)
     return fail(PA_ERR_SHAPE, "query heads per kv head %d exceeds %d", num_heads / num_kv_heads, PA_MAX_GROUP);
-  if (head_size != 64 && head_size != 128) return fail(PA_ERR_SHAPE, "head_size %d is not 64 or 128", head_size);
+  int rc = check_head_size(head_size);
+  if (rc) return rc;
   if (max_seq_len < 0) return fail(PA_ERR_SHAPE, "max_seq_len %d < 0", max_seq_len);
   if (split_tokens < 0 || split_tokens % PA_PARTITION_SIZE)
     return fail(PA_ERR_SHAPE, "split_tokens %d is not 0 or a positive multiple of %d", split_tokens,
@@ -191,7 +207,7 @@ int check_decode_args(void* out, const void* query, const void* key_cache, const
   int rc = check_plan_args(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, split_tokens);
   if (rc) return rc;
   if ((rc = check_dtypes(q_dtype, kv_cache_dtype))) return rc;
-  if (block_size != PA_BLOCK_SIZE) return fail(PA_ERR_SHAPE, "block_size %d is not %d", block_size, PA_BLOCK_SIZE);
+  if ((rc = check_block_size(block_size))) return rc;
   if (num_seqs == 0) return PA_OK;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens)
     return fail(PA_ERR_NULL, "out, query, key_cache, value_cache, block_tables and seq_lens must be non-NULL");
@@ -242,6 +258,7 @@ int fill_decode_args(pa::DecodeArgs& a, void* out, const void* query, const void
   a.num_kv_heads = num_kv_heads;
   a.group = num_heads / num_kv_heads;
   a.head_size = head_size;
+  a.block_size = block_size;
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_seq_len = max_seq_len;
@@ -296,8 +313,10 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
     // Persistent waves per compute unit, measured per cache type: the bf16
     // path streams best with one wave per SIMD, the fp8 path needs more waves
     // to overlap its in-register dequantisation with loads.
-    const int per_cu = kind == pa::KIND_FP8 ? PA_SK_WAVES_PER_CU_FP8
-                       : kind == pa::KIND_F32 ? PA_SK_WAVES_PER_CU_F32 : PA_SK_WAVES_PER_CU_BF16;
+    const bool b32 = block_size == 32;
+    const int per_cu = kind == pa::KIND_FP8 ? (b32 ? PA_SK_WAVES_PER_CU_BS32_FP8 : PA_SK_WAVES_PER_CU_FP8)
+                       : kind == pa::KIND_F32 ? (b32 ? PA_SK_WAVES_PER_CU_BS32_F32 : PA_SK_WAVES_PER_CU_F32)
+                                              : (b32 ? PA_SK_WAVES_PER_CU_BS32_BF16 : PA_SK_WAVES_PER_CU_BF16);
     const int waves = std::min(PA_SK_MAX_WAVES, device_cus() * per_cu);
     a.streamk_workgroups = std::max(1, waves / PA_WAVES);
   }
@@ -324,7 +343,7 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
 
 constexpr int kSharedSuffixSplit = 512;     // tokens per suffix split
 constexpr int kSharedTargetWaves = 1024;    // prefix waves the split count aims for (one per SIMD)
-constexpr int kSharedMinSplitBlocks = 32;   // fewest prefix blocks per wave
+constexpr int kSharedMinSplitTokens = 512;  // fewest prefix tokens per wave
 
 struct SharedPlan {
   int column_tiles = 1;
@@ -337,26 +356,29 @@ struct SharedPlan {
   size_t bytes = 0;
 };
 
-int check_shared_plan_args(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_seq_len,
-                           int num_groups, int max_group_size, int max_prefix_blocks) {
+int check_shared_plan_args(int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+                           int max_seq_len, int num_groups, int max_group_size, int max_prefix_blocks) {
   int rc = check_plan_args(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, 0);
   if (rc) return rc;
+  if ((rc = check_block_size(block_size))) return rc;
   if (num_groups < 0) return fail(PA_ERR_SHAPE, "num_groups %d < 0", num_groups);
   if (num_groups > 0 && max_group_size < 1)
     return fail(PA_ERR_SHAPE, "max_group_size %d must be positive with groups", max_group_size);
   if (max_prefix_blocks < 0) return fail(PA_ERR_SHAPE, "max_prefix_blocks %d < 0", max_prefix_blocks);
-  if ((int64_t)max_prefix_blocks * PA_BLOCK_SIZE > max_seq_len)
+  if ((int64_t)max_prefix_blocks * block_size > max_seq_len)
     return fail(PA_ERR_SHAPE, "max_prefix_blocks %d exceeds max_seq_len %d / %d", max_prefix_blocks, max_seq_len,
-                PA_BLOCK_SIZE);
+                block_size);
   return PA_OK;
 }
 
 // max_tiles: the kernel kind's column-tile limit (pa::max_column_tiles); the
 // workspace for 4 bounds that of every smaller limit (fewer tiles, more
-// member chunks, fewer prefix splits).
-SharedPlan make_shared_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_seq_len,
-                            int num_groups, int max_group_size, int max_prefix_blocks, int max_tiles = 4) {
+// member chunks, fewer prefix splits). Prefix splits count cache blocks.
+SharedPlan make_shared_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+                            int max_seq_len, int num_groups, int max_group_size, int max_prefix_blocks,
+                            int max_tiles = 4) {
   SharedPlan p;
+  const int min_split_blocks = kSharedMinSplitTokens / block_size;
   const int group = num_heads / num_kv_heads;
   const int64_t cols = (int64_t)std::max(1, max_group_size) * group;
   p.column_tiles = std::min(max_tiles, cols <= 16 ? 1 : (cols <= 32 ? 2 : 4));
@@ -365,8 +387,7 @@ SharedPlan make_shared_plan(int num_seqs, int num_heads, int num_kv_heads, int h
   if (num_groups > 0 && max_prefix_blocks > 0) {
     const int64_t base = (int64_t)num_groups * p.max_chunks * num_kv_heads;
     int64_t splits = std::max<int64_t>(1, (kSharedTargetWaves + base - 1) / base);
-    splits = std::min<int64_t>(splits, std::max(1, (max_prefix_blocks + kSharedMinSplitBlocks - 1) /
-                                                        kSharedMinSplitBlocks));
+    splits = std::min<int64_t>(splits, std::max(1, (max_prefix_blocks + min_split_blocks - 1) / min_split_blocks));
     p.prefix_split_blocks = (int)((max_prefix_blocks + splits - 1) / splits);
     p.max_prefix_splits = (max_prefix_blocks + p.prefix_split_blocks - 1) / p.prefix_split_blocks;
   }
@@ -406,8 +427,8 @@ int pa_kv_layout(int num_kv_heads, int head_size, int block_size, int q_dtype, i
   int rc = check_dtypes(q_dtype, kv_cache_dtype);
   if (rc) return rc;
   if (num_kv_heads <= 0) return fail(PA_ERR_SHAPE, "num_kv_heads %d must be positive", num_kv_heads);
-  if (head_size != 64 && head_size != 128) return fail(PA_ERR_SHAPE, "head_size %d is not 64 or 128", head_size);
-  if (block_size != PA_BLOCK_SIZE) return fail(PA_ERR_SHAPE, "block_size %d is not %d", block_size, PA_BLOCK_SIZE);
+  if ((rc = check_head_size(head_size))) return rc;
+  if ((rc = check_block_size(block_size))) return rc;
   const int eb = elem_bytes_of(q_dtype, kv_cache_dtype);
   const int64_t tile = (int64_t)head_size * block_size;
   desc->x = 16 / eb;
@@ -471,13 +492,14 @@ int pa_paged_attention_decode_split(void* out, const void* query, const void* ke
                      stream, split_tokens);
 }
 
-int pa_shared_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_seq_len,
-                              int num_groups, int max_group_size, int max_prefix_blocks, size_t* bytes) {
+int pa_shared_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size, int block_size,
+                              int max_seq_len, int num_groups, int max_group_size, int max_prefix_blocks,
+                              size_t* bytes) {
   if (!bytes) return fail(PA_ERR_NULL, "bytes is NULL");
-  int rc = check_shared_plan_args(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, num_groups,
-                                  max_group_size, max_prefix_blocks);
+  int rc = check_shared_plan_args(num_seqs, num_heads, num_kv_heads, head_size, block_size, max_seq_len,
+                                  num_groups, max_group_size, max_prefix_blocks);
   if (rc) return rc;
-  *bytes = make_shared_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, num_groups,
+  *bytes = make_shared_plan(num_seqs, num_heads, num_kv_heads, head_size, block_size, max_seq_len, num_groups,
                             max_group_size, max_prefix_blocks)
                .bytes;
   return ok();
@@ -498,8 +520,8 @@ int pa_paged_attention_decode_shared(void* out, const void* query, const void* k
                              num_blocks, scale, block_tables, max_blocks_per_seq, seq_lens, block_size,
                              max_seq_len, alibi_slopes, q_dtype, kv_cache_dtype, k_scale, v_scale, 0);
   if (rc) return rc;
-  if ((rc = check_shared_plan_args(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, num_groups,
-                                   max_group_size, max_prefix_blocks)))
+  if ((rc = check_shared_plan_args(num_seqs, num_heads, num_kv_heads, head_size, block_size, max_seq_len,
+                                   num_groups, max_group_size, max_prefix_blocks)))
     return rc;
   if (num_seqs == 0) return ok();
   if (!seq_prefix_blocks) return fail(PA_ERR_NULL, "seq_prefix_blocks must be non-NULL");
@@ -509,9 +531,10 @@ int pa_paged_attention_decode_shared(void* out, const void* query, const void* k
   if (!aligned(seq_prefix_blocks, 4) || (group_start && !aligned(group_start, 4)) ||
       (group_seqs && !aligned(group_seqs, 4)) || (group_prefix_blocks && !aligned(group_prefix_blocks, 4)))
     return fail(PA_ERR_ALIGN, "group arrays must be 4-byte aligned");
-  const int max_tiles = pa::max_column_tiles(q_dtype == PA_DTYPE_F32 ? 4 : 2, head_size);
-  const SharedPlan plan = make_shared_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, num_groups,
-                                           max_group_size, max_prefix_blocks, max_tiles);
+  const int max_tiles = pa::max_column_tiles(q_dtype == PA_DTYPE_F32 ? 4 : 2,
+                                             elem_bytes_of(q_dtype, kv_cache_dtype), head_size, block_size);
+  const SharedPlan plan = make_shared_plan(num_seqs, num_heads, num_kv_heads, head_size, block_size, max_seq_len,
+                                           num_groups, max_group_size, max_prefix_blocks, max_tiles);
   if (plan.max_prefix_splits > 65535) return fail(PA_ERR_SHAPE, "too many prefix splits");
   if ((rc = check_workspace(workspace, workspace_bytes, plan.bytes))) return rc;
 
@@ -587,8 +610,9 @@ int pa_kv_cache_append(void* key_cache, void* value_cache, const void* key, cons
   if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
   if (tokens_per_seq < 1) return fail(PA_ERR_SHAPE, "tokens_per_seq %d must be positive", tokens_per_seq);
   if (num_kv_heads <= 0) return fail(PA_ERR_SHAPE, "num_kv_heads %d must be positive", num_kv_heads);
-  if (head_size != 64 && head_size != 128) return fail(PA_ERR_SHAPE, "head_size %d is not 64 or 128", head_size);
-  if (block_size != PA_BLOCK_SIZE) return fail(PA_ERR_SHAPE, "block_size %d is not %d", block_size, PA_BLOCK_SIZE);
+  int rc = check_head_size(head_size);
+  if (rc) return rc;
+  if ((rc = check_block_size(block_size))) return rc;
   if (num_blocks <= 0) return fail(PA_ERR_SHAPE, "num_blocks %d must be positive", num_blocks);
   if (max_blocks_per_seq <= 0) return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d must be positive", max_blocks_per_seq);
   if ((int64_t)num_seqs * tokens_per_seq * num_kv_heads >= ((int64_t)1 << 31))
@@ -615,6 +639,7 @@ int pa_kv_cache_append(void* key_cache, void* value_cache, const void* key, cons
   a.tokens_per_seq = tokens_per_seq;
   a.num_kv_heads = num_kv_heads;
   a.head_size = head_size;
+  a.block_size = block_size;
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   const int in_kind = in_dtype == PA_DTYPE_F32 ? pa::KIND_F32 : pa::KIND_BF16;

@@ -2,9 +2,9 @@
 // paged cache, the step that precedes attention in every decode iteration
 // (the cache grows one token per step; vLLM 0.25.0 解读 §1). Token j of
 // sequence s goes to logical position p = positions[s] + j, i.e. physical
-// block block_tables[s, p / 16], slot p % 16 (10100.com retirement article,
-// §1), in the pages' layouts (same article, §2):
-//   K [num_blocks][num_kv_heads][D/x][16][x],  V [num_blocks][num_kv_heads][D][16].
+// block block_tables[s, p / B], slot p % B for blocks of B = 16 or 32 tokens
+// (10100.com retirement article, §1), in the pages' layouts (same article, §2):
+//   K [num_blocks][num_kv_heads][D/x][B][x],  V [num_blocks][num_kv_heads][D][B].
 // With an fp8 cache each element is stored as the E4M3FN code nearest to
 // x / scale (ties to even, saturating at 448; same article, §4, for the
 // scaled fp8 storage).
@@ -110,17 +110,18 @@ __global__ void __launch_bounds__(256) pa_append_kernel(const AppendArgs a, int 
   const int s = (int)(sh / a.num_kv_heads);
   const int p0 = a.positions[s];
   if (p0 < 0) return;
-  const int64_t blk = (int64_t)(p0 >> 4) + r;             // logical block of this run
-  const int64_t t_lo = blk * 16 > p0 ? blk * 16 : (int64_t)p0;
+  const int bs = a.block_size;                            // 16 or 32 tokens
+  const int64_t blk = (int64_t)(p0 / bs) + r;             // logical block of this run
+  const int64_t t_lo = blk * bs > p0 ? blk * bs : (int64_t)p0;
   const int64_t p_end = (int64_t)p0 + a.tokens_per_seq;
-  const int64_t t_hi = (blk + 1) * 16 < p_end ? (blk + 1) * 16 : p_end;
+  const int64_t t_hi = (blk + 1) * bs < p_end ? (blk + 1) * bs : p_end;
   if (t_lo >= t_hi || blk >= a.max_blocks_per_seq) return;
   const int b = a.block_tables[(int64_t)s * a.max_blocks_per_seq + blk];
   if (b < 0 || b >= a.num_blocks) return;
-  const int o0 = (int)(t_lo & 15);                        // first slot
-  const int n = (int)(t_hi - t_lo);                       // tokens in this run, 1..16
+  const int o0 = (int)(t_lo - blk * bs);                  // first slot
+  const int n = (int)(t_hi - t_lo);                       // tokens in this run, 1..bs
   const int j0 = (int)(t_lo - p0);                        // their first index among the new tokens
-  const int64_t tile = (int64_t)D * 16 * Pol::kElem;
+  const int64_t tile = (int64_t)D * bs * Pol::kElem;
   const int64_t base = ((int64_t)b * a.num_kv_heads + h) * tile;
   const int64_t row_stride = (int64_t)a.num_kv_heads * D;  // elements between consecutive tokens
   const int64_t row0 = ((int64_t)s * a.tokens_per_seq + j0) * row_stride + (int64_t)h * D;
@@ -133,20 +134,21 @@ __global__ void __launch_bounds__(256) pa_append_kernel(const AppendArgs a, int 
   // K: item i = c * n + t -> chunk c of token t, 16 bytes at row o0 + t.
   for (int i = lane; i < kChunks * n; i += 64) {
     const int c = i / n, t = i - c * n;
-    Pol::k_chunk(krow + t * row_stride + c * Pol::kX, kc + ((int64_t)c * 16 + o0 + t) * 16, ks);
+    Pol::k_chunk(krow + t * row_stride + c * Pol::kX, kc + ((int64_t)c * bs + o0 + t) * 16, ks);
   }
   // V: item i = d * n + t -> element d of token t at row d, slot o0 + t.
   for (int i = lane; i < D * n; i += 64) {
     const int d = i / n, t = i - d * n;
-    Pol::v_elem(vrow + t * row_stride + d, vc + ((int64_t)d * 16 + o0 + t) * Pol::kElem, vs);
+    Pol::v_elem(vrow + t * row_stride + d, vc + ((int64_t)d * bs + o0 + t) * Pol::kElem, vs);
   }
 }
 
 template <typename Pol, int D>
 hipError_t launch_append_t(const AppendArgs& a, hipStream_t stream) {
-  // A run of T tokens starting anywhere in a block touches at most
-  // floor((15 + T - 1) / 16) + 1 blocks.
-  const int runs = (15 + a.tokens_per_seq - 1) / 16 + 1;
+  // A run of T tokens starting anywhere in a block of B tokens touches at
+  // most floor((B - 1 + T - 1) / B) + 1 blocks.
+  const int bs = a.block_size;
+  const int runs = (bs - 1 + a.tokens_per_seq - 1) / bs + 1;
   const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * runs;
   const int64_t wgs = (items + 3) / 4;
   hipLaunchKernelGGL((pa_append_kernel<Pol, D>), dim3((unsigned)wgs), dim3(256), 0, stream, a, runs);
@@ -184,12 +186,16 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t*
 hipError_t launch_append(const AppendArgs& a, int in_kind, int cache_kind, hipStream_t stream) {
   const int key = (in_kind * 10 + cache_kind) * 1000 + a.head_size;
   switch (key) {
+    case (KIND_F32 * 10 + KIND_F32) * 1000 + 32: return launch_append_t<AppendPolicy<KIND_F32, 32>, 32>(a, stream);
     case (KIND_F32 * 10 + KIND_F32) * 1000 + 64: return launch_append_t<AppendPolicy<KIND_F32, 64>, 64>(a, stream);
     case (KIND_F32 * 10 + KIND_F32) * 1000 + 128: return launch_append_t<AppendPolicy<KIND_F32, 128>, 128>(a, stream);
+    case (KIND_BF16 * 10 + KIND_BF16) * 1000 + 32: return launch_append_t<AppendPolicy<KIND_BF16, 32>, 32>(a, stream);
     case (KIND_BF16 * 10 + KIND_BF16) * 1000 + 64: return launch_append_t<AppendPolicy<KIND_BF16, 64>, 64>(a, stream);
     case (KIND_BF16 * 10 + KIND_BF16) * 1000 + 128: return launch_append_t<AppendPolicy<KIND_BF16, 128>, 128>(a, stream);
+    case (KIND_BF16 * 10 + KIND_FP8) * 1000 + 32: return launch_append_t<QuantPolicy<unsigned short>, 32>(a, stream);
     case (KIND_BF16 * 10 + KIND_FP8) * 1000 + 64: return launch_append_t<QuantPolicy<unsigned short>, 64>(a, stream);
     case (KIND_BF16 * 10 + KIND_FP8) * 1000 + 128: return launch_append_t<QuantPolicy<unsigned short>, 128>(a, stream);
+    case (KIND_F32 * 10 + KIND_FP8) * 1000 + 32: return launch_append_t<QuantPolicy<float>, 32>(a, stream);
     case (KIND_F32 * 10 + KIND_FP8) * 1000 + 64: return launch_append_t<QuantPolicy<float>, 64>(a, stream);
     case (KIND_F32 * 10 + KIND_FP8) * 1000 + 128: return launch_append_t<QuantPolicy<float>, 128>(a, stream);
     default: return hipErrorInvalidValue;

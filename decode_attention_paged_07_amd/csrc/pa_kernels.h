@@ -30,6 +30,16 @@
 #ifndef PA_PIPE
 #define PA_PIPE 1
 #endif
+// 32-token blocks: stream-K waves per compute unit.
+#ifndef PA_SK_WAVES_PER_CU_BS32_BF16
+#define PA_SK_WAVES_PER_CU_BS32_BF16 PA_SK_WAVES_PER_CU_BF16
+#endif
+#ifndef PA_SK_WAVES_PER_CU_BS32_FP8
+#define PA_SK_WAVES_PER_CU_BS32_FP8 PA_SK_WAVES_PER_CU_FP8
+#endif
+#ifndef PA_SK_WAVES_PER_CU_BS32_F32
+#define PA_SK_WAVES_PER_CU_BS32_F32 PA_SK_WAVES_PER_CU_F32
+#endif
 // Upper bound on stream-K waves; sizes the segment workspace.
 #define PA_SK_MAX_WAVES 4096
 
@@ -67,15 +77,17 @@ struct DecodeArgs {
   int num_kv_heads;
   int group;
   int head_size;
+  int block_size;              // tokens per physical block: 16 or 32
   int num_blocks;
   int max_blocks_per_seq;
   int max_seq_len;
   int split_tokens;
   int num_splits;
   int streamk_workgroups;      // > 0 selects the stream-K scheduler
-  // split grid only: per-sequence count of leading blocks handled elsewhere
-  // (a shared prefix), clamped to [0, min(L / 16, max_first_block)];
-  // nullable. When set, every split writes partials and no reduce runs.
+  // split grid only: per-sequence count of leading physical blocks handled
+  // elsewhere (a shared prefix); in 16-token sub-blocks it is clamped to
+  // [0, min(L / 16, max_first_block)]; nullable. When set, every split writes
+  // partials and no reduce runs.
   const int32_t* first_block;
   int max_first_block;
 };
@@ -90,21 +102,22 @@ struct SharedArgs {
   const int32_t* group_start;          // [num_groups + 1] offsets into group_seqs
   const int32_t* group_seqs;           // [num_members] member sequence ids
   int num_members;
-  const int32_t* group_prefix_blocks;  // [num_groups] shared full blocks
+  const int32_t* group_prefix_blocks;  // [num_groups] shared full physical blocks
   int num_groups;
   int max_chunks;                      // chunks of members per group in the grid
   int members_per_chunk;
-  int prefix_split_blocks;             // prefix blocks per wave
+  int prefix_split_blocks;             // prefix 16-token sub-blocks per wave
   int max_prefix_splits;
   float* pre_out;                      // [S][H][max_prefix_splits][D]
   float* pre_max;                      // [S][H][max_prefix_splits] natural-log units
   float* pre_sum;                      // [S][H][max_prefix_splits]
 };
 
-// Most 16-column query tiles a prefix wave carries: four, except with fp32
-// queries at head_size 128, whose operands would not fit in registers.
-constexpr int max_column_tiles(int q_elem_bytes, int head_size) {
-  return (q_elem_bytes == 4 && head_size == 128) ? 2 : 4;
+// Most 16-column query tiles a prefix wave carries: four, except at
+// head_size 128 with fp32 queries, or with a bf16 cache in 32-token blocks,
+// whose operands would not fit in registers.
+constexpr int max_column_tiles(int q_elem_bytes, int kv_elem_bytes, int head_size, int block_size) {
+  return (head_size == 128 && (q_elem_bytes == 4 || (kv_elem_bytes == 2 && block_size == 32))) ? 2 : 4;
 }
 
 hipError_t launch_shared(const SharedArgs& a, int kind, int column_tiles, hipStream_t stream);
@@ -123,6 +136,7 @@ struct AppendArgs {
   int tokens_per_seq;
   int num_kv_heads;
   int head_size;
+  int block_size;              // tokens per cache block: 16 or 32
   int num_blocks;
   int max_blocks_per_seq;
 };

@@ -79,7 +79,8 @@ pa_split_reduce_kernel(const DecodeArgs a) {
   for (int p = lane; p < n; p += 64) tot += es[p] * fast_exp2((ml[p] - big_m) * kLog2e);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
-  constexpr int kPer = D / 64;
+  constexpr int kPer = D >= 64 ? D / 64 : 1;     // head elements per lane
+  if (lane * kPer >= D) return;                  // D = 32: lanes 32..63 idle
   float acc[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) acc[k] = 0.f;
@@ -98,13 +99,15 @@ pa_split_reduce_kernel(const DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // Stream-K: grid (num_workgroups), kWaves waves each; wave w of W in total
 // owns tiles [w*U, min(total, (w+1)*U)) with U = ceil(total / W) of the
-// total = num_kv_heads * T tiles, T = sum_s ceil(L_s / 16), ordered
+// total = num_kv_heads * T tiles, T = sum_s ceil(L_s / BS) (one tile per
+// BS-token block), ordered
 // (kv head, sequence, block). Pair p = kvh*S + s cut into several segments
 // writes segment partials at slot p + w (unique: both p and w grow along the
 // order) and records its first and last wave in seg_meta[p].
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ int blocks_of(int L) { return (L + kBlock - 1) / kBlock; }
+template <int BS>
+__device__ __forceinline__ int blocks_of(int L) { return (L + BS - 1) / BS; }
 
 template <typename P, int D, int NB, bool ALIBI>
 __global__ void __launch_bounds__(kWaves * 64)
@@ -118,7 +121,7 @@ pa_streamk_kernel(const DecodeArgs a) {
   int T = 0;
   for (int c0 = 0; c0 < S; c0 += 64) {
     const int s = c0 + lane;
-    T += wave_sum(s < S ? blocks_of(clamp_len(a.seq_lens[s], a.max_seq_len)) : 0);
+    T += wave_sum(s < S ? blocks_of<P::kBS>(clamp_len(a.seq_lens[s], a.max_seq_len)) : 0);
   }
   const int64_t total = (int64_t)a.num_kv_heads * T;
   if (total == 0) return;
@@ -134,7 +137,7 @@ pa_streamk_kernel(const DecodeArgs a) {
   int running = 0;
   for (int c0 = 0; c0 < S; c0 += 64) {
     const int s = c0 + lane;
-    const int nb = s < S ? blocks_of(clamp_len(a.seq_lens[s], a.max_seq_len)) : 0;
+    const int nb = s < S ? blocks_of<P::kBS>(clamp_len(a.seq_lens[s], a.max_seq_len)) : 0;
     const int incl = wave_incl_scan(nb, lane) + running;
     const int excl = incl - nb;
     const uint64_t hit = __builtin_amdgcn_ballot_w64(nb > 0 && excl <= r && r < incl);
@@ -152,7 +155,7 @@ pa_streamk_kernel(const DecodeArgs a) {
   int64_t u = u0;
   while (true) {
     const int L = clamp_len(a.seq_lens[seq], a.max_seq_len);
-    const int nbs = blocks_of(L);
+    const int nbs = blocks_of<P::kBS>(L);
     const int n = (int)min((int64_t)(nbs - blk), u1 - u);
     WaveAttn<P, D, NB, ALIBI> wa;
     wa.begin(a, seq, kvh);
@@ -268,14 +271,30 @@ static hipError_t launch_alibi(const DecodeArgs& a, hipStream_t stream, const La
                         : launch_mode<P, D, NB, false>(a, stream, hooks);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream, const LaunchHooks& hooks) {
+template <int BS>
+static hipError_t launch_decode_bs(const DecodeArgs& a, int kind, hipStream_t stream, const LaunchHooks& hooks) {
+  // A 32-token block is already two 16-row sub-tiles: one block per issue.
+  constexpr int nb_f32 = BS == 32 ? 1 : PA_NB_F32;
+  constexpr int nb_bf16 = BS == 32 ? 1 : PA_NB_BF16;
+  constexpr int nb_fp8 = BS == 32 ? 1 : PA_NB_FP8;
   switch (kind * 1000 + a.head_size) {
-    case KIND_F32 * 1000 + 64: return launch_alibi<PolicyF32<64>, 64, PA_NB_F32>(a, stream, hooks);
-    case KIND_F32 * 1000 + 128: return launch_alibi<PolicyF32<128>, 128, PA_NB_F32>(a, stream, hooks);
-    case KIND_BF16 * 1000 + 64: return launch_alibi<PolicyBf16<64>, 64, PA_NB_BF16>(a, stream, hooks);
-    case KIND_BF16 * 1000 + 128: return launch_alibi<PolicyBf16<128>, 128, PA_NB_BF16>(a, stream, hooks);
-    case KIND_FP8 * 1000 + 64: return launch_alibi<PolicyFp8<64>, 64, PA_NB_FP8>(a, stream, hooks);
-    case KIND_FP8 * 1000 + 128: return launch_alibi<PolicyFp8<128>, 128, PA_NB_FP8>(a, stream, hooks);
+    case KIND_F32 * 1000 + 32: return launch_alibi<PolicyF32<32, BS>, 32, nb_f32>(a, stream, hooks);
+    case KIND_F32 * 1000 + 64: return launch_alibi<PolicyF32<64, BS>, 64, nb_f32>(a, stream, hooks);
+    case KIND_F32 * 1000 + 128: return launch_alibi<PolicyF32<128, BS>, 128, nb_f32>(a, stream, hooks);
+    case KIND_BF16 * 1000 + 32: return launch_alibi<PolicyBf16<32, BS>, 32, nb_bf16>(a, stream, hooks);
+    case KIND_BF16 * 1000 + 64: return launch_alibi<PolicyBf16<64, BS>, 64, nb_bf16>(a, stream, hooks);
+    case KIND_BF16 * 1000 + 128: return launch_alibi<PolicyBf16<128, BS>, 128, nb_bf16>(a, stream, hooks);
+    case KIND_FP8 * 1000 + 32: return launch_alibi<PolicyFp8<32, BS>, 32, nb_fp8>(a, stream, hooks);
+    case KIND_FP8 * 1000 + 64: return launch_alibi<PolicyFp8<64, BS>, 64, nb_fp8>(a, stream, hooks);
+    case KIND_FP8 * 1000 + 128: return launch_alibi<PolicyFp8<128, BS>, 128, nb_fp8>(a, stream, hooks);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream, const LaunchHooks& hooks) {
+  switch (a.block_size) {
+    case 16: return launch_decode_bs<16>(a, kind, stream, hooks);
+    case 32: return launch_decode_bs<32>(a, kind, stream, hooks);
     default: return hipErrorInvalidValue;
   }
 }

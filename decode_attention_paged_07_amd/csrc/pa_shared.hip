@@ -32,6 +32,8 @@ namespace {
 template <typename P, int D, int NCT, bool ALIBI>
 struct GroupAttn {
   static constexpr int kDt = P::kDt;
+  static constexpr int kBS = P::kBS;
+  static constexpr int kSub = P::kSub;
   typename P::QRegs q[NCT];
   typename P::Lane lo;
   f32x4 o[NCT][kDt];
@@ -68,7 +70,7 @@ struct GroupAttn {
         const int L = clamp_len(a.seq_lens[col_seq[t]], a.max_seq_len);
         if (active[t]) slope2[t] = a.alibi_slopes[col_head[t]] * kLog2e;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) lane_bias[t][r] = slope2[t] * (float)(4 * q4 + r - (L - 1));
+        for (int r = 0; r < 4; ++r) lane_bias[t][r] = slope2[t] * (float)(tile_token<kBS>(0, q4, r) - (L - 1));
       }
       m[t] = m_true[t] = kNegInf;
       lsum[t] = 0.f;
@@ -77,19 +79,26 @@ struct GroupAttn {
     }
   }
 
-  __device__ void consume(const typename P::KRegs& kr, const typename P::VRegs& vr, int blk) {
+  __device__ void consume(const typename P::KRegs& kr, typename P::VRegs& vr, int blk) {
+    P::prepare_v(vr);
 #pragma unroll
     for (int t = 0; t < NCT; ++t) {
-      const f32x4 sc = P::qk(kr, q[t]);
-      f32x4 z;
-      if constexpr (ALIBI) {
-        const float base = (float)(blk * kBlock);
+      f32x4 z[kSub];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) z[r] = fmaf(sc[r], c, fmaf(slope2[t], base, lane_bias[t][r]));
-      } else {
-        z = sc * c;
+      for (int st = 0; st < kSub; ++st) {
+        const f32x4 sc = P::qk(kr, q[t], st);
+        if constexpr (ALIBI) {
+          const float base = (float)(blk * kBS + 8 * st);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) z[st][r] = fmaf(sc[r], c, fmaf(slope2[t], base, lane_bias[t][r]));
+        } else {
+          z[st] = sc * c;
+        }
       }
-      const float mx = quad_max(max4(z));
+      float mx = max4(z[0]);
+#pragma unroll
+      for (int st = 1; st < kSub; ++st) mx = fmaxf(mx, max4(z[st]));
+      mx = quad_max(mx);
       m_true[t] = fmaxf(m_true[t], mx);
       if (wave_any(mx > m[t] + kRescaleSlack)) {
         const float m_new = fmaxf(m[t], mx);
@@ -99,11 +108,14 @@ struct GroupAttn {
 #pragma unroll
         for (int dt = 0; dt < kDt; ++dt) o[t][dt] *= alpha;
       }
-      f32x4 p;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[r] - m[t]);
-      lsum[t] += (p[0] + p[1]) + (p[2] + p[3]);
-      P::pv(vr, p, o[t]);
+      for (int st = 0; st < kSub; ++st) {
+        f32x4 p;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[st][r] - m[t]);
+        lsum[t] += (p[0] + p[1]) + (p[2] + p[3]);
+        P::pv(vr, p, o[t], st);
+      }
     }
   }
 
@@ -167,7 +179,7 @@ __device__ __forceinline__ void prefix_unit(const SharedArgs& s, int group, int 
   const int m0 = g0 + chunk * s.members_per_chunk;
   if (m0 >= g1) return;
   const int count = min(s.members_per_chunk, g1 - m0);
-  const int pblocks = min(s.group_prefix_blocks[group], min(a.max_blocks_per_seq, a.max_first_block));
+  const int pblocks = min(max(s.group_prefix_blocks[group], 0), min(a.max_blocks_per_seq, a.max_first_block));
   const int b0 = split * s.prefix_split_blocks;
   const int b1 = min(pblocks, b0 + s.prefix_split_blocks);
   if (b0 >= b1) return;
@@ -227,10 +239,11 @@ __global__ void __launch_bounds__(64) pa_shared_merge_kernel(const SharedArgs s,
   const int lane = threadIdx.x;
   const int L = clamp_len(a.seq_lens[seq], a.max_seq_len);
   OutElem* out = reinterpret_cast<OutElem*>(a.out) + ((int64_t)seq * a.num_heads + h) * D;
-  constexpr int kPer = D / 64;
-  const int first = min(max(seq_prefix_blocks[seq], 0), min(L / kBlock, a.max_first_block));
+  constexpr int kPer = D >= 64 ? D / 64 : 1;     // head elements per lane
+  if (lane * kPer >= D) return;                  // D = 32: lanes 32..63 idle
+  const int first = min(max(seq_prefix_blocks[seq], 0), min(L / a.block_size, a.max_first_block));
   const int n_pre = first > 0 ? (first + s.prefix_split_blocks - 1) / s.prefix_split_blocks : 0;
-  const int t0 = first * kBlock;
+  const int t0 = first * a.block_size;
   const int n_suf = L > t0 ? (L - t0 + a.split_tokens - 1) / a.split_tokens : 0;
   if (n_pre + n_suf == 0) {
 #pragma unroll
@@ -279,38 +292,49 @@ hipError_t launch_prefix_nct(const SharedArgs& s, int nct, hipStream_t stream) {
     case 1: return launch_prefix<P, D, 1>(s, stream);
     case 2: return launch_prefix<P, D, 2>(s, stream);
     default:
-      if constexpr (max_column_tiles(sizeof(typename P::QElem), D) >= 4) return launch_prefix<P, D, 4>(s, stream);
+      if constexpr (max_column_tiles(sizeof(typename P::QElem), P::kKvElemBytes, D, P::kBS) >= 4)
+        return launch_prefix<P, D, 4>(s, stream);
       return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_shared(const SharedArgs& s, int kind, int column_tiles, hipStream_t stream) {
-  hipError_t err = hipSuccess;
-  {
-    switch (kind * 1000 + s.d.head_size) {
-      case KIND_F32 * 1000 + 64: err = launch_prefix_nct<PolicyF32<64>, 64>(s, column_tiles, stream); break;
-      case KIND_F32 * 1000 + 128: err = launch_prefix_nct<PolicyF32<128>, 128>(s, column_tiles, stream); break;
-      case KIND_BF16 * 1000 + 64: err = launch_prefix_nct<PolicyBf16<64>, 64>(s, column_tiles, stream); break;
-      case KIND_BF16 * 1000 + 128: err = launch_prefix_nct<PolicyBf16<128>, 128>(s, column_tiles, stream); break;
-      case KIND_FP8 * 1000 + 64: err = launch_prefix_nct<PolicyFp8<64>, 64>(s, column_tiles, stream); break;
-      case KIND_FP8 * 1000 + 128: err = launch_prefix_nct<PolicyFp8<128>, 128>(s, column_tiles, stream); break;
-      default: return hipErrorInvalidValue;
-    }
-    if (err != hipSuccess) return err;
+template <int BS>
+hipError_t launch_shared_main(const SharedArgs& s, int kind, int column_tiles, hipStream_t stream) {
+  switch (kind * 1000 + s.d.head_size) {
+    case KIND_F32 * 1000 + 32: return launch_prefix_nct<PolicyF32<32, BS>, 32>(s, column_tiles, stream);
+    case KIND_F32 * 1000 + 64: return launch_prefix_nct<PolicyF32<64, BS>, 64>(s, column_tiles, stream);
+    case KIND_F32 * 1000 + 128: return launch_prefix_nct<PolicyF32<128, BS>, 128>(s, column_tiles, stream);
+    case KIND_BF16 * 1000 + 32: return launch_prefix_nct<PolicyBf16<32, BS>, 32>(s, column_tiles, stream);
+    case KIND_BF16 * 1000 + 64: return launch_prefix_nct<PolicyBf16<64, BS>, 64>(s, column_tiles, stream);
+    case KIND_BF16 * 1000 + 128: return launch_prefix_nct<PolicyBf16<128, BS>, 128>(s, column_tiles, stream);
+    case KIND_FP8 * 1000 + 32: return launch_prefix_nct<PolicyFp8<32, BS>, 32>(s, column_tiles, stream);
+    case KIND_FP8 * 1000 + 64: return launch_prefix_nct<PolicyFp8<64, BS>, 64>(s, column_tiles, stream);
+    case KIND_FP8 * 1000 + 128: return launch_prefix_nct<PolicyFp8<128, BS>, 128>(s, column_tiles, stream);
+    default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_shared(const SharedArgs& s, int kind, int column_tiles, hipStream_t stream) {
+  hipError_t err = s.d.block_size == 32 ? launch_shared_main<32>(s, kind, column_tiles, stream)
+                   : s.d.block_size == 16 ? launch_shared_main<16>(s, kind, column_tiles, stream)
+                                          : hipErrorInvalidValue;
+  if (err != hipSuccess) return err;
   const dim3 grid(s.d.num_heads, s.d.num_seqs);
-  if (kind == KIND_F32) {
-    if (s.d.head_size == 64)
-      hipLaunchKernelGGL((pa_shared_merge_kernel<float, 64>), grid, dim3(64), 0, stream, s, s.d.first_block);
-    else
-      hipLaunchKernelGGL((pa_shared_merge_kernel<float, 128>), grid, dim3(64), 0, stream, s, s.d.first_block);
-  } else {
-    if (s.d.head_size == 64)
-      hipLaunchKernelGGL((pa_shared_merge_kernel<__bf16, 64>), grid, dim3(64), 0, stream, s, s.d.first_block);
-    else
-      hipLaunchKernelGGL((pa_shared_merge_kernel<__bf16, 128>), grid, dim3(64), 0, stream, s, s.d.first_block);
+  const bool f32 = kind == KIND_F32;
+  switch (s.d.head_size) {
+    case 32:
+      if (f32) hipLaunchKernelGGL((pa_shared_merge_kernel<float, 32>), grid, dim3(64), 0, stream, s, s.d.first_block);
+      else hipLaunchKernelGGL((pa_shared_merge_kernel<__bf16, 32>), grid, dim3(64), 0, stream, s, s.d.first_block);
+      break;
+    case 64:
+      if (f32) hipLaunchKernelGGL((pa_shared_merge_kernel<float, 64>), grid, dim3(64), 0, stream, s, s.d.first_block);
+      else hipLaunchKernelGGL((pa_shared_merge_kernel<__bf16, 64>), grid, dim3(64), 0, stream, s, s.d.first_block);
+      break;
+    default:
+      if (f32) hipLaunchKernelGGL((pa_shared_merge_kernel<float, 128>), grid, dim3(64), 0, stream, s, s.d.first_block);
+      else hipLaunchKernelGGL((pa_shared_merge_kernel<__bf16, 128>), grid, dim3(64), 0, stream, s, s.d.first_block);
   }
   return hipGetLastError();
 }

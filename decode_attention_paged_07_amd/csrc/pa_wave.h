@@ -99,34 +99,87 @@ __device__ __forceinline__ void store4(T* p, f32x4 v) {
 // Element-type policies: register shapes, lane offsets, loads, contractions.
 // Loads take a wave-uniform tile address plus this lane's byte offset, so the
 // address is one SGPR pair plus a loop-invariant VGPR.
+//
+// A policy covers one (physical block, kv head) tile of BS = 16 or 32 tokens
+// as BS/16 sub-tiles of 16 S rows; row 4*q4 + r of sub-tile t holds token
+// tile_token<BS>(t, q4, r). With 32-token blocks the two sub-tiles interleave
+// in runs of 8 tokens: a K load instruction then reads whole 128-byte lines
+// (8 tokens of a 16-byte chunk), and a V load gives each lane 8 consecutive
+// tokens of one head dim, so one instruction reads whole V rows; a row swap
+// between lane quads (split_rows) then hands each sub-tile its tokens.
+// Reading the two 16-token halves separately would split every cache line
+// between two instructions, which measured markedly slower.
 // ---------------------------------------------------------------------------
 
+template <int BS>
+__device__ __forceinline__ constexpr int tile_token(int t, int q4, int r) {
+  return BS == 16 ? 4 * q4 + r : 16 * (q4 >> 1) + 8 * t + 4 * (q4 & 1) + r;
+}
+// Token of K row rho (= 4*q4 + r) of sub-tile 0; sub-tile t adds 8*t.
+template <int BS>
+__device__ __forceinline__ constexpr int k_row_token(int rho) {
+  return BS == 16 ? rho : 16 * (rho >> 3) + (rho & 7);
+}
+
+// lo / hi: tokens 8*q4 .. +3 / 8*q4+4 .. +7 of lane quad q4 (a 32-token
+// tile). Afterwards lo holds sub-tile 0's tokens of this lane and hi sub-tile
+// 1's: quads 2k and 2k+1 exchange one half (v_permlane16_swap: odd rows of
+// the first operand trade places with even rows of the second).
+__device__ __forceinline__ void split_rows(unsigned& lo, unsigned& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(lo, hi, false, false);
+  lo = r[0];
+  hi = r[1];
+}
+
+template <bool C, typename A, typename B> struct Pick { using type = A; };
+template <typename A, typename B> struct Pick<false, A, B> { using type = B; };
+
 // bf16 query, bf16 cache (x = 8): K chunk c = 8 consecutive d at one token.
-template <int D>
+template <int D, int BS = 16>
 struct PolicyBf16 {
-  static constexpr int kKLoads = D / 32;     // 16x16x32 steps, one 16-byte load each
+  static constexpr int kBS = BS;
+  static constexpr int kKvElemBytes = 2;
+  static constexpr int kSub = BS / 16;       // 16-row sub-tiles per tile
+  static constexpr int kKLoads = D / 32;     // per sub-tile: 16x16x32 steps, one 16-byte load each
   static constexpr int kDt = D / 16;         // d-tiles of the PV product
-  using KRegs = u32x4[kKLoads];
-  using VRegs = u32x2[kDt];                  // 4 bf16 tokens of one d per tile
+  using VVec = typename Pick<BS == 16, u32x2, u32x4>::type;   // 2 bf16 tokens per dword
+  using KRegs = u32x4[kSub][kKLoads];
+  using VRegs = VVec[kDt];
   using QRegs = bf16x8[kKLoads];
   using QElem = __bf16;
   using OutElem = __bf16;
   struct Lane { uint32_t k, v; };
 
-  // K: lane l = i + 16*q4 reads chunk (4s + q4) at token i, byte (64s + l)*16.
-  // V: lane (i + 16*q4) of tile dt reads tokens 4*q4..+3 of d = 16*dt + i.
+  // K: lane (rho + 16*q4) of step s reads chunk (4s + q4) at token
+  //    k_row_token(rho) + 8t. V: lane (i + 16*q4) of tile dt reads BS/4
+  //    consecutive tokens from 4*q4 (BS/4 * q4) of d = 16*dt + i.
   __device__ static Lane lane_offsets(int lane) {
-    return {(uint32_t)lane * 16u, (uint32_t)((lane & 15) * 32 + (lane >> 4) * 8)};
+    const int q4 = lane >> 4, rho = lane & 15;
+    return {(uint32_t)(q4 * BS * 16 + k_row_token<BS>(rho) * 16), (uint32_t)(rho * BS * 2 + q4 * (BS / 4) * 2)};
   }
   __device__ static void load_k(const char* t, const Lane& lo, KRegs& k) {
 #pragma unroll
-    for (int s = 0; s < kKLoads; ++s)
-      k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(t + lo.k + s * 1024));
+    for (int st = 0; st < kSub; ++st)
+#pragma unroll
+      for (int s = 0; s < kKLoads; ++s)
+        k[st][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(t + lo.k + s * 4 * BS * 16 + st * 128));
   }
   __device__ static void load_v(const char* t, const Lane& lo, VRegs& v) {
 #pragma unroll
     for (int dt = 0; dt < kDt; ++dt)
-      v[dt] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(t + lo.v + dt * 512));
+      v[dt] = __builtin_nontemporal_load(reinterpret_cast<const VVec*>(t + lo.v + dt * 16 * BS * 2));
+  }
+  // After the loads have landed: dwords (2t, 2t+1) of v[dt] become sub-tile t's.
+  __device__ static void prepare_v(VRegs& v) {
+    if constexpr (BS == 32) {
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) {
+        unsigned w0 = v[dt][0], w1 = v[dt][1], w2 = v[dt][2], w3 = v[dt][3];
+        split_rows(w0, w2);
+        split_rows(w1, w3);
+        v[dt] = VVec{w0, w1, w2, w3};
+      }
+    }
   }
   // q in the d-order of load_k: step s, lane quad q4 -> d = 8*(4s+q4) + u.
   __device__ static void load_q(const QElem* qh, bool active, int q4, QRegs& q) {
@@ -137,59 +190,74 @@ struct PolicyBf16 {
       q[s] = __builtin_bit_cast(bf16x8, w);
     }
   }
-  __device__ static f32x4 qk(const KRegs& k, const QRegs& q) {
+  __device__ static f32x4 qk(const KRegs& k, const QRegs& q, int st) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < kKLoads; ++s)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[s]), q[s], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[st][s]), q[s], acc, 0, 0, 0);
     return acc;
   }
-  // Zero V of tokens 4*q4+u >= nvalid (only on a sequence's partial last block).
+  // Zero V of tokens >= nvalid (only on a sequence's partial last block).
   __device__ static void mask_v(VRegs& v, int q4, int nvalid) {
 #pragma unroll
     for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
-      for (int w = 0; w < 2; ++w) {
+      for (int w = 0; w < 2 * kSub; ++w) {
         unsigned x = v[dt][w];
-        const int t0 = 4 * q4 + 2 * w;
+        const int t0 = tile_token<BS>(w >> 1, q4, 2 * (w & 1));
         if (t0 >= nvalid) x &= 0xFFFF0000u;
         if (t0 + 1 >= nvalid) x &= 0x0000FFFFu;
         v[dt][w] = x;
       }
   }
-  __device__ static void pv(const VRegs& v, f32x4 p, f32x4 (&o)[kDt]) {
+  __device__ static void pv(const VRegs& v, f32x4 p, f32x4 (&o)[kDt], int st) {
     const s16x4 pb = pack_bf16x4(p);
 #pragma unroll
-    for (int dt = 0; dt < kDt; ++dt)
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v[dt]), pb, o[dt], 0, 0, 0);
+    for (int dt = 0; dt < kDt; ++dt) {
+      const u32x2 a = {v[dt][2 * st], v[dt][2 * st + 1]};
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), pb, o[dt], 0, 0, 0);
+    }
   }
 };
 
 // fp32 query, fp32 cache (x = 4): fp32 MFMA keeps full fp32 products.
-template <int D>
+template <int D, int BS = 16>
 struct PolicyF32 {
-  static constexpr int kKLoads = D / 16;     // 16 bytes = 4 d at one token
+  static constexpr int kBS = BS;
+  static constexpr int kKvElemBytes = 4;
+  static constexpr int kSub = BS / 16;
+  static constexpr int kKLoads = D / 16;     // per sub-tile: 16 bytes = 4 d at one token
   static constexpr int kDt = D / 16;
-  using KRegs = f32x4[kKLoads];
-  using VRegs = f32x4[kDt];                  // 4 fp32 tokens of one d per tile
+  using KRegs = f32x4[kSub][kKLoads];
+  using VRegs = f32x4[kSub][kDt];            // 4 fp32 tokens of one d per tile and sub-tile
   using QRegs = f32x4[kKLoads];
   using QElem = float;
   using OutElem = float;
   struct Lane { uint32_t k, v; };
 
+  // V: lane (i + 16*q4) of tile dt, sub-tile t reads tokens
+  // tile_token(t, q4, 0..3) (consecutive) of d = 16*dt + i. With 32-token
+  // blocks a V row is 128 bytes and one instruction reads half of each.
   __device__ static Lane lane_offsets(int lane) {
-    return {(uint32_t)lane * 16u, (uint32_t)((lane & 15) * 64 + (lane >> 4) * 16)};
+    const int q4 = lane >> 4, rho = lane & 15;
+    return {(uint32_t)(q4 * BS * 16 + k_row_token<BS>(rho) * 16),
+            (uint32_t)(rho * BS * 4 + tile_token<BS>(0, q4, 0) * 4)};
   }
   __device__ static void load_k(const char* t, const Lane& lo, KRegs& k) {
 #pragma unroll
-    for (int s = 0; s < kKLoads; ++s)
-      k[s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(t + lo.k + s * 1024));
+    for (int st = 0; st < kSub; ++st)
+#pragma unroll
+      for (int s = 0; s < kKLoads; ++s)
+        k[st][s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(t + lo.k + s * 4 * BS * 16 + st * 128));
   }
   __device__ static void load_v(const char* t, const Lane& lo, VRegs& v) {
 #pragma unroll
-    for (int dt = 0; dt < kDt; ++dt)
-      v[dt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(t + lo.v + dt * 1024));
+    for (int st = 0; st < kSub; ++st)
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt)
+        v[st][dt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(t + lo.v + dt * 16 * BS * 4 + st * 32));
   }
+  __device__ static void prepare_v(VRegs&) {}
   // load s holds d = 4*(4s+q4) + u, u = 0..3 (one MFMA step per u).
   __device__ static void load_q(const QElem* qh, bool active, int q4, QRegs& q) {
 #pragma unroll
@@ -199,55 +267,118 @@ struct PolicyF32 {
       q[s] = w;
     }
   }
-  __device__ static f32x4 qk(const KRegs& k, const QRegs& q) {
+  __device__ static f32x4 qk(const KRegs& k, const QRegs& q, int st) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < kKLoads; ++s)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k[s][u], q[s][u], acc, 0, 0, 0);
+      for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k[st][s][u], q[s][u], acc, 0, 0, 0);
     return acc;
   }
   __device__ static void mask_v(VRegs& v, int q4, int nvalid) {
 #pragma unroll
-    for (int dt = 0; dt < kDt; ++dt)
+    for (int st = 0; st < kSub; ++st)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (4 * q4 + u >= nvalid) v[dt][u] = 0.f;
+      for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (tile_token<BS>(st, q4, u) >= nvalid) v[st][dt][u] = 0.f;
   }
-  // 16x16x4: reduction slot q4 of step r is token 4*q4 + r.
-  __device__ static void pv(const VRegs& v, f32x4 p, f32x4 (&o)[kDt]) {
+  // 16x16x4: reduction slot q4 of step r is row 4*q4 + r.
+  __device__ static void pv(const VRegs& v, f32x4 p, f32x4 (&o)[kDt], int st) {
 #pragma unroll
     for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(v[dt][r], p[r], o[dt], 0, 0, 0);
+      for (int r = 0; r < 4; ++r) o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(v[st][dt][r], p[r], o[dt], 0, 0, 0);
   }
 };
 
 // bf16 query, fp8 e4m3fn cache (x = 16): codes are converted to bf16 in
 // registers (exact); k_scale and v_scale are applied as scalars outside.
-template <int D>
-struct PolicyFp8 {
-  static constexpr int kKLoads = D / 64;     // 16 bytes = 16 d at one token
+// The V side is common to every head size.
+template <int D, int BS>
+struct Fp8VPart {
+  static constexpr int kBS = BS;
+  static constexpr int kKvElemBytes = 1;
+  static constexpr int kSub = BS / 16;
   static constexpr int kDt = D / 16;
-  using KRegs = u32x4[kKLoads];
-  using VRegs = unsigned[kDt];               // 4 codes: tokens 4*q4..+3 of one d
-  using QRegs = bf16x8[2 * kKLoads];
+  using VVec = typename Pick<BS == 16, unsigned, u32x2>::type;   // 4 codes per dword
+  using VRegs = VVec[kDt];
   using QElem = __bf16;
   using OutElem = __bf16;
   struct Lane { uint32_t k, v; };
 
-  __device__ static Lane lane_offsets(int lane) {
-    return {(uint32_t)lane * 16u, (uint32_t)((lane & 15) * 16 + (lane >> 4) * 4)};
+  // Dword of sub-tile st: codes of tokens tile_token(st, q4, 0..3).
+  __device__ static unsigned vword(const VVec& w, int st) {
+    if constexpr (BS == 16) return w;
+    else return w[st];
   }
-  __device__ static void load_k(const char* t, const Lane& lo, KRegs& k) {
-#pragma unroll
-    for (int h = 0; h < kKLoads; ++h)
-      k[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(t + lo.k + h * 1024));
+  __device__ static void set_vword(VVec& w, int st, unsigned x) {
+    if constexpr (BS == 16) w = x;
+    else w[st] = x;
   }
+  // lane (i + 16*q4) of tile dt reads BS/4 consecutive codes of d = 16*dt + i.
+  __device__ static uint32_t v_offset(int lane) { return (uint32_t)((lane & 15) * BS + (lane >> 4) * (BS / 4)); }
   __device__ static void load_v(const char* t, const Lane& lo, VRegs& v) {
 #pragma unroll
     for (int dt = 0; dt < kDt; ++dt)
-      v[dt] = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(t + lo.v + dt * 256));
+      v[dt] = __builtin_nontemporal_load(reinterpret_cast<const VVec*>(t + lo.v + dt * 16 * BS));
+  }
+  __device__ static void prepare_v(VRegs& v) {
+    if constexpr (BS == 32) {
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) {
+        unsigned w0 = v[dt][0], w1 = v[dt][1];
+        split_rows(w0, w1);
+        v[dt] = VVec{w0, w1};
+      }
+    }
+  }
+  __device__ static void mask_v(VRegs& v, int q4, int nvalid) {
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+      for (int st = 0; st < kSub; ++st) {
+        unsigned x = vword(v[dt], st);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (tile_token<BS>(st, q4, u) >= nvalid) x &= ~(0xFFu << (8 * u));
+        set_vword(v[dt], st, x);
+      }
+  }
+  __device__ static void pv(const VRegs& v, f32x4 p, f32x4 (&o)[kDt], int st) {
+    const s16x4 pb = pack_bf16x4(p);
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt) {
+      const unsigned w = vword(v[dt], st);
+      u32x2 a;
+      a[0] = fp8x2_to_bf16x2<false>(w);
+      a[1] = fp8x2_to_bf16x2<true>(w);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), pb, o[dt], 0, 0, 0);
+    }
+  }
+};
+
+template <int D, int BS = 16>
+struct PolicyFp8 : Fp8VPart<D, BS> {
+  using Base = Fp8VPart<D, BS>;
+  using Lane = typename Base::Lane;
+  using QElem = typename Base::QElem;
+  static constexpr int kSub = Base::kSub;
+  static constexpr int kKLoads = D / 64;     // per sub-tile: 16 bytes = 16 d at one token
+  using KRegs = u32x4[kSub][kKLoads];
+  using QRegs = bf16x8[2 * kKLoads];
+
+  __device__ static Lane lane_offsets(int lane) {
+    const int q4 = lane >> 4, rho = lane & 15;
+    return {(uint32_t)(q4 * BS * 16 + k_row_token<BS>(rho) * 16), Base::v_offset(lane)};
+  }
+  __device__ static void load_k(const char* t, const Lane& lo, KRegs& k) {
+#pragma unroll
+    for (int st = 0; st < kSub; ++st)
+#pragma unroll
+      for (int h = 0; h < kKLoads; ++h)
+        k[st][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(t + lo.k + h * 4 * BS * 16 + st * 128));
   }
   // load h of lane quad q4 is chunk 4h + q4 (16 d); step 2h + half uses the
   // 8 d starting at 16*(4h+q4) + 8*half.
@@ -261,40 +392,57 @@ struct PolicyFp8 {
         q[2 * h + half] = __builtin_bit_cast(bf16x8, w);
       }
   }
-  __device__ static f32x4 qk(const KRegs& k, const QRegs& q) {
+  __device__ static f32x4 qk(const KRegs& k, const QRegs& q, int st) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < kKLoads; ++h)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         u32x4 a;
-        a[0] = fp8x2_to_bf16x2<false>(k[h][2 * half]);
-        a[1] = fp8x2_to_bf16x2<true>(k[h][2 * half]);
-        a[2] = fp8x2_to_bf16x2<false>(k[h][2 * half + 1]);
-        a[3] = fp8x2_to_bf16x2<true>(k[h][2 * half + 1]);
+        a[0] = fp8x2_to_bf16x2<false>(k[st][h][2 * half]);
+        a[1] = fp8x2_to_bf16x2<true>(k[st][h][2 * half]);
+        a[2] = fp8x2_to_bf16x2<false>(k[st][h][2 * half + 1]);
+        a[3] = fp8x2_to_bf16x2<true>(k[st][h][2 * half + 1]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), q[2 * h + half], acc, 0, 0, 0);
       }
     return acc;
   }
-  __device__ static void mask_v(VRegs& v, int q4, int nvalid) {
-#pragma unroll
-    for (int dt = 0; dt < kDt; ++dt) {
-      unsigned x = v[dt];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (4 * q4 + u >= nvalid) x &= ~(0xFFu << (8 * u));
-      v[dt] = x;
-    }
+};
+
+// Head size 32 with an fp8 cache: a token has only two 16-byte K chunks, so
+// each lane quad reads half a chunk. Quad q4 takes d = 8*q4 .. 8*q4 + 7
+// (chunk q4 >> 1, bytes 8*(q4 & 1)); one 16x16x32 step covers all 32 d.
+template <int BS>
+struct PolicyFp8<32, BS> : Fp8VPart<32, BS> {
+  using Base = Fp8VPart<32, BS>;
+  using Lane = typename Base::Lane;
+  using QElem = typename Base::QElem;
+  static constexpr int kSub = Base::kSub;
+  using KRegs = u32x2[kSub][1];
+  using QRegs = bf16x8[1];
+
+  __device__ static Lane lane_offsets(int lane) {
+    const int q4 = lane >> 4, rho = lane & 15;
+    return {(uint32_t)((q4 >> 1) * BS * 16 + k_row_token<BS>(rho) * 16 + (q4 & 1) * 8), Base::v_offset(lane)};
   }
-  __device__ static void pv(const VRegs& v, f32x4 p, f32x4 (&o)[kDt]) {
-    const s16x4 pb = pack_bf16x4(p);
+  __device__ static void load_k(const char* t, const Lane& lo, KRegs& k) {
 #pragma unroll
-    for (int dt = 0; dt < kDt; ++dt) {
-      u32x2 a;
-      a[0] = fp8x2_to_bf16x2<false>(v[dt]);
-      a[1] = fp8x2_to_bf16x2<true>(v[dt]);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), pb, o[dt], 0, 0, 0);
-    }
+    for (int st = 0; st < kSub; ++st)
+      k[st][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(t + lo.k + st * 128));
+  }
+  __device__ static void load_q(const QElem* qh, bool active, int q4, QRegs& q) {
+    u32x4 w = {0, 0, 0, 0};
+    if (active) w = *reinterpret_cast<const u32x4*>(qh + 8 * q4);
+    q[0] = __builtin_bit_cast(bf16x8, w);
+  }
+  __device__ static f32x4 qk(const KRegs& k, const QRegs& q, int st) {
+    u32x4 a;
+    a[0] = fp8x2_to_bf16x2<false>(k[st][0][0]);
+    a[1] = fp8x2_to_bf16x2<true>(k[st][0][0]);
+    a[2] = fp8x2_to_bf16x2<false>(k[st][0][1]);
+    a[3] = fp8x2_to_bf16x2<true>(k[st][0][1]);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), q[0], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                   0, 0, 0);
   }
 };
 
@@ -305,12 +453,14 @@ struct PolicyFp8 {
 template <typename P, int D, int NB, bool ALIBI>
 struct WaveAttn {
   static constexpr int kDt = P::kDt;
+  static constexpr int kBS = P::kBS;      // tokens per block (tile)
+  static constexpr int kSub = P::kSub;    // 16-row sub-tiles per tile
   typename P::QRegs q;
   typename P::Lane lo;
   f32x4 o[kDt];
   float m, m_true, lsum;
   float c, slope2;
-  float lane_bias[4];   // slope2 * (4*q4 + r), ALiBi only
+  float lane_bias[4];   // slope2 * (token of row 4*q4 + r in sub-tile 0), ALiBi only
   int lane, q4;
   bool active;          // this lane's column g is a real query head
 
@@ -331,7 +481,7 @@ struct WaveAttn {
     if constexpr (ALIBI) {
       if (active) slope2 = a.alibi_slopes[h] * kLog2e;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) lane_bias[r] = slope2 * (float)(4 * q4 + r);
+      for (int r = 0; r < 4; ++r) lane_bias[r] = slope2 * (float)tile_token<kBS>(0, q4, r);
     }
     m = m_true = kNegInf;
     lsum = 0.f;
@@ -369,8 +519,9 @@ struct WaveAttn {
 
   __device__ void run(const DecodeArgs& a, const char* kh, const char* vh, const int32_t* table_row, int b0,
                       int b1, int L) {
-    const int last_blk = (L - 1) >> 4;
-    const int tail = L - (last_blk << 4);                 // valid slots in the last block, 1..16
+    constexpr int kShift = kBS == 32 ? 5 : 4;
+    const int last_blk = (L - 1) >> kShift;
+    const int tail = L - (last_blk << kShift);           // valid slots in the last block, 1..kBS
     Cursor cur{b0, (b0 + lane < b1) ? table_row[b0 + lane] : 0};
     if constexpr (PA_PIPE) {
       // Two register buffers: the next group's loads are in flight while the
@@ -404,27 +555,34 @@ struct WaveAttn {
 
   __device__ void consume(typename P::KRegs (&kr)[NB], typename P::VRegs (&vr)[NB], int g0, int n, int L,
                           int last_blk, int tail) {
-    f32x4 z[NB];
+    f32x4 z[NB][kSub];
     float mx = kNegInf;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (j < n) {
-        const f32x4 s = P::qk(kr[j], q);
+        P::prepare_v(vr[j]);
         const int blk = g0 + j;
-        if constexpr (ALIBI) {
-          const float base = (float)(blk * kBlock - (L - 1));
 #pragma unroll
-          for (int r = 0; r < 4; ++r) z[j][r] = fmaf(s[r], c, fmaf(slope2, base, lane_bias[r]));
-        } else {
-          z[j] = s * c;
+        for (int st = 0; st < kSub; ++st) {
+          const f32x4 s = P::qk(kr[j], q, st);
+          if constexpr (ALIBI) {
+            const float base = (float)(blk * kBS + 8 * st - (L - 1));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) z[j][st][r] = fmaf(s[r], c, fmaf(slope2, base, lane_bias[r]));
+          } else {
+            z[j][st] = s * c;
+          }
         }
-        if (blk == last_blk && tail < kBlock) {
+        if (blk == last_blk && tail < kBS) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (4 * q4 + r >= tail) z[j][r] = kNegInf;
+          for (int st = 0; st < kSub; ++st)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (tile_token<kBS>(st, q4, r) >= tail) z[j][st][r] = kNegInf;
           P::mask_v(vr[j], q4, tail);
         }
-        mx = fmaxf(mx, max4(z[j]));
+#pragma unroll
+        for (int st = 0; st < kSub; ++st) mx = fmaxf(mx, max4(z[j][st]));
       }
     }
     mx = quad_max(mx);
@@ -440,11 +598,14 @@ struct WaveAttn {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (j < n) {
-        f32x4 p;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[j][r] - m);
-        lsum += (p[0] + p[1]) + (p[2] + p[3]);
-        P::pv(vr[j], p, o);
+        for (int st = 0; st < kSub; ++st) {
+          f32x4 p;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[j][st][r] - m);
+          lsum += (p[0] + p[1]) + (p[2] + p[3]);
+          P::pv(vr[j], p, o, st);
+        }
       }
     }
   }
@@ -485,12 +646,13 @@ __device__ __forceinline__ void split_unit(const DecodeArgs& a, int split, int k
   // With a shared prefix (first_block set), this kernel covers only the
   // sequence's own tokens after the prefix's first_block full blocks and
   // always writes partials, which a merge combines with the prefix's.
-  const int first = a.first_block ? min(max(a.first_block[seq], 0), min(L / kBlock, a.max_first_block)) : 0;
-  const int t0 = first * kBlock;
+  constexpr int kBS = P::kBS;
+  const int first = a.first_block ? min(max(a.first_block[seq], 0), min(L / kBS, a.max_first_block)) : 0;
+  const int t0 = first * kBS;
   const int t_begin = t0 + split * a.split_tokens;
   if (t_begin >= L) return;
-  const int b0 = t_begin / kBlock;
-  const int b1 = min((L + kBlock - 1) / kBlock, (t_begin + a.split_tokens) / kBlock);
+  const int b0 = t_begin / kBS;
+  const int b1 = min((L + kBS - 1) / kBS, (t_begin + a.split_tokens) / kBS);
   const int nsplit_seq = a.first_block ? 0 : (L + a.split_tokens - 1) / a.split_tokens;
 
   WaveAttn<P, D, NB, ALIBI> w;

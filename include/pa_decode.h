@@ -65,8 +65,10 @@ extern "C" {
 #define PA_KV_AUTO      0
 #define PA_KV_FP8_E4M3  1
 
-/* Fixed sizes: tokens per cache block, and the partition granularity of the
- * split-KV path (the 256-token partitions of the PR #47361 report). */
+/* Fixed sizes: the kernels' token sub-block (a cache block holds 16 or 32
+ * tokens, walked as one or two 16-token sub-blocks), and the partition
+ * granularity of the split-KV path (the 256-token partitions of the PR
+ * #47361 report). */
 #define PA_BLOCK_SIZE      16
 #define PA_PARTITION_SIZE  256
 #define PA_MAX_GROUP       16   /* num_heads / num_kv_heads */
@@ -131,12 +133,13 @@ int pa_workspace_bytes(int num_seqs, int num_heads, int head_size, int max_seq_l
  *   num_seqs     >= 0 (0 is a no-op).        num_heads, num_kv_heads: > 0,
  *                num_heads % num_kv_heads == 0, group <= PA_MAX_GROUP; query
  *                head h uses kv head h / (num_heads / num_kv_heads).
- *   head_size    64 or 128 (the head sizes of the PR #47361 report's test).
+ *   head_size    32, 64 or 128 (64 and 128 are the PR #47361 report's test sizes;
+ *                32 is among the 10100.com article's kernel instantiations, §5).
  *   num_blocks   physical blocks in each cache (> 0).
  *   scale        finite; multiplies q.k (not the ALiBi term).
  *   block_tables device int32 [num_seqs][max_blocks_per_seq], 4-B aligned.
  *   seq_lens     device int32 [num_seqs].
- *   block_size   must be PA_BLOCK_SIZE.
+ *   block_size   tokens per cache block: 16 or 32.
  *   max_seq_len  >= every seq_lens[s], <= max_blocks_per_seq * block_size.
  *   alibi_slopes device fp32 [num_heads] or NULL; adds
  *                slope[h] * (t - (seq_len - 1)) to the logit of token t.
@@ -204,19 +207,20 @@ int pa_hbm_gather_probe(const void* pool, size_t pool_bytes, int tile_bytes, con
  * the step before attention in every decode iteration (the cache grows one
  * token per step; "vLLM 0.25.0 解读" §1). Token j (0 <= j < tokens_per_seq)
  * of sequence s goes to logical position p = positions[s] + j, i.e. physical
- * block block_tables[s, p / 16], slot p % 16 (10100.com retirement article,
- * §1), written in the cache layouts described by pa_kv_layout.
+ * block block_tables[s, p / block_size], slot p % block_size (10100.com
+ * retirement article, §1), written in the cache layouts described by
+ * pa_kv_layout.
  *   key_cache, value_cache  device, the caches (16-B aligned); written only at
  *                the slots named by the positions.
  *   key, value   device, [num_seqs][tokens_per_seq][num_kv_heads][head_size],
  *                element type in_dtype, contiguous, 16-B aligned.
  *   num_seqs >= 0 (0 is a no-op); tokens_per_seq >= 1; num_kv_heads > 0;
- *   head_size 64 or 128; num_blocks > 0; max_blocks_per_seq > 0 (table
- *   stride); block_size must be PA_BLOCK_SIZE;
+ *   head_size 32, 64 or 128; num_blocks > 0; max_blocks_per_seq > 0 (table
+ *   stride); block_size 16 or 32;
  *   num_seqs * tokens_per_seq * num_kv_heads < 2^31.
  *   block_tables device int32 [num_seqs][max_blocks_per_seq]; positions device
  *   int32 [num_seqs]. A negative position skips the sequence; positions past
- *   max_blocks_per_seq*16 and table entries outside [0, num_blocks) are not
+ *   max_blocks_per_seq*block_size and table entries outside [0, num_blocks) are not
  *   written.
  *   in_dtype: PA_DTYPE_F32 or PA_DTYPE_BF16. kv_cache_dtype: PA_KV_AUTO (the
  *   cache holds in_dtype and the rows are copied unchanged) or
@@ -249,8 +253,8 @@ int pa_kv_cache_append(void* key_cache, void* value_cache, const void* key, cons
  *   group_seqs[group_start[g] .. group_start[g+1]) (num_members entries in
  *   all; each sequence in at most one group); group_prefix_blocks
  *   [num_groups]: P_g, the number of leading logical blocks all members map
- *   to the same physical blocks, each member holding at least P_g * 16
- *   tokens; seq_prefix_blocks [num_seqs]: P_g of the sequence's group, 0 if
+ *   to the same physical blocks, each member holding at least
+ *   P_g * block_size tokens; seq_prefix_blocks [num_seqs]: P_g of the sequence's group, 0 if
  *   it is in none. max_group_size >= the largest group (host), and
  *   max_prefix_blocks >= every P_g (host; P_g beyond it are cut to it).
  *   Sequences in no group are computed as by the plain call.
@@ -259,8 +263,8 @@ int pa_kv_cache_append(void* key_cache, void* value_cache, const void* key, cons
  * access outside the arrays (ids and offsets are clamped).
  */
 int pa_shared_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size,
-                              int max_seq_len, int num_groups, int max_group_size,
-                              int max_prefix_blocks, size_t* bytes);
+                              int block_size, int max_seq_len, int num_groups,
+                              int max_group_size, int max_prefix_blocks, size_t* bytes);
 
 int pa_paged_attention_decode_shared(void* out, const void* query, const void* key_cache,
                                      const void* value_cache, int num_seqs, int num_heads,

@@ -76,7 +76,8 @@ def call(pa, **over):
 @pytest.mark.parametrize("over,code", [
     (dict(out=None), -1), (dict(query=None), -1), (dict(key_cache=None), -1),
     (dict(value_cache=None), -1), (dict(block_tables=None), -1), (dict(seq_lens=None), -1),
-    (dict(head_size=96), -2), (dict(head_size=256), -2), (dict(block_size=32), -2),
+    (dict(head_size=96), -2), (dict(head_size=256), -2), (dict(head_size=16), -2), (dict(block_size=8), -2),
+    (dict(block_size=64), -2), (dict(block_size=32, max_seq_len=129), -2),
     (dict(num_heads=6, num_kv_heads=4), -2), (dict(num_heads=64, num_kv_heads=2), -2),
     (dict(num_kv_heads=0), -2), (dict(num_seqs=-1), -2), (dict(num_blocks=0), -2),
     (dict(max_blocks_per_seq=0), -2), (dict(max_seq_len=65), -2), (dict(max_seq_len=-1), -2),
@@ -154,6 +155,12 @@ def test_kv_layout_matches_generator(pa):
         c = workloads.make_case(cfg.with_(pool_blocks=16, num_seqs=1, seq_lens=("fixed", (5,))))
         assert k_shape[1:] == tuple(c.key_cache.shape[1:])
         assert v_shape[1:] == tuple(c.value_cache.shape[1:])
+        lay32 = pa.pa_kv_layout(cfg.num_kv_heads, cfg.head_size, 32, q, kv)
+        assert lay32["k_head_stride"] == cfg.head_size * 32 and lay32["x"] == lay["x"]
+        c32 = workloads.make_case(cfg.with_(pool_blocks=8, num_seqs=1, seq_lens=("fixed", (5,)), block_size=32))
+        k32, v32 = pa.kv_cache_shapes(8, cfg.num_kv_heads, cfg.head_size,
+                                      torch.float32 if q == 0 else torch.bfloat16, cfg.kv_dtype, 32)
+        assert k32 == tuple(c32.key_cache.shape) and v32 == tuple(c32.value_cache.shape)
 
 
 def test_tensor_call_refuses_cpu_tensors(pa):
@@ -207,7 +214,8 @@ APPEND = dict(key_cache=0x10000, value_cache=0x20000, key=0x30000, value=0x40000
 
 @pytest.mark.parametrize("over,code", [
     (dict(key_cache=None), -1), (dict(value=None), -1), (dict(positions=None), -1),
-    (dict(block_tables=None), -1), (dict(head_size=96), -2), (dict(block_size=32), -2),
+    (dict(block_tables=None), -1), (dict(head_size=96), -2), (dict(block_size=8), -2),
+    (dict(block_size=64), -2), (dict(block_size=24), -2),
     (dict(tokens_per_seq=0), -2), (dict(num_kv_heads=0), -2), (dict(num_blocks=0), -2),
     (dict(max_blocks_per_seq=0), -2), (dict(num_seqs=-1), -2),
     (dict(num_seqs=1 << 20, tokens_per_seq=1 << 10, num_kv_heads=8), -2),

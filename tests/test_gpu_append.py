@@ -23,14 +23,15 @@ def host(t):
     return t.numpy()
 
 
-def make(in_kind, kv_kind, S, T, hkv, d, pool, seed, positions=None, k_scale=None, v_scale=None):
-    """Random caches (garbage in every slot), a scattered table, new tokens."""
+def make(in_kind, kv_kind, S, T, hkv, d, pool, seed, positions=None, k_scale=None, v_scale=None, bs=16):
+    """Random caches (garbage in every slot) of bs-token blocks, a scattered
+    table, new tokens."""
     g = torch.Generator(device=DEV)
     g.manual_seed(seed)
     rng = np.random.default_rng(seed)
     elem = kv_kind if kv_kind != "e4m3fn" else "fp8_e4m3"
     x = 16 // workloads.generate.ELEM_BYTES[elem]
-    kshape, vshape = (pool, hkv, d // x, 16, x), (pool, hkv, d, 16)
+    kshape, vshape = (pool, hkv, d // x, bs, x), (pool, hkv, d, bs)
     if kv_kind == "e4m3fn":
         kc = torch.randint(0, 256, kshape, generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
         vc = torch.randint(0, 256, vshape, generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
@@ -40,7 +41,7 @@ def make(in_kind, kv_kind, S, T, hkv, d, pool, seed, positions=None, k_scale=Non
     max_blocks = pool // S
     table = rng.permutation(pool)[:S * max_blocks].reshape(S, max_blocks).astype(np.int32)
     if positions is None:
-        positions = rng.integers(-1, max_blocks * 16 - T + 1, S).astype(np.int32)
+        positions = rng.integers(-1, max_blocks * bs - T + 1, S).astype(np.int32)
     key = (torch.randn((S, T, hkv, d), generator=g, device=DEV) * 3).to(TORCH[in_kind])
     value = (torch.randn((S, T, hkv, d), generator=g, device=DEV) * 3).to(TORCH[in_kind])
     return dict(kc=kc, vc=vc, table=torch.from_numpy(table).to(DEV),
@@ -75,7 +76,8 @@ def check(c, in_kind, kv_kind, what):
 @pytest.mark.parametrize("in_kind,kv_kind,d", [("bf16", "bf16", 128), ("bf16", "bf16", 64),
                                                ("f32", "f32", 64), ("f32", "f32", 128),
                                                ("bf16", "e4m3fn", 128), ("bf16", "e4m3fn", 64),
-                                               ("f32", "e4m3fn", 128)])
+                                               ("f32", "e4m3fn", 128), ("bf16", "bf16", 32),
+                                               ("f32", "f32", 32), ("bf16", "e4m3fn", 32)])
 @pytest.mark.parametrize("T", [1, 3, 16, 19])
 def test_append_matches_oracle(in_kind, kv_kind, d, T):
     ks, vs = (0.021, 0.037) if kv_kind == "e4m3fn" else (None, None)
@@ -119,13 +121,14 @@ def grow_tables(case):
     """Give every sequence whose next token starts a new block a fresh,
     unused physical block (what the block allocator does before the append)."""
     meta = case.meta
+    bs = case.cfg.block_size
     used = set(meta.used_blocks.tolist())
     free = (b for b in range(case.cfg.pool_blocks) if b not in used)
     table = case.block_tables.cpu().numpy()
     for s, n in enumerate(meta.seq_lens.tolist()):
-        if n % 16 == 0:
-            assert n // 16 < table.shape[1], "table has no room for the next block"
-            table[s, n // 16] = next(free)
+        if n % bs == 0:
+            assert n // bs < table.shape[1], "table has no room for the next block"
+            table[s, n // bs] = next(free)
     case.block_tables = torch.from_numpy(table).to(DEV)
     meta.block_tables = table
 

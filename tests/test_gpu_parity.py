@@ -83,6 +83,15 @@ def test_head_size_64(name):
     check(workloads.make_case(cfg, device=DEV), what=f"{name}-d64")
 
 
+@pytest.mark.parametrize("name", ["gqa", "fp8", "mha", "long", "tiny128"])
+@pytest.mark.parametrize("split", [0, 256])
+def test_head_size_32(name, split):
+    """Head size 32: one K chunk step for bf16, two for f32, and half-chunk
+    K loads for the fp8 cache (a token has only two 16-byte chunks)."""
+    cfg = SMALL[name].with_(head_size=32)
+    check(workloads.make_case(cfg, device=DEV), split_tokens=split, what=f"{name}-d32")
+
+
 @pytest.mark.parametrize("group", [1, 2, 3, 4, 7, 8, 16])
 @pytest.mark.parametrize("kv", ["auto", "fp8_e4m3"])
 def test_group_sizes(group, kv):

@@ -17,7 +17,7 @@ DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
 def run_shared(case, groups=None):
     import decode_attention_paged_07_amd as pa
     if groups is None:
-        groups = pa.find_prefix_groups(case.meta.block_tables, case.meta.seq_lens)
+        groups = pa.find_prefix_groups(case.meta.block_tables, case.meta.seq_lens, case.cfg.block_size)
     g = pa.prefix_groups(groups, case.cfg.num_seqs, DEV)
     out = torch.empty_like(case.query)
     pa.paged_attention_decode_shared(out, case.query, case.key_cache, case.value_cache, case.cfg.num_kv_heads,
@@ -29,7 +29,8 @@ def run_shared(case, groups=None):
 
 
 def check(case, what, groups=None, seqs=None):
-    print(f"[case] {what}: S={case.cfg.num_seqs} H={case.cfg.num_heads} Hkv={case.cfg.num_kv_heads} "
+    print(f"[case] {what}: bs={case.cfg.block_size} S={case.cfg.num_seqs} H={case.cfg.num_heads} "
+          f"Hkv={case.cfg.num_kv_heads} "
           f"D={case.cfg.head_size} kv={case.cfg.kv_dtype} groups={case.cfg.prefix_groups}", flush=True)
     out, groups = run_shared(case, groups)
     torch.cuda.synchronize()
@@ -54,6 +55,12 @@ SMALL = {
                                             prefix_groups=(5, 96)),
     "f32-d64-group4": workloads.TINY.with_(num_seqs=8, num_heads=8, num_kv_heads=4, pool_blocks=256,
                                            seq_lens=("uniform", 1, 100), prefix_groups=(4, 64)),
+    "gqa8-d32-group8": workloads.GQA.with_(num_seqs=16, pool_blocks=1024, seq_lens=("uniform", 1, 600),
+                                           prefix_groups=(8, 320), head_size=32),
+    "fp8-d32-group8": workloads.FP8.with_(num_seqs=16, pool_blocks=1024, seq_lens=("uniform", 1, 500),
+                                          prefix_groups=(8, 480), head_size=32),
+    "f32-d32-group4": workloads.TINY.with_(num_seqs=8, num_heads=8, num_kv_heads=4, pool_blocks=256,
+                                           seq_lens=("uniform", 1, 100), prefix_groups=(4, 64), head_size=32),
 }
 
 

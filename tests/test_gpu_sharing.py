@@ -66,8 +66,8 @@ def dense_reference(q, ks, vs, scale, kv_kind, k_scale=1.0, v_scale=1.0):
     return out
 
 
-@pytest.mark.parametrize("kv", ["auto", "fp8"])
-def test_parallel_sampling_shares_the_prompt(kv):
+@pytest.mark.parametrize("kv,bs", [("auto", 16), ("fp8", 16), ("auto", 32), ("fp8", 32)])
+def test_parallel_sampling_shares_the_prompt(kv, bs):
     """A 37-token prompt is written once; four children fork it, so all five
     sequences map the prompt to the same physical blocks. Each then decodes
     several tokens of its own: the first write into the shared, partially
@@ -75,7 +75,7 @@ def test_parallel_sampling_shares_the_prompt(kv):
     Every sequence must attend over exactly its own tokens."""
     import decode_attention_paged_07_amd as pa
     from tests import _run
-    hkv, h, d, bs, max_blocks = 2, 8, 128, 16, 8
+    hkv, h, d, max_blocks = 2, 8, 128, 8
     pool = pa.BlockPool(48, bs)
     fp8 = kv == "fp8"
     ks_, vs_ = (0.011, 0.013) if fp8 else (1.0, 1.0)
@@ -120,7 +120,7 @@ def test_parallel_sampling_shares_the_prompt(kv):
     def rnd(n):
         return torch.randn((n, hkv, d), generator=g, device=DEV).to(torch.bfloat16)
 
-    print(f"[case] parallel sampling kv={kv}", flush=True)
+    print(f"[case] parallel sampling kv={kv} block_size={bs}", flush=True)
     write(0, rnd(37), rnd(37))                                 # prompt: blocks 0..2, block 2 partial
     for c in (1, 2, 3, 4):
         rows[c] = np.zeros(max_blocks, np.int32)

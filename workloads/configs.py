@@ -64,5 +64,9 @@ FP8 = DecodeConfig("fp8", 256, 64, 8, 128, 16, 128 * 1024, "bf16", "fp8_e4m3",
 SHARED = DecodeConfig("shared", 128, 64, 8, 128, 16, 128 * 1024, "bf16", "auto",
                       ("uniform", 1, 512), False, 5, prefix_groups=(8, 4096))
 
+# The GQA workload with 32-token blocks: same lengths (same seed), same pool
+# capacity in tokens.
+GQA32 = GQA.with_(name="gqa32", block_size=32, pool_blocks=64 * 1024)
+
 CONFIGS = {c.name: c for c in (TINY, MHA, GQA, LONG, FP8)}
-EXTRA_CONFIGS = {c.name: c for c in (SHARED,)}
+EXTRA_CONFIGS = {c.name: c for c in (SHARED, GQA32)}
