@@ -17,8 +17,8 @@ Sources (cited by page title and section):
     to non-contiguous physical blocks through a per-sequence table; shared
     blocks).
 
-Parity status of each function is listed in ``decode_fp64.PINS`` and
-``kv_append.PINS``.
+Parity status of each function is listed in ``decode_fp64.PINS``,
+``kv_append.PINS`` and ``decode_fp8_compute.PINS``.
 """
 
 from .decode_fp64 import (  # noqa: F401
@@ -36,3 +36,10 @@ from .decode_fp64 import (  # noqa: F401
 )
 from .kv_append import PINS as APPEND_PINS  # noqa: F401,E402
 from .kv_append import append_tokens, quantise_e4m3fn  # noqa: F401,E402
+from .decode_fp8_compute import PINS as FP8_COMPUTE_PINS  # noqa: F401,E402
+from .decode_fp8_compute import (  # noqa: F401,E402
+    mx_dequantise,
+    mx_quantise_e4m3,
+    paged_decode_fp8_compute,
+    round_to_e4m3fn,
+)

@@ -54,3 +54,27 @@ def worked_example(alibi=False):
         "block_tables": np.array([[phys]], np.int32), "seq_lens": np.array([n], np.int32),
         "scale": scale, "alibi_slopes": slopes, "expect": expect,
     }
+
+
+def fp8_compute_example():
+    """Inputs (bf16 q bits, e4m3 caches in the pages' layouts, x = 16) and the
+    closed-form output of the hand-derived fp8-arithmetic example."""
+    rows = {r[0]: r[1:] for r in _rows("fp8_compute_example.txt")}
+    d, bs = int(rows["head_size"][0]), int(rows["block_size"][0])
+    scale = float(rows["scale"][0])
+    x, pool, phys = 16, 4, 2
+    k_pool = np.zeros((pool, 1, d // x, bs, x), np.uint8)
+    v_pool = np.zeros((pool, 1, d, bs), np.uint8)
+    k_pool[phys, 0, 0, 0, 0] = int(rows["k0"][0])
+    k_pool[phys, 0, 0, 1, 0] = int(rows["k1"][0])
+    for t, key in enumerate(("v0", "v1")):
+        for dd, code in enumerate(rows[key]):
+            v_pool[phys, 0, dd, t] = int(code)
+    q = np.zeros((1, 1, d), np.uint16)
+    q[0, 0, 0] = 0x3F80                                  # bf16 1.0
+    expect = np.zeros((1, 1, d))
+    expect[0, 0, 0] = float(rows["out0"][0])
+    expect[0, 0, 1] = float(rows["out1"][0])
+    return dict(query=q, key_cache=k_pool, value_cache=v_pool,
+                block_tables=np.array([[phys]], np.int32), seq_lens=np.array([2], np.int32),
+                scale=scale, q_code=int(rows["q_code_block0"][0]), expect=expect)
