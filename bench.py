@@ -38,6 +38,8 @@ WORKLOAD_TEXT = {
             "131072-block pool",
     "fp8": "fp8 e4m3 KV cache: 256 seqs, lognormal lens (median 4096, sigma 1, cap 16384, seed 4), "
            "64/8 heads, D=128, bs=16, bf16 q, 131072-block pool",
+    "fp8c": "fp8 e4m3 KV cache with fp8 arithmetic (MX fp8 q, e4m3 P, fp8 MFMA): 256 seqs, lognormal lens "
+            "(median 4096, sigma 1, cap 16384, seed 4), 64/8 heads, D=128, bs=16, bf16 q, 131072-block pool",
     "gqa32": "bf16 GQA decode with 32-token blocks: 128 seqs, lens U[1,8192] (seed 2), 64/8 heads, D=128, "
              "bs=32, 65536-block pool",
     "shared": "shared-prompt decode: 16 prompts of 4096 tokens x 8 samples each (128 seqs), own lens U[1,512] "
@@ -395,10 +397,16 @@ def cpu_baseline(case, budget_s: float):
             seqs = list(range(i, min(n, i + step)))
             h = workloads.host_arrays(case, seqs)           # host copy, not timed
             t0, c0 = time.perf_counter(), time.process_time()
-            ref = oracle.paged_decode(h["query"], h["key_cache"], h["value_cache"], h["block_tables"],
-                                      h["seq_lens"], h["scale"], q_kind=h["q_kind"],
-                                      kv_kind=h["kv_kind"], alibi_slopes=h["alibi_slopes"],
-                                      k_scale=h["k_scale"], v_scale=h["v_scale"])
+            if case.cfg.compute == "fp8":
+                ref = oracle.paged_decode_fp8_compute(h["query"], h["key_cache"], h["value_cache"],
+                                                      h["block_tables"], h["seq_lens"], h["scale"],
+                                                      k_scale=h["k_scale"], v_scale=h["v_scale"],
+                                                      alibi_slopes=h["alibi_slopes"])
+            else:
+                ref = oracle.paged_decode(h["query"], h["key_cache"], h["value_cache"], h["block_tables"],
+                                          h["seq_lens"], h["scale"], q_kind=h["q_kind"],
+                                          kv_kind=h["kv_kind"], alibi_slopes=h["alibi_slopes"],
+                                          k_scale=h["k_scale"], v_scale=h["v_scale"])
             wall += time.perf_counter() - t0
             cpu += time.process_time() - c0
             done.append((seqs, ref))
@@ -410,7 +418,8 @@ def cpu_baseline(case, budget_s: float):
     tokens = int(case.meta.seq_lens[:nseq].astype("int64").sum())
     return {
         "value": nseq / wall, "unit": "seqs/s", "cores": cores, "kind": "oracle",
-        "sample": f"first {nseq} of {n} sequences ({tokens} tokens), fp64 numpy oracle, "
+        "sample": f"first {nseq} of {n} sequences ({tokens} tokens), fp64 numpy oracle"
+                  f"{' (fp8-arithmetic definition)' if case.cfg.compute == 'fp8' else ''}, "
                   f"host copy untimed, {wall:.1f} s wall",
         "cpu_util": round(cpu / wall, 2) if wall > 0 else None,
     }, done
@@ -488,7 +497,7 @@ def main():
                                   case.scale, case.block_tables, case.seq_lens, cfg.block_size,
                                   case.max_seq_len, alibi_slopes=case.alibi_slopes,
                                   kv_cache_dtype=cfg.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale,
-                                  split_tokens=args.split)
+                                  split_tokens=args.split, compute=cfg.compute)
 
     for _ in range(args.warmup):
         step()
@@ -527,6 +536,8 @@ def main():
     dtype = {"f32": "f32", "bf16": "bf16"}[cfg.q_dtype]
     if cfg.kv_dtype == "fp8_e4m3":
         dtype = "bf16 (fp8 e4m3 KV dequantised to bf16)"
+    if cfg.compute == "fp8":
+        dtype = "fp8 (e4m3 MFMA operands: MX-scaled q, e4m3 K, P and V; fp32 accumulation)"
     rec = {
         "metric": METRIC,
         "value": round(seqs_per_s, 1),
@@ -579,7 +590,13 @@ def main():
         base, done = cpu_baseline(case, args.cpu_seconds)
         worst = (0.0, 0.0)
         for seqs, ref in done:
-            worst = tuple(max(a, b) for a, b in zip(worst, _run.compare(out, ref, cfg.q_dtype, seqs=seqs)))
+            extra = None
+            if cfg.compute == "fp8":            # rounding-boundary allowance of the fp8 arithmetic
+                import workloads
+                from tests import _fp8tol
+                extra = _fp8tol.row_bounds(workloads.host_arrays(case, seqs))
+            worst = tuple(max(a, b) for a, b in
+                          zip(worst, _run.compare(out, ref, cfg.q_dtype, seqs=seqs, extra=extra)))
         base["gpu_speedup"] = round(seqs_per_s / base["value"], 1)
         rec["cpu_baseline"] = base
         rec["parity_on_sample"] = {"max_abs": float(f"{worst[0]:.3e}"), "max_rel": float(f"{worst[1]:.3e}")}

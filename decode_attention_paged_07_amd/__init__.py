@@ -26,7 +26,7 @@ from .build import LIB_PATH
 
 __all__ = [
     "PA_OK", "PA_ERR_NULL", "PA_ERR_SHAPE", "PA_ERR_DTYPE", "PA_ERR_WORKSPACE", "PA_ERR_ALIGN",
-    "PA_ERR_HIP", "PA_DTYPE_F32", "PA_DTYPE_BF16", "PA_KV_AUTO", "PA_KV_FP8_E4M3",
+    "PA_ERR_HIP", "PA_DTYPE_F32", "PA_DTYPE_BF16", "PA_KV_AUTO", "PA_KV_FP8_E4M3", "PA_KV_FP8_E4M3_COMPUTE",
     "PA_BLOCK_SIZE", "PA_PARTITION_SIZE", "PA_MAX_GROUP",
     "pa_paged_attention_decode", "pa_paged_attention_decode_split", "pa_decode_plan",
     "pa_workspace_bytes", "pa_kv_layout", "pa_last_error", "pa_version", "pa_timing_enable",
@@ -51,6 +51,7 @@ PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
 PA_KV_AUTO = 0
 PA_KV_FP8_E4M3 = 1
+PA_KV_FP8_E4M3_COMPUTE = 2
 PA_BLOCK_SIZE = 16
 PA_PARTITION_SIZE = 256
 PA_MAX_GROUP = 16
@@ -434,7 +435,7 @@ def _need(cond, msg):
 def paged_attention_decode(out, query, key_cache, value_cache, num_kv_heads, scale, block_tables,
                            seq_lens, block_size, max_seq_len, alibi_slopes=None,
                            kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0, *, workspace=None,
-                           split_tokens=0) -> None:
+                           split_tokens=0, compute="auto") -> None:
     """Write softmax(scale*q.K^T + alibi).V for every (sequence, query head) into ``out``.
 
     out, query: [num_seqs, num_heads, head_size], float32 or bfloat16, contiguous, on one GPU.
@@ -442,11 +443,19 @@ def paged_attention_decode(out, query, key_cache, value_cache, num_kv_heads, sca
     kv_cache_dtype "auto", uint8 / float8_e4m3fn codes for "fp8" / "fp8_e4m3".
     block_tables int32 [num_seqs, max_blocks]; seq_lens int32 [num_seqs].
     alibi_slopes: float32 [num_heads] or None. k_scale / v_scale: float or one-element float32
-    tensor (used for the fp8 cache only). Runs asynchronously on the current stream.
+    tensor (used for the fp8 cache only). compute: "auto" (bf16/f32 arithmetic) or "fp8"
+    (fp8 cache only: MX-scaled fp8 q and e4m3 P on fp8 MFMA, PA_KV_FP8_E4M3_COMPUTE).
+    Runs asynchronously on the current stream.
     """
     if kv_cache_dtype not in _KV_NAMES:
         raise TypeError(f"kv_cache_dtype {kv_cache_dtype!r} is not one of {sorted(_KV_NAMES)}")
     kvd = _KV_NAMES[kv_cache_dtype]
+    if compute not in ("auto", "fp8"):
+        raise TypeError(f"compute {compute!r} is not 'auto' or 'fp8'")
+    if compute == "fp8":
+        if kvd != PA_KV_FP8_E4M3:
+            raise TypeError("compute='fp8' needs the fp8 cache")
+        kvd = PA_KV_FP8_E4M3_COMPUTE
     if query.dtype not in _Q_DTYPES:
         raise TypeError(f"query dtype {query.dtype} is not float32 or bfloat16")
     qd = _Q_DTYPES[query.dtype]
@@ -479,8 +488,8 @@ def paged_attention_decode(out, query, key_cache, value_cache, num_kv_heads, sca
               and alibi_slopes.device == dev and alibi_slopes.is_contiguous(),
               "alibi_slopes must be contiguous float32 [num_heads] on the query's device")
         slopes_ptr = alibi_slopes.data_ptr()
-    ks = _device_scalar(k_scale, dev) if kvd == PA_KV_FP8_E4M3 else None
-    vs = _device_scalar(v_scale, dev) if kvd == PA_KV_FP8_E4M3 else None
+    ks = _device_scalar(k_scale, dev) if kvd != PA_KV_AUTO else None
+    vs = _device_scalar(v_scale, dev) if kvd != PA_KV_AUTO else None
     if workspace is None:
         _, _, need = pa_decode_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len,
                                     split_tokens)

@@ -37,8 +37,12 @@ bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+bool is_fp8_cache(int kv_cache_dtype) {
+  return kv_cache_dtype == PA_KV_FP8_E4M3 || kv_cache_dtype == PA_KV_FP8_E4M3_COMPUTE;
+}
+
 int elem_bytes_of(int q_dtype, int kv_cache_dtype) {
-  if (kv_cache_dtype == PA_KV_FP8_E4M3) return 1;
+  if (is_fp8_cache(kv_cache_dtype)) return 1;
   return q_dtype == PA_DTYPE_F32 ? 4 : 2;
 }
 
@@ -50,8 +54,7 @@ int check_head_size(int head_size) {
   return PA_OK;
 }
 
-// Cache blocks of 16 or 32 tokens; the kernels walk either as 16-token
-// sub-blocks.
+// Cache blocks of 16 or 32 tokens.
 int check_block_size(int block_size) {
   if (block_size != 16 && block_size != 32) return fail(PA_ERR_SHAPE, "block_size %d is not 16 or 32", block_size);
   return PA_OK;
@@ -60,9 +63,10 @@ int check_block_size(int block_size) {
 int check_dtypes(int q_dtype, int kv_cache_dtype) {
   if (q_dtype != PA_DTYPE_F32 && q_dtype != PA_DTYPE_BF16)
     return fail(PA_ERR_DTYPE, "q_dtype %d is not PA_DTYPE_F32 or PA_DTYPE_BF16", q_dtype);
-  if (kv_cache_dtype != PA_KV_AUTO && kv_cache_dtype != PA_KV_FP8_E4M3)
-    return fail(PA_ERR_DTYPE, "kv_cache_dtype %d is not PA_KV_AUTO or PA_KV_FP8_E4M3", kv_cache_dtype);
-  if (kv_cache_dtype == PA_KV_FP8_E4M3 && q_dtype != PA_DTYPE_BF16)
+  if (kv_cache_dtype != PA_KV_AUTO && !is_fp8_cache(kv_cache_dtype))
+    return fail(PA_ERR_DTYPE, "kv_cache_dtype %d is not PA_KV_AUTO, PA_KV_FP8_E4M3 or PA_KV_FP8_E4M3_COMPUTE",
+                kv_cache_dtype);
+  if (is_fp8_cache(kv_cache_dtype) && q_dtype != PA_DTYPE_BF16)
     return fail(PA_ERR_DTYPE, "the fp8 e4m3 cache requires bf16 queries");
   return PA_OK;
 }
@@ -245,7 +249,7 @@ int fill_decode_args(pa::DecodeArgs& a, void* out, const void* query, const void
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.alibi_slopes = alibi_slopes;
-  const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
+  const bool fp8 = is_fp8_cache(kv_cache_dtype);
   a.k_scale = fp8 ? k_scale : nullptr;
   a.v_scale = fp8 ? v_scale : nullptr;
   a.k_block_stride_bytes = tile * num_kv_heads;
@@ -262,6 +266,7 @@ int fill_decode_args(pa::DecodeArgs& a, void* out, const void* query, const void
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_seq_len = max_seq_len;
+  if (kv_cache_dtype == PA_KV_FP8_E4M3_COMPUTE) return pa::KIND_FP8MX;
   return fp8 ? pa::KIND_FP8 : (q_dtype == PA_DTYPE_F32 ? pa::KIND_F32 : pa::KIND_BF16);
 }
 
@@ -310,14 +315,18 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
   a.split_tokens = plan.split_tokens;
   a.num_splits = plan.num_splits;
   if (plan.streamk) {
-    // Persistent waves per compute unit, measured per cache type: the bf16
-    // path streams best with one wave per SIMD, the fp8 path needs more waves
-    // to overlap its in-register dequantisation with loads.
+    // Persistent waves per compute unit, measured per cache type and block
+    // size: each wave keeps one block's loads in flight, and throughput peaks
+    // at a total of about 8-12 MiB in flight (bf16, 16-token blocks: one wave
+    // per SIMD; fp8 needs more waves to overlap its conversions; 32-token
+    // blocks carry twice the bytes per wave). A fraction leaves some compute
+    // units without a workgroup, which measured faster than spreading them.
     const bool b32 = block_size == 32;
-    const int per_cu = kind == pa::KIND_FP8 ? (b32 ? PA_SK_WAVES_PER_CU_BS32_FP8 : PA_SK_WAVES_PER_CU_FP8)
-                       : kind == pa::KIND_F32 ? (b32 ? PA_SK_WAVES_PER_CU_BS32_F32 : PA_SK_WAVES_PER_CU_F32)
-                                              : (b32 ? PA_SK_WAVES_PER_CU_BS32_BF16 : PA_SK_WAVES_PER_CU_BF16);
-    const int waves = std::min(PA_SK_MAX_WAVES, device_cus() * per_cu);
+    const double per_cu = kind == pa::KIND_FP8MX ? (b32 ? PA_SK_WAVES_PER_CU_BS32_FP8MX : PA_SK_WAVES_PER_CU_FP8MX)
+                          : kind == pa::KIND_FP8 ? (b32 ? PA_SK_WAVES_PER_CU_BS32_FP8 : PA_SK_WAVES_PER_CU_FP8)
+                          : kind == pa::KIND_F32 ? (b32 ? PA_SK_WAVES_PER_CU_BS32_F32 : PA_SK_WAVES_PER_CU_F32)
+                                                 : (b32 ? PA_SK_WAVES_PER_CU_BS32_BF16 : PA_SK_WAVES_PER_CU_BF16);
+    const int waves = std::min(PA_SK_MAX_WAVES, (int)(device_cus() * per_cu));
     a.streamk_workgroups = std::max(1, waves / PA_WAVES);
   }
   pa::LaunchHooks hooks;
@@ -523,6 +532,8 @@ int pa_paged_attention_decode_shared(void* out, const void* query, const void* k
   if ((rc = check_shared_plan_args(num_seqs, num_heads, num_kv_heads, head_size, block_size, max_seq_len,
                                    num_groups, max_group_size, max_prefix_blocks)))
     return rc;
+  if (kv_cache_dtype == PA_KV_FP8_E4M3_COMPUTE)
+    return fail(PA_ERR_DTYPE, "the shared-prefix call has no fp8-arithmetic variant; use PA_KV_FP8_E4M3");
   if (num_seqs == 0) return ok();
   if (!seq_prefix_blocks) return fail(PA_ERR_NULL, "seq_prefix_blocks must be non-NULL");
   if (num_groups > 0 && (!group_start || !group_prefix_blocks || (num_members > 0 && !group_seqs)))
@@ -605,8 +616,9 @@ int pa_kv_cache_append(void* key_cache, void* value_cache, const void* key, cons
                        const float* v_scale, void* stream) {
   if (in_dtype != PA_DTYPE_F32 && in_dtype != PA_DTYPE_BF16)
     return fail(PA_ERR_DTYPE, "in_dtype %d is not PA_DTYPE_F32 or PA_DTYPE_BF16", in_dtype);
-  if (kv_cache_dtype != PA_KV_AUTO && kv_cache_dtype != PA_KV_FP8_E4M3)
-    return fail(PA_ERR_DTYPE, "kv_cache_dtype %d is not PA_KV_AUTO or PA_KV_FP8_E4M3", kv_cache_dtype);
+  if (kv_cache_dtype != PA_KV_AUTO && !is_fp8_cache(kv_cache_dtype))
+    return fail(PA_ERR_DTYPE, "kv_cache_dtype %d is not PA_KV_AUTO, PA_KV_FP8_E4M3 or PA_KV_FP8_E4M3_COMPUTE",
+                kv_cache_dtype);
   if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
   if (tokens_per_seq < 1) return fail(PA_ERR_SHAPE, "tokens_per_seq %d must be positive", tokens_per_seq);
   if (num_kv_heads <= 0) return fail(PA_ERR_SHAPE, "num_kv_heads %d must be positive", num_kv_heads);
@@ -632,7 +644,7 @@ int pa_kv_cache_append(void* key_cache, void* value_cache, const void* key, cons
   a.value = value;
   a.block_tables = block_tables;
   a.positions = positions;
-  const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
+  const bool fp8 = is_fp8_cache(kv_cache_dtype);
   a.k_scale = fp8 ? k_scale : nullptr;
   a.v_scale = fp8 ? v_scale : nullptr;
   a.num_seqs = num_seqs;

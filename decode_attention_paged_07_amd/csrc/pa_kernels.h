@@ -30,12 +30,18 @@
 #ifndef PA_PIPE
 #define PA_PIPE 1
 #endif
+#ifndef PA_SK_WAVES_PER_CU_FP8MX
+#define PA_SK_WAVES_PER_CU_FP8MX 8
+#endif
+#ifndef PA_SK_WAVES_PER_CU_BS32_FP8MX
+#define PA_SK_WAVES_PER_CU_BS32_FP8MX 4
+#endif
 // 32-token blocks: stream-K waves per compute unit.
 #ifndef PA_SK_WAVES_PER_CU_BS32_BF16
-#define PA_SK_WAVES_PER_CU_BS32_BF16 PA_SK_WAVES_PER_CU_BF16
+#define PA_SK_WAVES_PER_CU_BS32_BF16 3
 #endif
 #ifndef PA_SK_WAVES_PER_CU_BS32_FP8
-#define PA_SK_WAVES_PER_CU_BS32_FP8 PA_SK_WAVES_PER_CU_FP8
+#define PA_SK_WAVES_PER_CU_BS32_FP8 4
 #endif
 #ifndef PA_SK_WAVES_PER_CU_BS32_F32
 #define PA_SK_WAVES_PER_CU_BS32_F32 PA_SK_WAVES_PER_CU_F32
@@ -45,7 +51,8 @@
 
 namespace pa {
 
-enum Kind { KIND_F32 = 0, KIND_BF16 = 1, KIND_FP8 = 2 };
+// KIND_FP8MX: fp8 cache with fp8 arithmetic (MX-scaled q, e4m3 P).
+enum Kind { KIND_F32 = 0, KIND_BF16 = 1, KIND_FP8 = 2, KIND_FP8MX = 3 };
 
 // Everything a launch needs, passed by value as the kernel argument.
 struct DecodeArgs {

@@ -287,6 +287,9 @@ static hipError_t launch_decode_bs(const DecodeArgs& a, int kind, hipStream_t st
     case KIND_FP8 * 1000 + 32: return launch_alibi<PolicyFp8<32, BS>, 32, nb_fp8>(a, stream, hooks);
     case KIND_FP8 * 1000 + 64: return launch_alibi<PolicyFp8<64, BS>, 64, nb_fp8>(a, stream, hooks);
     case KIND_FP8 * 1000 + 128: return launch_alibi<PolicyFp8<128, BS>, 128, nb_fp8>(a, stream, hooks);
+    case KIND_FP8MX * 1000 + 32: return launch_alibi<PolicyFp8Mx<32, BS>, 32, 1>(a, stream, hooks);
+    case KIND_FP8MX * 1000 + 64: return launch_alibi<PolicyFp8Mx<64, BS>, 64, 1>(a, stream, hooks);
+    case KIND_FP8MX * 1000 + 128: return launch_alibi<PolicyFp8Mx<128, BS>, 128, 1>(a, stream, hooks);
     default: return hipErrorInvalidValue;
   }
 }

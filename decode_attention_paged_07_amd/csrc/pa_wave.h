@@ -446,6 +446,154 @@ struct PolicyFp8<32, BS> : Fp8VPart<32, BS> {
   }
 };
 
+// bf16 query, fp8 e4m3fn cache, fp8 arithmetic (the pages' fp8-compute
+// variant, 10100.com §4: the decode runs on fp8 operands and converts once
+// at the output). q is quantised to MX fp8 (blocks of 32 consecutive head
+// dims, one power-of-two scale each); S = K q^T runs on the block-scaled
+// v_mfma_scale_f32_16x16x128_f8f6f4, whose B scales carry q's MX exponents,
+// and O += V^T P on v_mfma_f32_16x16x32_fp8_fp8. Each block's P is quantised
+// to e4m3 relative to 2^ceil(block max); no operand is converted to a wider
+// type.
+//
+// Operand layout of the 16x16x128 MFMA (checked on the GPU with a one-wave
+// probe): lane (i + 16*q4) supplies k = 16*q4 + j from bytes j = 0..15 and
+// k = 64 + 16*q4 + (j - 16) from bytes 16..31; the scale of row i, k-block b
+// (32 consecutive k) comes from lane (i + 16*b). With d = k, lane quad q4's
+// bytes are K chunks q4 and 4 + q4 (the 16-byte loads of PolicyFp8) and its
+// scale is that of q's MX block q4.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// E4M3FN code of y: nearest, ties to even, magnitude saturated at 448,
+// NaN -> 0x7F, sign kept.
+__device__ __forceinline__ unsigned e4m3_code(float y) {
+  if (__builtin_isnan(y)) return 0x7Fu;
+  const float mag = fminf(__builtin_fabsf(y), 448.0f);
+  const unsigned c = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(mag, 0.0f, 0, false) & 0x7Fu;
+  return c | ((__float_as_uint(y) >> 24) & 0x80u);
+}
+
+// MX shared exponent of a block with largest magnitude amax (OCP MX rule for
+// e4m3, whose largest power of two is 2^8): floor(log2 amax) - 8, clamped to
+// the e8m0 range; -127 for an all-zero block, 127 for an infinite amax.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (amax == 0.f) return -127;
+  if (__builtin_isinf(amax)) return 127;
+  const int e = __builtin_amdgcn_frexp_expf(amax) - 1 - 8;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+template <int D, int BS = 16>
+struct PolicyFp8Mx : Fp8VPart<D, BS> {
+  using Base = Fp8VPart<D, BS>;
+  using Lane = typename Base::Lane;
+  using QElem = typename Base::QElem;
+  using VRegs = typename Base::VRegs;
+  static constexpr bool kFp8Math = true;
+  static constexpr int kSub = Base::kSub;
+  static constexpr int kDt = Base::kDt;
+  static constexpr int kKLoads = D == 128 ? 2 : 1;
+  using KRegs = u32x4[kSub][kKLoads];
+  struct QRegs {
+    i32x8 codes;   // MX e4m3 codes of this lane's 32 k slots
+    int scale;     // e8m0 scale of q's MX block q4
+  };
+
+  // Lane quad q4 reads K chunk q4 (and 4 + q4 at D = 128). At D = 32 only
+  // chunks 0 and 1 exist: quads 2 and 3 re-read chunk q4 & 1, which their
+  // zero q codes cancel.
+  __device__ static Lane lane_offsets(int lane) {
+    const int q4 = lane >> 4, rho = lane & 15;
+    const int chunk = D == 32 ? (q4 & 1) : q4;
+    return {(uint32_t)(chunk * BS * 16 + k_row_token<BS>(rho) * 16), Base::v_offset(lane)};
+  }
+  __device__ static void load_k(const char* t, const Lane& lo, KRegs& k) {
+#pragma unroll
+    for (int st = 0; st < kSub; ++st)
+#pragma unroll
+      for (int h = 0; h < kKLoads; ++h)
+        k[st][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(t + lo.k + h * 4 * BS * 16 + st * 128));
+  }
+
+  // Quantise the lane's slots of q (d = 16*q4 + j and, at D = 128,
+  // 64 + 16*q4 + j) with the exponent of the MX block each belongs to; quads
+  // 2k and 2k+1 together hold a block, so one exchange gives its amax.
+  __device__ static void load_q(const QElem* qh, bool active, int q4, QRegs& q) {
+    float a[16], b[16];
+    const bool has_a = active && 16 * q4 < D, has_b = active && D == 128;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 wa = {0, 0, 0, 0}, wb = {0, 0, 0, 0};
+      if (has_a) wa = *reinterpret_cast<const u32x4*>(qh + 16 * q4 + 8 * h);
+      if (has_b) wb = *reinterpret_cast<const u32x4*>(qh + 64 + 16 * q4 + 8 * h);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[8 * h + 2 * u] = __uint_as_float(wa[u] << 16);
+        a[8 * h + 2 * u + 1] = __uint_as_float(wa[u] & 0xFFFF0000u);
+        b[8 * h + 2 * u] = __uint_as_float(wb[u] << 16);
+        b[8 * h + 2 * u + 1] = __uint_as_float(wb[u] & 0xFFFF0000u);
+      }
+    }
+    float ma = 0.f, mb = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      ma = fmaxf(ma, __builtin_fabsf(a[j]));
+      mb = fmaxf(mb, __builtin_fabsf(b[j]));
+    }
+    ma = fmaxf(ma, __shfl_xor(ma, 16, 64));
+    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+    const int xa = mx_exponent(ma), xb = mx_exponent(mb);   // blocks q4 >> 1 and 2 + (q4 >> 1)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      unsigned ca = 0, cb = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        ca |= e4m3_code(__builtin_ldexpf(a[4 * w + u], -xa)) << (8 * u);
+        cb |= e4m3_code(__builtin_ldexpf(b[4 * w + u], -xb)) << (8 * u);
+      }
+      q.codes[w] = (int)ca;
+      q.codes[4 + w] = (int)cb;
+    }
+    // Block q4's exponent: quad 0 holds block 0 (its a), quad 3 block 3 (its
+    // b); block 1 is quad 2's a, block 2 quad 1's b.
+    const int lane = threadIdx.x & 63;
+    const int from_up = __shfl(xa, (lane + 16) & 63, 64);
+    const int from_down = __shfl(xb, (lane + 48) & 63, 64);
+    const int x = q4 == 0 ? xa : q4 == 1 ? from_up : q4 == 2 ? from_down : xb;
+    q.scale = 32 * q4 < D ? 127 + x : 127;
+  }
+  __device__ static f32x4 qk(const KRegs& k, const QRegs& q, int st) {
+    i32x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] = (int)k[st][0][u];
+    if constexpr (kKLoads == 2) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[4 + u] = (int)k[st][1][u];
+    }
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, q.codes, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0,
+                                                            q.scale);
+  }
+  // O += 2^e * V^T P on v_mfma_f32_16x16x32_fp8_fp8 (k = 8*q4 + j from byte j
+  // of lane quad q4): bytes 0-3 of A and B are sub-tile 0's four rows of the
+  // quad, bytes 4-7 sub-tile 1's (zero with 16-token blocks). Each block's
+  // product is formed from zero and added to O in fp32 with the exact factor
+  // 2^e, so the sum over blocks is an fp32 sum.
+  __device__ static void pv8(const VRegs& v, unsigned p0, unsigned p1, float f, f32x4 (&o)[kDt]) {
+    const long b = (long)(((unsigned long)p1 << 32) | p0);
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt) {
+      const unsigned w1 = kSub == 2 ? Base::vword(v[dt], kSub - 1) : 0u;
+      const long a = (long)(((unsigned long)w1 << 32) | Base::vword(v[dt], 0));
+      const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[dt][r] = fmaf(t[r], f, o[dt][r]);
+    }
+  }
+};
+
+// Whether a policy runs the fp8 arithmetic (PolicyFp8Mx).
+template <typename P, typename = void> struct Fp8Math { static constexpr bool value = false; };
+template <typename P> struct Fp8Math<P, decltype((void)P::kFp8Math)> { static constexpr bool value = P::kFp8Math; };
+
 // ---------------------------------------------------------------------------
 // One wave's attention over a run of blocks of one (sequence, kv head).
 // ---------------------------------------------------------------------------
@@ -587,27 +735,64 @@ struct WaveAttn {
     }
     mx = quad_max(mx);
     m_true = fmaxf(m_true, mx);
-    if (wave_any(mx > m + kRescaleSlack)) {
-      const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - m_new);
+    if constexpr (Fp8Math<P>::value) {
+      consume_fp8(vr[0], z[0], mx);
+    } else {
+      if (wave_any(mx > m + kRescaleSlack)) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - m_new);
+        m = m_new;
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kDt; ++dt) o[dt] *= alpha;
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (j < n) {
+#pragma unroll
+          for (int st = 0; st < kSub; ++st) {
+            f32x4 p;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[j][st][r] - m);
+            lsum += (p[0] + p[1]) + (p[2] + p[3]);
+            P::pv(vr[j], p, o, st);
+          }
+        }
+      }
+    }
+  }
+
+  // fp8 arithmetic: this block's P is quantised to e4m3 relative to
+  // mb = ceil(block max) (so every p <= 1), multiplied with V on fp8
+  // operands, and brought to the running reference m by the exact factor
+  // 2^(mb - m); m stays an integer.
+  __device__ void consume_fp8(const typename P::VRegs& vr, const f32x4 (&z)[kSub], float mx) {
+    static_assert(NB == 1, "the fp8 arithmetic takes one block per issue");
+    const float mb = ceilf(mx);
+    if (wave_any(mb > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mb);
+      const float alpha = m == kNegInf ? 0.f : __builtin_ldexpf(1.f, (int)(m - m_new));
       m = m_new;
       lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) o[dt] *= alpha;
     }
+    unsigned pw[2] = {0u, 0u};
+    float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if (j < n) {
+    for (int st = 0; st < kSub; ++st) {
+      f32x4 p;
 #pragma unroll
-        for (int st = 0; st < kSub; ++st) {
-          f32x4 p;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[j][st][r] - m);
-          lsum += (p[0] + p[1]) + (p[2] + p[3]);
-          P::pv(vr[j], p, o, st);
-        }
-      }
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[st][r] - mb);
+      unsigned w = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      w = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], (int)w, true);
+      pw[st] = w;
+      s += (__builtin_amdgcn_cvt_f32_fp8((int)w, 0) + __builtin_amdgcn_cvt_f32_fp8((int)w, 1)) +
+           (__builtin_amdgcn_cvt_f32_fp8((int)w, 2) + __builtin_amdgcn_cvt_f32_fp8((int)w, 3));
     }
+    const int e = (int)(mb - m);
+    P::pv8(vr, pw[0], pw[1], __builtin_ldexpf(1.f, e), o);
+    lsum += __builtin_ldexpf(s, e);
   }
 
   __device__ void finish() { lsum = quad_sum(lsum); }

@@ -64,6 +64,17 @@ extern "C" {
  * 10100.com retirement article, §4. FP8 requires q_dtype = BF16. */
 #define PA_KV_AUTO      0
 #define PA_KV_FP8_E4M3  1
+/* The same E4M3FN cache with the attention arithmetic itself in fp8 (the
+ * variant of the 10100.com article, §4, that computes in fp8 and converts
+ * once at the output): q is quantised to MX fp8 (32 consecutive head dims
+ * share a power-of-two scale 2^X, X = floor(log2 max|q|) - 8, elements the
+ * nearest e4m3 of q / 2^X, saturating at 448); S = K q^T and O = V^T P run
+ * on fp8 operands with fp32 accumulation; each cache block's probabilities
+ * are quantised to e4m3 as p = 2^(z - ceil(max z)) (z the log2-domain
+ * logits of that block), and out = v_scale * sum_b 2^ceil_b sum_t p_t V_t /
+ * sum_b 2^ceil_b sum_t p_t. Requires bf16 queries. Not accepted by
+ * pa_paged_attention_decode_shared. */
+#define PA_KV_FP8_E4M3_COMPUTE  2
 
 /* Fixed sizes: the kernels' token sub-block (a cache block holds 16 or 32
  * tokens, walked as one or two 16-token sub-blocks), and the partition
@@ -228,7 +239,8 @@ int pa_hbm_gather_probe(const void* pool, size_t pool_bytes, int tile_bytes, con
  *   value / scale (float32 quotient, ties to even, magnitude saturated at
  *   448, NaN -> 0x7F, sign kept), scale = *k_scale for K and *v_scale for V
  *   (device fp32 scalars; NULL = 1.0), the inverse of the decode call's
- *   dequantisation (10100.com article, §4).
+ *   dequantisation (10100.com article, §4). PA_KV_FP8_E4M3_COMPUTE stores
+ *   the same codes.
  * Two tokens naming the same slot leave either one. Asynchronous on `stream`;
  * no allocation; host-side validation as for the decode call.
  */

@@ -9,7 +9,7 @@ import torch
 TOL = {"f32": (1e-5, 1e-5), "bf16": (1e-2, 1e-2)}   # (atol, rtol) by output dtype
 
 
-def run_hip(case, split_tokens=0, workspace=None, out=None):
+def run_hip(case, split_tokens=0, workspace=None, out=None, compute="auto"):
     import decode_attention_paged_07_amd as pa
     if out is None:
         out = torch.empty_like(case.query)
@@ -18,8 +18,18 @@ def run_hip(case, split_tokens=0, workspace=None, out=None):
         case.block_tables, case.seq_lens, case.cfg.block_size, case.max_seq_len,
         alibi_slopes=case.alibi_slopes, kv_cache_dtype=case.cfg.kv_dtype,
         k_scale=case.k_scale, v_scale=case.v_scale, workspace=workspace,
-        split_tokens=split_tokens)
+        split_tokens=split_tokens, compute=compute)
     return out
+
+
+def run_oracle_fp8(case, seqs=None):
+    """The fp8-arithmetic oracle on the same inputs (fp8 cache, bf16 q)."""
+    import oracle
+    import workloads
+    h = workloads.host_arrays(case, seqs)
+    return oracle.paged_decode_fp8_compute(h["query"], h["key_cache"], h["value_cache"], h["block_tables"],
+                                           h["seq_lens"], h["scale"], k_scale=h["k_scale"],
+                                           v_scale=h["v_scale"], alibi_slopes=h["alibi_slopes"])
 
 
 def run_oracle(case, seqs=None):
@@ -32,8 +42,9 @@ def run_oracle(case, seqs=None):
                                v_scale=h["v_scale"])
 
 
-def compare(gpu: torch.Tensor, ref: np.ndarray, dtype: str, seqs=None, what=""):
-    """Element-wise |gpu - ref| <= atol + rtol*|ref|; returns (max_abs, max_rel)."""
+def compare(gpu: torch.Tensor, ref: np.ndarray, dtype: str, seqs=None, what="", extra=None):
+    """Element-wise |gpu - ref| <= atol + rtol*|ref| (+ extra, an element-wise
+    allowance); returns (max_abs, max_rel)."""
     atol, rtol = TOL[dtype]
     g = gpu.float().cpu().numpy().astype(np.float64)
     if seqs is not None:
@@ -41,6 +52,8 @@ def compare(gpu: torch.Tensor, ref: np.ndarray, dtype: str, seqs=None, what=""):
     assert g.shape == ref.shape, (g.shape, ref.shape)
     err = np.abs(g - ref)
     bound = atol + rtol * np.abs(ref)
+    if extra is not None:
+        bound = bound + extra
     bad = ~(err <= bound)             # NaN counts as a failure
     max_abs = float(np.nanmax(err)) if err.size else 0.0
     sig = np.abs(ref) > 1e-3

@@ -82,7 +82,7 @@ def call(pa, **over):
     (dict(num_kv_heads=0), -2), (dict(num_seqs=-1), -2), (dict(num_blocks=0), -2),
     (dict(max_blocks_per_seq=0), -2), (dict(max_seq_len=65), -2), (dict(max_seq_len=-1), -2),
     (dict(scale=float("inf")), -2), (dict(scale=float("nan")), -2),
-    (dict(q_dtype=7), -3), (dict(kv_cache_dtype=5), -3), (dict(q_dtype=0, kv_cache_dtype=1), -3),
+    (dict(q_dtype=7), -3), (dict(kv_cache_dtype=5), -3), (dict(q_dtype=0, kv_cache_dtype=1), -3), (dict(q_dtype=0, kv_cache_dtype=2), -3),
     (dict(out=0x10008), -5), (dict(query=0x20004), -5), (dict(key_cache=0x30002), -5),
     (dict(block_tables=0x50002), -5), (dict(alibi_slopes=0x70001), -5),
     (dict(out=0x20000 + 64), -2),                                  # overlaps query
@@ -219,7 +219,7 @@ APPEND = dict(key_cache=0x10000, value_cache=0x20000, key=0x30000, value=0x40000
     (dict(tokens_per_seq=0), -2), (dict(num_kv_heads=0), -2), (dict(num_blocks=0), -2),
     (dict(max_blocks_per_seq=0), -2), (dict(num_seqs=-1), -2),
     (dict(num_seqs=1 << 20, tokens_per_seq=1 << 10, num_kv_heads=8), -2),
-    (dict(in_dtype=5), -3), (dict(kv_cache_dtype=2), -3),
+    (dict(in_dtype=5), -3), (dict(kv_cache_dtype=3), -3),
     (dict(key=0x30008), -5), (dict(value_cache=0x20004), -5), (dict(positions=0x60002), -5),
 ])
 def test_append_validation_rejects(pa, over, code):

@@ -38,6 +38,9 @@ class DecodeConfig:
     # (a multiple of block_size); their lengths are prefix_tokens plus the
     # drawn length. None: no sharing.
     prefix_groups: tuple | None = None
+    # "auto": the cache type's arithmetic; "fp8": fp8 arithmetic on an fp8
+    # cache (MX-quantised q, e4m3 P).
+    compute: str = "auto"
 
     @property
     def group(self) -> int:
@@ -68,5 +71,8 @@ SHARED = DecodeConfig("shared", 128, 64, 8, 128, 16, 128 * 1024, "bf16", "auto",
 # capacity in tokens.
 GQA32 = GQA.with_(name="gqa32", block_size=32, pool_blocks=64 * 1024)
 
+# The fp8 workload with fp8 arithmetic (same inputs, same seed).
+FP8C = FP8.with_(name="fp8c", compute="fp8")
+
 CONFIGS = {c.name: c for c in (TINY, MHA, GQA, LONG, FP8)}
-EXTRA_CONFIGS = {c.name: c for c in (SHARED, GQA32)}
+EXTRA_CONFIGS = {c.name: c for c in (SHARED, GQA32, FP8C)}
