@@ -94,6 +94,46 @@ def _counter_per_dispatch(run_dir, kernel):
     return statistics.median(vals), len(vals)
 
 
+def summarise_shared(stats_dir):
+    """Write the committed summary of a --kernel-trace --stats run of
+    ``bench.py --config shared`` (its log, <dir>.log, beside the directory)."""
+    import csv
+    with open(os.path.join(stats_dir, "run_kernel_stats.csv")) as f:
+        rows = [r for r in csv.DictReader(f) if "pa::" in r["Name"] or "_ZN2pa" in r["Name"]]
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    with open(os.path.join(stats_dir, "run_kernel_trace.csv")) as f:
+        tr = next(r for r in csv.DictReader(f) if "pa_shared_kernel" in r["Kernel_Name"])
+    rec = _last_json(stats_dir.rstrip("/") + ".log")
+    rel = os.path.relpath(os.path.abspath(stats_dir), ROOT)
+    lines = [
+        "# rocprofv3 summary: shared-prefix decode (pa_shared_kernel + pa_shared_merge_kernel)", "",
+        f"Workload: {WORKLOAD_TEXT['shared']}", "",
+        "Command (run from /tmp with the repository at /root/repo):",
+        f"  rocprofv3 --kernel-trace --stats --output-format csv -d {rel} -o run -- "
+        "python3 bench.py --config shared --steps 20 --warmup 5", "",
+        "The bench times the shared-prefix call and then the plain decode call on the same batch, so both "
+        "appear below", "(pa_streamk_kernel + pa_streamk_reduce_kernel are the plain call).", "",
+        "Kernel stats (ns): name | calls | average | min | max",
+    ]
+    for r in rows:
+        lines.append(f"  {r['Name'][:100]} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']}")
+    lines += [
+        "", f"pa_shared_kernel resources: grid {tr['Grid_Size_X']} threads, workgroup {tr['Workgroup_Size_X']}, "
+        f"VGPR {tr['VGPR_Count']}, AGPR {tr['Accum_VGPR_Count']}, SGPR {tr['SGPR_Count']}, "
+        f"LDS {tr['LDS_Block_Size']} B, scratch {tr['Scratch_Size']} B", "",
+        "Bench line of the --stats run:",
+        f"  shared call {rec['ms_per_step']:.5f} ms vs plain decode {rec['plain_decode_ms']:.5f} ms: "
+        f"{rec['speedup_vs_plain']:.3f}x;",
+        f"  logical K/V bytes {rec['logical_kv_bytes']}, unique (shared prompt counted once per group) "
+        f"{rec['unique_kv_bytes']},",
+        f"  unique-byte rate {rec['unique_gbps']:.1f} GB/s",
+    ]
+    path = os.path.join(ROOT, "profiles", "pa_shared_kernel_shared_rocprof.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {path}")
+
+
 def summarise_profiles(config, stats_dir, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, append=0):
     """Write the committed summaries of one workload's rocprofv3 runs.
 
@@ -435,6 +475,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
+    ap.add_argument("--summarise-shared", metavar="STATS",
+                    help="write the shared-prefix rocprofv3 summary from a --stats run of --config shared")
     ap.add_argument("--summarise", nargs=5, metavar=("STATS", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="write profiles/ summaries from rocprofv3 csv run directories (no GPU)")
     ap.add_argument("--append", type=int, default=0, metavar="T",
@@ -445,6 +487,9 @@ def main():
                     help="only run 1 GiB probe reads and 1 GiB fills (counter calibration)")
     args = ap.parse_args()
 
+    if args.summarise_shared:
+        summarise_shared(args.summarise_shared)
+        return
     if args.summarise:
         summarise_profiles(args.config, *args.summarise, append=args.append)
         return

@@ -92,9 +92,9 @@ struct DecodeArgs {
   int num_splits;
   int streamk_workgroups;      // > 0 selects the stream-K scheduler
   // split grid only: per-sequence count of leading physical blocks handled
-  // elsewhere (a shared prefix); in 16-token sub-blocks it is clamped to
-  // [0, min(L / 16, max_first_block)]; nullable. When set, every split writes
-  // partials and no reduce runs.
+  // elsewhere (a shared prefix), clamped to [0, min(L / block_size,
+  // max_first_block)]; nullable. When set, every split writes partials and no
+  // reduce runs.
   const int32_t* first_block;
   int max_first_block;
 };
@@ -113,7 +113,7 @@ struct SharedArgs {
   int num_groups;
   int max_chunks;                      // chunks of members per group in the grid
   int members_per_chunk;
-  int prefix_split_blocks;             // prefix 16-token sub-blocks per wave
+  int prefix_split_blocks;             // prefix blocks per wave
   int max_prefix_splits;
   float* pre_out;                      // [S][H][max_prefix_splits][D]
   float* pre_max;                      // [S][H][max_prefix_splits] natural-log units

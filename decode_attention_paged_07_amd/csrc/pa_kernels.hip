@@ -19,7 +19,7 @@
 //    ordered kv head, sequence, block; a pair cut by a share boundary is
 //    finished by a merge kernel. Ragged lengths then cost no tail imbalance.
 //
-// Contraction mapping (per 16-token block; 16x16 fp32 MFMA results):
+// Contraction mapping (per 16 tokens of a block; 16x16 fp32 MFMA results):
 //   S[t][g] = sum_d K[t][d] q[g][d]: A = K tile (rows = tokens), B = q
 //     (columns = query heads of the group, zero-padded to 16). Result lane
 //     (g + 16*q4) holds S[4*q4 + r][g], r = 0..3.

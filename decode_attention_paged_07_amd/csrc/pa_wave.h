@@ -2,7 +2,7 @@
 // pa_shared.hip): vector types, wave reductions, and the element-type
 // policies that load K/V tiles straight into MFMA operand registers.
 //
-// Contraction mapping (per 16-token block; 16x16 fp32 MFMA results):
+// Contraction mapping (per 16 tokens of a block; 16x16 fp32 MFMA results):
 //   S[t][g] = sum_d K[t][d] q[g][d]: A = K tile (rows = tokens), B = q
 //     (columns = query heads, zero-padded to 16). Result lane (g + 16*q4)
 //     holds S[4*q4 + r][g], r = 0..3.
@@ -31,7 +31,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBlock = 16;
 constexpr int kWaves = PA_WAVES;          // waves per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

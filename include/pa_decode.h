@@ -76,10 +76,9 @@ extern "C" {
  * pa_paged_attention_decode_shared. */
 #define PA_KV_FP8_E4M3_COMPUTE  2
 
-/* Fixed sizes: the kernels' token sub-block (a cache block holds 16 or 32
- * tokens, walked as one or two 16-token sub-blocks), and the partition
- * granularity of the split-KV path (the 256-token partitions of the PR
- * #47361 report). */
+/* Sizes: the default tokens per cache block (16; 32 is also accepted), and
+ * the partition granularity of the split-KV path (the 256-token partitions
+ * of the PR #47361 report). */
 #define PA_BLOCK_SIZE      16
 #define PA_PARTITION_SIZE  256
 #define PA_MAX_GROUP       16   /* num_heads / num_kv_heads */
