@@ -629,12 +629,20 @@ def find_prefix_groups(block_tables, seq_lens, block_size=PA_BLOCK_SIZE, min_pre
 
 def paged_attention_decode_shared(out, query, key_cache, value_cache, num_kv_heads, scale, block_tables,
                                   seq_lens, block_size, max_seq_len, groups: PrefixGroups, alibi_slopes=None,
-                                  kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0, *, workspace=None) -> None:
+                                  kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0, *, workspace=None,
+                                  compute="auto") -> None:
     """paged_attention_decode for a batch with shared-prefix groups (PrefixGroups):
-    each shared K/V block is read once per group. Same result as the plain call."""
+    each shared K/V block is read once per group. Same result as the plain call
+    (compute as for paged_attention_decode)."""
     if kv_cache_dtype not in _KV_NAMES:
         raise TypeError(f"kv_cache_dtype {kv_cache_dtype!r} is not one of {sorted(_KV_NAMES)}")
     kvd = _KV_NAMES[kv_cache_dtype]
+    if compute not in ("auto", "fp8"):
+        raise TypeError(f"compute {compute!r} is not 'auto' or 'fp8'")
+    if compute == "fp8":
+        if kvd != PA_KV_FP8_E4M3:
+            raise TypeError("compute='fp8' needs the fp8 cache")
+        kvd = PA_KV_FP8_E4M3_COMPUTE
     if query.dtype not in _Q_DTYPES:
         raise TypeError(f"query dtype {query.dtype} is not float32 or bfloat16")
     dev = query.device
@@ -663,8 +671,8 @@ def paged_attention_decode_shared(out, query, key_cache, value_cache, num_kv_hea
         _need(alibi_slopes.dtype == torch.float32 and alibi_slopes.shape == (num_heads,)
               and alibi_slopes.device == dev, "alibi_slopes must be float32 [num_heads] on the query's device")
         slopes_ptr = alibi_slopes.data_ptr()
-    ks = _device_scalar(k_scale, dev) if kvd == PA_KV_FP8_E4M3 else None
-    vs = _device_scalar(v_scale, dev) if kvd == PA_KV_FP8_E4M3 else None
+    ks = _device_scalar(k_scale, dev) if kvd != PA_KV_AUTO else None
+    vs = _device_scalar(v_scale, dev) if kvd != PA_KV_AUTO else None
     if workspace is None:
         need = pa_shared_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, block_size, max_seq_len,
                                          groups.num_groups, groups.max_group_size, groups.max_prefix_blocks)

@@ -532,8 +532,6 @@ int pa_paged_attention_decode_shared(void* out, const void* query, const void* k
   if ((rc = check_shared_plan_args(num_seqs, num_heads, num_kv_heads, head_size, block_size, max_seq_len,
                                    num_groups, max_group_size, max_prefix_blocks)))
     return rc;
-  if (kv_cache_dtype == PA_KV_FP8_E4M3_COMPUTE)
-    return fail(PA_ERR_DTYPE, "the shared-prefix call has no fp8-arithmetic variant; use PA_KV_FP8_E4M3");
   if (num_seqs == 0) return ok();
   if (!seq_prefix_blocks) return fail(PA_ERR_NULL, "seq_prefix_blocks must be non-NULL");
   if (num_groups > 0 && (!group_start || !group_prefix_blocks || (num_members > 0 && !group_seqs)))

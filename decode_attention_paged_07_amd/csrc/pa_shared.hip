@@ -100,21 +100,25 @@ struct GroupAttn {
       for (int st = 1; st < kSub; ++st) mx = fmaxf(mx, max4(z[st]));
       mx = quad_max(mx);
       m_true[t] = fmaxf(m_true[t], mx);
-      if (wave_any(mx > m[t] + kRescaleSlack)) {
-        const float m_new = fmaxf(m[t], mx);
-        const float alpha = fast_exp2(m[t] - m_new);
-        m[t] = m_new;
-        lsum[t] *= alpha;
+      if constexpr (Fp8Math<P>::value) {
+        fp8_block_update<P>(vr, z, mx, m[t], lsum[t], o[t]);
+      } else {
+        if (wave_any(mx > m[t] + kRescaleSlack)) {
+          const float m_new = fmaxf(m[t], mx);
+          const float alpha = fast_exp2(m[t] - m_new);
+          m[t] = m_new;
+          lsum[t] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < kDt; ++dt) o[t][dt] *= alpha;
-      }
+          for (int dt = 0; dt < kDt; ++dt) o[t][dt] *= alpha;
+        }
 #pragma unroll
-      for (int st = 0; st < kSub; ++st) {
-        f32x4 p;
+        for (int st = 0; st < kSub; ++st) {
+          f32x4 p;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[st][r] - m[t]);
-        lsum[t] += (p[0] + p[1]) + (p[2] + p[3]);
-        P::pv(vr, p, o[t], st);
+          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[st][r] - m[t]);
+          lsum[t] += (p[0] + p[1]) + (p[2] + p[3]);
+          P::pv(vr, p, o[t], st);
+        }
       }
     }
   }
@@ -312,6 +316,9 @@ hipError_t launch_shared_main(const SharedArgs& s, int kind, int column_tiles, h
     case KIND_FP8 * 1000 + 32: return launch_prefix_nct<PolicyFp8<32, BS>, 32>(s, column_tiles, stream);
     case KIND_FP8 * 1000 + 64: return launch_prefix_nct<PolicyFp8<64, BS>, 64>(s, column_tiles, stream);
     case KIND_FP8 * 1000 + 128: return launch_prefix_nct<PolicyFp8<128, BS>, 128>(s, column_tiles, stream);
+    case KIND_FP8MX * 1000 + 32: return launch_prefix_nct<PolicyFp8Mx<32, BS>, 32>(s, column_tiles, stream);
+    case KIND_FP8MX * 1000 + 64: return launch_prefix_nct<PolicyFp8Mx<64, BS>, 64>(s, column_tiles, stream);
+    case KIND_FP8MX * 1000 + 128: return launch_prefix_nct<PolicyFp8Mx<128, BS>, 128>(s, column_tiles, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -593,6 +593,40 @@ struct PolicyFp8Mx : Fp8VPart<D, BS> {
 template <typename P, typename = void> struct Fp8Math { static constexpr bool value = false; };
 template <typename P> struct Fp8Math<P, decltype((void)P::kFp8Math)> { static constexpr bool value = P::kFp8Math; };
 
+// fp8 arithmetic, one block of one query column tile: P is quantised to e4m3
+// relative to mb = ceil(block max mx) (so every p <= 1), multiplied with V on
+// fp8 operands, and brought to the running reference m by the exact factor
+// 2^(mb - m); m stays an integer and is raised lazily like the other paths'.
+template <typename P>
+__device__ __forceinline__ void fp8_block_update(const typename P::VRegs& vr, const f32x4 (&z)[P::kSub], float mx,
+                                                 float& m, float& lsum, f32x4 (&o)[P::kDt]) {
+  const float mb = ceilf(mx);
+  if (wave_any(mb > m + kRescaleSlack)) {
+    const float m_new = fmaxf(m, mb);
+    const float alpha = m == kNegInf ? 0.f : __builtin_ldexpf(1.f, (int)(m - m_new));
+    m = m_new;
+    lsum *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < P::kDt; ++dt) o[dt] *= alpha;
+  }
+  unsigned pw[2] = {0u, 0u};
+  float s = 0.f;
+#pragma unroll
+  for (int st = 0; st < P::kSub; ++st) {
+    f32x4 p;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[st][r] - mb);
+    unsigned w = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+    w = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], (int)w, true);
+    pw[st] = w;
+    s += (__builtin_amdgcn_cvt_f32_fp8((int)w, 0) + __builtin_amdgcn_cvt_f32_fp8((int)w, 1)) +
+         (__builtin_amdgcn_cvt_f32_fp8((int)w, 2) + __builtin_amdgcn_cvt_f32_fp8((int)w, 3));
+  }
+  const int e = (int)(mb - m);
+  P::pv8(vr, pw[0], pw[1], __builtin_ldexpf(1.f, e), o);
+  lsum += __builtin_ldexpf(s, e);
+}
+
 // ---------------------------------------------------------------------------
 // One wave's attention over a run of blocks of one (sequence, kv head).
 // ---------------------------------------------------------------------------
@@ -761,37 +795,9 @@ struct WaveAttn {
     }
   }
 
-  // fp8 arithmetic: this block's P is quantised to e4m3 relative to
-  // mb = ceil(block max) (so every p <= 1), multiplied with V on fp8
-  // operands, and brought to the running reference m by the exact factor
-  // 2^(mb - m); m stays an integer.
   __device__ void consume_fp8(const typename P::VRegs& vr, const f32x4 (&z)[kSub], float mx) {
     static_assert(NB == 1, "the fp8 arithmetic takes one block per issue");
-    const float mb = ceilf(mx);
-    if (wave_any(mb > m + kRescaleSlack)) {
-      const float m_new = fmaxf(m, mb);
-      const float alpha = m == kNegInf ? 0.f : __builtin_ldexpf(1.f, (int)(m - m_new));
-      m = m_new;
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < kDt; ++dt) o[dt] *= alpha;
-    }
-    unsigned pw[2] = {0u, 0u};
-    float s = 0.f;
-#pragma unroll
-    for (int st = 0; st < kSub; ++st) {
-      f32x4 p;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[st][r] - mb);
-      unsigned w = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-      w = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], (int)w, true);
-      pw[st] = w;
-      s += (__builtin_amdgcn_cvt_f32_fp8((int)w, 0) + __builtin_amdgcn_cvt_f32_fp8((int)w, 1)) +
-           (__builtin_amdgcn_cvt_f32_fp8((int)w, 2) + __builtin_amdgcn_cvt_f32_fp8((int)w, 3));
-    }
-    const int e = (int)(mb - m);
-    P::pv8(vr, pw[0], pw[1], __builtin_ldexpf(1.f, e), o);
-    lsum += __builtin_ldexpf(s, e);
+    fp8_block_update<P>(vr, z, mx, m, lsum, o);
   }
 
   __device__ void finish() { lsum = quad_sum(lsum); }

@@ -72,8 +72,7 @@ extern "C" {
  * on fp8 operands with fp32 accumulation; each cache block's probabilities
  * are quantised to e4m3 as p = 2^(z - ceil(max z)) (z the log2-domain
  * logits of that block), and out = v_scale * sum_b 2^ceil_b sum_t p_t V_t /
- * sum_b 2^ceil_b sum_t p_t. Requires bf16 queries. Not accepted by
- * pa_paged_attention_decode_shared. */
+ * sum_b 2^ceil_b sum_t p_t. Requires bf16 queries. */
 #define PA_KV_FP8_E4M3_COMPUTE  2
 
 /* Sizes: the default tokens per cache block (16; 32 is also accepted), and

@@ -102,3 +102,28 @@ def test_full_size_fp8_compute_sampled():
           f"mean_abs={dev.mean():.3e}; fp8-arith oracle vs exact max_abs={np.abs(ref - exact).max():.3e}",
           flush=True)
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_shared_prefix_fp8_compute(bs):
+    """The shared-prefix call with fp8 arithmetic: prefix blocks read once per
+    group, each block's P quantised by the same rule, so the same oracle."""
+    import decode_attention_paged_07_amd as pa
+    cfg = SMALL.with_(num_seqs=16, pool_blocks=16384 // bs, seq_lens=("uniform", 1, 500), prefix_groups=(8, 480),
+                      block_size=bs)
+    case = workloads.make_case(cfg, device=DEV)
+    groups = pa.find_prefix_groups(case.meta.block_tables, case.meta.seq_lens, bs)
+    assert groups
+    g = pa.prefix_groups(groups, cfg.num_seqs, DEV)
+    out = torch.empty_like(case.query)
+    print(f"[case] shared fp8 compute bs={bs}", flush=True)
+    pa.paged_attention_decode_shared(out, case.query, case.key_cache, case.value_cache, cfg.num_kv_heads,
+                                     case.scale, case.block_tables, case.seq_lens, bs, case.max_seq_len, g,
+                                     kv_cache_dtype="fp8", k_scale=case.k_scale, v_scale=case.v_scale,
+                                     compute="fp8")
+    torch.cuda.synchronize()
+    ref = _run.run_oracle_fp8(case)
+    extra = _fp8tol.row_bounds(workloads.host_arrays(case))
+    mabs, _ = _run.compare(out, ref, "bf16", what=f"shared fp8 compute bs{bs}", extra=extra)
+    print(f"[ok] shared fp8 compute bs{bs}: max_abs={mabs:.2e}", flush=True)
+
