@@ -94,6 +94,48 @@ def _counter_per_dispatch(run_dir, kernel):
     return statistics.median(vals), len(vals)
 
 
+SQ_COUNTERS = ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+               "SQ_INSTS_VMEM_RD", "SQ_VALU_MFMA_BUSY_CYCLES")
+
+
+def summarise_sq(config, pmc_dir):
+    """Write the instruction-mix summary of one ``rocprofv3 --pmc`` run of the
+    SQ_COUNTERS over ``bench.py --config CONFIG`` (its log, <dir>.log, beside
+    the directory): per-dispatch medians for the decode kernel."""
+    import csv
+    import statistics
+    vals = {}
+    with open(os.path.join(pmc_dir, "run_counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if "pa_streamk_kernel" in r["Kernel_Name"]:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    med = {k: statistics.median(v) for k, v in vals.items()}
+    rec = _last_json(pmc_dir.rstrip("/") + ".log")
+    waves = med.get("SQ_WAVES", 0.0)
+    rel = os.path.relpath(os.path.abspath(pmc_dir), ROOT)
+    lines = [
+        f"# rocprofv3 instruction mix: pa_streamk_kernel, {WORKLOAD_TEXT[config]}", "",
+        f"kernel source sha256[:16]: {rec['kernel_sha']}", "",
+        "Command (run from /tmp with the repository at /root/repo):",
+        f"  rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d {rel} -o run -- "
+        f"python3 bench.py --config {config} --steps 3 --warmup 1 --no-cpu-baseline --no-ceiling", "",
+        "Per dispatch (median over dispatches), summed over the device:",
+    ]
+    for k in SQ_COUNTERS:
+        if k in med:
+            per_wave = f"  ({med[k] / waves:,.0f} per wave)" if waves and k.startswith("SQ_INSTS") else ""
+            lines.append(f"  {k:26s} {med[k]:>18,.0f}{per_wave}")
+    lines.append("")
+    lines.append(f"Algorithmic K+V bytes per launch: {rec['roofline']['algorithmic_bytes_per_launch']:,}")
+    if waves:
+        lines.append(f"Bytes per VMEM read instruction: "
+                     f"{rec['roofline']['algorithmic_bytes_per_launch'] / med.get('SQ_INSTS_VMEM_RD', 1):,.0f}")
+    path = os.path.join(ROOT, "profiles", f"pa_streamk_kernel_{config}_sq_counters.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {path}")
+
+
 def summarise_shared(stats_dir):
     """Write the committed summary of a --kernel-trace --stats run of
     ``bench.py --config shared`` (its log, <dir>.log, beside the directory)."""
@@ -475,6 +517,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
+    ap.add_argument("--summarise-sq", metavar="PMC_DIR",
+                    help="write the instruction-mix summary from a --pmc run of SQ_COUNTERS over --config")
     ap.add_argument("--summarise-shared", metavar="STATS",
                     help="write the shared-prefix rocprofv3 summary from a --stats run of --config shared")
     ap.add_argument("--summarise", nargs=5, metavar=("STATS", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
@@ -487,6 +531,9 @@ def main():
                     help="only run 1 GiB probe reads and 1 GiB fills (counter calibration)")
     args = ap.parse_args()
 
+    if args.summarise_sq:
+        summarise_sq(args.config, args.summarise_sq)
+        return
     if args.summarise_shared:
         summarise_shared(args.summarise_shared)
         return

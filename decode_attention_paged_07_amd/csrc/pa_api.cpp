@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -115,15 +116,15 @@ Plan make_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size, int
 
 // Compute units of the current device (queried once per device).
 int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];        // 0 = not yet queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 int check_plan_args(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_seq_len,

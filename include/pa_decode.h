@@ -21,8 +21,9 @@
  * Conventions for every entry point:
  *  - Pointers named "device" are HIP device addresses; all others are host.
  *    The caller owns every buffer; the library allocates nothing, keeps no
- *    per-call state, writes only `out` and `workspace`, and never blocks the
- *    host: kernels are queued on `stream` (a hipStream_t; NULL = the null
+ *    per-call state, writes only the buffers each call documents as outputs
+ *    (`out` and `workspace` for the decode calls, the caches for append and
+ *    block copies), and never blocks the host: kernels are queued on `stream` (a hipStream_t; NULL = the null
  *    stream). No host synchronisation and no allocation happen inside a call,
  *    so it can be captured into a HIP graph.
  *  - Every argument is validated on the host before any HIP call; on failure
@@ -105,16 +106,21 @@ int pa_kv_layout(int num_kv_heads, int head_size, int block_size, int q_dtype,
                  int kv_cache_dtype, pa_layout_desc* desc);
 
 /*
- * Launch plan. The split-KV path divides each sequence into splits of
- * split_tokens tokens (a multiple of PA_PARTITION_SIZE); one workgroup handles
+ * Launch plan. requested_split_tokens == 0 selects the default stream-K plan:
+ * a persistent grid whose waves take equal, contiguous shares of all
+ * (kv head, sequence, block) tiles; a (sequence, kv head) pair cut by a share
+ * boundary leaves segment partials in the workspace and a small merge kernel
+ * combines them (log-sum-exp merge). Its outputs are split_tokens = 0,
+ * num_splits = 0 and its workspace size (layout private to the library).
+ *
+ * A positive multiple of PA_PARTITION_SIZE selects the split grid: each
+ * sequence is divided into splits of split_tokens tokens; one wave handles
  * one (sequence, kv head, split) and the query heads that share that kv head.
  * Sequences longer than one split write per-split partial results into the
- * workspace and a reduce kernel merges them (log-sum-exp merge).
- *
- * requested_split_tokens: 0 = library's choice; otherwise a positive multiple
- * of PA_PARTITION_SIZE. Outputs (any may be NULL): chosen split_tokens,
- * num_splits = ceil(max_seq_len / split_tokens) (>= 1), and the workspace
- * bytes this plan needs (0 when num_splits == 1). Host only; no HIP call.
+ * workspace and a reduce kernel merges them. Outputs (any may be NULL): the
+ * split_tokens, num_splits = ceil(max_seq_len / split_tokens) (>= 1), and the
+ * workspace bytes this plan needs (0 when num_splits == 1). Host only; no HIP
+ * call.
  *
  * Workspace layout for num_splits = P > 1, all fp32, each array starting at a
  * 256-byte-aligned offset from the workspace base, in this order:
@@ -153,8 +159,8 @@ int pa_workspace_bytes(int num_seqs, int num_heads, int head_size, int max_seq_l
  *   alibi_slopes device fp32 [num_heads] or NULL; adds
  *                slope[h] * (t - (seq_len - 1)) to the logit of token t.
  *   q_dtype, kv_cache_dtype: see above.
- *   k_scale, v_scale: device fp32 scalars or NULL (= 1.0); used only when
- *                kv_cache_dtype is PA_KV_FP8_E4M3.
+ *   k_scale, v_scale: device fp32 scalars or NULL (= 1.0); used only with
+ *                the fp8 cache (PA_KV_FP8_E4M3 or PA_KV_FP8_E4M3_COMPUTE).
  *   workspace    device, >= the plan's workspace bytes (may be NULL when the
  *                plan needs none), 16-B aligned.
  *   stream       hipStream_t or NULL.
