@@ -10,7 +10,8 @@
 // scaled fp8 storage).
 //
 // One wave per (sequence, kv head, physical block touched): the wave stores
-// the run of new tokens that falls in that block. Lanes walk the run with the
+// the run of new tokens that falls in that block. The run's input rows are
+// read along the rows into LDS first; the stores then walk the run with the
 // token index fastest, so each store instruction covers consecutive slots:
 // for K, 16-byte rows of one chunk (contiguous 16*run bytes); for V, elements
 // of one dim row (contiguous run*elem bytes). A single token per block (the
@@ -96,14 +97,31 @@ struct QuantPolicy {
   }
 };
 
+// Orders this wave's LDS writes before its later LDS reads (each wave owns
+// its own LDS tile, so no workgroup barrier is involved).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One workgroup = one wave per (sequence, kv head, physical block touched).
+// The run's token rows are first staged through LDS with 16-byte loads along
+// each row (consecutive lanes, consecutive bytes); the cache stores then read
+// their elements from LDS. Reading the input directly in the stores' lane
+// order (token fastest) would make every lane of a V store load from a
+// different row.
 template <typename Pol, int D>
-__global__ void __launch_bounds__(256) pa_append_kernel(const AppendArgs a, int runs_per_pair) {
+__global__ void __launch_bounds__(64) pa_append_kernel(const AppendArgs a, int runs_per_pair) {
   using In = typename Pol::In;
   constexpr int kChunks = D / Pol::kX;
-  const int lane = threadIdx.x & 63;
-  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * runs_per_pair;
-  if (item >= items) return;
+  constexpr int kRow = D * (int)sizeof(In);               // bytes of one token row
+  constexpr int kPitch = kRow + 16;                       // LDS row pitch, spreads banks
+  constexpr int kPieces = kRow / 16;
+  __shared__ __align__(16) char ktile[32 * kPitch];       // one run: at most 32 tokens
+  __shared__ __align__(16) char vtile[32 * kPitch];
+  const int lane = threadIdx.x;
+  const int64_t item = blockIdx.x;
   const int r = (int)(item % runs_per_pair);
   const int64_t sh = item / runs_per_pair;                // s * Hkv + h
   const int h = (int)(sh % a.num_kv_heads);
@@ -121,25 +139,36 @@ __global__ void __launch_bounds__(256) pa_append_kernel(const AppendArgs a, int 
   const int o0 = (int)(t_lo - blk * bs);                  // first slot
   const int n = (int)(t_hi - t_lo);                       // tokens in this run, 1..bs
   const int j0 = (int)(t_lo - p0);                        // their first index among the new tokens
-  const int64_t tile = (int64_t)D * bs * Pol::kElem;
-  const int64_t base = ((int64_t)b * a.num_kv_heads + h) * tile;
-  const int64_t row_stride = (int64_t)a.num_kv_heads * D;  // elements between consecutive tokens
-  const int64_t row0 = ((int64_t)s * a.tokens_per_seq + j0) * row_stride + (int64_t)h * D;
-  const In* krow = reinterpret_cast<const In*>(a.key) + row0;
-  const In* vrow = reinterpret_cast<const In*>(a.value) + row0;
+  const int64_t tile_bytes = (int64_t)D * bs * Pol::kElem;
+  const int64_t base = ((int64_t)b * a.num_kv_heads + h) * tile_bytes;
+  const int64_t row_stride = (int64_t)a.num_kv_heads * kRow;   // bytes between consecutive tokens
+  const int64_t row0 = ((int64_t)s * a.tokens_per_seq + j0) * row_stride + (int64_t)h * kRow;
+  const char* krow = reinterpret_cast<const char*>(a.key) + row0;
+  const char* vrow = reinterpret_cast<const char*>(a.value) + row0;
   const float ks = a.k_scale ? *a.k_scale : 1.f;
   const float vs = a.v_scale ? *a.v_scale : 1.f;
   char* kc = reinterpret_cast<char*>(a.key_cache) + base;
   char* vc = reinterpret_cast<char*>(a.value_cache) + base;
+  // K and V rows of the run are loaded together (one round trip to memory).
+  for (int i = lane; i < n * kPieces; i += 64) {
+    const int t = i / kPieces, piece = i - t * kPieces;
+    const int64_t src = t * row_stride + piece * 16;
+    const int dst = t * kPitch + piece * 16;
+    *reinterpret_cast<u32x4a*>(ktile + dst) = *reinterpret_cast<const u32x4a*>(krow + src);
+    *reinterpret_cast<u32x4a*>(vtile + dst) = *reinterpret_cast<const u32x4a*>(vrow + src);
+  }
+  wave_sync();
   // K: item i = c * n + t -> chunk c of token t, 16 bytes at row o0 + t.
   for (int i = lane; i < kChunks * n; i += 64) {
     const int c = i / n, t = i - c * n;
-    Pol::k_chunk(krow + t * row_stride + c * Pol::kX, kc + ((int64_t)c * bs + o0 + t) * 16, ks);
+    Pol::k_chunk(reinterpret_cast<const In*>(ktile + t * kPitch) + c * Pol::kX,
+                 kc + ((int64_t)c * bs + o0 + t) * 16, ks);
   }
   // V: item i = d * n + t -> element d of token t at row d, slot o0 + t.
   for (int i = lane; i < D * n; i += 64) {
     const int d = i / n, t = i - d * n;
-    Pol::v_elem(vrow + t * row_stride + d, vc + ((int64_t)d * bs + o0 + t) * Pol::kElem, vs);
+    Pol::v_elem(reinterpret_cast<const In*>(vtile + t * kPitch) + d, vc + ((int64_t)d * bs + o0 + t) * Pol::kElem,
+                vs);
   }
 }
 
@@ -150,8 +179,7 @@ hipError_t launch_append_t(const AppendArgs& a, hipStream_t stream) {
   const int bs = a.block_size;
   const int runs = (bs - 1 + a.tokens_per_seq - 1) / bs + 1;
   const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * runs;
-  const int64_t wgs = (items + 3) / 4;
-  hipLaunchKernelGGL((pa_append_kernel<Pol, D>), dim3((unsigned)wgs), dim3(256), 0, stream, a, runs);
+  hipLaunchKernelGGL((pa_append_kernel<Pol, D>), dim3((unsigned)items), dim3(64), 0, stream, a, runs);
   return hipGetLastError();
 }
 
