@@ -351,9 +351,21 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
 
 // ---- shared-prefix decode -------------------------------------------------------
 
-constexpr int kSharedSuffixSplit = 512;     // tokens per suffix split
-constexpr int kSharedTargetWaves = 1024;    // prefix waves the split count aims for (one per SIMD)
-constexpr int kSharedMinSplitTokens = 512;  // fewest prefix tokens per wave
+#ifndef PA_SHARED_SUFFIX_SPLIT
+#define PA_SHARED_SUFFIX_SPLIT 512
+#endif
+#ifndef PA_SHARED_TARGET_WAVES
+#define PA_SHARED_TARGET_WAVES 512
+#endif
+#ifndef PA_SHARED_MIN_SPLIT_TOKENS
+#define PA_SHARED_MIN_SPLIT_TOKENS 512
+#endif
+#ifndef PA_SHARED_MAX_TILES
+#define PA_SHARED_MAX_TILES 4
+#endif
+constexpr int kSharedSuffixSplit = PA_SHARED_SUFFIX_SPLIT;        // tokens per suffix split
+constexpr int kSharedTargetWaves = PA_SHARED_TARGET_WAVES;        // prefix waves the split count aims for
+constexpr int kSharedMinSplitTokens = PA_SHARED_MIN_SPLIT_TOKENS; // fewest prefix tokens per wave
 
 struct SharedPlan {
   int column_tiles = 1;
@@ -541,8 +553,9 @@ int pa_paged_attention_decode_shared(void* out, const void* query, const void* k
   if (!aligned(seq_prefix_blocks, 4) || (group_start && !aligned(group_start, 4)) ||
       (group_seqs && !aligned(group_seqs, 4)) || (group_prefix_blocks && !aligned(group_prefix_blocks, 4)))
     return fail(PA_ERR_ALIGN, "group arrays must be 4-byte aligned");
-  const int max_tiles = pa::max_column_tiles(q_dtype == PA_DTYPE_F32 ? 4 : 2,
-                                             elem_bytes_of(q_dtype, kv_cache_dtype), head_size, block_size);
+  const int max_tiles = std::min(PA_SHARED_MAX_TILES,
+                                 pa::max_column_tiles(q_dtype == PA_DTYPE_F32 ? 4 : 2,
+                                                      elem_bytes_of(q_dtype, kv_cache_dtype), head_size, block_size));
   const SharedPlan plan = make_shared_plan(num_seqs, num_heads, num_kv_heads, head_size, block_size, max_seq_len,
                                            num_groups, max_group_size, max_prefix_blocks, max_tiles);
   if (plan.max_prefix_splits > 65535) return fail(PA_ERR_SHAPE, "too many prefix splits");
