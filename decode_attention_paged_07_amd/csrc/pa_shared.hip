@@ -234,46 +234,47 @@ __global__ void __launch_bounds__(kWaves * 64) pa_shared_kernel(const SharedArgs
   }
 }
 
-// Merge of prefix and suffix partials: grid (num_heads, num_seqs), 64 threads.
+// Merge of prefix and suffix partials: grid (num_kv_heads, num_seqs), 256
+// threads; thread e covers 4 consecutive dims (16-byte loads) of query head
+// kvh*G + e / (D/4).
 template <typename OutElem, int D>
-__global__ void __launch_bounds__(64) pa_shared_merge_kernel(const SharedArgs s, const int32_t* seq_prefix_blocks) {
+__global__ void __launch_bounds__(256) pa_shared_merge_kernel(const SharedArgs s, const int32_t* seq_prefix_blocks) {
   const DecodeArgs& a = s.d;
-  const int h = blockIdx.x;
+  const int kvh = blockIdx.x;
   const int seq = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int G = a.group;
   const int L = clamp_len(a.seq_lens[seq], a.max_seq_len);
-  OutElem* out = reinterpret_cast<OutElem*>(a.out) + ((int64_t)seq * a.num_heads + h) * D;
-  constexpr int kPer = D >= 64 ? D / 64 : 1;     // head elements per lane
-  if (lane * kPer >= D) return;                  // D = 32: lanes 32..63 idle
+  OutElem* out = reinterpret_cast<OutElem*>(a.out) + ((int64_t)seq * a.num_heads + kvh * G) * D;
   const int first = min(max(seq_prefix_blocks[seq], 0), min(L / a.block_size, a.max_first_block));
   const int n_pre = first > 0 ? (first + s.prefix_split_blocks - 1) / s.prefix_split_blocks : 0;
   const int t0 = first * a.block_size;
   const int n_suf = L > t0 ? (L - t0 + a.split_tokens - 1) / a.split_tokens : 0;
-  if (n_pre + n_suf == 0) {
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) out[lane * kPer + k] = from_f32<OutElem>(0.f);
-    return;
-  }
-  const int64_t pre_row = ((int64_t)seq * a.num_heads + h) * s.max_prefix_splits;
-  const int64_t suf_row = ((int64_t)seq * a.num_heads + h) * a.num_splits;
-  auto ml = [&](int i) { return i < n_pre ? s.pre_max[pre_row + i] : a.max_logits[suf_row + i - n_pre]; };
-  auto es = [&](int i) { return i < n_pre ? s.pre_sum[pre_row + i] : a.exp_sums[suf_row + i - n_pre]; };
   const int n = n_pre + n_suf;
-  float big_m = kNegInf;
-  for (int i = 0; i < n; ++i) big_m = fmaxf(big_m, ml(i));
-  float tot = 0.f, acc[kPer];
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) acc[k] = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const float wgt = es(i) * fast_exp2((ml(i) - big_m) * kLog2e);
-    tot += wgt;
-    const float* src = i < n_pre ? s.pre_out + (pre_row + i) * D : a.tmp_out + (suf_row + i - n_pre) * D;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) acc[k] += wgt * src[lane * kPer + k];
+  for (int e = threadIdx.x; e < G * (D / 4); e += 256) {
+    const int g = e / (D / 4);
+    const int d4 = e - g * (D / 4);
+    OutElem* dst = out + (int64_t)g * D + 4 * d4;
+    if (n == 0) {
+      store4(dst, f32x4{0.f, 0.f, 0.f, 0.f});
+      continue;
+    }
+    const int64_t row = (int64_t)seq * a.num_heads + kvh * G + g;
+    const int64_t pre_row = row * s.max_prefix_splits;
+    const int64_t suf_row = row * a.num_splits;
+    auto ml = [&](int i) { return i < n_pre ? s.pre_max[pre_row + i] : a.max_logits[suf_row + i - n_pre]; };
+    auto es = [&](int i) { return i < n_pre ? s.pre_sum[pre_row + i] : a.exp_sums[suf_row + i - n_pre]; };
+    float big_m = kNegInf;
+    for (int i = 0; i < n; ++i) big_m = fmaxf(big_m, ml(i));
+    float tot = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < n; ++i) {
+      const float wgt = es(i) * fast_exp2((ml(i) - big_m) * kLog2e);
+      tot += wgt;
+      const float* src = i < n_pre ? s.pre_out + (pre_row + i) * D : a.tmp_out + (suf_row + i - n_pre) * D;
+      acc += wgt * *reinterpret_cast<const f32x4*>(src + 4 * d4);
+    }
+    store4(dst, acc * (1.f / tot));
   }
-  const float inv = 1.f / tot;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) out[lane * kPer + k] = from_f32<OutElem>(acc[k] * inv);
 }
 
 template <typename P, int D, int NCT>
@@ -328,20 +329,20 @@ hipError_t launch_shared(const SharedArgs& s, int kind, int column_tiles, hipStr
                    : s.d.block_size == 16 ? launch_shared_main<16>(s, kind, column_tiles, stream)
                                           : hipErrorInvalidValue;
   if (err != hipSuccess) return err;
-  const dim3 grid(s.d.num_heads, s.d.num_seqs);
+  const dim3 grid(s.d.num_kv_heads, s.d.num_seqs);
   const bool f32 = kind == KIND_F32;
   switch (s.d.head_size) {
     case 32:
-      if (f32) hipLaunchKernelGGL((pa_shared_merge_kernel<float, 32>), grid, dim3(64), 0, stream, s, s.d.first_block);
-      else hipLaunchKernelGGL((pa_shared_merge_kernel<__bf16, 32>), grid, dim3(64), 0, stream, s, s.d.first_block);
+      if (f32) hipLaunchKernelGGL((pa_shared_merge_kernel<float, 32>), grid, dim3(256), 0, stream, s, s.d.first_block);
+      else hipLaunchKernelGGL((pa_shared_merge_kernel<__bf16, 32>), grid, dim3(256), 0, stream, s, s.d.first_block);
       break;
     case 64:
-      if (f32) hipLaunchKernelGGL((pa_shared_merge_kernel<float, 64>), grid, dim3(64), 0, stream, s, s.d.first_block);
-      else hipLaunchKernelGGL((pa_shared_merge_kernel<__bf16, 64>), grid, dim3(64), 0, stream, s, s.d.first_block);
+      if (f32) hipLaunchKernelGGL((pa_shared_merge_kernel<float, 64>), grid, dim3(256), 0, stream, s, s.d.first_block);
+      else hipLaunchKernelGGL((pa_shared_merge_kernel<__bf16, 64>), grid, dim3(256), 0, stream, s, s.d.first_block);
       break;
     default:
-      if (f32) hipLaunchKernelGGL((pa_shared_merge_kernel<float, 128>), grid, dim3(64), 0, stream, s, s.d.first_block);
-      else hipLaunchKernelGGL((pa_shared_merge_kernel<__bf16, 128>), grid, dim3(64), 0, stream, s, s.d.first_block);
+      if (f32) hipLaunchKernelGGL((pa_shared_merge_kernel<float, 128>), grid, dim3(256), 0, stream, s, s.d.first_block);
+      else hipLaunchKernelGGL((pa_shared_merge_kernel<__bf16, 128>), grid, dim3(256), 0, stream, s, s.d.first_block);
   }
   return hipGetLastError();
 }
