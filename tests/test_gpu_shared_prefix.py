@@ -105,3 +105,18 @@ def test_full_size_shared_workload_sampled():
     out, (mabs, mrel) = check(case, "shared full size", seqs=seqs)
     print(f"[full] shared: sampled seqs {seqs} max_abs={mabs:.2e} max_rel={mrel:.2e}", flush=True)
     assert torch.isfinite(out.float()).all()
+
+
+def test_no_groups_is_the_plain_decode():
+    """With no groups the shared call runs only its per-sequence part and the
+    merge; it must still equal the oracle (and the plain call)."""
+    import decode_attention_paged_07_amd as pa
+    case = workloads.make_case(SMALL["gqa8-group8"], device=DEV)
+    g = pa.prefix_groups([], case.cfg.num_seqs, DEV)
+    out = torch.empty_like(case.query)
+    print("[case] shared call without groups", flush=True)
+    pa.paged_attention_decode_shared(out, case.query, case.key_cache, case.value_cache, case.cfg.num_kv_heads,
+                                     case.scale, case.block_tables, case.seq_lens, case.cfg.block_size,
+                                     case.max_seq_len, g)
+    torch.cuda.synchronize()
+    _run.compare(out, _run.run_oracle(case), case.cfg.q_dtype, what="no groups")
