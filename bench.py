@@ -47,13 +47,101 @@ WORKLOAD_TEXT = {
 }
 
 
+def _build_flags():
+    """The hipcc flags the in-tree build uses (read from build.py by path, so
+    the library need not be importable)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_pa_build_flags", os.path.join(ROOT, "decode_attention_paged_07_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.HIP_FLAGS
+
+
 def kernel_sha(kernel: str = "pa_streamk_kernel") -> str:
-    """sha256 prefix over the source files that define ``kernel``."""
+    """sha256 prefix over the source files that define ``kernel`` and the
+    compiler flags they are built with."""
     h = hashlib.sha256()
     for name in KERNEL_SRC[kernel]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(_build_flags()).encode())
     return h.hexdigest()[:16]
+
+
+LIB_PATH = os.path.join(ROOT, "decode_attention_paged_07_amd", "libpa_decode.so")
+
+
+def code_object_kernels(lib_path: str = LIB_PATH) -> dict:
+    """{demangled kernel name: resources} from the AMDGPU metadata note of the
+    gfx950 code object inside the built library. Per lane: 'vgpr' is the
+    number of registers the code uses (architectural + accumulator), 'agpr'
+    the accumulator part. The allocation the hardware makes is set by the
+    kernel descriptor and can be larger."""
+    import struct
+
+    with open(lib_path, "rb") as f:
+        data = f.read()
+    out = {}
+    base = data.find(b"__CLANG_OFFLOAD_BUNDLE__")
+    while base >= 0:                                  # one bundle per translation unit
+        n = struct.unpack_from("<Q", data, base + 24)[0]
+        off = base + 32
+        for _ in range(n):
+            o, size, tlen = struct.unpack_from("<QQQ", data, off)
+            triple = data[off + 24:off + 24 + tlen].decode()
+            off += 24 + tlen
+            if triple.endswith("gfx950"):
+                out.update(_code_object_kernels(data[base + o:base + o + size]))
+        base = data.find(b"__CLANG_OFFLOAD_BUNDLE__", base + 1)
+    if not out:
+        raise ValueError(f"no gfx950 code object in {lib_path}")
+    return out
+
+
+def _code_object_kernels(elf: bytes) -> dict:
+    import struct
+    import subprocess
+
+    import msgpack
+    shoff = struct.unpack_from("<Q", elf, 0x28)[0]
+    shentsize, shnum = struct.unpack_from("<HH", elf, 0x3A)
+    meta = None
+    for i in range(shnum):
+        sh = shoff + i * shentsize
+        if struct.unpack_from("<I", elf, sh + 4)[0] != 7:        # SHT_NOTE
+            continue
+        p, end = struct.unpack_from("<QQ", elf, sh + 0x18)
+        end += p
+        while p + 12 <= end:
+            namesz, descsz, ntype = struct.unpack_from("<III", elf, p)
+            d0 = p + 12 + ((namesz + 3) & ~3)
+            if elf[p + 12:p + 12 + namesz].rstrip(b"\0") == b"AMDGPU" and ntype == 32:   # NT_AMDGPU_METADATA
+                meta = msgpack.unpackb(elf[d0:d0 + descsz], raw=False)
+            p = d0 + ((descsz + 3) & ~3)
+    if meta is None:
+        raise ValueError("no AMDGPU metadata note in a gfx950 code object")
+    kernels = meta["amdhsa.kernels"]
+    names = subprocess.run(["c++filt"], input="\n".join(k[".name"] for k in kernels), capture_output=True,
+                           text=True, check=True).stdout.splitlines()
+    return {d: {"vgpr": k[".vgpr_count"], "agpr": k.get(".agpr_count", 0), "sgpr": k[".sgpr_count"],
+                "scratch": k[".private_segment_fixed_size"], "lds": k[".group_segment_fixed_size"]}
+            for d, k in zip(names, kernels)}
+
+
+def resources_text(trace_row) -> str:
+    """Launch shape and registers of a kernel from a rocprofv3 kernel-trace
+    row, with the register use the code object records."""
+    alloc = 2 * int(trace_row["VGPR_Count"])
+    text = (f"grid {trace_row['Grid_Size_X']} threads, workgroup {trace_row['Workgroup_Size_X']}, "
+            f"{alloc} registers per lane allocated (at most {512 // max(alloc, 1)} waves per SIMD; rocprofv3's "
+            f"VGPR_Count column reads {trace_row['VGPR_Count']}: it counts 4 registers per allocation granule, "
+            f"gfx950 allocates 8)")
+    r = code_object_kernels().get(trace_row["Kernel_Name"])
+    if r is not None:
+        text += f", of which the code uses {r['vgpr']} ({r['vgpr'] - r['agpr']} VGPR + {r['agpr']} AGPR)"
+    return text + (f", SGPR {trace_row['SGPR_Count']}, LDS {trace_row['LDS_Block_Size']} B, "
+                   f"scratch {trace_row['Scratch_Size']} B")
 
 
 def kv_bytes(case) -> int:
@@ -160,9 +248,7 @@ def summarise_shared(stats_dir):
     for r in rows:
         lines.append(f"  {r['Name'][:100]} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']}")
     lines += [
-        "", f"pa_shared_kernel resources: grid {tr['Grid_Size_X']} threads, workgroup {tr['Workgroup_Size_X']}, "
-        f"VGPR {tr['VGPR_Count']}, AGPR {tr['Accum_VGPR_Count']}, SGPR {tr['SGPR_Count']}, "
-        f"LDS {tr['LDS_Block_Size']} B, scratch {tr['Scratch_Size']} B", "",
+        "", f"pa_shared_kernel resources: {resources_text(tr)}", "",
         "Bench line of the --stats run:",
         f"  shared call {rec['ms_per_step']:.5f} ms vs plain decode {rec['plain_decode_ms']:.5f} ms: "
         f"{rec['speedup_vs_plain']:.3f}x;",
@@ -243,9 +329,7 @@ def summarise_profiles(config, stats_dir, fetch_dir, write_dir, cal_fetch_dir, c
               "  name | calls | average | min | max"]
     for r in stats:
         lines.append(f"  {r['Name'][:80]} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']}")
-    lines += ["", f"Dominant kernel resources: grid {tr['Grid_Size_X']} threads, workgroup {tr['Workgroup_Size_X']}, "
-              f"VGPR {tr['VGPR_Count']}, AGPR {tr['Accum_VGPR_Count']}, SGPR {tr['SGPR_Count']}, "
-              f"LDS {tr['LDS_Block_Size']} B, scratch {tr['Scratch_Size']} B", "",
+    lines += ["", f"Dominant kernel resources: {resources_text(tr)}", "",
               f"Counters per dispatch of {kernel} (median over {n_f} / {n_w} dispatches):",
               f"  FETCH_SIZE {fetch:.0f} KiB x {f_fac:.4f} (1 GiB probe read read as {cal_f:.0f} KiB)",
               f"  WRITE_SIZE {write:.0f} KiB x {w_fac:.4f} (1 GiB fill read as {cal_w:.0f} KiB)",
