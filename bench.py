@@ -121,23 +121,48 @@ def _code_object_kernels(elf: bytes) -> dict:
             p = d0 + ((descsz + 3) & ~3)
     if meta is None:
         raise ValueError("no AMDGPU metadata note in a gfx950 code object")
+    alloc = _descriptor_vgpr_alloc(elf, shoff, shentsize, shnum)
     kernels = meta["amdhsa.kernels"]
     names = subprocess.run(["c++filt"], input="\n".join(k[".name"] for k in kernels), capture_output=True,
                            text=True, check=True).stdout.splitlines()
     return {d: {"vgpr": k[".vgpr_count"], "agpr": k.get(".agpr_count", 0), "sgpr": k[".sgpr_count"],
-                "scratch": k[".private_segment_fixed_size"], "lds": k[".group_segment_fixed_size"]}
+                "scratch": k[".private_segment_fixed_size"], "lds": k[".group_segment_fixed_size"],
+                "alloc": alloc.get(k[".symbol"])}
             for d, k in zip(names, kernels)}
+
+
+def _descriptor_vgpr_alloc(elf: bytes, shoff: int, shentsize: int, shnum: int) -> dict:
+    """{kernel descriptor symbol: registers per lane the hardware allocates}.
+    The 64-byte kernel descriptor holds COMPUTE_PGM_RSRC1 at byte 48; its low 6
+    bits are the granulated VGPR count, in granules of 8 registers on gfx950."""
+    import struct
+    secs = [struct.unpack_from("<IIQQQQIIQQ", elf, shoff + i * shentsize) for i in range(shnum)]
+    out = {}
+    for name, stype, flags, addr, off, size, link, info, align, entsize in secs:
+        if stype != 2:                                   # SHT_SYMTAB
+            continue
+        stroff = secs[link][4]
+        for j in range(size // 24):
+            st_name, st_info, st_other, st_shndx, st_value, st_size = struct.unpack_from("<IBBHQQ", elf, off + 24 * j)
+            end = elf.index(b"\0", stroff + st_name)
+            sym = elf[stroff + st_name:end].decode()
+            if not sym.endswith(".kd") or st_shndx == 0 or st_shndx >= len(secs):
+                continue
+            s_addr, s_off = secs[st_shndx][3], secs[st_shndx][4]
+            rsrc1 = struct.unpack_from("<I", elf, s_off + (st_value - s_addr) + 48)[0]
+            out[sym] = ((rsrc1 & 0x3F) + 1) * 8
+    return out
 
 
 def resources_text(trace_row) -> str:
     """Launch shape and registers of a kernel from a rocprofv3 kernel-trace
     row, with the register use the code object records."""
-    alloc = 2 * int(trace_row["VGPR_Count"])
+    r = code_object_kernels().get(trace_row["Kernel_Name"])
+    alloc = r["alloc"] if r is not None and r["alloc"] else 2 * int(trace_row["VGPR_Count"])
     text = (f"grid {trace_row['Grid_Size_X']} threads, workgroup {trace_row['Workgroup_Size_X']}, "
             f"{alloc} registers per lane allocated (at most {512 // max(alloc, 1)} waves per SIMD; rocprofv3's "
             f"VGPR_Count column reads {trace_row['VGPR_Count']}: it counts 4 registers per allocation granule, "
             f"gfx950 allocates 8)")
-    r = code_object_kernels().get(trace_row["Kernel_Name"])
     if r is not None:
         text += f", of which the code uses {r['vgpr']} ({r['vgpr'] - r['agpr']} VGPR + {r['agpr']} AGPR)"
     return text + (f", SGPR {trace_row['SGPR_Count']}, LDS {trace_row['LDS_Block_Size']} B, "
