@@ -611,8 +611,12 @@ def cpu_baseline(case, budget_s: float):
                 break
     nseq = sum(len(s) for s, _ in done)
     tokens = int(case.meta.seq_lens[:nseq].astype("int64").sum())
+    cfg = case.cfg
+    e_kv = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}[cfg.q_dtype if cfg.kv_dtype == "auto" else cfg.kv_dtype]
+    sample_bytes = tokens * cfg.num_kv_heads * cfg.head_size * 2 * e_kv
     return {
         "value": nseq / wall, "unit": "seqs/s", "cores": cores, "kind": "oracle",
+        "kv_gbps": round(sample_bytes / wall / 1e9, 3),
         "sample": f"first {nseq} of {n} sequences ({tokens} tokens), fp64 numpy oracle"
                   f"{' (fp8-arithmetic definition)' if case.cfg.compute == 'fp8' else ''}, "
                   f"host copy untimed, {wall:.1f} s wall",

@@ -79,47 +79,65 @@ struct GroupAttn {
     }
   }
 
+  // Phase by phase over the column tiles (all q.K^T products, then all
+  // maxima, one uniform test for any rescale, then all P.V), so the tiles'
+  // independent MFMA chains interleave instead of running one tile at a time
+  // between branches. Each tile's rescale decision is the same as tile by tile.
   __device__ void consume(const typename P::KRegs& kr, typename P::VRegs& vr, int blk) {
     P::prepare_v(vr);
+    f32x4 z[NCT][kSub];
+    float mx[NCT];
 #pragma unroll
-    for (int t = 0; t < NCT; ++t) {
-      f32x4 z[kSub];
+    for (int t = 0; t < NCT; ++t)
 #pragma unroll
       for (int st = 0; st < kSub; ++st) {
         const f32x4 sc = P::qk(kr, q[t], st);
         if constexpr (ALIBI) {
           const float base = (float)(blk * kBS + 8 * st);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) z[st][r] = fmaf(sc[r], c, fmaf(slope2[t], base, lane_bias[t][r]));
+          for (int r = 0; r < 4; ++r) z[t][st][r] = fmaf(sc[r], c, fmaf(slope2[t], base, lane_bias[t][r]));
         } else {
-          z[st] = sc * c;
+          z[t][st] = sc * c;
         }
       }
-      float mx = max4(z[0]);
 #pragma unroll
-      for (int st = 1; st < kSub; ++st) mx = fmaxf(mx, max4(z[st]));
-      mx = quad_max(mx);
-      m_true[t] = fmaxf(m_true[t], mx);
-      if constexpr (Fp8Math<P>::value) {
-        fp8_block_update<P>(vr, z, mx, m[t], lsum[t], o[t]);
-      } else {
-        if (wave_any(mx > m[t] + kRescaleSlack)) {
-          const float m_new = fmaxf(m[t], mx);
-          const float alpha = fast_exp2(m[t] - m_new);
-          m[t] = m_new;
-          lsum[t] *= alpha;
+    for (int t = 0; t < NCT; ++t) {
+      float v = max4(z[t][0]);
 #pragma unroll
-          for (int dt = 0; dt < kDt; ++dt) o[t][dt] *= alpha;
+      for (int st = 1; st < kSub; ++st) v = fmaxf(v, max4(z[t][st]));
+      mx[t] = quad_max(v);
+      m_true[t] = fmaxf(m_true[t], mx[t]);
+    }
+    if constexpr (Fp8Math<P>::value) {
+#pragma unroll
+      for (int t = 0; t < NCT; ++t) fp8_block_update<P>(vr, z[t], mx[t], m[t], lsum[t], o[t]);
+    } else {
+      bool need = false;
+#pragma unroll
+      for (int t = 0; t < NCT; ++t) need = need || mx[t] > m[t] + kRescaleSlack;
+      if (wave_any(need)) {
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) {
+          if (wave_any(mx[t] > m[t] + kRescaleSlack)) {
+            const float m_new = fmaxf(m[t], mx[t]);
+            const float alpha = fast_exp2(m[t] - m_new);
+            m[t] = m_new;
+            lsum[t] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < kDt; ++dt) o[t][dt] *= alpha;
+          }
         }
+      }
+#pragma unroll
+      for (int t = 0; t < NCT; ++t)
 #pragma unroll
         for (int st = 0; st < kSub; ++st) {
           f32x4 p;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[st][r] - m[t]);
+          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[t][st][r] - m[t]);
           lsum[t] += (p[0] + p[1]) + (p[2] + p[3]);
           P::pv(vr, p, o[t], st);
         }
-      }
     }
   }
 
@@ -227,9 +245,14 @@ __global__ void __launch_bounds__(kWaves * 64) pa_shared_kernel(const SharedArgs
     x /= kv_groups;
     prefix_unit<P, D, NCT, ALIBI>(s, x / s.max_chunks, x % s.max_chunks, kvg, split);
   } else {
+    // Split index slowest: split 0 (the first tokens after each sequence's
+    // prefix, where every grouped sequence's own tokens start) is dispatched
+    // right after the prefix items; the higher splits, empty unless a
+    // sequence is long past its prefix, come last and mostly exit at once.
     x -= prefix_wgs;
-    const int split = x % s.d.num_splits;
-    x /= s.d.num_splits;
+    const int per_split = kv_groups * s.d.num_seqs;
+    const int split = x / per_split;
+    x -= split * per_split;
     split_unit<P, D, 1, ALIBI>(s.d, split, x % kv_groups, x / kv_groups);
   }
 }
