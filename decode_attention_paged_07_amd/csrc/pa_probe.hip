@@ -40,13 +40,16 @@ pa_read_probe_kernel(const u32x4p* __restrict__ buf, uint64_t words, unsigned* _
 // Gather probe: wave w reads whole tiles ids[w], ids[w + W], ... (W waves in
 // the grid), DEPTH tiles in flight before any is consumed. A tile is WPL KiB;
 // lane l reads 16-byte words l, l+64, ... of it. Ids are clamped into the pool.
+// The wave index is made wave-uniform so the ids are scalar loads: a vector
+// load of the next id would join the tile loads' in-order count, and each
+// step would wait one extra memory latency for it before issuing its tiles.
 template <int WPL, int DEPTH>
 __global__ void __launch_bounds__(256)
 pa_gather_probe_kernel(const u32x4p* __restrict__ pool, uint64_t pool_tiles, const int32_t* __restrict__ ids,
                        int num_tiles, unsigned* __restrict__ sink) {
   constexpr int kWords = WPL * 64;
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wave = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = gridDim.x * 4;
   u32x4p acc = {0u, 0u, 0u, 0u};
   for (int i = wave; i < num_tiles; i += W * DEPTH) {

@@ -69,3 +69,8 @@ def test_descriptor_allocation_covers_the_registers_used(kernels):
     for name, r in kernels.items():
         assert r["alloc"] is not None and r["alloc"] % 8 == 0, name
         assert r["alloc"] >= r["vgpr"], f"{name}: allocates {r['alloc']}, uses {r['vgpr']}"
+
+
+def test_no_kernel_spills_to_scratch(kernels):
+    spilling = {name: r["scratch"] for name, r in kernels.items() if r["scratch"]}
+    assert not spilling, spilling
