@@ -109,6 +109,57 @@ pa_split_reduce_kernel(const DecodeArgs a) {
 template <int BS>
 __device__ __forceinline__ int blocks_of(int L) { return (L + BS - 1) / BS; }
 
+// Block counts of sequences c0 + 64*j + lane, j < K: the loads are
+// unconditional (index clamped, count masked) so all K are in flight together
+// and a scan over seq_lens waits one memory latency per 64*K sequences.
+template <int BS, int K>
+__device__ __forceinline__ void block_counts(const DecodeArgs& a, int c0, int lane, int (&nb)[K]) {
+  const int S = a.num_seqs;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int s = c0 + 64 * j + lane;
+    const int L = a.seq_lens[min(s, S - 1)];
+    nb[j] = blocks_of<BS>(clamp_len(L, a.max_seq_len)) & -(int)(s < S);
+  }
+}
+
+// Total blocks over all sequences.
+template <int BS, int K>
+__device__ int total_blocks(const DecodeArgs& a, int lane) {
+  int T = 0;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += 64 * K) {
+    int nb[K];
+    block_counts<BS, K>(a, c0, lane, nb);
+#pragma unroll
+    for (int j = 0; j < K; ++j) T += wave_sum(nb[j]);
+  }
+  return T;
+}
+
+// The sequence whose block range (in sequence order) holds block r, and the
+// block's index within it.
+template <int BS, int K>
+__device__ void find_block(const DecodeArgs& a, int lane, int r, int& seq, int& blk) {
+  int running = 0;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += 64 * K) {
+    int nb[K];
+    block_counts<BS, K>(a, c0, lane, nb);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int incl = wave_incl_scan(nb[j], lane) + running;
+      const int excl = incl - nb[j];
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(nb[j] > 0 && excl <= r && r < incl);
+      if (hit) {
+        const int ln = __builtin_ctzll(hit);
+        seq = c0 + 64 * j + ln;
+        blk = r - __builtin_amdgcn_readlane(excl, ln);
+        return;
+      }
+      running = __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+}
+
 template <typename P, int D, int NB, bool ALIBI>
 __global__ void __launch_bounds__(kWaves * 64)
 pa_streamk_kernel(const DecodeArgs a) {
@@ -118,11 +169,10 @@ pa_streamk_kernel(const DecodeArgs a) {
   const int nwaves = gridDim.x * kWaves;
   const int S = a.num_seqs;
 
-  int T = 0;
-  for (int c0 = 0; c0 < S; c0 += 64) {
-    const int s = c0 + lane;
-    T += wave_sum(s < S ? blocks_of<P::kBS>(clamp_len(a.seq_lens[s], a.max_seq_len)) : 0);
-  }
+  // Batches of up to 128 sequences take one two-chunk batch, longer ones
+  // batches of eight chunks.
+  constexpr int kBS = P::kBS;
+  const int T = S <= 128 ? total_blocks<kBS, 2>(a, lane) : total_blocks<kBS, 8>(a, lane);
   const int64_t total = (int64_t)a.num_kv_heads * T;
   if (total == 0) return;
   const int64_t U = (total + nwaves - 1) / nwaves;
@@ -134,21 +184,10 @@ pa_streamk_kernel(const DecodeArgs a) {
   int kvh = (int)(u0 / T);
   const int r = (int)(u0 - (int64_t)kvh * T);
   int seq = 0, blk = 0;
-  int running = 0;
-  for (int c0 = 0; c0 < S; c0 += 64) {
-    const int s = c0 + lane;
-    const int nb = s < S ? blocks_of<P::kBS>(clamp_len(a.seq_lens[s], a.max_seq_len)) : 0;
-    const int incl = wave_incl_scan(nb, lane) + running;
-    const int excl = incl - nb;
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(nb > 0 && excl <= r && r < incl);
-    if (hit) {
-      const int ln = __builtin_ctzll(hit);
-      seq = c0 + ln;
-      blk = r - __builtin_amdgcn_readlane(excl, ln);
-      break;
-    }
-    running = __builtin_amdgcn_readlane(incl, 63);
-  }
+  if (S <= 128)
+    find_block<kBS, 2>(a, lane, r, seq, blk);
+  else
+    find_block<kBS, 8>(a, lane, r, seq, blk);
 
   float v_scale = 1.f;
   if (a.v_scale) v_scale = *a.v_scale;

@@ -131,6 +131,25 @@ def test_zero_length_sequences():
     _run.compare(out, ref, "bf16", seqs=[1, 3], what="zero-length neighbours")
 
 
+@pytest.mark.parametrize("num_seqs", [129, 1100])
+def test_many_sequences(num_seqs):
+    # More than 128 sequences take the stream-K start-up scan in batches of
+    # 8 x 64 sequences; 1100 spans three batches, the last one partial, and
+    # about a fifth of the sequences are empty, some at chunk boundaries.
+    rng = np.random.default_rng(num_seqs)
+    lens = rng.integers(1, 41, num_seqs)
+    lens[rng.random(num_seqs) < 0.2] = 0
+    lens[[i for i in (63, 64, 127, 128, 511, 512) if i < num_seqs]] = 0
+    cfg = workloads.GQA.with_(num_seqs=num_seqs, num_heads=8, num_kv_heads=2, pool_blocks=4096,
+                              seq_lens=("fixed", tuple(int(x) for x in lens)))
+    print(f"[case] {num_seqs} sequences, {int((lens == 0).sum())} empty", flush=True)
+    case = workloads.make_case(cfg, device=DEV, poison=True)
+    out = _run.run_hip(case)
+    torch.cuda.synchronize()
+    ref = _run.run_oracle(case)
+    _run.compare(out, ref, "bf16", what=f"{num_seqs} sequences")
+
+
 def test_max_seq_len_above_longest():
     cfg = workloads.GQA.with_(num_seqs=5, pool_blocks=256, seq_lens=("uniform", 1, 400))
     case = workloads.make_case(cfg, device=DEV, max_seq_len=3000)
