@@ -160,6 +160,154 @@ __device__ void find_block(const DecodeArgs& a, int lane, int r, int& seq, int& 
   }
 }
 
+// Register-set copy: arrays element by element, anything else by assignment.
+template <typename T>
+__device__ __forceinline__ void assign(T& d, const T& s) { d = s; }
+template <typename T, int N>
+__device__ __forceinline__ void assign(T (&d)[N], const T (&s)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) assign(d[i], s[i]);
+}
+
+// One wave's stream-K share as a single block pipeline. The (sequence, kv
+// head) pairs of the share follow one another without a pause: the next
+// pair's q rows and first 64 table entries are loaded when the current pair
+// starts, and its first block's K/V loads are issued before the current
+// pair's last block is computed, the way a pair's own next block is.
+template <typename P, int D, bool ALIBI>
+__device__ __forceinline__ void streamk_share(const DecodeArgs& a, int w, int seq, int kvh, int blk, int64_t units,
+                                              float v_scale) {
+  using OutElem = typename P::OutElem;
+  using KRegs = typename P::KRegs;
+  using VRegs = typename P::VRegs;
+  constexpr int kBS = P::kBS;
+  constexpr int kShift = kBS == 32 ? 5 : 4;
+  const int S = a.num_seqs;
+  const unsigned top = (unsigned)(a.num_blocks - 1);
+
+  struct Seg {   // blocks [b0, b1) of the pair (seq, kvh); nbs blocks of L tokens in all
+    int seq, kvh, b0, b1, nbs, L;
+  };
+  auto make_seg = [&](int s, int k, int b0, int64_t left) {
+    Seg g;
+    g.seq = s;
+    g.kvh = k;
+    g.b0 = b0;
+    g.L = clamp_len(a.seq_lens[s], a.max_seq_len);
+    g.nbs = blocks_of<kBS>(g.L);
+    g.b1 = b0 + (int)min((int64_t)(g.nbs - b0), left);
+    return g;
+  };
+
+  WaveAttn<P, D, 1, ALIBI> wa;
+  wa.init_lane(a);
+  const int lane = wa.lane;
+
+  Seg cur = make_seg(seq, kvh, blk, units);
+  int64_t left = units - (cur.b1 - cur.b0);   // units of the share after cur
+  float sl;
+  wa.load_pair_q(a, cur.seq, cur.kvh, wa.q, sl);
+  wa.reset(sl);
+  const int32_t* trow = a.block_tables + (int64_t)cur.seq * a.max_blocks_per_seq;
+  int chunk = cur.b0;   // lane i of tbl holds the entry of block chunk + i
+  int tbl = trow[min(chunk + lane, cur.b1 - 1)];
+
+  // The share's next pair, prefetched.
+  Seg nx{};
+  bool has_nx = false;
+  typename P::QRegs qn;
+  float sln = 0.f;
+  int tbl_n = 0;
+  auto prefetch = [&]() {
+    has_nx = false;
+    if (left <= 0) return;
+    int s = cur.seq, k = cur.kvh;
+    do {
+      if (++s == S) {
+        s = 0;
+        ++k;
+      }
+    } while (k < a.num_kv_heads && clamp_len(a.seq_lens[s], a.max_seq_len) == 0);
+    if (k >= a.num_kv_heads) return;   // only with inconsistent inputs
+    nx = make_seg(s, k, 0, left);
+    has_nx = true;
+    wa.load_pair_q(a, nx.seq, nx.kvh, qn, sln);
+    tbl_n = a.block_tables[(int64_t)nx.seq * a.max_blocks_per_seq + min(lane, nx.b1 - 1)];
+  };
+  prefetch();
+
+  const char* kbase = reinterpret_cast<const char*>(a.key_cache);
+  const char* vbase = reinterpret_cast<const char*>(a.value_cache);
+  auto load_block = [&](int k, unsigned phys, KRegs (&kr)[1], VRegs (&vr)[1]) {
+    phys = phys < top ? phys : top;
+    const int64_t off = (int64_t)phys * a.k_block_stride_bytes;   // K and V tiles share strides
+    P::load_k(kbase + (int64_t)k * a.k_head_stride_bytes + off, wa.lo, kr[0]);
+    P::load_v(vbase + (int64_t)k * a.v_head_stride_bytes + off, wa.lo, vr[0]);
+  };
+  auto issue_cur = [&](int g, KRegs (&kr)[1], VRegs (&vr)[1]) {   // block g of cur
+    if (g - chunk >= 64) {
+      chunk += 64;
+      tbl = trow[min(chunk + lane, cur.b1 - 1)];
+    }
+    load_block(cur.kvh, (unsigned)__builtin_amdgcn_readlane(tbl, g - chunk), kr, vr);
+  };
+
+  int last_blk = (cur.L - 1) >> kShift;
+  int tail = cur.L - (last_blk << kShift);   // valid slots in the last block, 1..kBS
+  int g = cur.b0;
+  // Computes block g of cur (in kr/vr) after issuing its successor into
+  // kn/vn; false once the share is done.
+  auto step = [&](KRegs (&kr)[1], VRegs (&vr)[1], KRegs (&kn)[1], VRegs (&vn)[1]) -> bool {
+    const bool more = g + 1 < cur.b1;
+    if (more)
+      issue_cur(g + 1, kn, vn);
+    else if (has_nx)
+      load_block(nx.kvh, (unsigned)__builtin_amdgcn_readlane(tbl_n, 0), kn, vn);
+    wa.consume(kr, vr, g, 1, cur.L, last_blk, tail);
+    if (more) {
+      ++g;
+      return true;
+    }
+    wa.finish();
+    const int64_t pair = (int64_t)cur.kvh * S + cur.seq;
+    const int64_t h0 = (int64_t)cur.seq * a.num_heads + cur.kvh * a.group;
+    if (cur.b0 == 0 && cur.b1 == cur.nbs) {
+      wa.store_rows(reinterpret_cast<OutElem*>(a.out) + h0 * D, D, v_scale);
+    } else {
+      const int64_t slot = pair + w;
+      wa.store_rows(a.seg_out + slot * a.group * D, D, v_scale);
+      if (wa.active && wa.q4 == 0) {
+        a.seg_max[slot * a.group + (lane & 15)] = wa.m;
+        a.seg_sum[slot * a.group + (lane & 15)] = wa.lsum;
+      }
+    }
+    if (lane == 0) {
+      if (cur.b0 == 0) a.seg_meta[2 * pair] = w;
+      if (cur.b1 == cur.nbs) a.seg_meta[2 * pair + 1] = w;
+    }
+    if (!has_nx) return false;
+    // On to the prefetched pair, whose first block is already in kn/vn.
+    cur = nx;
+    left -= cur.b1 - cur.b0;
+    assign(wa.q, qn);
+    wa.reset(sln);
+    trow = a.block_tables + (int64_t)cur.seq * a.max_blocks_per_seq;
+    chunk = 0;
+    tbl = tbl_n;
+    last_blk = (cur.L - 1) >> kShift;
+    tail = cur.L - (last_blk << kShift);
+    g = 0;
+    prefetch();
+    return true;
+  };
+
+  KRegs ka[1], kb[1];
+  VRegs va[1], vb[1];
+  issue_cur(cur.b0, ka, va);
+  while (step(ka, va, kb, vb) && step(kb, vb, ka, va)) {
+  }
+}
+
 template <typename P, int D, int NB, bool ALIBI>
 __global__ void __launch_bounds__(kWaves * 64)
 pa_streamk_kernel(const DecodeArgs a) {
@@ -191,45 +339,50 @@ pa_streamk_kernel(const DecodeArgs a) {
 
   float v_scale = 1.f;
   if (a.v_scale) v_scale = *a.v_scale;
-  int64_t u = u0;
-  while (true) {
-    const int L = clamp_len(a.seq_lens[seq], a.max_seq_len);
-    const int nbs = blocks_of<P::kBS>(L);
-    const int n = (int)min((int64_t)(nbs - blk), u1 - u);
-    WaveAttn<P, D, NB, ALIBI> wa;
-    wa.begin(a, seq, kvh);
-    const char* kh = reinterpret_cast<const char*>(a.key_cache) + (int64_t)kvh * a.k_head_stride_bytes;
-    const char* vh = reinterpret_cast<const char*>(a.value_cache) + (int64_t)kvh * a.v_head_stride_bytes;
-    wa.run(a, kh, vh, a.block_tables + (int64_t)seq * a.max_blocks_per_seq, blk, blk + n, L);
-    wa.finish();
-    const int64_t pair = (int64_t)kvh * S + seq;
-    const int64_t h0 = (int64_t)seq * a.num_heads + kvh * a.group;
-    if (blk == 0 && n == nbs) {
-      wa.store_rows(reinterpret_cast<OutElem*>(a.out) + h0 * D, D, v_scale);
-    } else {
-      const int64_t slot = pair + w;
-      wa.store_rows(a.seg_out + slot * a.group * D, D, v_scale);
-      if (wa.active && wa.q4 == 0) {
-        a.seg_max[slot * a.group + (lane & 15)] = wa.m;
-        a.seg_sum[slot * a.group + (lane & 15)] = wa.lsum;
+  if constexpr (NB == 1) {
+    streamk_share<P, D, ALIBI>(a, w, seq, kvh, blk, u1 - u0, v_scale);
+  } else {
+    // Several blocks per iteration: one pair at a time.
+    int64_t u = u0;
+    while (true) {
+      const int L = clamp_len(a.seq_lens[seq], a.max_seq_len);
+      const int nbs = blocks_of<P::kBS>(L);
+      const int n = (int)min((int64_t)(nbs - blk), u1 - u);
+      WaveAttn<P, D, NB, ALIBI> wa;
+      wa.begin(a, seq, kvh);
+      const char* kh = reinterpret_cast<const char*>(a.key_cache) + (int64_t)kvh * a.k_head_stride_bytes;
+      const char* vh = reinterpret_cast<const char*>(a.value_cache) + (int64_t)kvh * a.v_head_stride_bytes;
+      wa.run(a, kh, vh, a.block_tables + (int64_t)seq * a.max_blocks_per_seq, blk, blk + n, L);
+      wa.finish();
+      const int64_t pair = (int64_t)kvh * S + seq;
+      const int64_t h0 = (int64_t)seq * a.num_heads + kvh * a.group;
+      if (blk == 0 && n == nbs) {
+        wa.store_rows(reinterpret_cast<OutElem*>(a.out) + h0 * D, D, v_scale);
+      } else {
+        const int64_t slot = pair + w;
+        wa.store_rows(a.seg_out + slot * a.group * D, D, v_scale);
+        if (wa.active && wa.q4 == 0) {
+          a.seg_max[slot * a.group + (lane & 15)] = wa.m;
+          a.seg_sum[slot * a.group + (lane & 15)] = wa.lsum;
+        }
       }
-    }
-    if (lane == 0) {
-      if (blk == 0) a.seg_meta[2 * pair] = w;
-      if (blk + n == nbs) a.seg_meta[2 * pair + 1] = w;
-    }
-    u += n;
-    if (u >= u1) break;
-    // Next pair with at least one block (one exists: u < u1 <= total; the
-    // kv-head bound only guards against inconsistent inputs).
-    blk = 0;
-    do {
-      if (++seq == S) {
-        seq = 0;
-        ++kvh;
+      if (lane == 0) {
+        if (blk == 0) a.seg_meta[2 * pair] = w;
+        if (blk + n == nbs) a.seg_meta[2 * pair + 1] = w;
       }
-    } while (kvh < a.num_kv_heads && clamp_len(a.seq_lens[seq], a.max_seq_len) == 0);
-    if (kvh >= a.num_kv_heads) break;
+      u += n;
+      if (u >= u1) break;
+      // Next pair with at least one block (one exists: u < u1 <= total; the
+      // kv-head bound only guards against inconsistent inputs).
+      blk = 0;
+      do {
+        if (++seq == S) {
+          seq = 0;
+          ++kvh;
+        }
+      } while (kvh < a.num_kv_heads && clamp_len(a.seq_lens[seq], a.max_seq_len) == 0);
+      if (kvh >= a.num_kv_heads) break;
+    }
   }
 }
 

@@ -647,20 +647,39 @@ struct WaveAttn {
 
   // Query rows of heads kvh*G + g (zero for padded columns g >= G).
   __device__ void begin(const DecodeArgs& a, int seq, int kvh) {
+    init_lane(a);
+    float sl;
+    load_pair_q(a, seq, kvh, q, sl);
+    reset(sl);
+  }
+
+  // The part of the set-up that is the same for every (sequence, kv head).
+  __device__ void init_lane(const DecodeArgs& a) {
     lane = threadIdx.x & 63;
     q4 = lane >> 4;
-    const int g = lane & 15;
-    active = g < a.group;
-    const int h = kvh * a.group + (active ? g : 0);
+    active = (lane & 15) < a.group;
     lo = P::lane_offsets(lane);
-    const auto* qh = reinterpret_cast<const typename P::QElem*>(a.query) + ((int64_t)seq * a.num_heads + h) * D;
-    P::load_q(qh, active, q4, q);
     float k_scale = 1.f;
     if (a.k_scale) k_scale = *a.k_scale;
     c = a.scale * kLog2e * k_scale;
-    slope2 = 0.f;
+  }
+
+  // q rows of the pair's query heads into qq, and this column's ALiBi slope
+  // (log2 units; 0 without ALiBi) into sl.
+  __device__ void load_pair_q(const DecodeArgs& a, int seq, int kvh, typename P::QRegs& qq, float& sl) const {
+    const int h = kvh * a.group + (active ? (lane & 15) : 0);
+    const auto* qh = reinterpret_cast<const typename P::QElem*>(a.query) + ((int64_t)seq * a.num_heads + h) * D;
+    P::load_q(qh, active, q4, qq);
+    sl = 0.f;
     if constexpr (ALIBI) {
-      if (active) slope2 = a.alibi_slopes[h] * kLog2e;
+      if (active) sl = a.alibi_slopes[h] * kLog2e;
+    }
+  }
+
+  // Empty softmax state for a new pair with ALiBi slope sl.
+  __device__ void reset(float sl) {
+    slope2 = sl;
+    if constexpr (ALIBI) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) lane_bias[r] = slope2 * (float)tile_token<kBS>(0, q4, r);
     }
