@@ -136,12 +136,12 @@ __device__ int total_blocks(const DecodeArgs& a, int lane) {
   return T;
 }
 
-// The sequence whose block range (in sequence order) holds block r, and the
-// block's index within it.
+// The sequence whose block range (in sequence order, counted from sequence
+// c_begin) holds block r, and the block's index within it.
 template <int BS, int K>
-__device__ void find_block(const DecodeArgs& a, int lane, int r, int& seq, int& blk) {
+__device__ void find_block(const DecodeArgs& a, int lane, int r, int& seq, int& blk, int c_begin = 0) {
   int running = 0;
-  for (int c0 = 0; c0 < a.num_seqs; c0 += 64 * K) {
+  for (int c0 = c_begin; c0 < a.num_seqs; c0 += 64 * K) {
     int nb[K];
     block_counts<BS, K>(a, c0, lane, nb);
 #pragma unroll
@@ -317,10 +317,26 @@ pa_streamk_kernel(const DecodeArgs a) {
   const int nwaves = gridDim.x * kWaves;
   const int S = a.num_seqs;
 
-  // Batches of up to 128 sequences take one two-chunk batch, longer ones
-  // batches of eight chunks.
+  // Up to 128 sequences: one two-chunk batch. More: batches of 16 chunks
+  // (1024 sequences), whose block totals lane b of bsum keeps for batch b, so
+  // the locate below scans only the batch that holds the wave's first tile.
   constexpr int kBS = P::kBS;
-  const int T = S <= 128 ? total_blocks<kBS, 2>(a, lane) : total_blocks<kBS, 8>(a, lane);
+  constexpr int kBig = 16;
+  int T = 0, bsum = 0;
+  if (S <= 128) {
+    T = total_blocks<kBS, 2>(a, lane);
+  } else {
+    for (int c0 = 0, b = 0; c0 < S; c0 += 64 * kBig, ++b) {
+      int nb[kBig];
+      block_counts<kBS, kBig>(a, c0, lane, nb);
+      int t = 0;
+#pragma unroll
+      for (int j = 0; j < kBig; ++j) t += nb[j];
+      const int bt = wave_sum(t);
+      if (lane == b) bsum = bt;
+      T += bt;
+    }
+  }
   const int64_t total = (int64_t)a.num_kv_heads * T;
   if (total == 0) return;
   const int64_t U = (total + nwaves - 1) / nwaves;
@@ -332,10 +348,17 @@ pa_streamk_kernel(const DecodeArgs a) {
   int kvh = (int)(u0 / T);
   const int r = (int)(u0 - (int64_t)kvh * T);
   int seq = 0, blk = 0;
-  if (S <= 128)
+  if (S <= 128) {
     find_block<kBS, 2>(a, lane, r, seq, blk);
-  else
-    find_block<kBS, 8>(a, lane, r, seq, blk);
+  } else if (S <= 64 * 64 * kBig) {
+    const int incl = wave_incl_scan(bsum, lane);
+    const int excl = incl - bsum;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(bsum > 0 && excl <= r && r < incl);
+    const int b = hit ? __builtin_ctzll(hit) : 0;
+    find_block<kBS, kBig>(a, lane, r - __builtin_amdgcn_readlane(excl, b), seq, blk, 64 * kBig * b);
+  } else {
+    find_block<kBS, kBig>(a, lane, r, seq, blk);
+  }
 
   float v_scale = 1.f;
   if (a.v_scale) v_scale = *a.v_scale;
