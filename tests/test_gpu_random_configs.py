@@ -56,3 +56,31 @@ def test_random_config(seed):
         ref = _run.run_oracle(case)
     _run.compare(out, ref, cfg.q_dtype, what=f"random seed {seed}", extra=extra)
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("kind,bs,alibi", [("bf16", 16, True), ("bf16", 32, False), ("fp8", 16, False),
+                                           ("fp8", 32, True), ("f32", 16, True), ("fp8c", 16, True)])
+def test_many_short_sequences(kind, bs, alibi):
+    # 600 short sequences over about 1024 stream-K waves: each wave's share
+    # runs through several (sequence, kv head) pairs, so the pipeline's
+    # prefetched next pair (q rows, ALiBi slope, first table entries and first
+    # block) is exercised for every cache type.
+    rng = np.random.default_rng(7 + bs + 100 * alibi)
+    lens = rng.integers(1, 71, 600)
+    lens[rng.random(600) < 0.15] = 0
+    base = workloads.FP8 if kind.startswith("fp8") else workloads.GQA
+    cfg = base.with_(name=f"short_{kind}", num_seqs=600, num_heads=8, num_kv_heads=2, head_size=128, block_size=bs,
+                     seq_lens=("fixed", tuple(int(x) for x in lens)), alibi=alibi,
+                     q_dtype="f32" if kind == "f32" else "bf16", pool_blocks=4096 * 16 // bs, seed=bs,
+                     compute="fp8" if kind == "fp8c" else "auto")
+    print(f"[case] {kind} bs={bs} alibi={alibi}: 600 sequences, {int((lens == 0).sum())} empty", flush=True)
+    case = workloads.make_case(cfg, device=DEV, poison=True)
+    out = _run.run_hip(case, compute=cfg.compute)
+    torch.cuda.synchronize()
+    extra = None
+    if cfg.compute == "fp8":
+        ref = _run.run_oracle_fp8(case)
+        extra = _fp8tol.row_bounds(workloads.host_arrays(case))
+    else:
+        ref = _run.run_oracle(case)
+    _run.compare(out, ref, cfg.q_dtype, what=f"600 short sequences, {kind}", extra=extra)
