@@ -27,7 +27,7 @@ from .build import LIB_PATH
 __all__ = [
     "PA_OK", "PA_ERR_NULL", "PA_ERR_SHAPE", "PA_ERR_DTYPE", "PA_ERR_WORKSPACE", "PA_ERR_ALIGN",
     "PA_ERR_HIP", "PA_DTYPE_F32", "PA_DTYPE_BF16", "PA_KV_AUTO", "PA_KV_FP8_E4M3", "PA_KV_FP8_E4M3_COMPUTE",
-    "PA_BLOCK_SIZE", "PA_PARTITION_SIZE", "PA_MAX_GROUP",
+    "PA_BLOCK_SIZE", "PA_PARTITION_SIZE", "PA_MAX_GROUP", "PA_MAX_SEQS",
     "pa_paged_attention_decode", "pa_paged_attention_decode_split", "pa_decode_plan",
     "pa_workspace_bytes", "pa_kv_layout", "pa_last_error", "pa_version", "pa_timing_enable",
     "pa_timing_read", "pa_timing_read_append", "pa_hbm_read_probe", "pa_hbm_gather_probe", "pa_kv_cache_append",
@@ -55,6 +55,7 @@ PA_KV_FP8_E4M3_COMPUTE = 2
 PA_BLOCK_SIZE = 16
 PA_PARTITION_SIZE = 256
 PA_MAX_GROUP = 16
+PA_MAX_SEQS = 65535
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

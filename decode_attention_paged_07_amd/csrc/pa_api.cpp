@@ -130,6 +130,7 @@ int device_cus() {
 int check_plan_args(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_seq_len,
                     int split_tokens) {
   if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
+  if (num_seqs > PA_MAX_SEQS) return fail(PA_ERR_SHAPE, "num_seqs %d exceeds %d", num_seqs, PA_MAX_SEQS);
   if (num_heads <= 0 || num_kv_heads <= 0)
     return fail(PA_ERR_SHAPE, "num_heads %d and num_kv_heads %d must be positive", num_heads, num_kv_heads);
   if (num_heads % num_kv_heads)
@@ -142,6 +143,9 @@ int check_plan_args(int num_seqs, int num_heads, int num_kv_heads, int head_size
   if (split_tokens < 0 || split_tokens % PA_PARTITION_SIZE)
     return fail(PA_ERR_SHAPE, "split_tokens %d is not 0 or a positive multiple of %d", split_tokens,
                 PA_PARTITION_SIZE);
+  if (split_tokens > 0 && ((int64_t)max_seq_len + split_tokens - 1) / split_tokens > PA_MAX_SEQS)
+    return fail(PA_ERR_SHAPE, "max_seq_len %d needs more than %d splits of %d tokens", max_seq_len, PA_MAX_SEQS,
+                split_tokens);
   // Index arithmetic inside the kernels: rows of the workspace and of q/out fit in int64,
   // per-dimension sizes fit in int32 (checked by the types above).
   return PA_OK;

@@ -49,13 +49,17 @@
 namespace pa {
 
 // ---------------------------------------------------------------------------
-// Split grid: grid (num_splits, ceil(num_kv_heads / kWaves), num_seqs).
+// Split grid: grid (ceil(num_kv_heads / kWaves), num_seqs, num_splits). The
+// split index varies slowest, so every sequence's first split is dispatched
+// before any second one: with ragged lengths the grid (sized by max_seq_len)
+// ends in splits past most sequences' ends, which exit at once, instead of
+// interleaving them with the work.
 // ---------------------------------------------------------------------------
 
 template <typename P, int D, int NB, bool ALIBI>
 __global__ void __launch_bounds__(kWaves * 64)
 pa_split_kernel(const DecodeArgs a) {
-  split_unit<P, D, NB, ALIBI>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  split_unit<P, D, NB, ALIBI>(a, blockIdx.z, blockIdx.x, blockIdx.y);
 }
 
 // Merge of the split partials: grid (num_heads, num_seqs), 64 threads.
@@ -459,7 +463,7 @@ static hipError_t launch_mode(const DecodeArgs& a, hipStream_t stream, const Lau
                        stream, a);
   } else {
     hipLaunchKernelGGL((pa_split_kernel<P, D, NB, ALIBI>),
-                       dim3(a.num_splits, (a.num_kv_heads + kWaves - 1) / kWaves, a.num_seqs), dim3(kWaves * 64), 0,
+                       dim3((a.num_kv_heads + kWaves - 1) / kWaves, a.num_seqs, a.num_splits), dim3(kWaves * 64), 0,
                        stream, a);
   }
   err = hipGetLastError();

@@ -82,6 +82,7 @@ extern "C" {
 #define PA_BLOCK_SIZE      16
 #define PA_PARTITION_SIZE  256
 #define PA_MAX_GROUP       16   /* num_heads / num_kv_heads */
+#define PA_MAX_SEQS        65535 /* num_seqs, and num_splits of a split plan: a grid dimension */
 
 /*
  * Cache layouts (the pages' layouts, 10100.com retirement article, §2), with
@@ -145,7 +146,7 @@ int pa_workspace_bytes(int num_seqs, int num_heads, int head_size, int max_seq_l
  *                16-byte aligned, must not overlap `query`.
  *   query        device, [num_seqs][num_heads][head_size], q_dtype, contiguous, 16-B aligned.
  *   key_cache    device, layout above, 16-B aligned.  value_cache  likewise.
- *   num_seqs     >= 0 (0 is a no-op).        num_heads, num_kv_heads: > 0,
+ *   num_seqs     0 .. PA_MAX_SEQS (0 is a no-op). num_heads, num_kv_heads: > 0,
  *                num_heads % num_kv_heads == 0, group <= PA_MAX_GROUP; query
  *                head h uses kv head h / (num_heads / num_kv_heads).
  *   head_size    32, 64 or 128 (64 and 128 are the PR #47361 report's test sizes;

@@ -81,6 +81,7 @@ def call(pa, **over):
     (dict(num_heads=6, num_kv_heads=4), -2), (dict(num_heads=64, num_kv_heads=2), -2),
     (dict(num_kv_heads=0), -2), (dict(num_seqs=-1), -2), (dict(num_blocks=0), -2),
     (dict(max_blocks_per_seq=0), -2), (dict(max_seq_len=65), -2), (dict(max_seq_len=-1), -2),
+    (dict(num_seqs=65536, query=1 << 40), -2),
     (dict(scale=float("inf")), -2), (dict(scale=float("nan")), -2),
     (dict(q_dtype=7), -3), (dict(kv_cache_dtype=5), -3), (dict(q_dtype=0, kv_cache_dtype=1), -3), (dict(q_dtype=0, kv_cache_dtype=2), -3),
     (dict(out=0x10008), -5), (dict(query=0x20004), -5), (dict(key_cache=0x30002), -5),
@@ -107,6 +108,17 @@ def test_split_size_must_be_partition_multiple(pa):
     assert rc == -2
     with pytest.raises(ValueError):
         pa.pa_decode_plan(2, 8, 2, 128, 4096, 100)
+
+
+def test_grid_dimension_limits(pa):
+    # num_seqs and the number of splits each become a launch grid dimension
+    assert pa.PA_MAX_SEQS == 65535
+    assert pa.pa_decode_plan(65535, 8, 2, 128, 4096, 0)[1] == 0
+    with pytest.raises(ValueError):
+        pa.pa_decode_plan(65536, 8, 2, 128, 4096, 0)
+    assert pa.pa_decode_plan(2, 8, 2, 128, 65535 * 256, 256)[1] == 65535
+    with pytest.raises(ValueError):
+        pa.pa_decode_plan(2, 8, 2, 128, 65535 * 256 + 1, 256)
 
 
 def test_plan_partition_counts_follow_the_pages(pa):
