@@ -16,8 +16,9 @@
 //    report's benchmark snippet) and a reduce kernel merges them;
 //  * stream-K (the default): a persistent grid in which every wave takes an
 //    equal, contiguous share of all (block, kv head) tiles of the batch,
-//    ordered kv head, sequence, block; a pair cut by a share boundary is
-//    finished by a merge kernel. Ragged lengths then cost no tail imbalance.
+//    ordered kv head, sequence, block, and runs it as one block pipeline
+//    across the pairs it spans; a pair cut by a share boundary is finished by
+//    a merge kernel. Ragged lengths then leave every wave the same work.
 //
 // Contraction mapping (per 16 tokens of a block; 16x16 fp32 MFMA results):
 //   S[t][g] = sum_d K[t][d] q[g][d]: A = K tile (rows = tokens), B = q
