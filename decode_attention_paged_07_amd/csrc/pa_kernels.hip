@@ -90,10 +90,22 @@ pa_split_reduce_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < kPer; ++k) acc[k] = 0.f;
   const float* tmp = a.tmp_out + row0 * D + lane * kPer;
-  for (int p = 0; p < n; ++p) {
-    const float wgt = es[p] * fast_exp2((ml[p] - big_m) * kLog2e);
+  // Eight splits per step, their loads in flight together (index clamped,
+  // weight zeroed past n); the valid splits add in order p = 0, 1, ...
+  constexpr int kU = 8;
+  for (int p0 = 0; p0 < n; p0 += kU) {
+    float wgt[kU], part[kU][kPer];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) acc[k] += wgt * tmp[(int64_t)p * D + k];
+    for (int u = 0; u < kU; ++u) {
+      const int p = min(p0 + u, n - 1);
+      wgt[u] = es[p] * fast_exp2((ml[p] - big_m) * kLog2e) * (float)(p0 + u < n);
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) part[u][k] = tmp[(int64_t)p * D + k];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) acc[k] += wgt[u] * part[u][k];
   }
   const float inv = 1.f / tot;
   OutElem* out = reinterpret_cast<OutElem*>(a.out) + ((int64_t)seq * a.num_heads + h) * D + lane * kPer;
