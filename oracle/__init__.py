@@ -18,7 +18,7 @@ Sources (cited by page title and section):
     blocks).
 
 Parity status of each function is listed in ``decode_fp64.PINS``,
-``kv_append.PINS`` and ``decode_fp8_compute.PINS``.
+``kv_append.PINS``, ``decode_fp8_compute.PINS`` and ``mla_decode.PINS``.
 """
 
 from .decode_fp64 import (  # noqa: F401
@@ -43,3 +43,5 @@ from .decode_fp8_compute import (  # noqa: F401,E402
     paged_decode_fp8_compute,
     round_to_e4m3fn,
 )
+from .mla_decode import PINS as MLA_PINS  # noqa: F401,E402
+from .mla_decode import gather_latent, mla_decode  # noqa: F401,E402
