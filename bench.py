@@ -26,9 +26,11 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0
 METRIC = "paged decode attn: seqs/s + effective KV-read HBM GB/s (% of MI355X peak)"
 CSRC = os.path.join(ROOT, "decode_attention_paged_07_amd", "csrc")
-KERNEL_SRC = {"pa_streamk_kernel": ("pa_kernels.hip", "pa_wave.h", "pa_kernels.h"),
-              "pa_split_kernel": ("pa_kernels.hip", "pa_wave.h", "pa_kernels.h"),
-              "pa_append_kernel": ("pa_append.hip", "pa_kernels.h")}
+KERNEL_SRC = {"pa_streamk_kernel": ("pa_kernels.hip", "pa_sched.h", "pa_wave.h", "pa_kernels.h"),
+              "pa_split_kernel": ("pa_kernels.hip", "pa_sched.h", "pa_wave.h", "pa_kernels.h"),
+              "pa_append_kernel": ("pa_append.hip", "pa_kernels.h"),
+              "pa_mla_streamk_kernel": ("pa_mla.hip", "pa_sched.h", "pa_wave.h", "pa_kernels.h")}
+PEAK_BF16_TFLOPS = 2500.0
 WORKLOAD_TEXT = {
     "tiny": "tiny fp32 paged decode: 2 seqs {17,40}, 4/4 heads, D=64, bs=16, 16-block pool",
     "mha": "bf16 MHA decode: 64 seqs x 4096, 32/32 heads, D=128, bs=16, 32768-block pool",
@@ -44,6 +46,10 @@ WORKLOAD_TEXT = {
              "bs=32, 65536-block pool",
     "shared": "shared-prompt decode: 16 prompts of 4096 tokens x 8 samples each (128 seqs), own lens U[1,512] "
               "(seed 5), 64/8 heads, D=128, bs=16, bf16, 131072-block pool",
+    "mla": "latent-cache (MLA) decode: 256 seqs, lens U[1,8192] (seed 6), 16 query heads (one GPU's share of "
+           "128 over 8), one latent head of [c_kv 512, k_rope 64], bf16, bs=16, 131072-block pool",
+    "mla128": "latent-cache (MLA) decode: 256 seqs, lens U[1,8192] (seed 7), 128 query heads, one latent head "
+              "of [c_kv 512, k_rope 64], bf16, bs=16, 131072-block pool",
 }
 
 
@@ -571,6 +577,128 @@ def bench_shared(case, steps, warmup):
     }
 
 
+def time_steps(step, steps, warmup, dev):
+    """Event-timed mean over exactly ``steps`` calls after ``warmup`` untimed
+    ones (synchronised on both sides), then the same loop again with the
+    library's per-kernel HIP events. Returns (ms_per_step, partition kernel
+    (total ms, launches), reduce kernel (total ms, launches), ms_per_step of
+    the second loop)."""
+    import torch
+
+    import decode_attention_paged_07_amd as pa
+    for _ in range(warmup):
+        step()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / steps
+    print(f"[bench] {steps} steps, {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+    pa.pa_timing_read()                       # drop anything recorded earlier
+    pa.pa_timing_enable(True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pa.pa_timing_enable(False)
+    part_ms, part_n, red_ms, red_n = pa.pa_timing_read()
+    return ms_per_step, (part_ms, part_n), (red_ms, red_n), e0.elapsed_time(e1) / steps
+
+
+def mla_cpu_baseline(case, out, budget_s: float):
+    """The MLA oracle timed on the host over the first sequences (about
+    budget_s of work), with the GPU output checked on them."""
+    import threadpoolctl
+
+    import oracle
+    import workloads
+    from tests import _run
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    n = case.cfg.num_seqs
+    wall, i, worst = 0.0, 0, (0.0, 0.0)
+    per_seq = None
+    with threadpoolctl.threadpool_limits(limits=cores):
+        while i < n and wall < budget_s:
+            step = 1 if per_seq is None else max(1, min(n - i, int((budget_s - wall) / per_seq)))
+            seqs = list(range(i, min(n, i + step)))
+            h = workloads.mla_host_arrays(case, seqs)     # host copy, not timed
+            t0 = time.perf_counter()
+            ref = oracle.mla_decode(h["query"], h["latent_cache"], h["block_tables"], h["seq_lens"], h["scale"],
+                                    512, q_kind="bf16", kv_kind="bf16")
+            wall += time.perf_counter() - t0
+            worst = tuple(max(a, b) for a, b in zip(worst, _run.compare(out, ref, "bf16", seqs=seqs)))
+            i += len(seqs)
+            per_seq = wall / i
+    tokens = int(case.meta.seq_lens[:i].astype("int64").sum())
+    return {
+        "value": i / wall, "unit": "seqs/s", "cores": cores, "kind": "oracle",
+        "kv_gbps": round(tokens * 576 * 2 / wall / 1e9, 3),
+        "sample": f"first {i} of {n} sequences ({tokens} tokens), fp64 numpy MLA oracle, host copy untimed, "
+                  f"{wall:.1f} s wall",
+    }, {"max_abs": float(f"{worst[0]:.3e}"), "max_rel": float(f"{worst[1]:.3e}")}
+
+
+def bench_mla(config, args, dev):
+    """One latent-cache decode call per step (stream-K kernel + merge)."""
+    import torch
+
+    import decode_attention_paged_07_amd as pa
+    import workloads
+    cfg = workloads.MLA_CONFIGS[config]
+    print(f"[bench] building {config} inputs", file=sys.stderr, flush=True)
+    case = workloads.make_mla_case(cfg, device=dev)
+    out = torch.empty(cfg.num_seqs, cfg.num_heads, 512, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        pa.mla_decode(out, case.query, case.latent_cache, case.scale, case.block_tables, case.seq_lens,
+                      case.max_seq_len)
+
+    ms, (part_ms, part_n), (red_ms, red_n), ms_ev = time_steps(step, args.steps, args.warmup, dev)
+    tokens = int(case.meta.seq_lens.astype("int64").sum())
+    nbytes = tokens * 576 * 2
+    flops = tokens * cfg.num_heads * 2 * (576 + 512)
+    part_avg = part_ms / max(part_n, 1)
+    achieved = nbytes / (part_avg / 1e3) / 1e9
+    tflops = flops / (part_avg / 1e3) / 1e12
+    kernel = "pa_mla_streamk_kernel"
+    rec = {
+        "metric": METRIC, "value": round(cfg.num_seqs / (ms / 1e3), 1), "unit": "seqs/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) values, seeded lengths and block tables)",
+        "config": {"workload": WORKLOAD_TEXT[config], "num_seqs": cfg.num_seqs, "num_heads": cfg.num_heads,
+                   "latent_dim": 512, "rope_dim": 64, "block_size": cfg.block_size, "pool_blocks": cfg.pool_blocks,
+                   "tokens": tokens, "max_seq_len": case.max_seq_len, "kv_bytes": nbytes,
+                   "scheduler": "stream-K"},
+        "effective_kv_gbps": round(nbytes / (ms / 1e3) / 1e9, 1),
+        "frac_of_peak_hbm": round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic_from_profiles(kernel, config), "avg_launch_ms": round(part_avg, 5),
+                     "algorithmic_bytes_per_launch": nbytes},
+        "mfma": {"algorithmic_flops_per_launch": flops, "achieved_tflops": round(tflops, 1),
+                 "peak_tflops": PEAK_BF16_TFLOPS, "frac": round(tflops / PEAK_BF16_TFLOPS, 4)},
+        "reduce_avg_ms": round(red_ms / red_n, 5) if red_n else 0.0,
+        "ms_per_step_with_kernel_events": round(ms_ev, 5),
+        "kernel_sha": kernel_sha(kernel),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        step()
+        torch.cuda.synchronize()
+        base, parity = mla_cpu_baseline(case, out, args.cpu_seconds)
+        base["gpu_speedup"] = round(rec["value"] / base["value"], 1)
+        rec["cpu_baseline"] = base
+        rec["parity_on_sample"] = parity
+    return rec
+
+
 def cpu_baseline(case, budget_s: float):
     """Time the fp64 oracle on the host over the first sequences of the batch
     until about budget_s seconds of work, and check the GPU output on them."""
@@ -688,6 +816,9 @@ def main():
     import decode_attention_paged_07_amd as pa
     import workloads
 
+    if args.config in workloads.MLA_CONFIGS:
+        print(json.dumps(bench_mla(args.config, args, dev)), flush=True)
+        return
     cfg = {**workloads.CONFIGS, **workloads.EXTRA_CONFIGS}[args.config]
     print(f"[bench] building {args.config} inputs", file=sys.stderr, flush=True)
     case = workloads.make_case(cfg, device=dev)

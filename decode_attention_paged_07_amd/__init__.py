@@ -36,7 +36,8 @@ __all__ = [
     "pa_copy_blocks", "BlockPool", "copy_blocks", "pa_shared_workspace_bytes",
     "pa_paged_attention_decode_shared", "PrefixGroups", "prefix_groups", "find_prefix_groups",
     "paged_attention_decode_shared", "kv_cache_shapes", "LIB_PATH",
-    "PagedAttentionError",
+    "PagedAttentionError", "PA_MLA_LATENT_DIM", "PA_MLA_ROPE_DIM", "PA_MLA_MAX_HEADS",
+    "pa_mla_workspace_bytes", "pa_mla_decode", "mla_decode", "mla_cache_shape",
 ]
 
 PA_OK = 0
@@ -56,6 +57,9 @@ PA_BLOCK_SIZE = 16
 PA_PARTITION_SIZE = 256
 PA_MAX_GROUP = 16
 PA_MAX_SEQS = 65535
+PA_MLA_LATENT_DIM = 512
+PA_MLA_ROPE_DIM = 64
+PA_MLA_MAX_HEADS = 128
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -129,6 +133,11 @@ _lib.pa_paged_attention_decode_shared.argtypes = _DECODE_ARGS[:20] + [_c_int, _v
 _lib.pa_paged_attention_decode_shared.restype = _c_int
 _lib.pa_copy_blocks.argtypes = [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_size, _vp]
 _lib.pa_copy_blocks.restype = _c_int
+_lib.pa_mla_workspace_bytes.argtypes = [_c_int, _c_int, ctypes.POINTER(_c_size)]
+_lib.pa_mla_workspace_bytes.restype = _c_int
+_lib.pa_mla_decode.argtypes = [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_float, _vp, _c_int, _vp, _c_int,
+                               _c_int, _vp, _c_size, _vp]
+_lib.pa_mla_decode.restype = _c_int
 
 
 class PagedAttentionError(RuntimeError):
@@ -505,6 +514,64 @@ def paged_attention_decode(out, query, key_cache, value_cache, num_kv_heads, sca
         kvd, ks.data_ptr() if ks is not None else None, vs.data_ptr() if vs is not None else None,
         ws_ptr, ws_bytes, stream, int(split_tokens))
     _raise_for(rc, "paged_attention_decode")
+
+
+def pa_mla_workspace_bytes(num_seqs, num_heads) -> int:
+    out = _c_size(0)
+    _raise_for(_lib.pa_mla_workspace_bytes(num_seqs, num_heads, ctypes.byref(out)), "pa_mla_workspace_bytes")
+    return out.value
+
+
+def pa_mla_decode(out, query, latent_cache, num_seqs, num_heads, num_blocks, scale, block_tables,
+                  max_blocks_per_seq, seq_lens, block_size, max_seq_len, workspace, workspace_bytes,
+                  stream) -> int:
+    return _lib.pa_mla_decode(out, query, latent_cache, num_seqs, num_heads, num_blocks, scale, block_tables,
+                              max_blocks_per_seq, seq_lens, block_size, max_seq_len, workspace,
+                              workspace_bytes, stream)
+
+
+def mla_cache_shape(num_blocks, block_size=16):
+    """Shape of the bf16 latent cache: [num_blocks, 576/8, block_size, 8]."""
+    return (num_blocks, (PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM) // 8, block_size, 8)
+
+
+def mla_decode(out, query, latent_cache, scale, block_tables, seq_lens, max_seq_len, *,
+               workspace=None) -> None:
+    """Latent-cache (MLA) decode: out[s,h] = sum_t softmax_t(scale*q[s,h].row_t) * row_t[:512].
+
+    query bf16 [num_seqs, num_heads, 576] (absorbed query and rope query), out bf16
+    [num_seqs, num_heads, 512], latent_cache bf16 ``mla_cache_shape(num_blocks)``; block_tables
+    int32 [num_seqs, max_blocks]; seq_lens int32 [num_seqs]. Runs on the current stream.
+    """
+    dev = query.device
+    _need(dev.type == "cuda", "query must be on a GPU")
+    for name, t in (("out", out), ("query", query), ("latent_cache", latent_cache),
+                    ("block_tables", block_tables), ("seq_lens", seq_lens)):
+        _need(t.device == dev, f"{name} is not on the query's device")
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+    width = PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM
+    if query.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or latent_cache.dtype != torch.bfloat16:
+        raise TypeError("query, out and latent_cache must be bfloat16")
+    _need(query.dim() == 3 and query.shape[2] == width, f"query must be [num_seqs, num_heads, {width}]")
+    num_seqs, num_heads, _ = query.shape
+    _need(tuple(out.shape) == (num_seqs, num_heads, PA_MLA_LATENT_DIM),
+          f"out must be [num_seqs, num_heads, {PA_MLA_LATENT_DIM}]")
+    _need(latent_cache.dim() == 4, "latent_cache must be [num_blocks, 72, block_size, 8]")
+    num_blocks, block_size = latent_cache.shape[0], latent_cache.shape[2]
+    _need(tuple(latent_cache.shape) == mla_cache_shape(num_blocks, block_size),
+          f"latent_cache shape {tuple(latent_cache.shape)} != {mla_cache_shape(num_blocks, block_size)}")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == num_seqs, "block_tables must be int32 [num_seqs, max_blocks]")
+    _need(seq_lens.dtype == torch.int32 and seq_lens.shape == (num_seqs,), "seq_lens must be int32 [num_seqs]")
+    if workspace is None:
+        workspace = _workspace_for(dev, pa_mla_workspace_bytes(num_seqs, num_heads))
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = _lib.pa_mla_decode(out.data_ptr(), query.data_ptr(), latent_cache.data_ptr(), num_seqs, num_heads,
+                            num_blocks, float(scale), block_tables.data_ptr(), block_tables.shape[1],
+                            seq_lens.data_ptr(), block_size, int(max_seq_len), ws_ptr, ws_bytes, stream)
+    _raise_for(rc, "mla_decode")
 
 
 def kv_cache_append(key_cache, value_cache, key, value, block_tables, positions,

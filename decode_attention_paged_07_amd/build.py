@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG_DIR)
 LIB_NAME = "libpa_decode.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = [os.path.join(PKG_DIR, "csrc", f)
-           for f in ("pa_kernels.hip", "pa_shared.hip", "pa_append.hip", "pa_probe.hip", "pa_api.cpp", "pa_blocks.cpp")]
+           for f in ("pa_kernels.hip", "pa_shared.hip", "pa_append.hip", "pa_mla.hip", "pa_probe.hip", "pa_api.cpp",
+                     "pa_blocks.cpp")]
 INCLUDE = os.path.join(ROOT, "include")
 
 # Packed-fp32 VALU instructions stay disabled in device code: plain float

@@ -431,6 +431,42 @@ SharedPlan make_shared_plan(int num_seqs, int num_heads, int num_kv_heads, int h
   return p;
 }
 
+// ---- latent-cache (MLA) decode --------------------------------------------------
+
+// Stream-K plan of the MLA kernel: one wave per 16-head group and share (one
+// wave per SIMD: each needs more than 256 registers), at most two groups per
+// workgroup (18 KiB of LDS each), more groups split over `chunks` workgroups
+// per share.
+struct MlaPlan {
+  int head_groups, waves_per_wg, chunks, max_shares;
+  size_t off[4];
+  size_t bytes;
+};
+
+MlaPlan make_mla_plan(int num_seqs, int num_heads) {
+  MlaPlan p{};
+  p.head_groups = (num_heads + 15) / 16;
+  p.waves_per_wg = std::min(p.head_groups, 2);
+  p.chunks = (p.head_groups + p.waves_per_wg - 1) / p.waves_per_wg;
+  p.max_shares = PA_MLA_MAX_WAVES / (p.waves_per_wg * p.chunks);
+  const size_t hpad = (size_t)p.head_groups * 16;
+  const size_t slots = (size_t)num_seqs + p.max_shares;
+  p.off[0] = 0;
+  p.off[1] = round_up(slots * hpad * PA_MLA_LATENT_DIM * sizeof(float), 256);
+  p.off[2] = p.off[1] + round_up(slots * hpad * sizeof(float), 256);
+  p.off[3] = p.off[2] + round_up(slots * hpad * sizeof(float), 256);
+  p.bytes = p.off[3] + round_up((size_t)num_seqs * 2 * sizeof(int32_t), 256);
+  return p;
+}
+
+int check_mla_plan_args(int num_seqs, int num_heads) {
+  if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
+  if (num_seqs > PA_MAX_SEQS) return fail(PA_ERR_SHAPE, "num_seqs %d exceeds %d", num_seqs, PA_MAX_SEQS);
+  if (num_heads <= 0 || num_heads > PA_MLA_MAX_HEADS)
+    return fail(PA_ERR_SHAPE, "num_heads %d is not in [1, %d]", num_heads, PA_MLA_MAX_HEADS);
+  return PA_OK;
+}
+
 }  // namespace
 
 // Error helpers for the other host translation units (pa_blocks.cpp).
@@ -686,6 +722,97 @@ int pa_kv_cache_append(void* key_cache, void* value_cache, const void* key, cons
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
 int pa_version(void) { return 100; }
+
+int pa_mla_workspace_bytes(int num_seqs, int num_heads, size_t* bytes) {
+  if (!bytes) return fail(PA_ERR_NULL, "bytes is NULL");
+  const int rc = check_mla_plan_args(num_seqs, num_heads);
+  if (rc) return rc;
+  *bytes = num_seqs == 0 ? 0 : make_mla_plan(num_seqs, num_heads).bytes;
+  return ok();
+}
+
+int pa_mla_decode(void* out, const void* query, const void* latent_cache, int num_seqs, int num_heads,
+                  int num_blocks, float scale, const int32_t* block_tables, int max_blocks_per_seq,
+                  const int32_t* seq_lens, int block_size, int max_seq_len, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  int rc = check_mla_plan_args(num_seqs, num_heads);
+  if (rc) return rc;
+  if (block_size != 16) return fail(PA_ERR_SHAPE, "block_size %d is not 16", block_size);
+  if (max_seq_len < 0) return fail(PA_ERR_SHAPE, "max_seq_len %d < 0", max_seq_len);
+  if (num_seqs == 0) return ok();
+  if (!out || !query || !latent_cache || !block_tables || !seq_lens)
+    return fail(PA_ERR_NULL, "out, query, latent_cache, block_tables and seq_lens must be non-NULL");
+  if (num_blocks <= 0) return fail(PA_ERR_SHAPE, "num_blocks %d must be positive", num_blocks);
+  if (max_blocks_per_seq <= 0) return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d must be positive", max_blocks_per_seq);
+  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PA_ERR_SHAPE, "max_seq_len %d exceeds max_blocks_per_seq*block_size = %lld", max_seq_len,
+                (long long)max_blocks_per_seq * block_size);
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(latent_cache, 16))
+    return fail(PA_ERR_ALIGN, "out, query and latent_cache must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(seq_lens, 4))
+    return fail(PA_ERR_ALIGN, "block_tables and seq_lens must be 4-byte aligned");
+  const size_t q_bytes = (size_t)num_seqs * num_heads * (PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM) * 2;
+  const size_t o_bytes = (size_t)num_seqs * num_heads * PA_MLA_LATENT_DIM * 2;
+  const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), q0 = reinterpret_cast<uintptr_t>(query);
+  if (o0 < q0 + q_bytes && q0 < o0 + o_bytes) return fail(PA_ERR_SHAPE, "out overlaps query");
+  const MlaPlan plan = make_mla_plan(num_seqs, num_heads);
+  if ((rc = check_workspace(workspace, workspace_bytes, plan.bytes))) return rc;
+
+  pa::MlaArgs a{};
+  pa::DecodeArgs& d = a.d;
+  d.out = out;
+  d.query = query;
+  d.key_cache = latent_cache;
+  d.value_cache = latent_cache;
+  d.block_tables = block_tables;
+  d.seq_lens = seq_lens;
+  char* ws = static_cast<char*>(workspace);
+  d.seg_out = reinterpret_cast<float*>(ws + plan.off[0]);
+  d.seg_max = reinterpret_cast<float*>(ws + plan.off[1]);
+  d.seg_sum = reinterpret_cast<float*>(ws + plan.off[2]);
+  d.seg_meta = reinterpret_cast<int32_t*>(ws + plan.off[3]);
+  d.k_block_stride_bytes = (int64_t)(PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM) * block_size * 2;
+  d.v_block_stride_bytes = d.k_block_stride_bytes;
+  d.scale = scale;
+  d.num_seqs = num_seqs;
+  d.num_heads = num_heads;
+  d.num_kv_heads = 1;
+  d.group = 16;
+  d.head_size = PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM;
+  d.block_size = block_size;
+  d.num_blocks = num_blocks;
+  d.max_blocks_per_seq = max_blocks_per_seq;
+  d.max_seq_len = max_seq_len;
+  a.head_groups = plan.head_groups;
+  a.waves_per_wg = plan.waves_per_wg;
+  a.chunks = plan.chunks;
+  // Shares: PA_MLA_WAVES_PER_CU waves per compute unit in all, a multiple of
+  // 8 so that the chunks of a share land on one XCD.
+  const int waves = device_cus() * PA_MLA_WAVES_PER_CU;
+  int shares = waves / (plan.waves_per_wg * plan.chunks);
+  shares = std::max(8, shares / 8 * 8);
+  a.shares = std::min(shares, plan.max_shares);
+  d.streamk_workgroups = a.shares * a.chunks;
+
+  pa::LaunchHooks hooks;
+  std::unique_lock<std::mutex> lock(g_timing.mu, std::defer_lock);
+  bool timed = false;
+  {
+    std::lock_guard<std::mutex> g(g_timing.mu);
+    timed = g_timing.on;
+  }
+  if (timed) {
+    lock.lock();
+    hooks.before_partition = record_begin;
+    hooks.after_partition = hook_part_end;
+    hooks.before_reduce = record_begin;
+    hooks.after_reduce = hook_red_end;
+  }
+  hipError_t err = pa::launch_mla(a, static_cast<hipStream_t>(stream), hooks);
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return ok();
+}
 
 int pa_timing_enable(int on) {
   std::lock_guard<std::mutex> g(g_timing.mu);

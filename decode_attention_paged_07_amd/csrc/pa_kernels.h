@@ -48,6 +48,11 @@
 #endif
 // Upper bound on stream-K waves; sizes the segment workspace.
 #define PA_SK_MAX_WAVES 4096
+// MLA stream-K waves per compute unit (each wave needs more than 256
+// registers per lane, so one per SIMD).
+#ifndef PA_MLA_WAVES_PER_CU
+#define PA_MLA_WAVES_PER_CU 4
+#endif
 
 namespace pa {
 
@@ -163,6 +168,19 @@ struct LaunchHooks {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream, const LaunchHooks& hooks);
+
+// Latent-cache (MLA) decode (pa_mla.hip). d carries the batch: key_cache is
+// the latent cache, head_size the row width, group 16 (heads per wave),
+// num_kv_heads 1; seg_* as for stream-K with slots [S + shares][head_groups*16].
+struct MlaArgs {
+  DecodeArgs d;
+  int head_groups;    // ceil(num_heads / 16)
+  int waves_per_wg;   // head groups per workgroup
+  int chunks;         // workgroups per share: ceil(head_groups / waves_per_wg)
+  int shares;         // stream-K shares (a multiple of 8 when chunks > 1)
+};
+
+hipError_t launch_mla(const MlaArgs& a, hipStream_t stream, const LaunchHooks& hooks);
 
 // Streaming read of `bytes` (a multiple of 16) from `buf` by `workgroups`
 // workgroups of 256 threads (pa_probe.hip).

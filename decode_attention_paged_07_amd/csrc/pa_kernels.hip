@@ -45,6 +45,7 @@
 #include <stdint.h>
 
 #include "pa_kernels.h"
+#include "pa_sched.h"
 #include "pa_wave.h"
 
 namespace pa {
@@ -123,59 +124,6 @@ pa_split_reduce_kernel(const DecodeArgs a) {
 // order) and records its first and last wave in seg_meta[p].
 // ---------------------------------------------------------------------------
 
-template <int BS>
-__device__ __forceinline__ int blocks_of(int L) { return (L + BS - 1) / BS; }
-
-// Block counts of sequences c0 + 64*j + lane, j < K: the loads are
-// unconditional (index clamped, count masked) so all K are in flight together
-// and a scan over seq_lens waits one memory latency per 64*K sequences.
-template <int BS, int K>
-__device__ __forceinline__ void block_counts(const DecodeArgs& a, int c0, int lane, int (&nb)[K]) {
-  const int S = a.num_seqs;
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const int s = c0 + 64 * j + lane;
-    const int L = a.seq_lens[min(s, S - 1)];
-    nb[j] = blocks_of<BS>(clamp_len(L, a.max_seq_len)) & -(int)(s < S);
-  }
-}
-
-// Total blocks over all sequences.
-template <int BS, int K>
-__device__ int total_blocks(const DecodeArgs& a, int lane) {
-  int T = 0;
-  for (int c0 = 0; c0 < a.num_seqs; c0 += 64 * K) {
-    int nb[K];
-    block_counts<BS, K>(a, c0, lane, nb);
-#pragma unroll
-    for (int j = 0; j < K; ++j) T += wave_sum(nb[j]);
-  }
-  return T;
-}
-
-// The sequence whose block range (in sequence order, counted from sequence
-// c_begin) holds block r, and the block's index within it.
-template <int BS, int K>
-__device__ void find_block(const DecodeArgs& a, int lane, int r, int& seq, int& blk, int c_begin = 0) {
-  int running = 0;
-  for (int c0 = c_begin; c0 < a.num_seqs; c0 += 64 * K) {
-    int nb[K];
-    block_counts<BS, K>(a, c0, lane, nb);
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const int incl = wave_incl_scan(nb[j], lane) + running;
-      const int excl = incl - nb[j];
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(nb[j] > 0 && excl <= r && r < incl);
-      if (hit) {
-        const int ln = __builtin_ctzll(hit);
-        seq = c0 + 64 * j + ln;
-        blk = r - __builtin_amdgcn_readlane(excl, ln);
-        return;
-      }
-      running = __builtin_amdgcn_readlane(incl, 63);
-    }
-  }
-}
 
 // Register-set copy: arrays element by element, anything else by assignment.
 template <typename T>
@@ -334,26 +282,9 @@ pa_streamk_kernel(const DecodeArgs a) {
   const int nwaves = gridDim.x * kWaves;
   const int S = a.num_seqs;
 
-  // Up to 128 sequences: one two-chunk batch. More: batches of 16 chunks
-  // (1024 sequences), whose block totals lane b of bsum keeps for batch b, so
-  // the locate below scans only the batch that holds the wave's first tile.
   constexpr int kBS = P::kBS;
-  constexpr int kBig = 16;
-  int T = 0, bsum = 0;
-  if (S <= 128) {
-    T = total_blocks<kBS, 2>(a, lane);
-  } else {
-    for (int c0 = 0, b = 0; c0 < S; c0 += 64 * kBig, ++b) {
-      int nb[kBig];
-      block_counts<kBS, kBig>(a, c0, lane, nb);
-      int t = 0;
-#pragma unroll
-      for (int j = 0; j < kBig; ++j) t += nb[j];
-      const int bt = wave_sum(t);
-      if (lane == b) bsum = bt;
-      T += bt;
-    }
-  }
+  int bsum = 0;
+  const int T = count_blocks<kBS>(a, lane, bsum);
   const int64_t total = (int64_t)a.num_kv_heads * T;
   if (total == 0) return;
   const int64_t U = (total + nwaves - 1) / nwaves;
@@ -365,17 +296,7 @@ pa_streamk_kernel(const DecodeArgs a) {
   int kvh = (int)(u0 / T);
   const int r = (int)(u0 - (int64_t)kvh * T);
   int seq = 0, blk = 0;
-  if (S <= 128) {
-    find_block<kBS, 2>(a, lane, r, seq, blk);
-  } else if (S <= 64 * 64 * kBig) {
-    const int incl = wave_incl_scan(bsum, lane);
-    const int excl = incl - bsum;
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(bsum > 0 && excl <= r && r < incl);
-    const int b = hit ? __builtin_ctzll(hit) : 0;
-    find_block<kBS, kBig>(a, lane, r - __builtin_amdgcn_readlane(excl, b), seq, blk, 64 * kBig * b);
-  } else {
-    find_block<kBS, kBig>(a, lane, r, seq, blk);
-  }
+  locate_block<kBS>(a, lane, r, bsum, seq, blk);
 
   float v_scale = 1.f;
   if (a.v_scale) v_scale = *a.v_scale;

@@ -296,6 +296,47 @@ int pa_paged_attention_decode_shared(void* out, const void* query, const void* k
                                      int max_prefix_blocks, void* workspace, size_t workspace_bytes,
                                      void* stream);
 
+/*
+ * Latent-cache (MLA) decode. Multi-head latent attention, as the 10100.com
+ * retirement article (§2) describes it: each token stores one compressed row
+ * [c_kv, k_rope] instead of separate K and V. The call computes the absorbed
+ * decode step, for every sequence s and query head h:
+ *
+ *     out[s,h,:] = sum_t softmax_t( scale * q[s,h,:] . row_t ) * row_t[0:512]
+ *
+ * over the first seq_lens[s] tokens, where row_t = [c_kv_t (512), k_rope_t
+ * (64)] (DeepSeek-V2's widths; the article's figures for them did not survive
+ * extraction). q[s,h,:] is the absorbed query [q_nope_h W_UK_h, q_rope_h]
+ * (576 wide); out is the latent output (512 wide) before the up-projection
+ * W_UV_h, which is outside this call.
+ *
+ *   query        device, bf16 [num_seqs][num_heads][576], 16-byte aligned
+ *   latent_cache device, bf16 [num_blocks][576/8][block_size][8] (the pages'
+ *                K layout, §2, with one kv head and x = 8), 16-byte aligned
+ *   out          device, bf16 [num_seqs][num_heads][512], 16-byte aligned,
+ *                not overlapping query
+ *   block_tables, seq_lens, max_seq_len: as for pa_paged_attention_decode
+ *   block_size   16; num_heads in [1, PA_MLA_MAX_HEADS]
+ *   workspace    device, at least pa_mla_workspace_bytes(num_seqs,
+ *                num_heads) bytes, 16-byte aligned (NULL allowed when that
+ *                size is 0); contents on entry do not matter, and on return
+ *                they are unspecified
+ *
+ * The schedule is stream-K over (sequence, block) tiles with one wave per 16
+ * query heads; a sequence cut by a share boundary is finished by a merge
+ * kernel. Errors, threading, ownership and device-value contracts as for
+ * pa_paged_attention_decode. Timed by pa_timing_* like the decode calls.
+ */
+#define PA_MLA_LATENT_DIM 512
+#define PA_MLA_ROPE_DIM   64
+#define PA_MLA_MAX_HEADS  128
+#define PA_MLA_MAX_WAVES  4096   /* bound on the persistent grid; sizes the workspace */
+int pa_mla_workspace_bytes(int num_seqs, int num_heads, size_t* bytes);
+int pa_mla_decode(void* out, const void* query, const void* latent_cache, int num_seqs, int num_heads,
+                  int num_blocks, float scale, const int32_t* block_tables, int max_blocks_per_seq,
+                  const int32_t* seq_lens, int block_size, int max_seq_len, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
 /* Text describing the last error returned on the calling thread ("" if none). */
 const char* pa_last_error(void);
 

@@ -57,8 +57,7 @@ def gather_latent(latent_cache: np.ndarray, table_row: np.ndarray, seq_len: int)
     for t in range(seq_len):
         phys = int(np.int64(table_row[t // bs]))
         slot = t % bs
-        for c in range(dx):
-            rows[t, c * x:(c + 1) * x] = latent_cache[phys, c, slot, :]
+        rows[t] = latent_cache[phys, :, slot, :].reshape(width)   # chunk-major: e = c*x + i
     return rows
 
 

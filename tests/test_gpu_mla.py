@@ -1,0 +1,110 @@
+"""GPU parity of the latent-cache (MLA) decode against the fp64 MLA oracle.
+
+The HIP path runs through the C ABI (pa_mla_decode via the binding). Inputs
+are bf16 with fp32 accumulation and bf16 output: element-wise
+|gpu - oracle| <= 1e-2 + 1e-2 * |oracle|.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests import _run
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+
+
+def run_mla(case, out=None):
+    import decode_attention_paged_07_amd as pa
+    if out is None:
+        out = torch.empty(case.cfg.num_seqs, case.cfg.num_heads, 512, dtype=torch.bfloat16, device=DEV)
+    pa.mla_decode(out, case.query, case.latent_cache, case.scale, case.block_tables, case.seq_lens,
+                  case.max_seq_len)
+    return out
+
+
+def oracle_mla(case, seqs=None):
+    import oracle
+    h = workloads.mla_host_arrays(case, seqs)
+    return oracle.mla_decode(h["query"], h["latent_cache"], h["block_tables"], h["seq_lens"], h["scale"], 512,
+                             q_kind="bf16", kv_kind="bf16")
+
+
+def check(case, seqs=None, what=""):
+    print(f"[case] mla {what} S={case.cfg.num_seqs} H={case.cfg.num_heads} "
+          f"lens={case.meta.seq_lens[:8].tolist()}", flush=True)
+    out = run_mla(case)
+    torch.cuda.synchronize()
+    ref = oracle_mla(case, seqs)
+    return out, _run.compare(out, ref, "bf16", seqs=seqs, what=what)
+
+
+def small(lens, heads=16, seed=11, poison=True, pool=None):
+    lens = list(lens)
+    need = sum(-(-n // 16) for n in lens)
+    cfg = workloads.MLA.with_(num_seqs=len(lens), num_heads=heads, pool_blocks=pool or need + 8)
+    return workloads.make_mla_case(cfg, seed=seed, device=DEV, seq_lens=lens, poison=poison)
+
+
+@pytest.mark.parametrize("lens", [[1], [16], [17, 40, 3], [255, 256, 257], [1000, 31, 512]])
+def test_ragged_lengths_poisoned_tails(lens):
+    check(small(lens), what=f"lens {lens}")
+
+
+@pytest.mark.parametrize("heads", [1, 8, 15, 17, 40, 64, 100, 128])
+def test_head_counts(heads):
+    check(small([70, 300, 5, 129], heads=heads, seed=heads), what=f"H={heads}")
+
+
+def test_zero_length_sequences_give_zero_rows():
+    case = small([0, 5, 0, 33], poison=True)
+    out, _ = check(case, what="zero lengths")
+    assert not out[0].any() and not out[2].any()
+
+
+def test_long_sequences_cut_into_many_segments():
+    # 8192 + 3000 tokens = 700 blocks over ~1000 shares: every share holds a
+    # block or none, so both sequences are merged from hundreds of segments.
+    check(small([8192, 3000]), what="segments")
+
+
+def test_long_sequences_many_heads():
+    check(small([6000, 2500, 17], heads=128, seed=5), what="segments H=128")
+
+
+def test_many_short_sequences():
+    rng = np.random.default_rng(8)
+    lens = rng.integers(1, 65, 300).tolist()
+    check(small(lens, seed=8, poison=False), what="300 short")
+
+
+def test_deterministic_run_to_run():
+    case = small([4000, 123, 77], seed=3)
+    a = run_mla(case)
+    b = run_mla(case)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_oversized_max_seq_len_and_table():
+    # The table is wider than the longest sequence and max_seq_len exceeds it.
+    lens = [40, 100]
+    cfg = workloads.MLA.with_(num_seqs=2, pool_blocks=20)
+    case = workloads.make_mla_case(cfg, seed=9, device=DEV, seq_lens=lens, max_seq_len=400, poison=True)
+    check(case, what="wide table")
+
+
+@pytest.mark.parametrize("name", ["mla", "mla128"])
+def test_full_size_workload_sampled(name):
+    cfg = workloads.MLA_CONFIGS[name]
+    case = workloads.make_mla_case(cfg, device=DEV)
+    lens = case.meta.seq_lens
+    seqs = sorted({0, cfg.num_seqs - 1, int(np.argmax(lens)), int(np.argmin(lens)), cfg.num_seqs // 2})
+    out, (max_abs, max_rel) = check(case, seqs=seqs, what=f"{name} sampled {seqs}")
+    print(f"[{name}] sampled max_abs={max_abs:.3e} max_rel={max_rel:.3e}", flush=True)
+    assert torch.isfinite(out.float()).all()
+    del case
+    torch.cuda.empty_cache()

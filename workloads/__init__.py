@@ -1,6 +1,8 @@
 """Seeded synthetic decode workloads (no attention arithmetic lives here)."""
 
-from .configs import CONFIGS, EXTRA_CONFIGS, FP8, FP8C, GQA, GQA32, LONG, MHA, SHARED, TINY, DecodeConfig  # noqa: F401
+from .configs import (  # noqa: F401
+    CONFIGS, EXTRA_CONFIGS, FP8, FP8C, GQA, GQA32, LONG, MHA, MLA, MLA128, MLA_CONFIGS, SHARED, TINY, DecodeConfig,
+)
 from .generate import (  # noqa: F401
     Case,
     Metadata,
@@ -11,4 +13,7 @@ from .generate import (  # noqa: F401
     kv_elem,
     make_case,
     make_metadata,
+    MlaCase,
+    make_mla_case,
+    mla_host_arrays,
 )

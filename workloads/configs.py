@@ -76,3 +76,13 @@ FP8C = FP8.with_(name="fp8c", compute="fp8")
 
 CONFIGS = {c.name: c for c in (TINY, MHA, GQA, LONG, FP8)}
 EXTRA_CONFIGS = {c.name: c for c in (SHARED, GQA32, FP8C)}
+
+# Latent-cache (MLA) decode, not one of the five reference workloads: rows of
+# [c_kv (512), k_rope (64)] in bf16, one latent head, 16-token blocks, lengths
+# and pool as in the GQA workload. "mla" is one GPU's share of a 128-head
+# model whose heads are split over 8 GPUs (16 query heads); "mla128" keeps all
+# 128 heads on one GPU. head_size holds the row width.
+MLA = DecodeConfig("mla", 256, 16, 1, 576, 16, 128 * 1024, "bf16", "auto",
+                   ("uniform", 1, 8192), False, 6)
+MLA128 = MLA.with_(name="mla128", num_heads=128, seed=7)
+MLA_CONFIGS = {c.name: c for c in (MLA, MLA128)}

@@ -28,6 +28,11 @@ Recipe (stated in full so both sides can be regenerated anywhere):
     x = 16 bytes / element size (10100.com article, §2, for the layouts).
   * ALiBi slopes 2^(-8 (i+1) / H) for query head i (the long-context
     workload's slopes with H = 32); scale = 1/sqrt(head_size).
+  * latent-cache (MLA) workloads (make_mla_case): the same metadata draw;
+    values query [S, H, 576] then the latent pool [num_blocks, 72, bs, 8],
+    each torch.randn in float32 cast to bf16; scale = 1/sqrt(128 + 64) (the
+    query-key width of DeepSeek-V2 heads before absorption: 128 without
+    position, 64 with).
 """
 
 from __future__ import annotations
@@ -319,3 +324,87 @@ def _to_np(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.contiguous().view(torch.int16).numpy().view(np.uint16)
     return t.contiguous().numpy()
+
+
+# ---------------------------------------------------------------------------
+# Latent-cache (MLA) workloads.
+# ---------------------------------------------------------------------------
+
+MLA_LATENT, MLA_ROPE = 512, 64
+
+
+@dataclass
+class MlaCase:
+    cfg: DecodeConfig
+    meta: Metadata
+    query: torch.Tensor           # bf16 [S, H, 576]
+    latent_cache: torch.Tensor    # bf16 [NB, 72, bs, 8]
+    block_tables: torch.Tensor
+    seq_lens: torch.Tensor
+    scale: float
+
+    @property
+    def max_seq_len(self) -> int:
+        return self.meta.max_seq_len
+
+
+def make_mla_case(cfg: DecodeConfig, seed: int | None = None, device="cpu", *, seq_lens=None,
+                  max_seq_len=None, poison: bool = False, num_heads: int | None = None) -> MlaCase:
+    """One MLA workload instance; poison=True writes NaN into every pool slot
+    no valid token uses and points unused table entries at a NaN block."""
+    seed = cfg.seed if seed is None else seed
+    if num_heads is not None:
+        cfg = cfg.with_(num_heads=num_heads)
+    width = MLA_LATENT + MLA_ROPE
+    meta = make_metadata(cfg, seed, seq_lens=seq_lens, max_seq_len=max_seq_len)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    query = _randn((cfg.num_seqs, cfg.num_heads, width), gen, device).to(torch.bfloat16)
+    pool = _fill_pool((cfg.pool_blocks, width // 8, cfg.block_size, 8), torch.bfloat16, gen, device)
+    table = meta.block_tables.copy()
+    if poison:
+        used = np.zeros(cfg.pool_blocks, dtype=bool)
+        used[meta.used_blocks] = True
+        unused = np.flatnonzero(~used)
+        if unused.size == 0:
+            raise ValueError("poison needs at least one unused pool block")
+        pool.index_fill_(0, torch.from_numpy(unused).to(pool.device), float("nan"))
+        bs = cfg.block_size
+        for s in range(cfg.num_seqs):
+            n = int(meta.seq_lens[s])
+            nblk = -(-n // bs)
+            table[s, nblk:] = int(unused[0])
+            if nblk and n % bs:
+                pool[int(table[s, nblk - 1]), :, n % bs:, :] = float("nan")
+    return MlaCase(cfg=cfg, meta=meta, query=query, latent_cache=pool,
+                   block_tables=torch.from_numpy(table).to(device),
+                   seq_lens=torch.from_numpy(meta.seq_lens).to(device),
+                   scale=1.0 / math.sqrt(128 + 64))
+
+
+def mla_host_arrays(case: MlaCase, seqs=None) -> dict:
+    """numpy inputs for the MLA oracle, restricted to ``seqs``; the referenced
+    physical blocks are copied and renumbered in ascending order (bf16 as
+    uint16 bit patterns)."""
+    cfg = case.cfg
+    seqs = list(range(cfg.num_seqs)) if seqs is None else list(seqs)
+    lens = case.meta.seq_lens[seqs].astype(np.int64)
+    table = case.block_tables.cpu().numpy()[seqs].astype(np.int64)
+    bs = cfg.block_size
+    nblk = [-(-int(n) // bs) for n in lens]
+    ids = np.unique(np.concatenate([table[i, :nblk[i]] for i in range(len(seqs))] + [np.zeros(0, np.int64)]))
+    if ids.size == 0:
+        ids = np.zeros(1, np.int64)
+    remap = {int(b): i for i, b in enumerate(ids.tolist())}
+    new_table = np.zeros_like(table)
+    for i in range(len(seqs)):
+        for j in range(nblk[i]):
+            new_table[i, j] = remap[int(table[i, j])]
+    pool = case.latent_cache.index_select(0, torch.from_numpy(ids).to(case.latent_cache.device)).cpu()
+    return {
+        "query": _to_np(case.query.cpu()[seqs]),
+        "latent_cache": _to_np(pool),
+        "block_tables": new_table.astype(np.int32),
+        "seq_lens": lens.astype(np.int32),
+        "scale": case.scale,
+    }
