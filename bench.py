@@ -16,6 +16,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -313,7 +314,7 @@ def summarise_profiles(config, stats_dir, fetch_dir, write_dir, cal_fetch_dir, c
         stats = [r for r in stats if "pa_append_kernel" in r["Name"]] + \
                 [r for r in stats if "pa_append_kernel" not in r["Name"]]
     top = stats[0]
-    kernel = "pa_" + top["Name"].split("pa_", 1)[1].split("<", 1)[0].split("I", 1)[0]
+    kernel = re.search(r"pa_[a-z0-9_]*?_kernel", top["Name"]).group(0)
     with open(os.path.join(stats_dir, "run_kernel_trace.csv")) as f:
         tr = next(r for r in csv.DictReader(f) if kernel in r["Kernel_Name"])
     rec = _last_json(stats_dir.rstrip("/") + ".log")

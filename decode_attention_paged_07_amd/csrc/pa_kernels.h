@@ -175,8 +175,8 @@ hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream, cons
 struct MlaArgs {
   DecodeArgs d;
   int head_groups;    // ceil(num_heads / 16)
-  int waves_per_wg;   // head groups per workgroup
-  int chunks;         // workgroups per share: ceil(head_groups / waves_per_wg)
+  int waves_per_wg;   // head groups per workgroup (1)
+  int chunks;         // workgroups per share (head_groups)
   int shares;         // stream-K shares (a multiple of 8 when chunks > 1)
 };
 

@@ -24,12 +24,14 @@
 //     tokens 4*q4 .. 4*q4+3 of column j, exactly the A layout of the next
 //     product. Products with 1 and 0 and sums with zeros are exact, so the
 //     bf16 values come back unchanged. The latent tile is read from HBM once
-//     and serves as both K and V. The only LDS use is each lane's own copy of
-//     its q pieces (a register extension; no barriers).
+//     and serves as both K and V.
+// Tiles go from HBM straight to LDS (global_load_lds_dwordx4), two buffers
+// per wave, so the next block's 18 KiB are in flight without holding
+// registers; each lane reads back only the slots its own loads wrote, so no
+// barrier is needed.
 // With more than 16 heads every 16-head group has its own wave on the same
-// share of blocks: two groups share a workgroup, more are split over
-// workgroups dispatched to the same XCD, so a tile's reads after the first
-// hit in L1 or L2.
+// share of blocks, in workgroups dispatched to the same XCD, so a tile's
+// reads after the first hit in L2.
 //
 // Scheduling is stream-K over (sequence, block) tiles, as for the decode
 // kernels: every share has the same number of blocks; a sequence cut by a
@@ -53,16 +55,28 @@ constexpr int kMlaVSteps = kMlaLatent / 32;            // steps that hold c_kv
 constexpr int kMlaDt = kMlaLatent / 16;                // 16-row output tiles
 constexpr int64_t kMlaBlockBytes = (int64_t)kMlaWidth * kMlaBS * 2;
 
-// Dynamic LDS: kMlaSteps * 64 16-byte slots per wave, each lane's own q
-// pieces (written and read back by the same lane; no barrier).
-extern __shared__ u32x4 mla_q_lds[];
+constexpr int kMlaTileVec = kMlaSteps * 64;            // 16-byte slots per tile (18 KiB)
 
+// s_waitcnt immediate (gfx9 encoding) of lgkmcnt(0) alone.
+constexpr int kWaitLgkm0 = 0xC07F;
+
+__device__ __forceinline__ s16x4 pack_bf16x4_pairs(f32x4 v) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 w = {__builtin_bit_cast(unsigned, __builtin_convertvector((f32x2{v[0], v[1]}), bf16x2)),
+                   __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2{v[2], v[3]}), bf16x2))};
+  return __builtin_bit_cast(s16x4, w);
+}
+
+// One wave's attention state for 16 query heads. The latent tiles are staged
+// in LDS: the tile's 18 KiB are copied by 18 direct global->LDS loads
+// (global_load_lds_dwordx4) in the cache layout, so slot s*64 + lane holds
+// chunk 4s + q4 of token (lane & 15), the A operand of S step s for this
+// lane. Each lane reads only the slots it loaded: no barrier.
 struct MlaWave {
-  u32x4* qs;            // this wave's q slots in LDS
+  bf16x8 q[kMlaSteps];
   f32x4 o[kMlaDt];
   s16x4 ident;          // B operand of the transposing product
   float m, lsum, c;
-  uint32_t koff;        // this lane's byte offset in a tile (step 0)
   int lane, q4;
   bool active;          // this lane's column is a real query head
 
@@ -71,9 +85,7 @@ struct MlaWave {
     q4 = lane >> 4;
     const int j = lane & 15;
     active = hg * 16 + j < a.d.num_heads;
-    koff = (uint32_t)(q4 * kMlaBS * 16 + j * 16);
     c = a.d.scale * kLog2e;
-    qs = mla_q_lds + (threadIdx.x >> 6) * (kMlaSteps * 64);
     // lane (j + 16*q4) holds I[4*q4 + u][j], u = 0..3.
     short e[4];
 #pragma unroll
@@ -81,8 +93,8 @@ struct MlaWave {
     ident = s16x4{e[0], e[1], e[2], e[3]};
   }
 
-  // q rows of heads hg*16 + column, in the d-order of the tile loads: step
-  // s, lane quad q4 -> d = 8*(4s + q4) + u.
+  // q rows of heads hg*16 + column, in the d-order of the tile: step s, lane
+  // quad q4 -> d = 8*(4s + q4) + u.
   __device__ void load_q(const MlaArgs& a, int seq, int hg) {
     const int h = hg * 16 + (active ? (lane & 15) : 0);
     const __bf16* qh = reinterpret_cast<const __bf16*>(a.d.query) + ((int64_t)seq * a.d.num_heads + h) * kMlaWidth;
@@ -90,7 +102,7 @@ struct MlaWave {
     for (int s = 0; s < kMlaSteps; ++s) {
       u32x4 w = {0, 0, 0, 0};
       if (active) w = *reinterpret_cast<const u32x4*>(qh + 8 * (4 * s + q4));
-      qs[s * 64 + lane] = w;
+      q[s] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
@@ -101,23 +113,73 @@ struct MlaWave {
     for (int dt = 0; dt < kMlaDt; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  __device__ void load_tile(const char* tile, u32x4 (&k)[kMlaSteps]) const {
+  // Copy one 18 KiB tile into buf: instruction s moves bytes
+  // [1024 s, 1024 s + 1024) of the tile, 16 per lane, to buf + 64 s.
+  __device__ void stage(const char* tile, u32x4* buf) const {
 #pragma unroll
     for (int s = 0; s < kMlaSteps; ++s)
-      k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + koff + s * 4 * kMlaBS * 16));
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(tile + s * 1024 + lane * 16),
+          (__attribute__((address_space(3))) void*)(buf + s * 64), 16, 0, 2 /* nt */);
   }
 
-  // One block; tokens >= nvalid (a sequence's partial last block) are masked
-  // by select: their logits become -inf and their values 0, since stale
-  // slots may hold NaN and 0 * NaN would poison the sums.
-  __device__ void consume(const u32x4 (&k)[kMlaSteps], int nvalid) {
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < kMlaSteps; ++s)
-      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[s]),
-                                                  __builtin_bit_cast(bf16x8, qs[s * 64 + lane]), z, 0, 0, 0);
-    z *= c;
+  // One block from buf, whose copy is the last but PENDING outstanding
+  // vector-memory operations. Tokens >= nvalid (a sequence's partial last
+  // block) get logit -inf by select, and their registers are zeroed before
+  // the value product (stale slots may hold NaN, and 0 * NaN would poison
+  // the sums).
+  // The tile's copy is waited for and its 18 slots of this lane are read in
+  // one asm block (which also waits for the reads): the compiler does not see
+  // LDS reads it would otherwise order after every outstanding copy,
+  // including the next block's. The outputs are early-clobber: a read's
+  // destination must not be the address register the later reads use.
+  template <int PENDING>
+  __device__ static void read_tile(const u32x4* buf, u32x4 (&k)[kMlaSteps]) {
+    const uint32_t addr = (uint32_t)(uintptr_t)buf;
+    asm volatile(
+        "s_waitcnt vmcnt(%18)\n\t"
+        "ds_read_b128 %0, %19 offset:0\n\t"
+        "ds_read_b128 %1, %19 offset:1024\n\t"
+        "ds_read_b128 %2, %19 offset:2048\n\t"
+        "ds_read_b128 %3, %19 offset:3072\n\t"
+        "ds_read_b128 %4, %19 offset:4096\n\t"
+        "ds_read_b128 %5, %19 offset:5120\n\t"
+        "ds_read_b128 %6, %19 offset:6144\n\t"
+        "ds_read_b128 %7, %19 offset:7168\n\t"
+        "ds_read_b128 %8, %19 offset:8192\n\t"
+        "ds_read_b128 %9, %19 offset:9216\n\t"
+        "ds_read_b128 %10, %19 offset:10240\n\t"
+        "ds_read_b128 %11, %19 offset:11264\n\t"
+        "ds_read_b128 %12, %19 offset:12288\n\t"
+        "ds_read_b128 %13, %19 offset:13312\n\t"
+        "ds_read_b128 %14, %19 offset:14336\n\t"
+        "ds_read_b128 %15, %19 offset:15360\n\t"
+        "ds_read_b128 %16, %19 offset:16384\n\t"
+        "ds_read_b128 %17, %19 offset:17408\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]),
+          "=&v"(k[7]), "=&v"(k[8]), "=&v"(k[9]), "=&v"(k[10]), "=&v"(k[11]), "=&v"(k[12]), "=&v"(k[13]),
+          "=&v"(k[14]), "=&v"(k[15]), "=&v"(k[16]), "=&v"(k[17])
+        : "n"(PENDING), "v"(addr + 16u * (threadIdx.x & 63))
+        : "memory");
+  }
+
+  template <int PENDING>
+  __device__ void consume(u32x4* buf, int nvalid) {
     const bool partial = nvalid < kMlaBS;
+    u32x4 k[kMlaSteps];
+    read_tile<PENDING>(buf, k);
+    if (partial && (lane & 15) >= nvalid) {
+#pragma unroll
+      for (int s = 0; s < kMlaSteps; ++s) k[s] = u32x4{0, 0, 0, 0};
+    }
+    f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};   // two chains in flight
+#pragma unroll
+    for (int s = 0; s < kMlaSteps; s += 2) {
+      z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[s]), q[s], z0, 0, 0, 0);
+      z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[s + 1]), q[s + 1], z1, 0, 0, 0);
+    }
+    f32x4 z = (z0 + z1) * c;
     if (partial) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -136,21 +198,22 @@ struct MlaWave {
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[r] - m);
     lsum += (p[0] + p[1]) + (p[2] + p[3]);
-    const s16x4 pb = pack_bf16x4(p);
+    const s16x4 pb = pack_bf16x4_pairs(p);
+    // Four transposes ahead of their value products.
 #pragma unroll
-    for (int s = 0; s < kMlaVSteps; ++s)
+    for (int s = 0; s < kMlaVSteps; s += 2) {
+      f32x4 vt[4];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const u32x2 half = {k[s][2 * hf], k[s][2 * hf + 1]};
-        f32x4 vt = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, half), ident,
-                                                             f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        if (partial) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (4 * q4 + r >= nvalid) vt[r] = 0.f;
-        }
-        o[2 * s + hf] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pack_bf16x4(vt), pb, o[2 * s + hf], 0, 0, 0);
+      for (int t = 0; t < 4; ++t) {
+        const u32x4 w = k[s + (t >> 1)];
+        const u32x2 hw = {w[2 * (t & 1)], w[2 * (t & 1) + 1]};
+        vt[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, hw), ident,
+                                                         f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        o[2 * s + t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pack_bf16x4_pairs(vt[t]), pb, o[2 * s + t], 0, 0, 0);
+    }
   }
 
   __device__ void finish() { lsum = quad_sum(lsum); }
@@ -170,10 +233,11 @@ struct MlaWave {
 };
 
 // One wave's share: tiles [u0, u0 + units) in (sequence, block) order, as one
-// block pipeline across the sequences it spans (the next block's loads are
-// in flight while the current one is computed, also across a sequence
-// boundary).
-__device__ void mla_share(const MlaArgs& a, int share, int hg, int seq, int blk, int64_t units) {
+// block pipeline across the sequences it spans. Two LDS tile buffers: while
+// one block is computed, the next block's copy (also across a sequence
+// boundary) is in flight into the other.
+__device__ __forceinline__ void mla_share(const MlaArgs& a, int share, int hg, int seq, int blk, int64_t units,
+                                          u32x4* __restrict__ buf0, u32x4* __restrict__ buf1) {
   const DecodeArgs& d = a.d;
   const int S = d.num_seqs;
   const unsigned top = (unsigned)(d.num_blocks - 1);
@@ -221,27 +285,34 @@ __device__ void mla_share(const MlaArgs& a, int share, int hg, int seq, int blk,
   prefetch();
 
   const char* base = reinterpret_cast<const char*>(d.key_cache);
-  auto load_block = [&](unsigned phys, u32x4 (&k)[kMlaSteps]) {
+  auto stage_block = [&](unsigned phys, u32x4* buf) {
     phys = phys < top ? phys : top;
-    wv.load_tile(base + (int64_t)phys * kMlaBlockBytes, k);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // earlier LDS reads of buf are complete
+    wv.stage(base + (int64_t)phys * kMlaBlockBytes, buf);
   };
-  auto issue_cur = [&](int g, u32x4 (&k)[kMlaSteps]) {
+  auto stage_cur = [&](int g, u32x4* buf) {
     if (g - chunk >= 64) {
       chunk += 64;
       tbl = trow[min(chunk + lane, cur.b1 - 1)];
     }
-    load_block((unsigned)__builtin_amdgcn_readlane(tbl, g - chunk), k);
+    stage_block((unsigned)__builtin_amdgcn_readlane(tbl, g - chunk), buf);
   };
 
   int g = cur.b0;
-  auto step = [&](u32x4 (&kr)[kMlaSteps], u32x4 (&kn)[kMlaSteps]) -> bool {
+  // Computes block g of cur (in bc) after starting its successor's copy into
+  // bn; false once the share is done.
+  auto step = [&](u32x4* bc, u32x4* bn) -> bool {
     const bool more = g + 1 < cur.b1;
-    if (more)
-      issue_cur(g + 1, kn);
-    else if (has_nx)
-      load_block((unsigned)__builtin_amdgcn_readlane(tbl_n, 0), kn);
     const int nvalid = min(kMlaBS, cur.L - g * kMlaBS);
-    wv.consume(kr, nvalid);
+    if (more) {
+      stage_cur(g + 1, bn);
+      wv.template consume<kMlaSteps>(bc, nvalid);   // all but the successor's copy complete
+    } else if (has_nx) {
+      stage_block((unsigned)__builtin_amdgcn_readlane(tbl_n, 0), bn);
+      wv.template consume<kMlaSteps>(bc, nvalid);
+    } else {
+      wv.template consume<0>(bc, nvalid);
+    }
     if (more) {
       ++g;
       return true;
@@ -275,23 +346,23 @@ __device__ void mla_share(const MlaArgs& a, int share, int hg, int seq, int blk,
     return true;
   };
 
-  u32x4 ka[kMlaSteps], kb[kMlaSteps];
-  issue_cur(cur.b0, ka);
-  while (step(ka, kb) && step(kb, ka)) {
+  stage_cur(cur.b0, buf0);
+  while (step(buf0, buf1) && step(buf1, buf0)) {
   }
 }
 
-// Grid: shares * chunks workgroups of waves_per_wg waves. Workgroup i takes
-// share 8*(i / (8*chunks)) + i % 8 and head-group chunk (i / 8) % chunks, so
-// the chunks of a share are 8 workgroup ids apart: the same XCD under the
-// round-robin dispatch of workgroups to the eight XCDs.
-__global__ void __launch_bounds__(256) pa_mla_streamk_kernel(const MlaArgs a) {
+// Grid: shares * head_groups workgroups of one wave (36 KiB of LDS each, so
+// four fit a compute unit). Workgroup i takes share 8*(i / (8*head_groups)) +
+// i % 8 and head group (i / 8) % head_groups, so the head groups of a share
+// are 8 workgroup ids apart: the same XCD under the round-robin dispatch of
+// workgroups to the eight XCDs.
+__global__ void __launch_bounds__(64) pa_mla_streamk_kernel(const MlaArgs a) {
+  __shared__ u32x4 tiles0[kMlaTileVec], tiles1[kMlaTileVec];   // two 18 KiB tile buffers
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.x;
   const int chunks = a.chunks;
   const int share = 8 * (i / (8 * chunks)) + i % 8;
-  const int chunk = (i / 8) % chunks;
-  const int hg = chunk * a.waves_per_wg + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hg = (i / 8) % chunks;
   if (hg >= a.head_groups || share >= a.shares) return;
 
   int bsum = 0;
@@ -303,52 +374,77 @@ __global__ void __launch_bounds__(256) pa_mla_streamk_kernel(const MlaArgs a) {
   if (u0 >= u1) return;
   int seq = 0, blk = 0;
   locate_block<kMlaBS>(a.d, lane, (int)u0, bsum, seq, blk);
-  mla_share(a, share, hg, seq, blk, u1 - u0);
+  mla_share(a, share, hg, seq, blk, u1 - u0, tiles0, tiles1);
 }
 
 // Merge of the segments of cut sequences, zero rows of empty ones: grid
-// (head_groups, num_seqs), 256 threads; one (sequence, 16-head group) each.
+// (num_seqs, ceil(num_heads / 4)), four waves of 64; one (sequence, head) row
+// per wave, eight of its 512 values per lane. The segments' weights are
+// computed one per lane; their rows are read eight segments at a time with
+// the loads in flight together, and added in segment order.
 __global__ void __launch_bounds__(256) pa_mla_reduce_kernel(const MlaArgs a) {
   const DecodeArgs& d = a.d;
-  const int hg = blockIdx.x;
-  const int seq = blockIdx.y;
-  const int hpad = a.head_groups * 16;
-  const int nh = min(16, d.num_heads - hg * 16);
+  const int seq = blockIdx.x;
+  const int h = blockIdx.y * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (h >= d.num_heads) return;
+  const int64_t hpad = (int64_t)a.head_groups * 16;
   const int L = clamp_len(d.seq_lens[seq], d.max_seq_len);
-  __bf16* out = reinterpret_cast<__bf16*>(d.out) + ((int64_t)seq * d.num_heads + hg * 16) * kMlaLatent;
+  __bf16* out = reinterpret_cast<__bf16*>(d.out) + ((int64_t)seq * d.num_heads + h) * kMlaLatent + 8 * lane;
   if (L == 0) {
-    for (int e = threadIdx.x; e < nh * kMlaLatent; e += 256) out[e] = static_cast<__bf16>(0.f);
+    store4(out, f32x4{0.f, 0.f, 0.f, 0.f});
+    store4(out + 4, f32x4{0.f, 0.f, 0.f, 0.f});
     return;
   }
   const int w0 = max(0, d.seg_meta[2 * seq]);
   const int w1 = min(a.shares - 1, d.seg_meta[2 * seq + 1]);
   if (w0 >= w1) return;   // one segment: written directly
-  for (int e = threadIdx.x; e < nh * (kMlaLatent / 4); e += 256) {
-    const int h = e / (kMlaLatent / 4);
-    const int d4 = e - h * (kMlaLatent / 4);
-    float big_m = kNegInf;
-    for (int w = w0; w <= w1; ++w) big_m = fmaxf(big_m, d.seg_max[(int64_t)(seq + w) * hpad + hg * 16 + h]);
-    float tot = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int w = w0; w <= w1; ++w) {
-      const int64_t row = (int64_t)(seq + w) * hpad + hg * 16 + h;
-      const float f = fast_exp2(d.seg_max[row] - big_m) * d.seg_sum[row];
-      tot += f;
-      acc += f * *reinterpret_cast<const f32x4*>(d.seg_out + row * kMlaLatent + 4 * d4);
+  auto row = [&](int w) { return (int64_t)(seq + w) * hpad + h; };
+  float big_m = kNegInf;
+  for (int w = w0 + lane; w <= w1; w += 64) big_m = fmaxf(big_m, d.seg_max[row(w)]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) big_m = fmaxf(big_m, __shfl_xor(big_m, off, 64));
+  float tot = 0.f;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int c = w0; c <= w1; c += 64) {
+    const int n = min(64, w1 - c + 1);
+    float f = 0.f;
+    if (lane < n) f = fast_exp2(d.seg_max[row(c + lane)] - big_m) * d.seg_sum[row(c + lane)];
+    tot += f;
+    constexpr int kU = 8;
+    for (int u = 0; u < n; u += kU) {
+      f32x4 v0[kU], v1[kU];
+      float fw[kU];
+#pragma unroll
+      for (int k = 0; k < kU; ++k) {
+        const int idx = min(u + k, n - 1);
+        fw[k] = u + k < n ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), idx)) : 0.f;
+        const float* src = d.seg_out + row(c + idx) * kMlaLatent + 8 * lane;
+        v0[k] = *reinterpret_cast<const f32x4*>(src);
+        v1[k] = *reinterpret_cast<const f32x4*>(src + 4);
+      }
+#pragma unroll
+      for (int k = 0; k < kU; ++k) {
+        acc0 += fw[k] * v0[k];
+        acc1 += fw[k] * v1[k];
+      }
     }
-    store4(out + (int64_t)h * kMlaLatent + 4 * d4, acc * (1.f / tot));
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+  const float inv = 1.f / tot;
+  store4(out, acc0 * inv);
+  store4(out + 4, acc1 * inv);
 }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream, const LaunchHooks& hooks) {
   if (hooks.before_partition) hooks.before_partition(stream);
-  const size_t lds = (size_t)a.waves_per_wg * kMlaSteps * 64 * sizeof(u32x4);
-  hipLaunchKernelGGL(pa_mla_streamk_kernel, dim3(a.shares * a.chunks), dim3(a.waves_per_wg * 64), lds, stream, a);
+  hipLaunchKernelGGL(pa_mla_streamk_kernel, dim3(a.shares * a.chunks), dim3(64), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (hooks.after_partition) hooks.after_partition(stream);
   if (err != hipSuccess) return err;
   if (hooks.before_reduce) hooks.before_reduce(stream);
-  hipLaunchKernelGGL(pa_mla_reduce_kernel, dim3(a.head_groups, a.d.num_seqs), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(pa_mla_reduce_kernel, dim3(a.d.num_seqs, (a.d.num_heads + 3) / 4), dim3(256), 0, stream, a);
   err = hipGetLastError();
   if (hooks.after_reduce) hooks.after_reduce(stream);
   return err;

@@ -1,0 +1,105 @@
+"""Checks on the built latent-cache (MLA) kernel's gfx950 code, no GPU needed.
+
+* The tile reads are one asm block of ds_read_b128 whose outputs are
+  early-clobber: no read may write a register that a later read of the same
+  block uses as its address, or the returning data would redirect the later
+  reads (the compiler treats an asm block's outputs as written at once).
+* Residency of the persistent grid: each one-wave workgroup uses 36 KiB of
+  LDS and more than 256 registers per lane, so a compute unit holds four of
+  them (one wave per SIMD), the number the launch plan sizes the grid by; no
+  scratch.
+"""
+
+import os
+import re
+import struct
+import subprocess
+import tempfile
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OBJDUMP = "/opt/rocm/llvm/bin/llvm-objdump"
+LDS_PER_CU = 160 * 1024
+REGISTERS_PER_SIMD_LANE = 512
+
+
+@pytest.fixture(scope="module")
+def lib_path():
+    import __graft_entry__
+    b = __graft_entry__._build_module()
+    if not os.path.exists(b.LIB_PATH):
+        b.build()
+    return b.LIB_PATH
+
+
+def gfx950_code_objects(path):
+    with open(path, "rb") as f:
+        data = f.read()
+    base = data.find(b"__CLANG_OFFLOAD_BUNDLE__")
+    while base >= 0:
+        n = struct.unpack_from("<Q", data, base + 24)[0]
+        off = base + 32
+        for _ in range(n):
+            o, size, tlen = struct.unpack_from("<QQQ", data, off)
+            triple = data[off + 24:off + 24 + tlen].decode()
+            off += 24 + tlen
+            if triple.endswith("gfx950"):
+                yield data[base + o:base + o + size]
+        base = data.find(b"__CLANG_OFFLOAD_BUNDLE__", base + 1)
+
+
+def mla_kernel_asm(path):
+    for elf in gfx950_code_objects(path):
+        if b"pa_mla_streamk_kernel" not in elf:
+            continue
+        with tempfile.NamedTemporaryFile(suffix=".co") as f:
+            f.write(elf)
+            f.flush()
+            text = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", f.name], capture_output=True, text=True,
+                                  check=True).stdout
+        m = re.search(r"<_ZN2pa21pa_mla_streamk_kernel[^>]*>:\n(.*?)(?:\n\n|\Z)", text, flags=re.S)
+        assert m, "pa_mla_streamk_kernel not found in the disassembly"
+        return m.group(1)
+    raise AssertionError("no gfx950 code object holds pa_mla_streamk_kernel")
+
+
+@pytest.mark.skipif(not os.path.exists(OBJDUMP), reason="llvm-objdump not installed")
+def test_tile_reads_never_overwrite_their_address(lib_path):
+    asm = mla_kernel_asm(lib_path)
+    groups, cur = [], []
+    for line in asm.splitlines():
+        m = re.search(r"ds_read_b128 v\[(\d+):(\d+)\], v(\d+)", line)
+        if m:
+            cur.append(tuple(int(x) for x in m.groups()))
+        elif cur:
+            groups.append(cur)
+            cur = []
+    if cur:
+        groups.append(cur)
+    tile_groups = [g for g in groups if len(g) >= 16]
+    assert tile_groups, "expected 18-read tile groups"
+    for g in tile_groups:
+        for i, (lo, hi, _) in enumerate(g):
+            later = {a for _, _, a in g[i + 1:]}
+            assert not any(lo <= a <= hi for a in later), f"read into v[{lo}:{hi}] clobbers a later address"
+
+
+def test_persistent_grid_is_resident(lib_path):
+    k = {name: r for name, r in bench.code_object_kernels(lib_path).items() if "pa_mla_streamk_kernel" in name}
+    assert len(k) == 1
+    (res,) = k.values()
+    assert res["scratch"] == 0
+    assert res["lds"] <= 36 * 1024 + 1024
+    waves_per_cu = int(re.search(r"#define PA_MLA_WAVES_PER_CU (\d+)",
+                                 open(os.path.join(ROOT, "decode_attention_paged_07_amd", "csrc",
+                                                   "pa_kernels.h")).read()).group(1))
+    assert waves_per_cu * res["lds"] <= LDS_PER_CU
+    per_simd = math_ceil_div(waves_per_cu, 4)
+    assert per_simd * (res["alloc"] or res["vgpr"]) <= REGISTERS_PER_SIMD_LANE
+
+
+def math_ceil_div(a, b):
+    return -(-a // b)
