@@ -409,8 +409,8 @@ def read_ceiling(dev, nbytes=4 << 30, reps=10):
 
 
 def gather_ceilings(dev, pool_bytes=8 << 30, read_bytes=2 << 30, reps=10):
-    """Markdown table of the library's gather probe: whole tiles of 2, 4 and
-    8 KiB read from an 8 GiB pool in pool order or in a seeded random order
+    """Markdown table of the library's gather probe: whole tiles of 2, 4, 8
+    and 18 KiB (a latent-cache block) read from an 8 GiB pool in pool order or in a seeded random order
     (as a block table scatters them), over waves per CU and tiles in flight."""
     import numpy as np
     import torch
@@ -424,7 +424,7 @@ def gather_ceilings(dev, pool_bytes=8 << 30, read_bytes=2 << 30, reps=10):
     rng = np.random.default_rng(11)
     lines = ["| tile bytes | order | waves/CU | tiles in flight per wave | GB/s |", "|---|---|---|---|---|"]
     best = {}
-    for tile in (2048, 4096, 8192):
+    for tile in (2048, 4096, 8192, 18432):
         n = read_bytes // tile
         for order in ("pool", "random"):
             ids = np.arange(n) if order == "pool" else rng.permutation(pool_bytes // tile)[:n]

@@ -644,8 +644,8 @@ int pa_hbm_read_probe(const void* buf, size_t bytes, int workgroups, unsigned* s
 int pa_hbm_gather_probe(const void* pool, size_t pool_bytes, int tile_bytes, const int32_t* ids, int num_tiles,
                         int depth, int workgroups, unsigned* sink, void* stream) {
   if (!pool || !ids || !sink) return fail(PA_ERR_NULL, "pool, ids and sink must be non-NULL");
-  if (tile_bytes != 1024 && tile_bytes != 2048 && tile_bytes != 4096 && tile_bytes != 8192)
-    return fail(PA_ERR_SHAPE, "tile_bytes %d is not 1024, 2048, 4096 or 8192", tile_bytes);
+  if (tile_bytes != 1024 && tile_bytes != 2048 && tile_bytes != 4096 && tile_bytes != 8192 && tile_bytes != 18432)
+    return fail(PA_ERR_SHAPE, "tile_bytes %d is not 1024, 2048, 4096, 8192 or 18432", tile_bytes);
   if (pool_bytes < (size_t)tile_bytes) return fail(PA_ERR_SHAPE, "pool of %zu bytes holds no tile", pool_bytes);
   if (num_tiles < 1 || num_tiles > (1 << 28))
     return fail(PA_ERR_SHAPE, "num_tiles %d is outside [1, 1<<28]", num_tiles);

@@ -97,6 +97,7 @@ hipError_t launch_gather_probe(const void* pool, uint64_t pool_bytes, int tile_b
     case 2048: launch_gather<2>(pool, pool_tiles, ids, num_tiles, depth, workgroups, sink, stream); break;
     case 4096: launch_gather<4>(pool, pool_tiles, ids, num_tiles, depth, workgroups, sink, stream); break;
     case 8192: launch_gather<8>(pool, pool_tiles, ids, num_tiles, depth, workgroups, sink, stream); break;
+    case 18432: launch_gather<18>(pool, pool_tiles, ids, num_tiles, depth, workgroups, sink, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -210,7 +210,8 @@ int pa_hbm_read_probe(const void* buf, size_t bytes, int workgroups, unsigned* s
  * (block, kv head) K or V tile. Wave w of the grid reads tiles w, w+W, ...
  * (W = 4*workgroups waves of 64 lanes), `depth` tiles in flight before any
  * is consumed. pool: device, 16-B aligned, pool_bytes >= tile_bytes.
- * tile_bytes: 1024, 2048, 4096 or 8192. ids: device int32 [num_tiles];
+ * tile_bytes: 1024, 2048, 4096, 8192 or 18432 (one 16-token block of the
+ * latent cache). ids: device int32 [num_tiles];
  * entries outside the pool are clamped into it; num_tiles in [1, 1<<28].
  * depth: 1 or 2.
  * workgroups in [1, 1<<20]; sink as for pa_hbm_read_probe.
