@@ -1,6 +1,6 @@
 """Checks on the built latent-cache (MLA) kernel's gfx950 code, no GPU needed.
 
-* The tile reads are one asm block of ds_read_b128 whose outputs are
+* The tile reads (ds_read_b128) are an asm block whose outputs are
   early-clobber: no read may write a register that a later read of the same
   block uses as its address, or the returning data would redirect the later
   reads (the compiler treats an asm block's outputs as written at once).
@@ -66,12 +66,11 @@ def mla_kernel_asm(path):
     raise AssertionError("no gfx950 code object holds pa_mla_streamk_kernel")
 
 
-@pytest.mark.skipif(not os.path.exists(OBJDUMP), reason="llvm-objdump not installed")
-def test_tile_reads_never_overwrite_their_address(lib_path):
-    asm = mla_kernel_asm(lib_path)
+def read_groups(asm, op):
+    """Runs of consecutive `op` reads: (first dest reg, last dest reg, address reg) each."""
     groups, cur = [], []
     for line in asm.splitlines():
-        m = re.search(r"ds_read_b128 v\[(\d+):(\d+)\], v(\d+)", line)
+        m = re.search(op + r" v\[(\d+):(\d+)\], v(\d+)", line)
         if m:
             cur.append(tuple(int(x) for x in m.groups()))
         elif cur:
@@ -79,12 +78,18 @@ def test_tile_reads_never_overwrite_their_address(lib_path):
             cur = []
     if cur:
         groups.append(cur)
-    tile_groups = [g for g in groups if len(g) >= 16]
-    assert tile_groups, "expected 18-read tile groups"
-    for g in tile_groups:
+    return groups
+
+
+@pytest.mark.skipif(not os.path.exists(OBJDUMP), reason="llvm-objdump not installed")
+@pytest.mark.parametrize("op", ["ds_read_b128"])
+def test_tile_reads_never_overwrite_their_address(lib_path, op):
+    groups = [g for g in read_groups(mla_kernel_asm(lib_path), op) if len(g) >= 16]
+    assert groups, f"expected asm groups of 16 or more {op}"
+    for g in groups:
         for i, (lo, hi, _) in enumerate(g):
             later = {a for _, _, a in g[i + 1:]}
-            assert not any(lo <= a <= hi for a in later), f"read into v[{lo}:{hi}] clobbers a later address"
+            assert not any(lo <= a <= hi for a in later), f"{op} into v[{lo}:{hi}] clobbers a later address"
 
 
 def test_persistent_grid_is_resident(lib_path):
