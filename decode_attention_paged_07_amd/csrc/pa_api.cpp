@@ -458,6 +458,15 @@ MlaPlan make_mla_plan(int num_seqs, int num_heads) {
   return p;
 }
 
+// MLA stream-K workgroups (one wave each) per compute unit with a single
+// 16-head group. With more groups the kernel is compute-bound and fills all
+// four SIMDs (PA_MLA_WAVES_PER_CU); with one group it is bound by its reads,
+// which two waves per compute unit sustain as well as four, with half the
+// shares and so half the partial outputs the merge reads.
+#ifndef PA_MLA_WAVES_PER_CU_ONE_GROUP
+#define PA_MLA_WAVES_PER_CU_ONE_GROUP 2
+#endif
+
 int check_mla_plan_args(int num_seqs, int num_heads) {
   if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
   if (num_seqs > PA_MAX_SEQS) return fail(PA_ERR_SHAPE, "num_seqs %d exceeds %d", num_seqs, PA_MAX_SEQS);
@@ -786,9 +795,9 @@ int pa_mla_decode(void* out, const void* query, const void* latent_cache, int nu
   a.head_groups = plan.head_groups;
   a.waves_per_wg = plan.waves_per_wg;
   a.chunks = plan.chunks;
-  // Shares: PA_MLA_WAVES_PER_CU waves per compute unit in all, a multiple of
-  // 8 so that the chunks of a share land on one XCD.
-  const int waves = device_cus() * PA_MLA_WAVES_PER_CU;
+  // Shares: the waves per compute unit of the knobs in all, a multiple of 8
+  // so that the head groups of a share land on one XCD.
+  const int waves = device_cus() * (plan.head_groups == 1 ? PA_MLA_WAVES_PER_CU_ONE_GROUP : PA_MLA_WAVES_PER_CU);
   int shares = waves / (plan.waves_per_wg * plan.chunks);
   shares = std::max(8, shares / 8 * 8);
   a.shares = std::min(shares, plan.max_shares);

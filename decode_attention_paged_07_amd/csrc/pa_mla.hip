@@ -389,19 +389,32 @@ __global__ void __launch_bounds__(256) pa_mla_reduce_kernel(const MlaArgs a) {
   const int lane = threadIdx.x & 63;
   if (h >= d.num_heads) return;
   const int64_t hpad = (int64_t)a.head_groups * 16;
-  const int L = clamp_len(d.seq_lens[seq], d.max_seq_len);
+  // The length and the segment bounds are read together (the bounds are
+  // only used when the length is non-zero).
+  const int len = d.seq_lens[seq];
+  const int m0 = d.seg_meta[2 * seq], m1 = d.seg_meta[2 * seq + 1];
+  const int L = clamp_len(len, d.max_seq_len);
   __bf16* out = reinterpret_cast<__bf16*>(d.out) + ((int64_t)seq * d.num_heads + h) * kMlaLatent + 8 * lane;
   if (L == 0) {
     store4(out, f32x4{0.f, 0.f, 0.f, 0.f});
     store4(out + 4, f32x4{0.f, 0.f, 0.f, 0.f});
     return;
   }
-  const int w0 = max(0, d.seg_meta[2 * seq]);
-  const int w1 = min(a.shares - 1, d.seg_meta[2 * seq + 1]);
+  const int w0 = max(0, m0);
+  const int w1 = min(a.shares - 1, m1);
   if (w0 >= w1) return;   // one segment: written directly
   auto row = [&](int w) { return (int64_t)(seq + w) * hpad + h; };
-  float big_m = kNegInf;
-  for (int w = w0 + lane; w <= w1; w += 64) big_m = fmaxf(big_m, d.seg_max[row(w)]);
+  // Up to 64 segments: lane i keeps segment w0 + i's max and sum from one
+  // read. More: the maxima are gathered first, the sums read per chunk.
+  const bool one_chunk = w1 - w0 < 64;
+  float sm = kNegInf, ss = 0.f;
+  if (one_chunk && w0 + lane <= w1) {
+    sm = d.seg_max[row(w0 + lane)];
+    ss = d.seg_sum[row(w0 + lane)];
+  }
+  float big_m = sm;
+  if (!one_chunk)
+    for (int w = w0 + lane; w <= w1; w += 64) big_m = fmaxf(big_m, d.seg_max[row(w)]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) big_m = fmaxf(big_m, __shfl_xor(big_m, off, 64));
   float tot = 0.f;
@@ -409,7 +422,12 @@ __global__ void __launch_bounds__(256) pa_mla_reduce_kernel(const MlaArgs a) {
   for (int c = w0; c <= w1; c += 64) {
     const int n = min(64, w1 - c + 1);
     float f = 0.f;
-    if (lane < n) f = fast_exp2(d.seg_max[row(c + lane)] - big_m) * d.seg_sum[row(c + lane)];
+    if (lane < n) {
+      if (one_chunk)
+        f = fast_exp2(sm - big_m) * ss;
+      else
+        f = fast_exp2(d.seg_max[row(c + lane)] - big_m) * d.seg_sum[row(c + lane)];
+    }
     tot += f;
     constexpr int kU = 8;
     for (int u = 0; u < n; u += kU) {

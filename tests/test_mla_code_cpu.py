@@ -98,9 +98,9 @@ def test_persistent_grid_is_resident(lib_path):
     (res,) = k.values()
     assert res["scratch"] == 0
     assert res["lds"] <= 36 * 1024 + 1024
-    waves_per_cu = int(re.search(r"#define PA_MLA_WAVES_PER_CU (\d+)",
-                                 open(os.path.join(ROOT, "decode_attention_paged_07_amd", "csrc",
-                                                   "pa_kernels.h")).read()).group(1))
+    csrc = os.path.join(ROOT, "decode_attention_paged_07_amd", "csrc")
+    knobs = open(os.path.join(csrc, "pa_kernels.h")).read() + open(os.path.join(csrc, "pa_api.cpp")).read()
+    waves_per_cu = max(int(x) for x in re.findall(r"#define PA_MLA_WAVES_PER_CU\w* (\d+)", knobs))
     assert waves_per_cu * res["lds"] <= LDS_PER_CU
     per_simd = math_ceil_div(waves_per_cu, 4)
     assert per_simd * (res["alloc"] or res["vgpr"]) <= REGISTERS_PER_SIMD_LANE
