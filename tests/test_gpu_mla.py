@@ -137,3 +137,25 @@ def test_captured_call_replays_like_eager():
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
     _run.compare(got, oracle_mla(case), "bf16", what="graph mla")
+
+
+def test_shared_physical_blocks():
+    # Later sequences map their first 20 blocks to sequence 0's (read-only
+    # sharing of a prompt's blocks); each result is still per sequence.
+    cfg = workloads.MLA.with_(num_seqs=4, pool_blocks=200)
+    # No NaN poison here: a shorter sequence's partial last block can be a
+    # block that a longer one uses in full.
+    case = workloads.make_mla_case(cfg, seed=23, device=DEV, seq_lens=[700, 500, 900, 100],
+                                   share_prefix_blocks=20)
+    tbl = case.block_tables.cpu().numpy()
+    assert (tbl[1, :20] == tbl[0, :20]).all() and (tbl[2, :20] == tbl[0, :20]).all()
+    check(case, what="shared blocks")
+
+
+@pytest.mark.parametrize("scale", [0.0, 1.0])
+def test_scale_edge_values(scale):
+    # scale 0: every token weighs the same (the mean of the c_kv rows); scale 1
+    # (about 14x the workload's): a sharply peaked softmax.
+    case = small([37, 400, 1], seed=29)
+    case.scale = scale
+    check(case, what=f"scale {scale}")

@@ -349,14 +349,18 @@ class MlaCase:
 
 
 def make_mla_case(cfg: DecodeConfig, seed: int | None = None, device="cpu", *, seq_lens=None,
-                  max_seq_len=None, poison: bool = False, num_heads: int | None = None) -> MlaCase:
+                  max_seq_len=None, poison: bool = False, num_heads: int | None = None,
+                  share_prefix_blocks: int = 0) -> MlaCase:
     """One MLA workload instance; poison=True writes NaN into every pool slot
-    no valid token uses and points unused table entries at a NaN block."""
+    no valid token uses and points unused table entries at a NaN block.
+    share_prefix_blocks > 0 maps the first blocks of every long enough
+    sequence to sequence 0's physical blocks (read-only sharing)."""
     seed = cfg.seed if seed is None else seed
     if num_heads is not None:
         cfg = cfg.with_(num_heads=num_heads)
     width = MLA_LATENT + MLA_ROPE
-    meta = make_metadata(cfg, seed, seq_lens=seq_lens, max_seq_len=max_seq_len)
+    meta = make_metadata(cfg, seed, seq_lens=seq_lens, max_seq_len=max_seq_len,
+                         share_prefix_blocks=share_prefix_blocks)
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
     query = _randn((cfg.num_seqs, cfg.num_heads, width), gen, device).to(torch.bfloat16)
