@@ -433,9 +433,10 @@ SharedPlan make_shared_plan(int num_seqs, int num_heads, int num_kv_heads, int h
 
 // ---- latent-cache (MLA) decode --------------------------------------------------
 
-// Stream-K plan of the MLA kernel: one single-wave workgroup per 16-head
-// group and share (one wave per SIMD: each needs more than 256 registers;
-// 36 KiB of LDS per wave for two tile buffers).
+// Stream-K plan of the MLA kernel: one wave per 16-head group and share (one
+// wave per SIMD: each needs more than 256 registers), up to four groups in a
+// workgroup that shares one pair of 18 KiB LDS tile buffers, more groups in
+// `chunks` workgroups per share.
 struct MlaPlan {
   int head_groups, waves_per_wg, chunks, max_shares;
   size_t off[4];
@@ -445,7 +446,7 @@ struct MlaPlan {
 MlaPlan make_mla_plan(int num_seqs, int num_heads) {
   MlaPlan p{};
   p.head_groups = (num_heads + 15) / 16;
-  p.waves_per_wg = 1;
+  p.waves_per_wg = std::min(p.head_groups, 4);
   p.chunks = (p.head_groups + p.waves_per_wg - 1) / p.waves_per_wg;
   p.max_shares = PA_MLA_MAX_WAVES / (p.waves_per_wg * p.chunks);
   const size_t hpad = (size_t)p.head_groups * 16;

@@ -113,11 +113,12 @@ struct MlaWave {
     for (int dt = 0; dt < kMlaDt; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Copy one 18 KiB tile into buf: instruction s moves bytes
-  // [1024 s, 1024 s + 1024) of the tile, 16 per lane, to buf + 64 s.
+  // Copy slots [S0, S1) of one 18 KiB tile into buf: instruction s moves
+  // bytes [1024 s, 1024 s + 1024) of the tile, 16 per lane, to buf + 64 s.
+  template <int S0, int S1>
   __device__ void stage(const char* tile, u32x4* buf) const {
 #pragma unroll
-    for (int s = 0; s < kMlaSteps; ++s)
+    for (int s = S0; s < S1; ++s)
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(tile + s * 1024 + lane * 16),
           (__attribute__((address_space(3))) void*)(buf + s * 64), 16, 0, 2 /* nt */);
@@ -232,12 +233,18 @@ struct MlaWave {
   }
 };
 
-// One wave's share: tiles [u0, u0 + units) in (sequence, block) order, as one
-// block pipeline across the sequences it spans. Two LDS tile buffers: while
-// one block is computed, the next block's copy (also across a sequence
-// boundary) is in flight into the other.
+// A workgroup's share: tiles [u0, u0 + units) in (sequence, block) order, as
+// one block pipeline across the sequences it spans. Its W waves (one per
+// 16-head group) share two LDS tile buffers: while one block is computed,
+// the next block's copy (also across a sequence boundary) is in flight into
+// the other. Wave w copies slots [18 w / W, 18 (w + 1) / W) of each tile.
+// With W > 1 each block starts with a barrier: each wave first waits for its
+// own copies, so after it the tile is complete in LDS, and every wave is
+// past the previous block, whose buffer the next copy overwrites.
+template <int W, int WAVE>
 __device__ __forceinline__ void mla_share(const MlaArgs& a, int share, int hg, int seq, int blk, int64_t units,
                                           u32x4* __restrict__ buf0, u32x4* __restrict__ buf1) {
+  constexpr int kS0 = kMlaSteps * WAVE / W, kS1 = kMlaSteps * (WAVE + 1) / W;
   const DecodeArgs& d = a.d;
   const int S = d.num_seqs;
   const unsigned top = (unsigned)(d.num_blocks - 1);
@@ -288,7 +295,7 @@ __device__ __forceinline__ void mla_share(const MlaArgs& a, int share, int hg, i
   auto stage_block = [&](unsigned phys, u32x4* buf) {
     phys = phys < top ? phys : top;
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // earlier LDS reads of buf are complete
-    wv.stage(base + (int64_t)phys * kMlaBlockBytes, buf);
+    wv.template stage<kS0, kS1>(base + (int64_t)phys * kMlaBlockBytes, buf);
   };
   auto stage_cur = [&](int g, u32x4* buf) {
     if (g - chunk >= 64) {
@@ -304,14 +311,21 @@ __device__ __forceinline__ void mla_share(const MlaArgs& a, int share, int hg, i
   auto step = [&](u32x4* bc, u32x4* bn) -> bool {
     const bool more = g + 1 < cur.b1;
     const int nvalid = min(kMlaBS, cur.L - g * kMlaBS);
+    // The tile reads wait for all but the successor's copy (one wave), or
+    // not at all (several waves: the barrier has).
+    constexpr int kPending = W == 1 ? kS1 - kS0 : 63;
+    if constexpr (W > 1) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of bc
+      __builtin_amdgcn_s_barrier();
+    }
     if (more) {
       stage_cur(g + 1, bn);
-      wv.template consume<kMlaSteps>(bc, nvalid);   // all but the successor's copy complete
+      wv.template consume<kPending>(bc, nvalid);
     } else if (has_nx) {
       stage_block((unsigned)__builtin_amdgcn_readlane(tbl_n, 0), bn);
-      wv.template consume<kMlaSteps>(bc, nvalid);
+      wv.template consume<kPending>(bc, nvalid);
     } else {
-      wv.template consume<0>(bc, nvalid);
+      wv.template consume<W == 1 ? 0 : 63>(bc, nvalid);
     }
     if (more) {
       ++g;
@@ -351,19 +365,22 @@ __device__ __forceinline__ void mla_share(const MlaArgs& a, int share, int hg, i
   }
 }
 
-// Grid: shares * head_groups workgroups of one wave (36 KiB of LDS each, so
-// four fit a compute unit). Workgroup i takes share 8*(i / (8*head_groups)) +
-// i % 8 and head group (i / 8) % head_groups, so the head groups of a share
-// are 8 workgroup ids apart: the same XCD under the round-robin dispatch of
-// workgroups to the eight XCDs.
-__global__ void __launch_bounds__(64) pa_mla_streamk_kernel(const MlaArgs a) {
+// Grid: shares * chunks workgroups of W waves (36 KiB of LDS each). Wave w of
+// workgroup i takes share 8*(i / (8*chunks)) + i % 8 and head group
+// ((i / 8) % chunks) * W + w, so the chunks of a share are 8 workgroup ids
+// apart: the same XCD under the round-robin dispatch of workgroups to the
+// eight XCDs. A wave past the last head group runs with no active lane (it
+// still copies its slots and meets the barriers).
+template <int W>
+__global__ void __launch_bounds__(64 * W) pa_mla_streamk_kernel(const MlaArgs a) {
   __shared__ u32x4 tiles0[kMlaTileVec], tiles1[kMlaTileVec];   // two 18 KiB tile buffers
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = blockIdx.x;
   const int chunks = a.chunks;
   const int share = 8 * (i / (8 * chunks)) + i % 8;
-  const int hg = (i / 8) % chunks;
-  if (hg >= a.head_groups || share >= a.shares) return;
+  const int hg = ((i / 8) % chunks) * W + wave;
+  if (share >= a.shares) return;   // uniform over the workgroup
 
   int bsum = 0;
   const int T = count_blocks<kMlaBS>(a.d, lane, bsum);
@@ -374,7 +391,13 @@ __global__ void __launch_bounds__(64) pa_mla_streamk_kernel(const MlaArgs a) {
   if (u0 >= u1) return;
   int seq = 0, blk = 0;
   locate_block<kMlaBS>(a.d, lane, (int)u0, bsum, seq, blk);
-  mla_share(a, share, hg, seq, blk, u1 - u0, tiles0, tiles1);
+  // Each wave runs its own instantiation (its copy slots); all meet the same barriers.
+  switch (wave) {
+    case 0: mla_share<W, 0>(a, share, hg, seq, blk, u1 - u0, tiles0, tiles1); break;
+    case 1: if constexpr (W > 1) mla_share<W, 1 % W>(a, share, hg, seq, blk, u1 - u0, tiles0, tiles1); break;
+    case 2: if constexpr (W > 2) mla_share<W, 2 % W>(a, share, hg, seq, blk, u1 - u0, tiles0, tiles1); break;
+    default: if constexpr (W > 3) mla_share<W, 3 % W>(a, share, hg, seq, blk, u1 - u0, tiles0, tiles1); break;
+  }
 }
 
 // Merge of the segments of cut sequences, zero rows of empty ones: grid
@@ -457,7 +480,14 @@ __global__ void __launch_bounds__(256) pa_mla_reduce_kernel(const MlaArgs a) {
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream, const LaunchHooks& hooks) {
   if (hooks.before_partition) hooks.before_partition(stream);
-  hipLaunchKernelGGL(pa_mla_streamk_kernel, dim3(a.shares * a.chunks), dim3(64), 0, stream, a);
+  const dim3 grid(a.shares * a.chunks);
+  switch (a.waves_per_wg) {
+    case 1: hipLaunchKernelGGL(pa_mla_streamk_kernel<1>, grid, dim3(64), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(pa_mla_streamk_kernel<2>, grid, dim3(128), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(pa_mla_streamk_kernel<3>, grid, dim3(192), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(pa_mla_streamk_kernel<4>, grid, dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t err = hipGetLastError();
   if (hooks.after_partition) hooks.after_partition(stream);
   if (err != hipSuccess) return err;
