@@ -159,3 +159,18 @@ def test_scale_edge_values(scale):
     case = small([37, 400, 1], seed=29)
     case.scale = scale
     check(case, what=f"scale {scale}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_configurations(seed):
+    # Seeded random head counts (1..128: one to eight head groups, so one to
+    # four waves per workgroup and one or two workgroups per share), batch
+    # sizes and lengths (zero-length sequences included), NaN-poisoned tails.
+    rng = np.random.default_rng(1000 + seed)
+    heads = int(rng.integers(1, 129))
+    n = int(rng.integers(1, 41))
+    lens = rng.integers(0, 3001, n)
+    lens[rng.random(n) < 0.1] = 0
+    lens[0] = max(int(lens[0]), 1)
+    case = small(lens.tolist(), heads=heads, seed=seed)
+    check(case, what=f"random seed {seed}: H={heads} S={n}")
