@@ -25,13 +25,13 @@
 //     product. Products with 1 and 0 and sums with zeros are exact, so the
 //     bf16 values come back unchanged. The latent tile is read from HBM once
 //     and serves as both K and V.
-// Tiles go from HBM straight to LDS (global_load_lds_dwordx4), two buffers
-// per wave, so the next block's 18 KiB are in flight without holding
-// registers; each lane reads back only the slots its own loads wrote, so no
-// barrier is needed.
-// With more than 16 heads every 16-head group has its own wave on the same
-// share of blocks, in workgroups dispatched to the same XCD, so a tile's
-// reads after the first hit in L2.
+// Tiles go from HBM straight to LDS (global_load_lds_dwordx4) into two
+// buffers per workgroup, so the next block's 18 KiB are in flight without
+// holding registers. With 16 heads or fewer a workgroup is one wave, which
+// reads back only what its own copies wrote: no barrier. With more heads, up
+// to four 16-head groups are waves of one workgroup that share the buffers
+// (each copies part of every tile; one barrier per block), and more groups
+// take several workgroups per share, dispatched to the same XCD.
 //
 // Scheduling is stream-K over (sequence, block) tiles, as for the decode
 // kernels: every share has the same number of blocks; a sequence cut by a
@@ -68,10 +68,9 @@ __device__ __forceinline__ s16x4 pack_bf16x4_pairs(f32x4 v) {
 }
 
 // One wave's attention state for 16 query heads. The latent tiles are staged
-// in LDS: the tile's 18 KiB are copied by 18 direct global->LDS loads
-// (global_load_lds_dwordx4) in the cache layout, so slot s*64 + lane holds
-// chunk 4s + q4 of token (lane & 15), the A operand of S step s for this
-// lane. Each lane reads only the slots it loaded: no barrier.
+// in LDS by direct global->LDS loads (global_load_lds_dwordx4) in the cache
+// layout, so slot s*64 + lane holds chunk 4s + q4 of token (lane & 15), the A
+// operand of S step s for this lane.
 struct MlaWave {
   bf16x8 q[kMlaSteps];
   f32x4 o[kMlaDt];
