@@ -763,6 +763,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="with --config gqa: skip the fp8-cache workload measured beside it")
     ap.add_argument("--summarise-sq", metavar="PMC_DIR",
                     help="write the instruction-mix summary from a --pmc run of SQ_COUNTERS over --config")
     ap.add_argument("--summarise-shared", metavar="STATS",
@@ -821,14 +823,43 @@ def main():
         print(json.dumps(bench_mla(args.config, args, dev)), flush=True)
         return
     cfg = {**workloads.CONFIGS, **workloads.EXTRA_CONFIGS}[args.config]
-    print(f"[bench] building {args.config} inputs", file=sys.stderr, flush=True)
+    if cfg.prefix_groups or args.append:
+        print(f"[bench] building {args.config} inputs", file=sys.stderr, flush=True)
+        case = workloads.make_case(cfg, device=dev)
+        if cfg.prefix_groups:
+            print(json.dumps(bench_shared(case, args.steps, args.warmup)), flush=True)
+        else:
+            print(json.dumps(bench_append(case, args.append, args.steps, args.warmup)), flush=True)
+        return
+    rec = bench_decode(args.config, args, dev, ceiling=not args.no_ceiling)
+    if args.config == "gqa" and args.split == 0 and not args.no_secondary:
+        # The second target workload (the fp8 e4m3 cache), measured in the same
+        # run and reported beside the headline figure.
+        torch.cuda.empty_cache()
+        sec = bench_decode("fp8", args, dev, ceiling=False)
+        rec["secondary"] = {k: sec[k] for k in ("ms_per_step", "value", "unit", "dtype", "config",
+                                                 "effective_kv_gbps", "frac_of_peak_hbm", "roofline",
+                                                 "reduce_avg_ms", "kernel_sha", "cpu_baseline")
+                            if k in sec}
+        rec["secondary"]["target_frac_of_peak_hbm"] = 0.60
+        if "parity_on_sample" in sec:
+            rec["secondary"]["parity_on_sample"] = sec["parity_on_sample"]
+    print(json.dumps(rec), flush=True)
+
+
+def bench_decode(name, args, dev, ceiling=True):
+    """One decode workload: exactly args.steps timed steps after args.warmup,
+    then the same loop with the library's kernel events for the dominant
+    kernel's launch time, the read ceiling (optional) and the host oracle
+    baseline. Returns the JSON record."""
+    import torch
+
+    import decode_attention_paged_07_amd as pa
+    import workloads
+
+    cfg = {**workloads.CONFIGS, **workloads.EXTRA_CONFIGS}[name]
+    print(f"[bench] building {name} inputs", file=sys.stderr, flush=True)
     case = workloads.make_case(cfg, device=dev)
-    if cfg.prefix_groups:
-        print(json.dumps(bench_shared(case, args.steps, args.warmup)), flush=True)
-        return
-    if args.append:
-        print(json.dumps(bench_append(case, args.append, args.steps, args.warmup)), flush=True)
-        return
     out = torch.empty_like(case.query)
     split_tokens, num_splits, _ = pa.pa_decode_plan(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads,
                                                     cfg.head_size, case.max_seq_len, args.split)
@@ -853,7 +884,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] {args.steps} steps, {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+    print(f"[bench] {name}: {args.steps} steps, {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
 
     # The same loop again with the library's per-kernel HIP events (recorded on
     # the stream the kernels run on) for the dominant kernel's launch time.
@@ -893,7 +924,7 @@ def main():
         "dtype": dtype,
         "data": "synthetic (seeded N(0,1) values, seeded lengths and block tables)",
         "config": {
-            "workload": WORKLOAD_TEXT[args.config],
+            "workload": WORKLOAD_TEXT[name],
             "num_seqs": cfg.num_seqs, "num_heads": cfg.num_heads, "num_kv_heads": cfg.num_kv_heads,
             "head_size": cfg.head_size, "block_size": cfg.block_size, "pool_blocks": cfg.pool_blocks,
             "tokens": int(case.meta.seq_lens.astype("int64").sum()), "max_seq_len": case.max_seq_len,
@@ -910,7 +941,7 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": traffic_from_profiles(kernel_name, args.config),
+            "traffic": traffic_from_profiles(kernel_name, name),
             "avg_launch_ms": round(part_avg, 5),
             "algorithmic_bytes_per_launch": nbytes,
         },
@@ -919,12 +950,12 @@ def main():
         "kernel_sha": kernel_sha(kernel_name),
         "cpu_baseline": None,
     }
-    if not args.no_ceiling:
+    if ceiling:
         ceil = read_ceiling(dev)
         ceil["decode_frac_of_ceiling"] = round(achieved / ceil["gbps"], 4)
         rec["read_ceiling"] = ceil
     if not args.no_cpu_baseline:
-        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        print(f"[bench] {name}: timing the oracle on the host", file=sys.stderr, flush=True)
         step()
         torch.cuda.synchronize()
         from tests import _run
@@ -933,7 +964,6 @@ def main():
         for seqs, ref in done:
             extra = None
             if cfg.compute == "fp8":            # rounding-boundary allowance of the fp8 arithmetic
-                import workloads
                 from tests import _fp8tol
                 extra = _fp8tol.row_bounds(workloads.host_arrays(case, seqs))
             worst = tuple(max(a, b) for a, b in
@@ -941,7 +971,8 @@ def main():
         base["gpu_speedup"] = round(seqs_per_s / base["value"], 1)
         rec["cpu_baseline"] = base
         rec["parity_on_sample"] = {"max_abs": float(f"{worst[0]:.3e}"), "max_rel": float(f"{worst[1]:.3e}")}
-    print(json.dumps(rec), flush=True)
+    del case, out
+    return rec
 
 
 if __name__ == "__main__":

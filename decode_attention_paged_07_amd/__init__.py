@@ -61,6 +61,9 @@ PA_MLA_LATENT_DIM = 512
 PA_MLA_ROPE_DIM = 64
 PA_MLA_MAX_HEADS = 128
 
+# PA_DECODE_LIB names another build of the library to load instead of the
+# in-tree one (e.g. a host-sanitizer build); it must exist like the default.
+LIB_PATH = os.environ.get("PA_DECODE_LIB") or LIB_PATH
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
@@ -414,26 +417,53 @@ def kv_cache_shapes(num_blocks, num_kv_heads, head_size, q_dtype=torch.bfloat16,
             (num_blocks, num_kv_heads, head_size, block_size))
 
 
+def _capturing() -> bool:
+    """Whether the current stream is capturing a graph."""
+    return torch.cuda.is_current_stream_capturing()
+
+
 def _device_scalar(v, device):
+    """A one-element float32 device tensor holding v. A Python float becomes a
+    device tensor filled by a kernel (no host-to-device copy, so it can be
+    captured); eager calls cache it per (device, value). Under graph capture it
+    is made afresh and not cached: the fill runs only when the graph replays."""
     if isinstance(v, torch.Tensor):
         if v.dtype != torch.float32 or v.numel() != 1 or v.device != device:
             raise ValueError("k_scale/v_scale tensors must be one float32 element on the query's device")
         return v
+    if _capturing():
+        return torch.full((1,), float(v), dtype=torch.float32, device=device)
     key = (device, float(v))
     t = _scalars.get(key)
     if t is None:
-        t = torch.tensor([float(v)], dtype=torch.float32, device=device)
+        t = torch.full((1,), float(v), dtype=torch.float32, device=device)
         _scalars[key] = t
     return t
 
 
+_retired: list = []   # replaced workspaces: kept alive, kernels still queued on their stream may write them
+
+
 def _workspace_for(device, nbytes):
+    """A workspace of at least nbytes for a call on the current stream.
+
+    Eager calls share one cached buffer per (device, stream), so calls on
+    different streams never share one; a buffer outgrown by a larger call is
+    kept alive, since kernels still queued may write it. Under graph capture the
+    call gets a buffer of its own from torch's allocator (the graph's memory
+    pool, like any temporary of a captured op) that is never cached: the graph's
+    replays use it alone, and later eager calls cannot replace it."""
     if nbytes == 0:
         return None
-    t = _workspaces.get(device)
+    if _capturing():
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    t = _workspaces.get(key)
     if t is None or t.numel() < nbytes:
+        if t is not None:
+            _retired.append(t)
         t = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        _workspaces[device] = t
+        _workspaces[key] = t
     return t
 
 
@@ -507,12 +537,15 @@ def paged_attention_decode(out, query, key_cache, value_cache, num_kv_heads, sca
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = _lib.pa_paged_attention_decode_split(
-        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), num_seqs,
-        num_heads, num_kv_heads, head_size, num_blocks, float(scale), block_tables.data_ptr(),
-        block_tables.shape[1], seq_lens.data_ptr(), block_size, int(max_seq_len), slopes_ptr, qd,
-        kvd, ks.data_ptr() if ks is not None else None, vs.data_ptr() if vs is not None else None,
-        ws_ptr, ws_bytes, stream, int(split_tokens))
+    args = (out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), num_seqs,
+            num_heads, num_kv_heads, head_size, num_blocks, float(scale), block_tables.data_ptr(),
+            block_tables.shape[1], seq_lens.data_ptr(), block_size, int(max_seq_len), slopes_ptr, qd,
+            kvd, ks.data_ptr() if ks is not None else None, vs.data_ptr() if vs is not None else None,
+            ws_ptr, ws_bytes, stream)
+    if split_tokens:
+        rc = _lib.pa_paged_attention_decode_split(*args, int(split_tokens))
+    else:
+        rc = _lib.pa_paged_attention_decode(*args)
     _raise_for(rc, "paged_attention_decode")
 
 

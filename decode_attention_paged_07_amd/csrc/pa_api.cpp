@@ -78,7 +78,8 @@ int check_dtypes(int q_dtype, int kv_cache_dtype) {
 // wave gets an equal share of all (block, kv head) tiles. Workspace carving:
 //   split:    tmp_out [S][H][P][D] | max_logits [S][H][P] | exp_sums [S][H][P]
 //   stream-K: seg_out [slots][G][D] | seg_max [slots][G] | seg_sum [slots][G] | seg_meta [S*Hkv][2]
-// with slots = S*Hkv + PA_SK_MAX_WAVES; each array 256-byte aligned.
+// with slots = S*Hkv + sk_waves (the persistent grid's waves); each array
+// 256-byte aligned.
 struct Plan {
   bool streamk;
   int split_tokens;
@@ -88,7 +89,7 @@ struct Plan {
 };
 
 Plan make_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_seq_len,
-               int split_tokens) {
+               int split_tokens, int sk_waves) {
   Plan p{};
   if (split_tokens > 0) {
     p.split_tokens = split_tokens;
@@ -105,7 +106,7 @@ Plan make_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size, int
   p.streamk = true;
   const size_t group = (size_t)(num_heads / num_kv_heads);
   const size_t pairs = (size_t)num_seqs * num_kv_heads;
-  const size_t slots = pairs + PA_SK_MAX_WAVES;
+  const size_t slots = pairs + (size_t)sk_waves;
   p.off[0] = 0;
   p.off[1] = round_up(slots * group * head_size * sizeof(float), 256);
   p.off[2] = p.off[1] + round_up(slots * group * sizeof(float), 256);
@@ -125,6 +126,32 @@ int device_cus() {
     cached[dev].store(n, std::memory_order_relaxed);
   }
   return n;
+}
+
+// Stream-K waves of the persistent grid for a kernel kind and block size.
+// Waves per compute unit, measured per cache type and block size: each wave
+// keeps one block's loads in flight, and throughput peaks at a total of about
+// 8-12 MiB in flight (bf16, 16-token blocks: one wave per SIMD; fp8 needs
+// more waves to overlap its conversions; 32-token blocks carry twice the bytes
+// per wave). A fraction leaves some compute units without a workgroup, which
+// measured faster than spreading them.
+int streamk_waves(int kind, int block_size) {
+  const bool b32 = block_size == 32;
+  const double per_cu = kind == pa::KIND_FP8MX ? (b32 ? PA_SK_WAVES_PER_CU_BS32_FP8MX : PA_SK_WAVES_PER_CU_FP8MX)
+                        : kind == pa::KIND_FP8 ? (b32 ? PA_SK_WAVES_PER_CU_BS32_FP8 : PA_SK_WAVES_PER_CU_FP8)
+                        : kind == pa::KIND_F32 ? (b32 ? PA_SK_WAVES_PER_CU_BS32_F32 : PA_SK_WAVES_PER_CU_F32)
+                                               : (b32 ? PA_SK_WAVES_PER_CU_BS32_BF16 : PA_SK_WAVES_PER_CU_BF16);
+  const int waves = std::min(PA_SK_MAX_WAVES, (int)(device_cus() * per_cu));
+  return std::max(1, waves / PA_WAVES) * PA_WAVES;
+}
+
+// The most stream-K waves any kind or block size launches on this device: the
+// slot count pa_decode_plan and pa_workspace_bytes size the workspace for.
+int streamk_waves_bound() {
+  int w = 0;
+  for (int kind : {pa::KIND_F32, pa::KIND_BF16, pa::KIND_FP8, pa::KIND_FP8MX})
+    for (int bs : {16, 32}) w = std::max(w, streamk_waves(kind, bs));
+  return w;
 }
 
 int check_plan_args(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_seq_len,
@@ -297,14 +324,14 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
                              max_seq_len, alibi_slopes, q_dtype, kv_cache_dtype, k_scale, v_scale, split_tokens);
   if (rc) return rc;
   if (num_seqs == 0) return ok();
-  const Plan plan = make_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, split_tokens);
-  if ((rc = check_workspace(workspace, workspace_bytes, plan.bytes))) return rc;
-
   pa::DecodeArgs a;
   const int kind = fill_decode_args(a, out, query, key_cache, value_cache, num_seqs, num_heads, num_kv_heads,
                                     head_size, num_blocks, scale, block_tables, max_blocks_per_seq, seq_lens,
                                     block_size, max_seq_len, alibi_slopes, q_dtype, kv_cache_dtype, k_scale,
                                     v_scale);
+  const int sk_waves = split_tokens == 0 ? streamk_waves(kind, block_size) : 0;
+  const Plan plan = make_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, split_tokens, sk_waves);
+  if ((rc = check_workspace(workspace, workspace_bytes, plan.bytes))) return rc;
   char* ws = static_cast<char*>(workspace);
   if (plan.bytes && !plan.streamk) {
     a.tmp_out = reinterpret_cast<float*>(ws + plan.off[0]);
@@ -319,21 +346,7 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
   }
   a.split_tokens = plan.split_tokens;
   a.num_splits = plan.num_splits;
-  if (plan.streamk) {
-    // Persistent waves per compute unit, measured per cache type and block
-    // size: each wave keeps one block's loads in flight, and throughput peaks
-    // at a total of about 8-12 MiB in flight (bf16, 16-token blocks: one wave
-    // per SIMD; fp8 needs more waves to overlap its conversions; 32-token
-    // blocks carry twice the bytes per wave). A fraction leaves some compute
-    // units without a workgroup, which measured faster than spreading them.
-    const bool b32 = block_size == 32;
-    const double per_cu = kind == pa::KIND_FP8MX ? (b32 ? PA_SK_WAVES_PER_CU_BS32_FP8MX : PA_SK_WAVES_PER_CU_FP8MX)
-                          : kind == pa::KIND_FP8 ? (b32 ? PA_SK_WAVES_PER_CU_BS32_FP8 : PA_SK_WAVES_PER_CU_FP8)
-                          : kind == pa::KIND_F32 ? (b32 ? PA_SK_WAVES_PER_CU_BS32_F32 : PA_SK_WAVES_PER_CU_F32)
-                                                 : (b32 ? PA_SK_WAVES_PER_CU_BS32_BF16 : PA_SK_WAVES_PER_CU_BF16);
-    const int waves = std::min(PA_SK_MAX_WAVES, (int)(device_cus() * per_cu));
-    a.streamk_workgroups = std::max(1, waves / PA_WAVES);
-  }
+  if (plan.streamk) a.streamk_workgroups = sk_waves / PA_WAVES;
   pa::LaunchHooks hooks;
   std::unique_lock<std::mutex> lock(g_timing.mu, std::defer_lock);
   bool timed = false;
@@ -516,7 +529,8 @@ int pa_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size,
                    size_t* workspace_bytes) {
   int rc = check_plan_args(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, requested_split_tokens);
   if (rc) return rc;
-  const Plan p = make_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, requested_split_tokens);
+  const Plan p = make_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, requested_split_tokens,
+                           requested_split_tokens == 0 ? streamk_waves_bound() : 0);
   if (split_tokens) *split_tokens = p.split_tokens;   // 0 for the stream-K plan
   if (num_splits) *num_splits = p.num_splits;         // 0 for the stream-K plan
   if (workspace_bytes) *workspace_bytes = p.bytes;
@@ -529,10 +543,11 @@ int pa_workspace_bytes(int num_seqs, int num_heads, int head_size, int max_seq_l
   // valid num_kv_heads (stream-K grows with the group size G = H / Hkv).
   int rc = check_plan_args(num_seqs, num_heads, num_heads, head_size, max_seq_len, PA_PARTITION_SIZE);
   if (rc) return rc;
-  size_t best = make_plan(num_seqs, num_heads, num_heads, head_size, max_seq_len, PA_PARTITION_SIZE).bytes;
+  size_t best = make_plan(num_seqs, num_heads, num_heads, head_size, max_seq_len, PA_PARTITION_SIZE, 0).bytes;
+  const int waves = streamk_waves_bound();
   for (int g = 1; g <= PA_MAX_GROUP && g <= num_heads; ++g)
     if (num_heads % g == 0)
-      best = std::max(best, make_plan(num_seqs, num_heads, num_heads / g, head_size, max_seq_len, 0).bytes);
+      best = std::max(best, make_plan(num_seqs, num_heads, num_heads / g, head_size, max_seq_len, 0, waves).bytes);
   *bytes = best;
   return ok();
 }

@@ -41,13 +41,27 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // Wave-level helpers.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float quad_max(float v) {   // over lanes l, l^16, l^32, l^48
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
+// Reductions over lanes l, l^16, l^32, l^48 (the four lane quads of a
+// 16-column MFMA result) on gfx950's VALU row swaps, no LDS round trip:
+// v_permlane16_swap on two copies of v leaves rows (0, 0, 2, 2) in one and
+// (1, 1, 3, 3) in the other, so combining them pairs each lane with lane
+// l^16; v_permlane32_swap then leaves (lo, lo) and (hi, hi), pairing l with
+// l^32. Every lane of the wave must be active.
+template <typename Op>
+__device__ __forceinline__ float quad_reduce(float v, Op op) {
+  const unsigned b = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  v = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const unsigned c = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
+__device__ __forceinline__ float quad_max(float v) {
+  return quad_reduce(v, [](float x, float y) { return fmaxf(x, y); });
+}
+// The sum is formed in the same order on every lane: (row0 + row1) + (row2 + row3).
 __device__ __forceinline__ float quad_sum(float v) {
-  v += __shfl_xor(v, 16, 64);
-  return v + __shfl_xor(v, 32, 64);
+  return quad_reduce(v, [](float x, float y) { return x + y; });
 }
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll

@@ -120,8 +120,11 @@ int pa_kv_layout(int num_kv_heads, int head_size, int block_size, int q_dtype,
  * Sequences longer than one split write per-split partial results into the
  * workspace and a reduce kernel merges them. Outputs (any may be NULL): the
  * split_tokens, num_splits = ceil(max_seq_len / split_tokens) (>= 1), and the
- * workspace bytes this plan needs (0 when num_splits == 1). Host only; no HIP
- * call.
+ * workspace bytes this plan needs (0 when num_splits == 1). For the stream-K
+ * plan that is the size for the most waves any cache type launches on the
+ * current device (its compute-unit count is queried once; 256 is assumed
+ * where none can be queried); the decode call itself requires only the size
+ * for the grid it launches. No kernel launch.
  *
  * Workspace layout for num_splits = P > 1, all fp32, each array starting at a
  * 256-byte-aligned offset from the workspace base, in this order:
@@ -135,8 +138,9 @@ int pa_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_size,
                    int max_seq_len, int requested_split_tokens,
                    int* split_tokens, int* num_splits, size_t* workspace_bytes);
 
-/* Workspace bytes sufficient for every plan of this problem (the 256-token
- * plan needs the most). Host only. */
+/* Workspace bytes sufficient for every plan of this problem: the 256-token
+ * split plan and the stream-K plan of every valid num_kv_heads. No kernel
+ * launch (the device's compute-unit count is queried as for pa_decode_plan). */
 int pa_workspace_bytes(int num_seqs, int num_heads, int head_size, int max_seq_len,
                        size_t* bytes);
 

@@ -56,6 +56,42 @@ def worked_example(alibi=False):
     }
 
 
+def alibi_partitions():
+    """Inputs (pages' layouts, fp32, x = 4) and the closed-form per-partition
+    statistics and output of the hand-derived example in alibi_partitions.txt.
+    Returns the input arrays plus m [2], s [2], tmp [2, D] and expect [1, 1, D]."""
+    kv = {k: v for k, v in _rows("alibi_partitions.txt")}
+    n, d = int(kv["seq_len"]), int(kv["head_size"])
+    scale, slope = float(kv["scale"]), float(kv["slope"])
+    pool, mult, add = int(kv["pool"]), int(kv["table_mult"]), int(kv["table_add"])
+    bs, x = 16, 4
+    nblk = -(-n // bs)
+    table = np.array([[(mult * i + add) % pool for i in range(nblk)]], np.int32)
+    k_pool = np.zeros((pool, 1, d // x, bs, x), np.float32)
+    v_pool = np.zeros((pool, 1, d, bs), np.float32)
+    for t in range(n):
+        phys, slot = table[0, t // bs], t % bs
+        for dd in range(d):
+            k_pool[phys, 0, dd // x, slot, dd % x] = float((t + dd) % 7 - 3)
+        v_pool[phys, 0, 0, slot] = 1.0
+        v_pool[phys, 0, 1, slot] = 1.0 if t >= 256 else 0.0
+        v_pool[phys, 0, 2, slot] = 1.0 if t == n - 1 else 0.0
+    r = math.exp(-slope)
+    m = np.array([(255 - (n - 1)) * slope, 0.0])
+    s = np.array([(1 - r ** 256) / (1 - r), (1 - r ** (n - 256)) / (1 - r)])
+    tmp = np.zeros((2, d))
+    tmp[0, 0] = 1.0
+    tmp[1, 0], tmp[1, 1], tmp[1, 2] = 1.0, 1.0, 1.0 / s[1]
+    z = s[0] * math.exp(m[0]) + s[1]
+    expect = np.zeros((1, 1, d))
+    expect[0, 0, 0], expect[0, 0, 1], expect[0, 0, 2] = 1.0, s[1] / z, 1.0 / z
+    return {
+        "query": np.zeros((1, 1, d), np.float32), "key_cache": k_pool, "value_cache": v_pool,
+        "block_tables": table, "seq_lens": np.array([n], np.int32), "scale": scale,
+        "alibi_slopes": np.array([slope], np.float32), "m": m, "s": s, "tmp": tmp, "expect": expect,
+    }
+
+
 def fp8_compute_example():
     """Inputs (bf16 q bits, e4m3 caches in the pages' layouts, x = 16) and the
     closed-form output of the hand-derived fp8-arithmetic example."""

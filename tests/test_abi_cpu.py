@@ -142,7 +142,10 @@ def test_auto_plan_is_streamk_and_fits_workspace_bytes(pa):
         st, ns, wb = pa.pa_decode_plan(s, h, hkv, 128, L)
         assert (st, ns) == (0, 0)                      # stream-K scheduler
         g = h // hkv
-        slots = s * hkv + 4096
+        # one slot per (sequence, kv head) plus one per stream-K wave: at most
+        # 8 waves per compute unit on 256 compute units (MI355X; also the
+        # count assumed where no device can be queried)
+        slots = s * hkv + 8 * 256
 
         def up(v):
             return (v + 255) // 256 * 256

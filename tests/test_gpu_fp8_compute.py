@@ -86,8 +86,14 @@ def test_golden_example_on_gpu():
 
 def test_full_size_fp8_compute_sampled():
     """The fp8 workload (256 sequences, lognormal lengths up to 16384) in the
-    automatic launch plan; sampled sequences against the oracle. Also reports
-    the deviation from exact (bf16-arithmetic) attention."""
+    automatic launch plan; sampled sequences against the fp8-arithmetic oracle
+    (the oracle runs at well under a sequence per second, so the batch is
+    sampled) and against exact attention of the unquantised queries, within
+    the derived bound tests/_fp8tol.exact_attention_bound (q and P
+    quantisation) plus the kernel-to-oracle allowance and the bf16 output
+    tolerance. The fp8 arithmetic is not held to the 1e-2 tolerance of the
+    bf16-arithmetic paths against exact attention: its P carries three
+    mantissa bits."""
     cfg = workloads.FP8
     case = workloads.make_case(cfg, device=DEV)
     lens = case.meta.seq_lens
@@ -95,12 +101,16 @@ def test_full_size_fp8_compute_sampled():
     seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens))} |
                   set(int(i) for i in rng.choice(len(lens), 3, replace=False)))
     out, ref = check(case, seqs=seqs, what="fp8c-full")
-    exact = _run.run_oracle(case, seqs)
+    h = workloads.host_arrays(case, seqs)
+    extra = _fp8tol.row_bounds(h)
+    exact, bound = _fp8tol.exact_attention_bound(h)
     g = out.float().cpu().numpy()[seqs]
     dev = np.abs(g - exact)
+    allowed = 1e-2 + 1e-2 * np.abs(ref) + extra + bound
     print(f"[full] fp8 compute vs exact attention on seqs {seqs}: max_abs={dev.max():.3e} "
-          f"mean_abs={dev.mean():.3e}; fp8-arith oracle vs exact max_abs={np.abs(ref - exact).max():.3e}",
-          flush=True)
+          f"mean_abs={dev.mean():.3e}; largest derived bound {bound.max():.3e}; largest fraction of the "
+          f"allowance used {(dev / allowed).max():.3f}", flush=True)
+    assert (dev <= allowed).all()
     assert torch.isfinite(out.float()).all()
 
 

@@ -98,13 +98,14 @@ def test_oversized_max_seq_len_and_table():
 
 
 @pytest.mark.parametrize("name", ["mla", "mla128"])
-def test_full_size_workload_sampled(name):
+def test_full_size_workload_every_sequence(name):
+    """Both full-size latent-cache workloads (256 sequences of U[1, 8192]
+    tokens, 16 and 128 query heads) in the launch configuration the benchmark
+    times, every sequence against the oracle."""
     cfg = workloads.MLA_CONFIGS[name]
     case = workloads.make_mla_case(cfg, device=DEV)
-    lens = case.meta.seq_lens
-    seqs = sorted({0, cfg.num_seqs - 1, int(np.argmax(lens)), int(np.argmin(lens)), cfg.num_seqs // 2})
-    out, (max_abs, max_rel) = check(case, seqs=seqs, what=f"{name} sampled {seqs}")
-    print(f"[{name}] sampled max_abs={max_abs:.3e} max_rel={max_rel:.3e}", flush=True)
+    out, (max_abs, max_rel) = check(case, what=f"{name} full size, all {cfg.num_seqs} sequences")
+    print(f"[{name}] all sequences max_abs={max_abs:.3e} max_rel={max_rel:.3e}", flush=True)
     assert torch.isfinite(out.float()).all()
     del case
     torch.cuda.empty_cache()
@@ -137,6 +138,32 @@ def test_captured_call_replays_like_eager():
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
     _run.compare(got, oracle_mla(case), "bf16", what="graph mla")
+
+
+def test_replay_after_a_larger_eager_call():
+    """A call captured in a graph keeps a workspace of its own: a larger eager
+    call made after the capture (which outgrows the binding's cached workspace
+    and replaces it) does not disturb the replays, which still match the
+    oracle."""
+    cfg = workloads.MLA.with_(num_seqs=4, pool_blocks=400)
+    case = workloads.make_mla_case(cfg, seed=31, device=DEV, seq_lens=[1500, 20, 900, 700])
+    out = run_mla(case)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_mla(case, out)
+    torch.cuda.synchronize()
+    big_cfg = workloads.MLA.with_(num_seqs=48, num_heads=128, pool_blocks=3200)
+    big = workloads.make_mla_case(big_cfg, seed=32, device=DEV,
+                                  seq_lens=np.random.default_rng(32).integers(1, 1000, 48).tolist())
+    print("[case] graph replay after a larger eager call", flush=True)
+    for rep in range(2):
+        big_out = run_mla(big)
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        _run.compare(out, oracle_mla(case), "bf16", what=f"replay {rep} after a larger eager call")
+    _run.compare(big_out, oracle_mla(big, [0, 47]), "bf16", seqs=[0, 47], what="the larger eager call")
 
 
 def test_shared_physical_blocks():

@@ -204,11 +204,50 @@ def test_split_sizes_agree():
         assert (o - outs[0]).abs().max().item() < 2e-2
 
 
+def _split_partials(ws, s, h, ns, d):
+    """(tmp_out [S,H,P,D], max_logits [S,H,P], exp_sums [S,H,P]) from a split
+    plan's workspace, carved as pa_decode_plan documents: fp32 arrays, each at
+    a 256-byte-aligned offset."""
+    rows = s * h * ns
+
+    def up(v):
+        return (v + 255) // 256 * 256
+    f = ws.cpu().view(torch.float32).numpy()
+    tmp = f[:rows * d].reshape(s, h, ns, d)
+    o1 = up(rows * d * 4) // 4
+    ml = f[o1: o1 + rows].reshape(s, h, ns)
+    o2 = (up(rows * d * 4) + up(rows * 4)) // 4
+    es = f[o2: o2 + rows].reshape(s, h, ns)
+    return tmp, ml, es
+
+
+def _check_partials(case, ws, ns, what):
+    """The GPU's per-partition (tmp_out, max_logits, exp_sums) against the
+    oracle's partitioned form, for every partition a sequence uses."""
+    import oracle
+    s, h, d = case.query.shape
+    tmp, ml, es = _split_partials(ws, s, h, ns, d)
+    hst = workloads.host_arrays(case)
+    _, o_tmp, o_ml, o_es = oracle.paged_decode_partitioned(
+        hst["query"], hst["key_cache"], hst["value_cache"], hst["block_tables"], hst["seq_lens"],
+        hst["scale"], q_kind=hst["q_kind"], kv_kind=hst["kv_kind"], alibi_slopes=hst["alibi_slopes"],
+        k_scale=hst["k_scale"], v_scale=hst["v_scale"])
+    for si, n in enumerate(case.meta.seq_lens.tolist()):
+        used = math.ceil(n / 256)
+        if used <= 1:
+            continue                                   # one partition: written to out directly
+        np.testing.assert_allclose(ml[si, :, :used], o_ml[si, :, :used], rtol=1e-4, atol=1e-3,
+                                   err_msg=f"{what} max_logits seq {si}")
+        np.testing.assert_allclose(es[si, :, :used], o_es[si, :, :used], rtol=1e-2, atol=1e-2,
+                                   err_msg=f"{what} exp_sums seq {si}")
+        np.testing.assert_allclose(tmp[si, :, :used], o_tmp[si, :, :used], rtol=1e-2, atol=1e-2,
+                                   err_msg=f"{what} tmp_out seq {si}")
+
+
 def test_workspace_partials_match_oracle_partitions():
     """With 256-token splits the workspace holds the pages' per-partition
     (tmp_out, max_logits, exp_sums); compare them with the oracle's."""
     import decode_attention_paged_07_amd as pa
-    import oracle
     cfg = SMALL["long"].with_(seq_lens=("fixed", (1000, 513)))
     case = workloads.make_case(cfg, device=DEV)
     s, h, d = case.query.shape
@@ -217,46 +256,112 @@ def test_workspace_partials_match_oracle_partitions():
     ws = torch.full((wb,), 0, dtype=torch.uint8, device=DEV)
     _run.run_hip(case, split_tokens=256, workspace=ws)
     torch.cuda.synchronize()
-    rows = s * h * ns
+    _check_partials(case, ws, ns, "long-small")
 
-    def up(v):
-        return (v + 255) // 256 * 256
-    f = ws.cpu().view(torch.float32).numpy()
-    tmp = f[:rows * d].reshape(s, h, ns, d)
-    ml = f[up(rows * d * 4) // 4: up(rows * d * 4) // 4 + rows].reshape(s, h, ns)
-    off = (up(rows * d * 4) + up(rows * 4)) // 4
-    es = f[off: off + rows].reshape(s, h, ns)
-    hst = workloads.host_arrays(case)
-    _, o_tmp, o_ml, o_es = oracle.paged_decode_partitioned(
-        hst["query"], hst["key_cache"], hst["value_cache"], hst["block_tables"], hst["seq_lens"],
-        hst["scale"], q_kind="bf16", kv_kind="bf16", alibi_slopes=hst["alibi_slopes"])
-    for si, n in enumerate(case.meta.seq_lens.tolist()):
-        used = math.ceil(n / 256)
-        np.testing.assert_allclose(ml[si, :, :used], o_ml[si, :, :used], rtol=1e-4, atol=1e-3)
-        np.testing.assert_allclose(es[si, :, :used], o_es[si, :, :used], rtol=1e-2, atol=1e-2)
-        np.testing.assert_allclose(tmp[si, :, :used], o_tmp[si, :, :used], rtol=1e-2, atol=1e-2)
+
+def test_alibi_partition_golden_on_gpu():
+    """tests/golden/alibi_partitions.txt on the GPU: with 256-token splits the
+    workspace's max_logits are the hand-derived -5.5 and 0 (the ALiBi term is
+    zero on the newest token), the exp-sums and partial outputs their closed
+    forms; both plans give the closed-form output."""
+    import decode_attention_paged_07_amd as pa
+    ex = _golden.alibi_partitions()
+    t = {k: torch.from_numpy(v).to(DEV) for k, v in ex.items()
+         if isinstance(v, np.ndarray) and k in ("query", "key_cache", "value_cache", "block_tables", "seq_lens",
+                                                  "alibi_slopes")}
+    n = int(ex["seq_lens"][0])
+    st, ns, wb = pa.pa_decode_plan(1, 1, 1, 64, n, 256)
+    assert (st, ns) == (256, 2)
+    ws = torch.full((wb,), 0, dtype=torch.uint8, device=DEV)
+    for split in (256, 0):
+        print(f"[case] alibi partition golden split={split}", flush=True)
+        out = torch.full_like(t["query"], float("nan"))
+        pa.paged_attention_decode(out, t["query"], t["key_cache"], t["value_cache"], 1, ex["scale"],
+                                  t["block_tables"], t["seq_lens"], 16, n, alibi_slopes=t["alibi_slopes"],
+                                  split_tokens=split, workspace=ws if split else None)
+        torch.cuda.synchronize()
+        _run.compare(out, ex["expect"], "f32", what=f"alibi partition golden split={split}")
+        if split:
+            tmp, ml, es = _split_partials(ws, 1, 1, 2, 64)
+            np.testing.assert_allclose(ml[0, 0], ex["m"], rtol=0, atol=1e-5)
+            np.testing.assert_allclose(es[0, 0], ex["s"], rtol=1e-5, atol=0)
+            np.testing.assert_allclose(tmp[0, 0], ex["tmp"], rtol=1e-5, atol=1e-6)
+
+
+C_KV = {"auto": 0, "fp8_e4m3": 1}
+C_Q = {"f32": 0, "bf16": 1}
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("gqa", {}), ("fp8", {}), ("tiny128", {}), ("long", {"alibi": True}), ("mha", {"head_size": 64}),
+])
+def test_plain_c_entry_point(name, kw):
+    """pa_paged_attention_decode, the headline C entry, called directly through
+    ctypes with a workspace sized by pa_decode_plan."""
+    import ctypes
+    import decode_attention_paged_07_amd as pa
+    cfg = SMALL[name].with_(**kw)
+    case = workloads.make_case(cfg, device=DEV, poison=True)
+    s, h, d = case.query.shape
+    ks = vs = None
+    if cfg.kv_dtype != "auto":
+        ks = torch.tensor([case.k_scale], dtype=torch.float32, device=DEV)
+        vs = torch.tensor([case.v_scale], dtype=torch.float32, device=DEV)
+    _, _, need = pa.pa_decode_plan(s, h, cfg.num_kv_heads, d, case.max_seq_len, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    out = torch.full_like(case.query, float("nan"))
+    print(f"[case] plain C entry {name} {kw}", flush=True)
+    rc = pa.pa_paged_attention_decode(
+        out.data_ptr(), case.query.data_ptr(), case.key_cache.data_ptr(), case.value_cache.data_ptr(), s, h,
+        cfg.num_kv_heads, d, case.key_cache.shape[0], ctypes.c_float(case.scale), case.block_tables.data_ptr(),
+        case.block_tables.shape[1], case.seq_lens.data_ptr(), cfg.block_size, case.max_seq_len,
+        case.alibi_slopes.data_ptr() if case.alibi_slopes is not None else None, C_Q[cfg.q_dtype],
+        C_KV[cfg.kv_dtype], ks.data_ptr() if ks is not None else None, vs.data_ptr() if vs is not None else None,
+        ws.data_ptr(), need, torch.cuda.current_stream(DEV).cuda_stream)
+    assert rc == pa.PA_OK, pa.pa_last_error()
+    torch.cuda.synchronize()
+    _run.compare(out, _run.run_oracle(case), cfg.q_dtype, what=f"plain C entry {name}")
 
 
 # ---------------------------------------------------------------------------
-# Full-size workloads in the launch configuration the benchmark times
-# (automatic plan), compared on sampled sequences.
+# Full-size workloads: every sequence against the oracle, in the launch
+# configuration the benchmark times (the default stream-K plan) and in the
+# pages' 256-token partition plan.
 # ---------------------------------------------------------------------------
-
-def _sample(lens, k, seed):
-    order = np.argsort(lens)
-    rng = np.random.default_rng(seed)
-    pick = {int(order[0]), int(order[-1])}
-    pick.update(int(i) for i in rng.choice(len(lens), size=min(k, len(lens)), replace=False))
-    return sorted(pick)
-
 
 @pytest.mark.parametrize("name", ["gqa", "fp8", "mha", "long"])
-def test_full_size_sampled(name):
+def test_full_size_every_sequence(name):
     cfg = workloads.CONFIGS[name]
     case = workloads.make_case(cfg, device=DEV)
-    seqs = _sample(case.meta.seq_lens, 4 if name != "long" else 2, cfg.seed)
-    out, (mabs, mrel) = check(case, seqs=seqs, what=f"{name}-full")
-    print(f"[full] {name}: sampled seqs {seqs} max_abs={mabs:.2e} max_rel={mrel:.2e}", flush=True)
-    assert torch.isfinite(out.float()).all()
+    print(f"[case] {name} full size: {cfg.num_seqs} sequences, {int(case.meta.seq_lens.sum())} tokens",
+          flush=True)
+    ref = _run.run_oracle(case)
+    for split in (0, 256):
+        out = torch.full_like(case.query, float("nan"))
+        _run.run_hip(case, split_tokens=split, out=out)
+        torch.cuda.synchronize()
+        mabs, mrel = _run.compare(out, ref, cfg.q_dtype, what=f"{name}-full split={split}")
+        print(f"[full] {name} split={split}: all {cfg.num_seqs} sequences, max_abs={mabs:.2e} "
+              f"max_rel={mrel:.2e}", flush=True)
+        assert torch.isfinite(out.float()).all()
     del case, out
+    _free()
+
+
+def test_full_size_long_partition_partials():
+    """The long-context workload (8 x 32768 tokens, ALiBi) in the pages'
+    256-token partition plan: 128 partitions per sequence, every partition's
+    (tmp_out, max_logits, exp_sums) against the oracle's partitioned form."""
+    import decode_attention_paged_07_amd as pa
+    cfg = workloads.CONFIGS["long"]
+    case = workloads.make_case(cfg, device=DEV)
+    s, h, d = case.query.shape
+    st, ns, wb = pa.pa_decode_plan(s, h, cfg.num_kv_heads, d, case.max_seq_len, 256)
+    assert (st, ns) == (256, 128)
+    ws = torch.zeros(wb, dtype=torch.uint8, device=DEV)
+    print("[case] long full size, 256-token partials", flush=True)
+    _run.run_hip(case, split_tokens=256, workspace=ws)
+    torch.cuda.synchronize()
+    _check_partials(case, ws, ns, "long-full")
+    del case, ws
     _free()

@@ -191,3 +191,26 @@ def test_block_reference_is_the_ceiling():
                                       ex["scale"])
     v0 = oracle.e4m3fn_table()[ex["value_cache"][2, 0, :, 0]]
     np.testing.assert_allclose(out[0, 0], v0, rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("alibi", [False, True])
+def test_exact_attention_bound_holds_for_the_oracle(alibi):
+    """tests/_fp8tol.exact_attention_bound (q quantisation plus P quantisation)
+    bounds the fp8-arithmetic oracle's distance from exact attention of the
+    unquantised bf16 queries, on random caches with spread key magnitudes."""
+    from tests import _fp8tol
+    rng = np.random.default_rng(17)
+    torch.manual_seed(17)
+    spread = np.exp2(rng.integers(-2, 3, 24)).astype(np.float64)
+    q, kc, vc, table, lens = rand_case(rng, spread=spread, lens=(17, 64, 80))
+    slopes = np.array([0.5, 0.25, 0.125, 0.0625], np.float32) if alibi else None
+    h = dict(query=q, key_cache=kc, value_cache=vc, block_tables=table, seq_lens=lens, scale=0.2, k_scale=1.3,
+             v_scale=0.8, alibi_slopes=slopes)
+    out = f8.paged_decode_fp8_compute(q, kc, vc, table, lens, 0.2, k_scale=1.3, v_scale=0.8, alibi_slopes=slopes)
+    exact, bound = _fp8tol.exact_attention_bound(h)
+    direct = oracle.paged_decode(q, kc, vc, table, lens, 0.2, q_kind="bf16", kv_kind="e4m3fn",
+                                 alibi_slopes=slopes, k_scale=1.3, v_scale=0.8)
+    np.testing.assert_allclose(exact, direct, rtol=1e-12, atol=1e-13)
+    dev = np.abs(out - exact)
+    assert (dev <= bound + 1e-12).all()
+    assert dev.max() > 0 and (dev / np.maximum(bound, 1e-300)).max() > 1e-3   # not vacuous

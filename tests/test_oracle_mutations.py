@@ -108,3 +108,24 @@ def test_fp8_pin_catches_wrong_bias(monkeypatch):
     mine = ofp.e4m3fn_table()
     ok = ~np.isnan(ref)
     assert not np.array_equal(mine[ok], ref[ok])
+
+
+def _logits_alibi_unanchored(q_h, k_rows, scale, slope):
+    # wrong: ALiBi term slope * t, not zero on the newest token
+    logits = ofp._orig_logits(q_h, k_rows, scale, None)
+    if slope is not None:
+        logits = logits + np.float64(slope) * np.arange(k_rows.shape[0], dtype=np.float64)
+    return logits
+
+
+def test_alibi_anchor_pin_catches_unanchored_bias(monkeypatch):
+    """Softmax is shift-invariant, so the dense reference cannot see where the
+    ALiBi term is anchored; the hand-derived partition maxima can."""
+    from tests import _golden
+    ex = _golden.alibi_partitions()
+    args = (ex["query"], ex["key_cache"], ex["value_cache"], ex["block_tables"], ex["seq_lens"], ex["scale"])
+    monkeypatch.setattr(ofp, "head_logits", _logits_alibi_unanchored)
+    out, _, mx, _ = oracle.paged_decode_partitioned(*args, q_kind="f32", kv_kind="f32",
+                                                    alibi_slopes=ex["alibi_slopes"])
+    np.testing.assert_allclose(out, ex["expect"], rtol=1e-12, atol=1e-12)   # output unchanged
+    assert not np.allclose(mx[0, 0], ex["m"])                               # the maxima are not

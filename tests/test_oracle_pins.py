@@ -401,6 +401,28 @@ def test_partitioned_equals_direct(seq_len):
         assert np.isnan(mx[1, 0, -1])
 
 
+def test_alibi_anchor_of_partition_max_logits():
+    """tests/golden/alibi_partitions.txt: a hand-derived two-partition case in
+    which every logit is the ALiBi term alone. The per-partition maxima are
+    -5.5 and 0 only if the term is anchored at the newest token,
+    slope * (t - (L - 1)); the exp-sums, partial outputs and merged output are
+    the closed forms of the fixture."""
+    from tests import _golden
+    ex = _golden.alibi_partitions()
+    out, tmp, mx, es = oracle.paged_decode_partitioned(
+        ex["query"], ex["key_cache"], ex["value_cache"], ex["block_tables"], ex["seq_lens"], ex["scale"],
+        q_kind="f32", kv_kind="f32", alibi_slopes=ex["alibi_slopes"])
+    assert mx.shape == (1, 1, 2)
+    np.testing.assert_array_equal(mx[0, 0], ex["m"])
+    np.testing.assert_allclose(es[0, 0], ex["s"], rtol=1e-14)
+    np.testing.assert_allclose(tmp[0, 0], ex["tmp"], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(out, ex["expect"], rtol=1e-14, atol=1e-15)
+    direct = oracle.paged_decode(ex["query"], ex["key_cache"], ex["value_cache"], ex["block_tables"],
+                                 ex["seq_lens"], ex["scale"], q_kind="f32", kv_kind="f32",
+                                 alibi_slopes=ex["alibi_slopes"])
+    np.testing.assert_allclose(direct, ex["expect"], rtol=1e-14, atol=1e-15)
+
+
 def test_oracle_declares_a_pin_for_every_function():
     public = {"e4m3fn_table", "bf16_bits_to_f64", "gather_sequence", "head_logits",
               "attention_weights", "paged_decode", "paged_decode_partitioned",
