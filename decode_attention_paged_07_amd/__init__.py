@@ -28,7 +28,8 @@ __all__ = [
     "PA_OK", "PA_ERR_NULL", "PA_ERR_SHAPE", "PA_ERR_DTYPE", "PA_ERR_WORKSPACE", "PA_ERR_ALIGN",
     "PA_ERR_HIP", "PA_DTYPE_F32", "PA_DTYPE_BF16", "PA_KV_AUTO", "PA_KV_FP8_E4M3", "PA_KV_FP8_E4M3_COMPUTE",
     "PA_BLOCK_SIZE", "PA_PARTITION_SIZE", "PA_MAX_GROUP", "PA_MAX_SEQS",
-    "pa_paged_attention_decode", "pa_paged_attention_decode_split", "pa_decode_plan",
+    "pa_paged_attention_decode", "pa_paged_attention_decode_split", "pa_paged_attention_decode_noalloc",
+    "pa_decode_plan", "PA_NOALLOC_SCRATCH_BYTES",
     "pa_workspace_bytes", "pa_kv_layout", "pa_last_error", "pa_version", "pa_timing_enable",
     "pa_timing_read", "pa_timing_read_append", "pa_hbm_read_probe", "pa_hbm_gather_probe", "pa_kv_cache_append",
     "paged_attention_decode", "kv_cache_append", "PA_ERR_NOMEM", "pa_pool_create", "pa_pool_destroy",
@@ -60,6 +61,7 @@ PA_MAX_SEQS = 65535
 PA_MLA_LATENT_DIM = 512
 PA_MLA_ROPE_DIM = 64
 PA_MLA_MAX_HEADS = 128
+PA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # PA_DECODE_LIB names another build of the library to load instead of the
 # in-tree one (e.g. a host-sanitizer build); it must exist like the default.
@@ -87,6 +89,8 @@ _lib.pa_paged_attention_decode.argtypes = _DECODE_ARGS
 _lib.pa_paged_attention_decode.restype = _c_int
 _lib.pa_paged_attention_decode_split.argtypes = _DECODE_ARGS + [_c_int]
 _lib.pa_paged_attention_decode_split.restype = _c_int
+_lib.pa_paged_attention_decode_noalloc.argtypes = _DECODE_ARGS[:20] + [_vp]
+_lib.pa_paged_attention_decode_noalloc.restype = _c_int
 _lib.pa_decode_plan.argtypes = [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                 ctypes.POINTER(_c_int), ctypes.POINTER(_c_int), ctypes.POINTER(_c_size)]
 _lib.pa_decode_plan.restype = _c_int
@@ -191,6 +195,18 @@ def pa_paged_attention_decode_split(out, query, key_cache, value_cache, num_seqs
                                                 block_size, max_seq_len, alibi_slopes, q_dtype,
                                                 kv_cache_dtype, k_scale, v_scale, workspace,
                                                 workspace_bytes, stream, split_tokens)
+
+
+def pa_paged_attention_decode_noalloc(out, query, key_cache, value_cache, num_seqs, num_heads,
+                                      num_kv_heads, head_size, num_blocks, scale, block_tables,
+                                      max_blocks_per_seq, seq_lens, block_size, max_seq_len,
+                                      alibi_slopes, q_dtype, kv_cache_dtype, k_scale, v_scale,
+                                      stream) -> int:
+    return _lib.pa_paged_attention_decode_noalloc(out, query, key_cache, value_cache, num_seqs,
+                                                  num_heads, num_kv_heads, head_size, num_blocks,
+                                                  scale, block_tables, max_blocks_per_seq, seq_lens,
+                                                  block_size, max_seq_len, alibi_slopes, q_dtype,
+                                                  kv_cache_dtype, k_scale, v_scale, stream)
 
 
 def pa_decode_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len,

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG_DIR)
 LIB_NAME = "libpa_decode.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = [os.path.join(PKG_DIR, "csrc", f)
-           for f in ("pa_kernels.hip", "pa_shared.hip", "pa_append.hip", "pa_mla.hip", "pa_probe.hip", "pa_api.cpp",
+           for f in ("pa_kernels.hip", "pa_shared.hip", "pa_append.hip", "pa_mla.hip", "pa_probe.hip", "pa_noalloc.hip", "pa_api.cpp",
                      "pa_blocks.cpp")]
 INCLUDE = os.path.join(ROOT, "include")
 

@@ -503,6 +503,43 @@ __attribute__((visibility("hidden"))) int pa_internal_fail(int code, const char*
 }
 __attribute__((visibility("hidden"))) int pa_internal_ok() { return ok(); }
 
+// The decode call for the other host translation units (pa_noalloc.hip).
+__attribute__((visibility("hidden"))) int pa_internal_decode(
+    void* out, const void* query, const void* key_cache, const void* value_cache, int num_seqs, int num_heads,
+    int num_kv_heads, int head_size, int num_blocks, float scale, const int32_t* block_tables,
+    int max_blocks_per_seq, const int32_t* seq_lens, int block_size, int max_seq_len, const float* alibi_slopes,
+    int q_dtype, int kv_cache_dtype, const float* k_scale, const float* v_scale, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  return decode_impl(out, query, key_cache, value_cache, num_seqs, num_heads, num_kv_heads, head_size, num_blocks,
+                     scale, block_tables, max_blocks_per_seq, seq_lens, block_size, max_seq_len, alibi_slopes,
+                     q_dtype, kv_cache_dtype, k_scale, v_scale, workspace, workspace_bytes, stream, 0);
+}
+
+// Validates the decode arguments as the decode call does and returns, in
+// *bytes, the workspace its default (stream-K) plan needs on the current
+// device; no launch.
+__attribute__((visibility("hidden"))) int pa_internal_decode_bytes(
+    void* out, const void* query, const void* key_cache, const void* value_cache, int num_seqs, int num_heads,
+    int num_kv_heads, int head_size, int num_blocks, float scale, const int32_t* block_tables,
+    int max_blocks_per_seq, const int32_t* seq_lens, int block_size, int max_seq_len, const float* alibi_slopes,
+    int q_dtype, int kv_cache_dtype, const float* k_scale, const float* v_scale, size_t* bytes) {
+  *bytes = 0;
+  int rc = check_decode_args(out, query, key_cache, value_cache, num_seqs, num_heads, num_kv_heads, head_size,
+                             num_blocks, scale, block_tables, max_blocks_per_seq, seq_lens, block_size,
+                             max_seq_len, alibi_slopes, q_dtype, kv_cache_dtype, k_scale, v_scale, 0);
+  if (rc) return rc;
+  if (num_seqs == 0) return ok();
+  pa::DecodeArgs a;
+  const int kind = fill_decode_args(a, out, query, key_cache, value_cache, num_seqs, num_heads, num_kv_heads,
+                                    head_size, num_blocks, scale, block_tables, max_blocks_per_seq, seq_lens,
+                                    block_size, max_seq_len, alibi_slopes, q_dtype, kv_cache_dtype, k_scale,
+                                    v_scale);
+  *bytes = make_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, 0,
+                     streamk_waves(kind, block_size))
+               .bytes;
+  return ok();
+}
+
 extern "C" {
 
 int pa_kv_layout(int num_kv_heads, int head_size, int block_size, int q_dtype, int kv_cache_dtype,

@@ -195,6 +195,35 @@ int pa_paged_attention_decode_split(void* out, const void* query, const void* ke
                                     int split_tokens);
 
 /*
+ * Decode that allocates nothing, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The same computation, plan
+ * (stream-K) and kernels as pa_paged_attention_decode, with the workspace in
+ * a static device array of PA_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends. Arguments, validation and
+ * errors as for pa_paged_attention_decode, without the workspace arguments;
+ * in addition PA_ERR_WORKSPACE when the call needs more workspace than
+ * PA_NOALLOC_SCRATCH_BYTES (the need grows with num_seqs * num_kv_heads,
+ * the group size and head_size; nothing is launched then), and PA_ERR_HIP
+ * when the array's device address cannot be looked up (done once per device,
+ * on the first call with that device current). The call itself allocates
+ * nothing: no hipMalloc, no hipFree.
+ * Every call on a GPU uses that GPU's one array: calls whose executions may
+ * overlap (on different streams without ordering between them, or from
+ * several host threads) race on it and give wrong results. Calls ordered on
+ * one stream are safe. The array keeps the last call's contents; no call
+ * depends on them.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int pa_paged_attention_decode_noalloc(void* out, const void* query, const void* key_cache,
+                                      const void* value_cache, int num_seqs, int num_heads,
+                                      int num_kv_heads, int head_size, int num_blocks, float scale,
+                                      const int32_t* block_tables, int max_blocks_per_seq,
+                                      const int32_t* seq_lens, int block_size, int max_seq_len,
+                                      const float* alibi_slopes, int q_dtype, int kv_cache_dtype,
+                                      const float* k_scale, const float* v_scale, void* stream);
+
+/*
  * HBM read-bandwidth probe (measurement aid, not part of the decode path):
  * reads every byte of `buf` once with the decode kernels' load form
  * (16-byte non-temporal loads, 1 KiB contiguous per wave instruction) using
