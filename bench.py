@@ -30,7 +30,10 @@ CSRC = os.path.join(ROOT, "decode_attention_paged_07_amd", "csrc")
 KERNEL_SRC = {"pa_streamk_kernel": ("pa_kernels.hip", "pa_sched.h", "pa_wave.h", "pa_kernels.h"),
               "pa_split_kernel": ("pa_kernels.hip", "pa_sched.h", "pa_wave.h", "pa_kernels.h"),
               "pa_append_kernel": ("pa_append.hip", "pa_kernels.h"),
-              "pa_mla_streamk_kernel": ("pa_mla.hip", "pa_sched.h", "pa_wave.h", "pa_kernels.h")}
+              "pa_mla_streamk_kernel": ("pa_mla.hip", "pa_sched.h", "pa_wave.h", "pa_kernels.h"),
+              "pa_mla_wide_kernel": ("pa_mla_wide.hip", "pa_sched.h", "pa_wave.h", "pa_kernels.h")}
+# Head counts from which the latent-cache call runs its 32-heads-per-wave kernel.
+MLA_WIDE_MIN_HEADS = 65
 PEAK_BF16_TFLOPS = 2500.0
 WORKLOAD_TEXT = {
     "tiny": "tiny fp32 paged decode: 2 seqs {17,40}, 4/4 heads, D=64, bs=16, 16-block pool",
@@ -666,7 +669,7 @@ def bench_mla(config, args, dev):
     part_avg = part_ms / max(part_n, 1)
     achieved = nbytes / (part_avg / 1e3) / 1e9
     tflops = flops / (part_avg / 1e3) / 1e12
-    kernel = "pa_mla_streamk_kernel"
+    kernel = "pa_mla_wide_kernel" if cfg.num_heads >= MLA_WIDE_MIN_HEADS else "pa_mla_streamk_kernel"
     rec = {
         "metric": METRIC, "value": round(cfg.num_seqs / (ms / 1e3), 1), "unit": "seqs/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,

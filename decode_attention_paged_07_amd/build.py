@@ -20,27 +20,37 @@ ROOT = os.path.dirname(PKG_DIR)
 LIB_NAME = "libpa_decode.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = [os.path.join(PKG_DIR, "csrc", f)
-           for f in ("pa_kernels.hip", "pa_shared.hip", "pa_append.hip", "pa_mla.hip", "pa_probe.hip", "pa_noalloc.hip", "pa_api.cpp",
+           for f in ("pa_kernels.hip", "pa_shared.hip", "pa_append.hip", "pa_mla.hip", "pa_mla_wide.hip", "pa_probe.hip",
+                     "pa_noalloc.hip", "pa_api.cpp",
                      "pa_blocks.cpp")]
 INCLUDE = os.path.join(ROOT, "include")
 
 # Packed-fp32 VALU instructions stay disabled in device code: plain float
 # arithmetic is emitted as scalar-per-lane VALU ops.
-#
-# MFMA results go to ordinary VGPRs (amdgpu-mfma-vgpr-form). By default the
-# backend gives a kernel whose launch bounds allow more than 256 registers per
-# lane the accumulator-register (AGPR) form of every MFMA; the decode loop's
-# output accumulators then live in AGPRs, and since VALU code cannot operate
-# on AGPRs they are copied out and back around every block (about 40 % of the
-# loop's VALU instructions at head size 128). With the VGPR form those copies
-# disappear, each decode kernel needs fewer registers (bf16 at head size 128:
-# 218 instead of 236 per lane; the shared-prefix kernel: 314 instead of 442),
-# and outputs are bit-identical. Measured on MI355X: the shared-prefix call
-# 3-5 % faster, the decode workloads equal within 1 %.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wall", "-Wno-unused-function"]
+
+# MFMA results go to ordinary VGPRs (amdgpu-mfma-vgpr-form) in every source
+# but pa_mla_wide.hip. By default the backend gives a kernel whose launch
+# bounds allow more than 256 registers per lane the accumulator-register (AGPR)
+# form of every MFMA; the decode loop's output accumulators then live in
+# AGPRs, and since VALU code cannot operate on AGPRs they are copied out and
+# back around every block (about 40 % of the loop's VALU instructions at head
+# size 128). With the VGPR form those copies disappear, each decode kernel
+# needs fewer registers (bf16 at head size 128: 218 instead of 236 per lane;
+# the shared-prefix kernel: 314 instead of 442), and outputs are
+# bit-identical. Measured on MI355X: the shared-prefix call 3-5 % faster, the
+# decode workloads equal within 1 %. The 32-heads-per-wave latent-cache kernel
+# needs both register files (256 output accumulators beside 144 registers of
+# queries), which only the AGPR form provides; its VALU code touches the
+# accumulators only to rescale them, rarely, and at the end.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+SOURCE_FLAGS = {"pa_mla_wide.hip": []}
+
+
+def source_flags(src: str):
+    return SOURCE_FLAGS.get(os.path.basename(src), VGPR_FORM)
 
 
 def hipcc() -> str:
@@ -70,7 +80,7 @@ def build(verbose: bool = False, extra_flags=None, out_path: str = LIB_PATH, hos
     with tempfile.TemporaryDirectory(prefix="pa_build_") as objdir:
         def compile_one(src):
             obj = os.path.join(objdir, os.path.basename(src) + ".o")
-            rc, msgs = _run([hipcc(), *flags, "-I", INCLUDE, "-I", os.path.join(PKG_DIR, "csrc"),
+            rc, msgs = _run([hipcc(), *flags, *source_flags(src), "-I", INCLUDE, "-I", os.path.join(PKG_DIR, "csrc"),
                              "-c", src, "-o", obj], verbose)
             return src, obj, rc, msgs
 

@@ -446,24 +446,62 @@ SharedPlan make_shared_plan(int num_seqs, int num_heads, int num_kv_heads, int h
 
 // ---- latent-cache (MLA) decode --------------------------------------------------
 
-// Stream-K plan of the MLA kernel: one wave per 16-head group and share (one
-// wave per SIMD: each needs more than 256 registers), up to four groups in a
-// workgroup that shares one pair of 18 KiB LDS tile buffers, more groups in
-// `chunks` workgroups per share.
+// MLA stream-K workgroups (one wave each) per compute unit with a single
+// 16-head group. With more groups the 16-heads-per-wave kernel fills all four
+// SIMDs (PA_MLA_WAVES_PER_CU); with one group it is bound by its reads, which
+// two waves per compute unit sustain as well as four, with half the shares
+// and so half the partial outputs the merge reads.
+#ifndef PA_MLA_WAVES_PER_CU_ONE_GROUP
+#define PA_MLA_WAVES_PER_CU_ONE_GROUP 2
+#endif
+// Head counts from which the 32-heads-per-wave kernel (pa_mla_wide.hip) runs:
+// three or four of its waves fill a compute unit's SIMDs (its 88 KiB of LDS
+// admit one workgroup per compute unit); fewer heads fit the 16-heads-per-wave
+// kernel's single workgroup per share.
+#ifndef PA_MLA_WIDE_MIN_HEADS
+#define PA_MLA_WIDE_MIN_HEADS 65
+#endif
+
+// Stream-K plan of the MLA kernels.
+//  * 16 heads per wave (pa_mla.hip; fewer than PA_MLA_WIDE_MIN_HEADS heads):
+//    one wave per 16-head group and share (each needs more than 256 registers
+//    per lane, so one per SIMD), up to four groups in a workgroup that shares
+//    one pair of 18 KiB LDS tile buffers, more groups in `chunks` workgroups
+//    per share.
+//  * 32 heads per wave (pa_mla_wide.hip): one workgroup of ceil(H / 32) waves
+//    (one per SIMD) per share and compute unit.
+// Workspace: seg_out [slots][hpad][512] | seg_max [slots][hpad] |
+// seg_sum [slots][hpad] | seg_meta [S][2], slots = S + shares.
 struct MlaPlan {
-  int head_groups, waves_per_wg, chunks, max_shares;
+  bool wide;
+  int head_groups, waves_per_wg, chunks, shares, hpad;
   size_t off[4];
   size_t bytes;
 };
 
 MlaPlan make_mla_plan(int num_seqs, int num_heads) {
   MlaPlan p{};
-  p.head_groups = (num_heads + 15) / 16;
-  p.waves_per_wg = std::min(p.head_groups, 4);
-  p.chunks = (p.head_groups + p.waves_per_wg - 1) / p.waves_per_wg;
-  p.max_shares = PA_MLA_MAX_WAVES / (p.waves_per_wg * p.chunks);
-  const size_t hpad = (size_t)p.head_groups * 16;
-  const size_t slots = (size_t)num_seqs + p.max_shares;
+  p.wide = num_heads >= PA_MLA_WIDE_MIN_HEADS;
+  const int cus = device_cus();
+  if (p.wide) {
+    p.head_groups = (num_heads + 31) / 32;
+    p.waves_per_wg = p.head_groups;
+    p.chunks = 1;
+    p.shares = cus;
+    p.hpad = 32 * p.head_groups;
+  } else {
+    p.head_groups = (num_heads + 15) / 16;
+    p.waves_per_wg = std::min(p.head_groups, 4);
+    p.chunks = (p.head_groups + p.waves_per_wg - 1) / p.waves_per_wg;
+    // Shares: the waves per compute unit of the knobs in all, a multiple of 8
+    // so that the head groups of a share land on one XCD.
+    const int waves = cus * (p.head_groups == 1 ? PA_MLA_WAVES_PER_CU_ONE_GROUP : PA_MLA_WAVES_PER_CU);
+    const int shares = std::max(8, waves / (p.waves_per_wg * p.chunks) / 8 * 8);
+    p.shares = std::min(shares, PA_MLA_MAX_WAVES / (p.waves_per_wg * p.chunks));
+    p.hpad = 16 * p.head_groups;
+  }
+  const size_t hpad = (size_t)p.hpad;
+  const size_t slots = (size_t)num_seqs + p.shares;
   p.off[0] = 0;
   p.off[1] = round_up(slots * hpad * PA_MLA_LATENT_DIM * sizeof(float), 256);
   p.off[2] = p.off[1] + round_up(slots * hpad * sizeof(float), 256);
@@ -471,15 +509,6 @@ MlaPlan make_mla_plan(int num_seqs, int num_heads) {
   p.bytes = p.off[3] + round_up((size_t)num_seqs * 2 * sizeof(int32_t), 256);
   return p;
 }
-
-// MLA stream-K workgroups (one wave each) per compute unit with a single
-// 16-head group. With more groups the kernel is compute-bound and fills all
-// four SIMDs (PA_MLA_WAVES_PER_CU); with one group it is bound by its reads,
-// which two waves per compute unit sustain as well as four, with half the
-// shares and so half the partial outputs the merge reads.
-#ifndef PA_MLA_WAVES_PER_CU_ONE_GROUP
-#define PA_MLA_WAVES_PER_CU_ONE_GROUP 2
-#endif
 
 int check_mla_plan_args(int num_seqs, int num_heads) {
   if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
@@ -848,12 +877,9 @@ int pa_mla_decode(void* out, const void* query, const void* latent_cache, int nu
   a.head_groups = plan.head_groups;
   a.waves_per_wg = plan.waves_per_wg;
   a.chunks = plan.chunks;
-  // Shares: the waves per compute unit of the knobs in all, a multiple of 8
-  // so that the head groups of a share land on one XCD.
-  const int waves = device_cus() * (plan.head_groups == 1 ? PA_MLA_WAVES_PER_CU_ONE_GROUP : PA_MLA_WAVES_PER_CU);
-  int shares = waves / (plan.waves_per_wg * plan.chunks);
-  shares = std::max(8, shares / 8 * 8);
-  a.shares = std::min(shares, plan.max_shares);
+  a.shares = plan.shares;
+  a.hpad = plan.hpad;
+  a.wide = plan.wide ? 1 : 0;
   d.streamk_workgroups = a.shares * a.chunks;
 
   pa::LaunchHooks hooks;

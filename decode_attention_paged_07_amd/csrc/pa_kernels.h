@@ -174,13 +174,17 @@ hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream, cons
 // num_kv_heads 1; seg_* as for stream-K with slots [S + shares][head_groups*16].
 struct MlaArgs {
   DecodeArgs d;
-  int head_groups;    // ceil(num_heads / 16)
-  int waves_per_wg;   // head groups per workgroup (1)
-  int chunks;         // workgroups per share (head_groups)
+  int head_groups;    // head groups: ceil(num_heads / 16), or ceil(num_heads / 32) for the wide kernel
+  int waves_per_wg;   // head groups per workgroup
+  int chunks;         // workgroups per share
   int shares;         // stream-K shares (a multiple of 8 when chunks > 1)
+  int hpad;           // rows per slot in the segment partials (head groups x heads per group)
+  int wide;           // 1: pa_mla_wide_kernel (32 heads per wave, one workgroup per share)
 };
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream, const LaunchHooks& hooks);
+// The 32-heads-per-wave kernel alone (pa_mla_wide.hip).
+hipError_t launch_mla_wide(const MlaArgs& a, hipStream_t stream);
 
 // Streaming read of `bytes` (a multiple of 16) from `buf` by `workgroups`
 // workgroups of 256 threads (pa_probe.hip).

@@ -247,7 +247,6 @@ __device__ __forceinline__ void mla_share(const MlaArgs& a, int share, int hg, i
   const DecodeArgs& d = a.d;
   const int S = d.num_seqs;
   const unsigned top = (unsigned)(d.num_blocks - 1);
-  const int hpad = a.head_groups * 16;
   struct Seg {
     int seq, b0, b1, nbs, L;
   };
@@ -335,7 +334,7 @@ __device__ __forceinline__ void mla_share(const MlaArgs& a, int share, int hg, i
     if (cur.b0 == 0 && cur.b1 == cur.nbs) {
       wv.store_rows(reinterpret_cast<__bf16*>(d.out) + h0 * kMlaLatent, kMlaLatent);
     } else {
-      const int64_t row = (int64_t)(cur.seq + share) * hpad + hg * 16;   // slot (seq + share)
+      const int64_t row = (int64_t)(cur.seq + share) * a.hpad + hg * 16;   // slot (seq + share)
       wv.store_rows(d.seg_out + row * kMlaLatent, kMlaLatent);
       if (wv.active && wv.q4 == 0) {
         d.seg_max[row + (lane & 15)] = wv.m;
@@ -410,7 +409,7 @@ __global__ void __launch_bounds__(256) pa_mla_reduce_kernel(const MlaArgs a) {
   const int h = blockIdx.y * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (h >= d.num_heads) return;
-  const int64_t hpad = (int64_t)a.head_groups * 16;
+  const int64_t hpad = a.hpad;
   // The length and the segment bounds are read together (the bounds are
   // only used when the length is non-zero).
   const int len = d.seq_lens[seq];
@@ -479,15 +478,20 @@ __global__ void __launch_bounds__(256) pa_mla_reduce_kernel(const MlaArgs a) {
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream, const LaunchHooks& hooks) {
   if (hooks.before_partition) hooks.before_partition(stream);
-  const dim3 grid(a.shares * a.chunks);
-  switch (a.waves_per_wg) {
-    case 1: hipLaunchKernelGGL(pa_mla_streamk_kernel<1>, grid, dim3(64), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(pa_mla_streamk_kernel<2>, grid, dim3(128), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(pa_mla_streamk_kernel<3>, grid, dim3(192), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(pa_mla_streamk_kernel<4>, grid, dim3(256), 0, stream, a); break;
-    default: return hipErrorInvalidValue;
+  hipError_t err = hipSuccess;
+  if (a.wide) {
+    err = launch_mla_wide(a, stream);
+  } else {
+    const dim3 grid(a.shares * a.chunks);
+    switch (a.waves_per_wg) {
+      case 1: hipLaunchKernelGGL(pa_mla_streamk_kernel<1>, grid, dim3(64), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL(pa_mla_streamk_kernel<2>, grid, dim3(128), 0, stream, a); break;
+      case 3: hipLaunchKernelGGL(pa_mla_streamk_kernel<3>, grid, dim3(192), 0, stream, a); break;
+      case 4: hipLaunchKernelGGL(pa_mla_streamk_kernel<4>, grid, dim3(256), 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    err = hipGetLastError();
   }
-  hipError_t err = hipGetLastError();
   if (hooks.after_partition) hooks.after_partition(stream);
   if (err != hipSuccess) return err;
   if (hooks.before_reduce) hooks.before_reduce(stream);

@@ -31,7 +31,7 @@ __device__ __forceinline__ void block_counts(const DecodeArgs& a, int c0, int la
 
 // Total blocks over all sequences.
 template <int BS, int K>
-__device__ int total_blocks(const DecodeArgs& a, int lane) {
+__device__ __forceinline__ int total_blocks(const DecodeArgs& a, int lane) {
   int T = 0;
   for (int c0 = 0; c0 < a.num_seqs; c0 += 64 * K) {
     int nb[K];
@@ -45,7 +45,7 @@ __device__ int total_blocks(const DecodeArgs& a, int lane) {
 // The sequence whose block range (in sequence order, counted from sequence
 // c_begin) holds block r, and the block's index within it.
 template <int BS, int K>
-__device__ void find_block(const DecodeArgs& a, int lane, int r, int& seq, int& blk, int c_begin = 0) {
+__device__ __forceinline__ void find_block(const DecodeArgs& a, int lane, int r, int& seq, int& blk, int c_begin = 0) {
   int running = 0;
   for (int c0 = c_begin; c0 < a.num_seqs; c0 += 64 * K) {
     int nb[K];
@@ -73,7 +73,7 @@ __device__ void find_block(const DecodeArgs& a, int lane, int r, int& seq, int& 
 constexpr int kScanBig = 16;
 
 template <int BS>
-__device__ int count_blocks(const DecodeArgs& a, int lane, int& bsum) {
+__device__ __forceinline__ int count_blocks(const DecodeArgs& a, int lane, int& bsum) {
   bsum = 0;
   if (a.num_seqs <= 128) return total_blocks<BS, 2>(a, lane);
   int T = 0;
@@ -92,7 +92,7 @@ __device__ int count_blocks(const DecodeArgs& a, int lane, int& bsum) {
 
 // Sequence and block of tile r (0 <= r < T), with bsum from count_blocks.
 template <int BS>
-__device__ void locate_block(const DecodeArgs& a, int lane, int r, int bsum, int& seq, int& blk) {
+__device__ __forceinline__ void locate_block(const DecodeArgs& a, int lane, int r, int bsum, int& seq, int& blk) {
   if (a.num_seqs <= 128) {
     find_block<BS, 2>(a, lane, r, seq, blk);
   } else if (a.num_seqs <= 64 * 64 * kScanBig) {

@@ -356,15 +356,20 @@ int pa_paged_attention_decode_shared(void* out, const void* query, const void* k
  *                size is 0); contents on entry do not matter, and on return
  *                they are unspecified
  *
- * The schedule is stream-K over (sequence, block) tiles with one wave per 16
- * query heads; a sequence cut by a share boundary is finished by a merge
- * kernel. Errors, threading, ownership and device-value contracts as for
- * pa_paged_attention_decode. Timed by pa_timing_* like the decode calls.
+ * The schedule is stream-K: every workgroup of a persistent grid takes an
+ * equal share of the batch's tiles, and a sequence cut by a share boundary
+ * is finished by a merge kernel. Up to 64 heads, a wave holds 16 heads and a
+ * tile is one block; from 65 heads, a wave holds 32 heads, one workgroup holds
+ * them all, and a tile is two blocks. The workspace size depends on the head
+ * count and on the compute units of the current device (queried once; 256
+ * where none can be queried). Errors, threading, ownership and device-value
+ * contracts as for pa_paged_attention_decode. Timed by pa_timing_* like the
+ * decode calls.
  */
 #define PA_MLA_LATENT_DIM 512
 #define PA_MLA_ROPE_DIM   64
 #define PA_MLA_MAX_HEADS  128
-#define PA_MLA_MAX_WAVES  4096   /* bound on the persistent grid; sizes the workspace */
+#define PA_MLA_MAX_WAVES  4096   /* bound on the 16-heads-per-wave persistent grid */
 int pa_mla_workspace_bytes(int num_seqs, int num_heads, size_t* bytes);
 int pa_mla_decode(void* out, const void* query, const void* latent_cache, int num_seqs, int num_heads,
                   int num_blocks, float scale, const int32_t* block_tables, int max_blocks_per_seq,

@@ -99,6 +99,24 @@ def test_persistent_grid_is_resident(lib_path):
         check_resident(res)
 
 
+def test_wide_kernel_is_resident(lib_path):
+    """The 32-heads-per-wave kernel: one workgroup (one wave per SIMD) per
+    compute unit, so its LDS (two 36 KiB tile buffers and the accumulator
+    staging) fits one compute unit's, each wave fits a SIMD's 512 registers
+    per lane, and nothing spills to scratch."""
+    k = {name: r for name, r in bench.code_object_kernels(lib_path).items() if "pa_mla_wide_kernel" in name}
+    assert len(k) == 4                  # one to four 32-head waves per workgroup
+    for res in k.values():
+        assert res["scratch"] == 0
+        assert 72 * 1024 <= res["lds"] <= LDS_PER_CU
+        assert (res["alloc"] or res["vgpr"]) <= REGISTERS_PER_SIMD_LANE
+
+
+def test_bench_knows_which_kernel_runs():
+    src = open(os.path.join(ROOT, "decode_attention_paged_07_amd", "csrc", "pa_api.cpp")).read()
+    assert int(re.search(r"#define PA_MLA_WIDE_MIN_HEADS (\d+)", src).group(1)) == bench.MLA_WIDE_MIN_HEADS
+
+
 def check_resident(res):
     assert res["scratch"] == 0
     assert res["lds"] <= 36 * 1024 + 1024
