@@ -219,41 +219,68 @@ def _counter_per_dispatch(run_dir, kernel):
 
 SQ_COUNTERS = ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
                "SQ_INSTS_VMEM_RD", "SQ_VALU_MFMA_BUSY_CYCLES")
+# LDS and occupancy pass: rocprofv3's derived metrics (their expressions, from
+# rocprofv3 -L: OccupancyPercent = 400*sum(SQ_WAVE_CYCLES)/max(GRBM_GUI_ACTIVE)/CU_NUM/32,
+# LdsBankConflict = sum(SQ_LDS_BANK_CONFLICT)/(sum(SQ_LDS_IDX_ACTIVE)-sum(SQ_LDS_BANK_CONFLICT)),
+# LdsUtil = 100*sum(SQ_LDS_IDX_ACTIVE)/(max(GRBM_GUI_ACTIVE)*CU_NUM)) and the raw counters behind them.
+LDS_COUNTERS = ("OccupancyPercent", "LdsBankConflict", "LdsUtil", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+                "SQ_INSTS_LDS", "SQ_WAVES")
+COUNTER_SETS = {"sq_counters": ("instruction mix", SQ_COUNTERS),
+                "lds_occupancy": ("LDS bank conflicts, LDS use and occupancy", LDS_COUNTERS)}
 
 
-def summarise_sq(config, pmc_dir):
-    """Write the instruction-mix summary of one ``rocprofv3 --pmc`` run of the
-    SQ_COUNTERS over ``bench.py --config CONFIG`` (its log, <dir>.log, beside
-    the directory): per-dispatch medians for the decode kernel."""
+def bench_mode_flags(config):
+    """The bench flags of every profiled run of ``config`` (one workload per run)."""
+    return "--no-cpu-baseline --no-ceiling" + (" --no-secondary" if config == "gqa" else "")
+
+
+def summarise_counters(config, pmc_dir, kernel, label):
+    """Write the summary of one ``rocprofv3 --pmc`` run of COUNTER_SETS[label]
+    over ``bench.py --config CONFIG`` (its log, <dir>.log, beside the
+    directory): per-dispatch medians for ``kernel``."""
     import csv
     import statistics
+    title, counters = COUNTER_SETS[label]
     vals = {}
     with open(os.path.join(pmc_dir, "run_counter_collection.csv")) as f:
         for r in csv.DictReader(f):
-            if "pa_streamk_kernel" in r["Kernel_Name"]:
+            if kernel in r["Kernel_Name"]:
                 vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise ValueError(f"{kernel} not found in {pmc_dir}")
     med = {k: statistics.median(v) for k, v in vals.items()}
     rec = _last_json(pmc_dir.rstrip("/") + ".log")
     waves = med.get("SQ_WAVES", 0.0)
     rel = os.path.relpath(os.path.abspath(pmc_dir), ROOT)
     lines = [
-        f"# rocprofv3 instruction mix: pa_streamk_kernel, {WORKLOAD_TEXT[config]}", "",
+        f"# rocprofv3 {title}: {kernel}, {WORKLOAD_TEXT[config]}", "",
         f"kernel source sha256[:16]: {rec['kernel_sha']}", "",
-        "Command (run from /tmp with the repository at /root/repo):",
-        f"  rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d {rel} -o run -- "
-        f"python3 bench.py --config {config} --steps 3 --warmup 1 --no-cpu-baseline --no-ceiling", "",
-        "Per dispatch (median over dispatches), summed over the device:",
+        "Command (run from the repository root, TMPDIR=/tmp):",
+        f"  rocprofv3 --pmc {' '.join(counters)} --output-format csv -d {rel} -o run -- "
+        f"python3 bench.py --config {config} --steps 3 --warmup 1 {bench_mode_flags(config)}", "",
+        f"Per dispatch of {kernel} (median over {len(next(iter(vals.values())))} dispatches), summed over the device:",
     ]
-    for k in SQ_COUNTERS:
+    for k in counters:
         if k in med:
             per_wave = f"  ({med[k] / waves:,.0f} per wave)" if waves and k.startswith("SQ_INSTS") else ""
-            lines.append(f"  {k:26s} {med[k]:>18,.0f}{per_wave}")
+            fmt = f"{med[k]:>18,.4f}" if med[k] < 1000 and med[k] != int(med[k]) else f"{med[k]:>18,.0f}"
+            lines.append(f"  {k:26s} {fmt}{per_wave}")
     lines.append("")
-    lines.append(f"Algorithmic K+V bytes per launch: {rec['roofline']['algorithmic_bytes_per_launch']:,}")
-    if waves:
-        lines.append(f"Bytes per VMEM read instruction: "
-                     f"{rec['roofline']['algorithmic_bytes_per_launch'] / med.get('SQ_INSTS_VMEM_RD', 1):,.0f}")
-    path = os.path.join(ROOT, "profiles", f"pa_streamk_kernel_{config}_sq_counters.txt")
+    if label == "sq_counters":
+        algo = rec["roofline"]["algorithmic_bytes_per_launch"]
+        lines.append(f"Algorithmic bytes per launch: {algo:,}")
+        if med.get("SQ_INSTS_VMEM_RD"):
+            lines.append(f"Bytes per VMEM read instruction: {algo / med['SQ_INSTS_VMEM_RD']:,.0f}")
+    else:
+        if "OccupancyPercent" in med:
+            lines.append(f"Occupancy: {med['OccupancyPercent']:.1f} % of the 32 wave slots of a compute unit "
+                         f"({med['OccupancyPercent'] * 32 / 100:.1f} resident waves per CU on average)")
+        if "LdsBankConflict" in med:
+            lines.append(f"LDS bank conflicts: {med['LdsBankConflict']:.4f} conflict cycles per conflict-free "
+                         "LDS cycle")
+        if "LdsUtil" in med:
+            lines.append(f"LDS busy: {med['LdsUtil']:.1f} % of the kernel's cycles, averaged over compute units")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{config}_{label}.txt")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(f"wrote {path}")
@@ -273,7 +300,7 @@ def summarise_shared(stats_dir):
     lines = [
         "# rocprofv3 summary: shared-prefix decode (pa_shared_kernel + pa_shared_merge_kernel)", "",
         f"Workload: {WORKLOAD_TEXT['shared']}", "",
-        "Command (run from /tmp with the repository at /root/repo):",
+        "Command (run from the repository root, TMPDIR=/tmp):",
         f"  rocprofv3 --kernel-trace --stats --output-format csv -d {rel} -o run -- "
         "python3 bench.py --config shared --steps 20 --warmup 5", "",
         "The bench times the shared-prefix call and then the plain decode call on the same batch, so both "
@@ -332,7 +359,7 @@ def summarise_profiles(config, stats_dir, fetch_dir, write_dir, cal_fetch_dir, c
     if _last_json(write_dir.rstrip("/") + ".log")["kernel_sha"] != sha or rec["kernel_sha"] != sha:
         raise ValueError("the runs were taken from different kernel sources")
     rel = lambda d: os.path.relpath(os.path.abspath(d), ROOT)  # noqa: E731
-    mode = f"--append {append}" if append else "--no-cpu-baseline --no-ceiling"
+    mode = f"--append {append}" if append else bench_mode_flags(config)
     label = f"{config}_append{append}" if append else config
     cmds = {
         "stats": f"rocprofv3 --kernel-trace --stats --output-format csv -d {rel(stats_dir)} -o run -- "
@@ -358,7 +385,7 @@ def summarise_profiles(config, stats_dir, fetch_dir, write_dir, cal_fetch_dir, c
         json.dump(traffic, f, indent=1)
         f.write("\n")
     lines = [f"# rocprofv3 summary: {kernel}, {traffic['workload']}", "",
-             f"kernel source sha256[:16]: {sha}", "", "Commands (run from /tmp with the repository at /root/repo):"]
+             f"kernel source sha256[:16]: {sha}", "", "Commands (run from the repository root, TMPDIR=/tmp):"]
     lines += [f"  {k}: {v}" for k, v in cmds.items()]
     lines += ["", "Kernel stats (rocprofv3 --stats, ns):",
               "  name | calls | average | min | max"]
@@ -768,8 +795,9 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--no-secondary", action="store_true",
                     help="with --config gqa: skip the fp8-cache workload measured beside it")
-    ap.add_argument("--summarise-sq", metavar="PMC_DIR",
-                    help="write the instruction-mix summary from a --pmc run of SQ_COUNTERS over --config")
+    ap.add_argument("--summarise-counters", nargs=3, metavar=("PMC_DIR", "KERNEL", "SET"),
+                    help="write the summary of a --pmc run of COUNTER_SETS[SET] (sq_counters, lds_occupancy) "
+                         "over --config for KERNEL")
     ap.add_argument("--summarise-shared", metavar="STATS",
                     help="write the shared-prefix rocprofv3 summary from a --stats run of --config shared")
     ap.add_argument("--summarise", nargs=5, metavar=("STATS", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
@@ -782,8 +810,8 @@ def main():
                     help="only run 1 GiB probe reads and 1 GiB fills (counter calibration)")
     args = ap.parse_args()
 
-    if args.summarise_sq:
-        summarise_sq(args.config, args.summarise_sq)
+    if args.summarise_counters:
+        summarise_counters(args.config, *args.summarise_counters)
         return
     if args.summarise_shared:
         summarise_shared(args.summarise_shared)
