@@ -25,11 +25,12 @@
 // two halves of the head's tokens and meet through v_permlane32_swap.
 //
 // Tiles go from HBM straight to LDS (global_load_lds_dwordx4, each wave a part
-// of every tile) into two 36 KiB buffers used in turn; the next tile's copy is
-// in flight while the current one is computed, and one barrier per tile
-// separates them. The two buffers are distinct arrays named at compile time in
-// the code that reads and the code that writes them, so the compiler orders
-// reads of one only after copies into that one.
+// of every tile) into three 36 KiB buffers used in turn: while one tile is
+// computed the copies of the next two are in flight (one tile in flight per
+// CU leaves the copy latency exposed), and one barrier per tile separates them.
+// The buffers are distinct arrays named at compile time in the code that reads
+// and the code that writes them, so the compiler orders reads of one only
+// after copies into that one.
 //
 // Scheduling is the decode kernels' stream-K over (sequence, tile) units: every
 // workgroup takes an equal share; a sequence cut by a share boundary writes
@@ -74,6 +75,7 @@ static_assert(kSteps % PA_MLA_WIDE_KG == 0 && kDt % PA_MLA_WIDE_KV == 0, "groups
 
 __shared__ u32x4 mla_wide_tile0[2 * kBlockVec];
 __shared__ u32x4 mla_wide_tile1[2 * kBlockVec];
+__shared__ u32x4 mla_wide_tile2[2 * kBlockVec];
 // Per-wave staging of one output tile (16 floats per lane), the only route by
 // which the output accumulators reach ordinary registers. The accumulators
 // (256 registers per lane: 16 tiles of 32 d x 32 heads) fill the
@@ -86,7 +88,7 @@ __shared__ f32x4 mla_wide_stage[4 * 4 * 64];
 
 template <int B>
 __device__ __forceinline__ u32x4* tile_buf() {
-  return B == 0 ? mla_wide_tile0 : mla_wide_tile1;
+  return B == 0 ? mla_wide_tile0 : B == 1 ? mla_wide_tile1 : mla_wide_tile2;
 }
 
 // Eight fp32 values to the bf16x8 operand (round to nearest even).
@@ -97,16 +99,29 @@ __device__ __forceinline__ bf16x8 pack8(const float (&p)[16], int v0) {
   return r;
 }
 
-// Start of a tile: this wave's copies of the tile have landed (vmcnt(0)), its
-// reads of the previous tile are complete (release), every wave of the
-// workgroup has reached this point (barrier), and no read of the new tile is
-// moved above it (acquire). After it the tile is whole in LDS and the other
-// buffer is free for the next copy.
+// Start of a tile: at most N of this wave's copies into LDS are still in
+// flight (the next tiles'), its LDS reads have completed, and every wave of the
+// workgroup has reached this point; the empty asm statements keep the compiler
+// from moving LDS accesses across it. A workgroup fence is not used: its
+// release half waits for every copy in flight.
+template <int N>
 __device__ __forceinline__ void tile_barrier() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);   // vmcnt(N) lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  asm volatile("" ::: "memory");
+}
+
+// Element i of read-only per-call metadata (a block table, the sequence
+// lengths) at an index that is the same in every lane, as a scalar load: the
+// index is taken from the first lane, and the constant address space lets the
+// compiler read through the scalar cache.
+__device__ __forceinline__ int ld_uniform(const int32_t* p, int64_t i) {
+  const uint64_t u = (uint64_t)i;
+  const int64_t j = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(u >> 32)) << 32) |
+                              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u));
+  return ((const __attribute__((address_space(4))) int32_t*)p)[j];
 }
 
 // Max / sum of this lane and lane l ^ 32 (v_permlane32_swap on two copies).
@@ -236,9 +251,12 @@ struct WideWave {
     if (wave_any(mx > m + kRescaleSlack)) {
       const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - m_new);
+      // A head whose max is still -inf has a zero sum and zero accumulators:
+      // the first tile of a segment rescales nothing.
+      const bool live = wave_any(m != kNegInf && mx > m + kRescaleSlack);
       m = m_new;
       lsum *= alpha;
-      rescale(alpha);
+      if (live) rescale(alpha);
     }
     float p[16];
 #pragma unroll
@@ -285,22 +303,42 @@ struct WideWave {
 
   __device__ __forceinline__ void finish() { lsum = pair_reduce(lsum, [](float x, float y) { return x + y; }); }
 
-  // o / lsum for this lane's head: register v of tile dt is d = 32 dt +
-  // 8 (v / 4) + 4 h + v % 4, four consecutive d per register group. Every
-  // lane stages its tiles (the staging is per wave); inactive lanes store
-  // nothing.
+  // o / lsum into rows [row_base + h row_stride] for the nh heads of this
+  // wave (nh <= 32). Register v of tile dt is d = 32 dt + 8 (v / 4) + 4 h +
+  // v % 4 of this lane's head; each tile passes through the wave's LDS
+  // staging and comes back transposed, so that lane L holds d = 32 dt +
+  // 4 (L % 8) .. + 3 of head 8 k + L / 8, and one store instruction writes 128
+  // contiguous bytes (64 for bf16 rows) of each of eight rows instead of
+  // 32-byte pieces of 32 rows. The accumulators go to LDS as they are (only
+  // MFMAs and stores touch them); the scale is applied after the transpose.
   template <typename T>
-  __device__ __forceinline__ void store_rows(T* row_base, int64_t row_stride) const {
-    T* dst = row_base + (int64_t)(lane & 31) * row_stride + 4 * half;
+  __device__ __forceinline__ void store_rows(T* row_base, int64_t row_stride, int nh) const {
+    f32x4* t = mla_wide_stage + wave * 256;
+    int c = lane & 7, r = lane >> 3;
+    // Opaque to the optimiser, so that the addressing below is formed here
+    // (a rare path) rather than hoisted into registers the loop needs.
+    asm volatile("" : "+v"(c), "+v"(r));
+    const int src = (c >> 1) * 64 + (c & 1) * 32 + r;   // slot of chunk c of head r
     const float f = 1.f / lsum;
+    float fk[4];   // 1 / lsum of head 8 k + r
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      fk[k] = __int_as_float(__builtin_amdgcn_ds_bpermute((8 * k + r) * 4, __float_as_int(f)));
 #pragma unroll
     for (int dt = 0; dt < kDt; ++dt) {
-      const f32x16 x = through_lds(o[dt]);
-      if (active) {
+      const f32x16& x = o[dt];
+      t[lane] = f32x4{x[0], x[1], x[2], x[3]};
+      t[64 + lane] = f32x4{x[4], x[5], x[6], x[7]};
+      t[128 + lane] = f32x4{x[8], x[9], x[10], x[11]};
+      t[192 + lane] = f32x4{x[12], x[13], x[14], x[15]};
+      asm volatile("" ::: "memory");
+      f32x4 v[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          store4(dst + 32 * dt + 8 * g, f32x4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]} * f);
-      }
+      for (int k = 0; k < 4; ++k) v[k] = t[src + 8 * k];
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (8 * k + r < nh) store4(row_base + (int64_t)(8 * k + r) * row_stride + 32 * dt + 4 * c, v[k] * fk[k]);
     }
   }
 };
@@ -308,144 +346,181 @@ struct WideWave {
 // A workgroup's share: tiles [u0, u0 + units) in (sequence, tile) order, one
 // pipeline across the sequences it spans. Wave WAVE of W copies slots
 // [36 WAVE / W, 36 (WAVE + 1) / W) of every tile (slot s: 1 KiB s % 18 of the
-// tile's block s / 18). Each tile starts with a barrier: every wave has waited
-// for its own copies of the tile, so after it the tile is whole in LDS, and
-// every wave is past the previous tile, whose buffer the next copy refills.
+// tile's block s / 18; a tile with one block copies that block twice, so that
+// every tile costs each wave the same number of copy instructions).
+//
+// Two cursors walk the share: the staging cursor, two tiles ahead, and the
+// compute cursor. Step k (tile k of the share, in buffer k % 3) opens with a
+// barrier behind which every wave's copies of tile k have landed and every
+// wave is done with tile k - 1; it then starts the copy of tile k + 2 into
+// tile k - 1's buffer and computes tile k. Two tiles' copies are thus in flight
+// while one is computed.
 template <int W, int WAVE>
-__device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq, int tile, int64_t units) {
+__device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq, int tile, int units) {
   constexpr int kS0 = kCopySlots * WAVE / W, kS1 = kCopySlots * (WAVE + 1) / W;
+  constexpr int kCopies = kS1 - kS0;   // copy instructions per tile of this wave
+  // Descriptor bits of a staged tile besides its valid-token count (1..32).
+  constexpr int kLast = 64, kFirstOfSeq = 128, kLastOfSeq = 256;
   const DecodeArgs& d = a.d;
   const int S = d.num_seqs;
   const unsigned top = (unsigned)(d.num_blocks - 1);
   const int hg = WAVE;
-  struct Seg {   // tiles [t0, t1) of sequence seq; L tokens in nblk blocks, ntiles tiles in all
-    int seq, t0, t1, ntiles, nblk, L;
-  };
-  auto make_seg = [&](int s, int t0, int64_t left) {
-    Seg g;
-    g.seq = s;
-    g.t0 = t0;
-    g.L = clamp_len(d.seq_lens[s], d.max_seq_len);
-    g.nblk = blocks_of<kBS>(g.L);
-    g.ntiles = blocks_of<kTileTok>(g.L);
-    g.t1 = t0 + (int)min((int64_t)(g.ntiles - t0), left);
-    return g;
-  };
 
   WideWave wv;
   wv.init(a, hg);
   const int lane = wv.lane;
-  Seg cur = make_seg(seq, tile, units);
-  int64_t left = units - (cur.t1 - cur.t0);
-  wv.load_q(a, cur.seq, hg);
-  wv.reset();
-  const int32_t* trow = d.block_tables + (int64_t)cur.seq * d.max_blocks_per_seq;
-  int chunk = 2 * cur.t0;   // lane i of tbl holds the table entry of block chunk + i (clamped to the last)
-  int tbl = trow[min(chunk + lane, cur.nblk - 1)];
-
-  // The share's next sequence (its length and first 64 table entries).
-  Seg nx{};
-  bool has_nx = false;
-  int tbl_n = 0;
-  auto prefetch = [&]() {
-    has_nx = false;
-    if (left <= 0) return;
-    int s = cur.seq;
-    do {
-      ++s;
-    } while (s < S && clamp_len(d.seq_lens[s], d.max_seq_len) == 0);
-    if (s >= S) return;   // only with inconsistent inputs
-    nx = make_seg(s, 0, left);
-    has_nx = true;
-    tbl_n = d.block_tables[(int64_t)nx.seq * d.max_blocks_per_seq + min(lane, nx.nblk - 1)];
-  };
-  prefetch();
-
   const char* cache = reinterpret_cast<const char*>(d.key_cache);
-  // Copies this wave's slots of a tile (physical blocks p0, p1; p1 only when
-  // the tile's second block holds tokens) into buffer B.
-  auto stage = [&](auto bsel, unsigned p0, unsigned p1, bool two) {
+
+  // Staging cursor: tile st of sequence sseq (L tokens) is the next to copy;
+  // its segment of the share ends before tile st1; sleft tiles of the share
+  // follow that segment. Sequence lengths and table entries are read through
+  // the scalar cache (uniform loads; waiting for them never waits for copies).
+  int sseq = seq, st = tile, L = clamp_len(ld_uniform(d.seq_lens, seq), d.max_seq_len);
+  int st1 = min(blocks_of<kTileTok>(L), tile + units);
+  int sleft = units - (st1 - tile);
+  int sflags = (tile == 0 ? kFirstOfSeq : 0) | (st1 == blocks_of<kTileTok>(L) ? kLastOfSeq : 0);
+  bool sdone = false;
+  // Descriptor of the tile in each buffer: its sequence, and its token count
+  // with the kLast / kFirstOfSeq / kLastOfSeq bits.
+  int dseq[3], dinf[3];
+
+  // Takes the staging cursor's tile for buffer B: records its descriptor,
+  // sets its physical blocks (p1 = p0 when it has one block) and advances the
+  // cursor; false when the share has no tile left.
+  auto take = [&](auto bsel, unsigned& p0, unsigned& p1) -> bool {
     constexpr int B = decltype(bsel)::value;
+    if (sdone) return false;
+    const int64_t e = (int64_t)sseq * d.max_blocks_per_seq + 2 * st;
+    p0 = (unsigned)ld_uniform(d.block_tables, e);
+    p1 = (unsigned)ld_uniform(d.block_tables, e + (2 * st + 1 < blocks_of<kBS>(L) ? 1 : 0));
     p0 = p0 < top ? p0 : top;
     p1 = p1 < top ? p1 : top;
+    dseq[B] = sseq;
+    dinf[B] = min(kTileTok, L - st * kTileTok);
+    if (st + 1 < st1) {
+      ++st;
+    } else {
+      dinf[B] |= kLast | sflags;
+      int s = sseq;
+      if (sleft > 0) {
+        do {
+          ++s;
+        } while (s < S && clamp_len(ld_uniform(d.seq_lens, s), d.max_seq_len) == 0);
+      }
+      if (sleft > 0 && s < S) {   // s >= S only with inputs that disagree with the tile count
+        sseq = s;
+        L = clamp_len(ld_uniform(d.seq_lens, s), d.max_seq_len);
+        st = 0;
+        st1 = min(blocks_of<kTileTok>(L), sleft);
+        sleft -= st1;
+        sflags = kFirstOfSeq | (st1 == blocks_of<kTileTok>(L) ? kLastOfSeq : 0);
+      } else {
+        sdone = true;
+      }
+    }
+    return true;
+  };
+  // Byte address of copy slot s of the tile with blocks p0, p1, and its LDS slot.
+  auto slot_src = [&](int s, unsigned p0, unsigned p1) {
+    const int blk = s / (kCopySlots / 2), part = s % (kCopySlots / 2);
+    return cache + (int64_t)(blk ? p1 : p0) * kBlockBytes + part * 1024 + lane * 16;
+  };
+  auto slot_dst = [&](auto bsel, int s) {
+    constexpr int B = decltype(bsel)::value;
+    return tile_buf<B>() + (s / (kCopySlots / 2)) * kBlockVec + (s % (kCopySlots / 2)) * 64;
+  };
+  // Copies the next tile into buffer B straight from HBM to LDS.
+  auto stage = [&](auto bsel) -> bool {
+    unsigned p0, p1;
+    if (!take(bsel, p0, p1)) return false;
 #pragma unroll
-    for (int s = kS0; s < kS1; ++s) {
-      const int blk = s / (kCopySlots / 2), part = s % (kCopySlots / 2);
-      if (blk == 1 && !two) continue;
-      const char* src = cache + (int64_t)(blk ? p1 : p0) * kBlockBytes + part * 1024 + lane * 16;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(tile_buf<B>() + blk * kBlockVec +
-                                                                                  part * 64),
-                                       16, 0, 2 /* nt */);
-    }
+    for (int s = kS0; s < kS1; ++s)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)slot_src(s, p0, p1),
+                                       (__attribute__((address_space(3))) void*)slot_dst(bsel, s), 16, 0,
+                                       2 /* nt */);
+    return true;
   };
-  // Tile t of cur, or the first tile of the next sequence.
-  auto stage_cur = [&](auto bsel, int t) {
-    if (2 * t - chunk >= 64) {
-      chunk += 64;
-      tbl = trow[min(chunk + lane, cur.nblk - 1)];
-    }
-    const int nv = min(kTileTok, cur.L - t * kTileTok);
-    stage(bsel, (unsigned)__builtin_amdgcn_readlane(tbl, 2 * t - chunk),
-          (unsigned)__builtin_amdgcn_readlane(tbl, 2 * t + 1 - chunk), nv > kBS);
-  };
-  auto stage_next_seq = [&](auto bsel) {
-    stage(bsel, (unsigned)__builtin_amdgcn_readlane(tbl_n, 0), (unsigned)__builtin_amdgcn_readlane(tbl_n, 1),
-          nx.L > kBS);
+  // The same through registers, for the two tiles copied before the loop: the
+  // compiler's bookkeeping of copies into LDS, merged at the loop head, would
+  // otherwise make one of the loop's steps wait for every copy in flight.
+  auto stage_through_registers = [&](auto bsel) -> bool {
+    unsigned p0, p1;
+    if (!take(bsel, p0, p1)) return false;
+#pragma unroll
+    for (int s = kS0; s < kS1; ++s)
+      slot_dst(bsel, s)[lane] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(slot_src(s, p0, p1)));
+    return true;
   };
 
-  int t = cur.t0;
-  // Computes tile t of cur (in buffer B) after starting its successor's copy
-  // into the other buffer; false once the share is done.
+  // The first two tiles and the queries are waited for before the loop (the
+  // tiles are issued together and land together): the loop is then entered
+  // with nothing outstanding, as it is left at a segment end, and the
+  // compiler's count of outstanding loads stays exact inside it.
+  stage_through_registers(std::integral_constant<int, 0>{});
+  bool ahead = stage_through_registers(std::integral_constant<int, 1>{});   // the tile after the current one is staged
+  wv.load_q(a, seq, hg);
+  wv.reset();
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  // Computes the tile in buffer B; false once the share is done.
   auto step = [&](auto bsel) -> bool {
     constexpr int B = decltype(bsel)::value;
-    using Next = std::integral_constant<int, 1 - B>;
-    const bool more = t + 1 < cur.t1;
-    tile_barrier();
-    if (more)
-      stage_cur(Next{}, t + 1);
-    else if (has_nx)
-      stage_next_seq(Next{});
-    const int nvalid = min(kTileTok, cur.L - t * kTileTok);
+    // This wave's copies of the current tile have landed once no more than
+    // the next tile's copies are outstanding (vector memory reads complete in
+    // issue order).
+    if (ahead)
+      tile_barrier<kCopies>();
+    else
+      tile_barrier<0>();
+    const bool has_next = ahead;
+    ahead = stage(std::integral_constant<int, (B + 2) % 3>{});
+    const int inf = dinf[B];
+    const int nvalid = inf & 63;
     if (nvalid < kTileTok)
       wv.template compute<B, true>(nvalid);
     else
       wv.template compute<B, false>(kTileTok);
-    if (more) {
-      ++t;
-      return true;
-    }
+    if (!(inf & kLast)) return true;
+    // The segment ends with this tile: the next segment's queries are loaded
+    // while this one's rows are written.
     wv.finish();
-    const int64_t h0 = (int64_t)cur.seq * d.num_heads + hg * 32;
-    if (cur.t0 == 0 && cur.t1 == cur.ntiles) {
-      wv.store_rows(reinterpret_cast<__bf16*>(d.out) + h0 * kLatent, kLatent);
+    const float m_end = wv.m, l_end = wv.lsum;
+    if (has_next) wv.load_q(a, dseq[(B + 1) % 3], hg);
+    const int cseq = dseq[B];
+    const int nh = min(32, d.num_heads - hg * 32);
+    if ((inf & kFirstOfSeq) && (inf & kLastOfSeq)) {
+      wv.store_rows(reinterpret_cast<__bf16*>(d.out) + ((int64_t)cseq * d.num_heads + hg * 32) * kLatent, kLatent, nh);
     } else {
-      const int64_t row = (int64_t)(cur.seq + share) * a.hpad + hg * 32;   // slot (seq + share)
-      wv.store_rows(d.seg_out + row * kLatent, kLatent);
+      const int64_t row = (int64_t)(cseq + share) * a.hpad + hg * 32;   // slot (seq + share)
+      wv.store_rows(d.seg_out + row * kLatent, kLatent, nh);
+      float* mbase = d.seg_max;
+      float* sbase = d.seg_sum;
+      asm volatile("" : "+s"(mbase), "+s"(sbase));   // kept in scalar registers
+      float* const mrow = mbase + row;
+      float* const srow = sbase + row;
       if (wv.active && wv.half == 0) {
-        d.seg_max[row + (lane & 31)] = wv.m;
-        d.seg_sum[row + (lane & 31)] = wv.lsum;
+        mrow[lane & 31] = m_end;
+        srow[lane & 31] = l_end;
       }
     }
     if (hg == 0 && lane == 0) {
-      if (cur.t0 == 0) d.seg_meta[2 * cur.seq] = share;
-      if (cur.t1 == cur.ntiles) d.seg_meta[2 * cur.seq + 1] = share;
+      if (inf & kFirstOfSeq) d.seg_meta[2 * cseq] = share;
+      if (inf & kLastOfSeq) d.seg_meta[2 * cseq + 1] = share;
     }
-    if (!has_nx) return false;
-    cur = nx;
-    left -= cur.t1 - cur.t0;
-    wv.load_q(a, cur.seq, hg);
+    // Wait for the stores and the query loads here (with the copies in
+    // flight; a segment end is rare): left outstanding across the loop, they
+    // would keep the compiler from counting which loads have completed, and
+    // every later wait would become a wait for all of them.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (!has_next) return false;
     wv.reset();
-    trow = d.block_tables + (int64_t)cur.seq * d.max_blocks_per_seq;
-    chunk = 0;
-    tbl = tbl_n;
-    t = 0;
-    prefetch();
     return true;
   };
-  stage_cur(std::integral_constant<int, 0>{}, cur.t0);
-  while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
+  while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{}) &&
+         step(std::integral_constant<int, 2>{})) {
   }
+  // Nothing may be left in flight into LDS when the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 // Grid: one workgroup of W waves (32 heads each) per stream-K share.
@@ -466,10 +541,10 @@ pa_mla_wide_kernel(const MlaArgs a) {
   locate_block<kTileTok>(a.d, lane, (int)u0, bsum, seq, tile);
   // Each wave runs its own instantiation (its copy slots); all meet the same barriers.
   switch (wave) {
-    case 0: wide_share<W, 0>(a, share, seq, tile, u1 - u0); break;
-    case 1: if constexpr (W > 1) wide_share<W, 1 % W>(a, share, seq, tile, u1 - u0); break;
-    case 2: if constexpr (W > 2) wide_share<W, 2 % W>(a, share, seq, tile, u1 - u0); break;
-    default: if constexpr (W > 3) wide_share<W, 3 % W>(a, share, seq, tile, u1 - u0); break;
+    case 0: wide_share<W, 0>(a, share, seq, tile, (int)(u1 - u0)); break;
+    case 1: if constexpr (W > 1) wide_share<W, 1 % W>(a, share, seq, tile, (int)(u1 - u0)); break;
+    case 2: if constexpr (W > 2) wide_share<W, 2 % W>(a, share, seq, tile, (int)(u1 - u0)); break;
+    default: if constexpr (W > 3) wide_share<W, 3 % W>(a, share, seq, tile, (int)(u1 - u0)); break;
   }
 }
 
