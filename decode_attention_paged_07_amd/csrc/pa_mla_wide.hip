@@ -91,6 +91,18 @@ __device__ __forceinline__ u32x4* tile_buf() {
   return B == 0 ? mla_wide_tile0 : B == 1 ? mla_wide_tile1 : mla_wide_tile2;
 }
 
+// LDS layout of a cache block: chunk c (eight d of 16 tokens, 256 bytes) keeps
+// its 16-byte token granules in a row of its own, token t in slot
+// t ^ 4 (c % 4). A transposing read takes four tokens of four consecutive
+// chunks in one 16-lane group, which without the swizzle would all fall in the
+// same sixteen banks; with it each chunk's tokens sit in their own quarter of
+// the row. The 16-byte score reads cover whole rows and stay conflict-free.
+__device__ __forceinline__ int slot_of(int c, int t) { return t ^ (4 * (c & 3)); }
+// The copy of a 1 KiB piece (chunks 4 p .. 4 p + 3 of a block) writes lane L's
+// 16 bytes to slot L % 16 of chunk 4 p + L / 16, so lane L reads the token
+// that slot holds: granule L ^ 4 (L / 16) of the piece.
+__device__ __forceinline__ int src_granule(int lane) { return lane ^ ((lane >> 4) << 2); }
+
 // Eight fp32 values to the bf16x8 operand (round to nearest even).
 __device__ __forceinline__ bf16x8 pack8(const float (&p)[16], int v0) {
   bf16x8 r;
@@ -138,8 +150,8 @@ struct WideWave {
   float m, lsum, c;
   int lane, half, wave;
   bool active;        // this lane's head exists
-  uint32_t k_off;     // byte offset of this lane's S operand (step 0) in a tile buffer
-  uint32_t v_off;     // byte offset of this lane's transposing read (d-tile 0, block 0, first half)
+  uint32_t k_off[2];  // byte offset of this lane's S operand in a tile buffer, even / odd steps (step 0 / 1 less 512 B)
+  uint32_t v_off[2];  // byte offsets of this lane's transposing reads (d-tile 0, block 0; tokens 0-7, 8-15)
 
   __device__ __forceinline__ void init(const MlaArgs& a, int hg) {
     lane = threadIdx.x & 63;
@@ -148,14 +160,18 @@ struct WideWave {
     const int i = lane & 31;
     active = hg * 32 + i < a.d.num_heads;
     c = a.d.scale * kLog2e;
-    // S operand: token i (block i / 16, slot i % 16), chunk 2 s + h.
-    k_off = (uint32_t)((i >> 4) * kBlockBytes + (half * 16 + (i & 15)) * 16);
+    // S operand: token i (block i / 16), chunk 2 s + h, in its swizzled slot.
+    const int t = i & 15;
+    k_off[0] = (uint32_t)((i >> 4) * kBlockBytes + half * 256 + slot_of(half, t) * 16);
+    k_off[1] = (uint32_t)((i >> 4) * kBlockBytes + half * 256 + slot_of(2 + half, t) * 16);
     // Transposing read: lane 4u + w of 16-lane group G reads the 8 bytes of
     // token 4 (G / 2) + u (+ 8 for the second half of the token order) at
     // d = 16 (G % 2) + 4 w (+ 32 dt); lane j of the group then receives that
     // token range's four values of d = 16 (G % 2) + j.
     const int G = lane >> 4, mm = lane & 15, u = mm >> 2, w = mm & 3;
-    v_off = (uint32_t)((2 * (G & 1) + (w >> 1)) * 256 + (4 * (G >> 1) + u) * 16 + 8 * (w & 1));
+    const int vc = 2 * (G & 1) + (w >> 1);
+    v_off[0] = (uint32_t)(vc * 256 + slot_of(vc, 4 * (G >> 1) + u) * 16 + 8 * (w & 1));
+    v_off[1] = (uint32_t)(vc * 256 + slot_of(vc, 8 + 4 * (G >> 1) + u) * 16 + 8 * (w & 1));
   }
 
   __device__ __forceinline__ void load_q(const MlaArgs& a, int seq, int hg) {
@@ -224,7 +240,8 @@ struct WideWave {
     bf16x8 ka[2][kG];
     auto read_k = [&](int g, bf16x8 (&k)[kG]) {
 #pragma unroll
-      for (int j = 0; j < kG; ++j) k[j] = *reinterpret_cast<const bf16x8*>(base + k_off + 512 * (kG * g + j));
+      for (int j = 0; j < kG; ++j)
+        k[j] = *reinterpret_cast<const bf16x8*>(base + k_off[(kG * g + j) & 1] + 512 * (kG * g + j));
     };
     read_k(0, ka[0]);
 #pragma unroll
@@ -272,9 +289,9 @@ struct WideWave {
     auto read_v = [&](int b, int g, s16x8 (&v)[kV]) {
 #pragma unroll
       for (int j = 0; j < kV; ++j) {
-        const uint32_t off = v_off + (uint32_t)((kV * g + j) * 1024 + b * kBlockBytes);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off + 128));
+        const uint32_t off = (uint32_t)((kV * g + j) * 1024 + b * kBlockBytes);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + v_off[0] + off));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + v_off[1] + off));
         v[j] = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
     };
@@ -423,7 +440,7 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
   // Byte address of copy slot s of the tile with blocks p0, p1, and its LDS slot.
   auto slot_src = [&](int s, unsigned p0, unsigned p1) {
     const int blk = s / (kCopySlots / 2), part = s % (kCopySlots / 2);
-    return cache + (int64_t)(blk ? p1 : p0) * kBlockBytes + part * 1024 + lane * 16;
+    return cache + (int64_t)(blk ? p1 : p0) * kBlockBytes + part * 1024 + src_granule(lane) * 16;
   };
   auto slot_dst = [&](auto bsel, int s) {
     constexpr int B = decltype(bsel)::value;
