@@ -24,7 +24,7 @@
 // softmax state (running max, sum) is its head's; the two lane halves hold the
 // two halves of the head's tokens and meet through v_permlane32_swap.
 //
-// Tiles go from HBM straight to LDS (global_load_lds_dwordx4, each wave a part
+// Tiles go from HBM straight to LDS (buffer_load_dwordx4 ... lds, each wave a part
 // of every tile) into three 36 KiB buffers used in turn: while one tile is
 // computed the copies of the next two are in flight (one tile in flight per
 // CU leaves the copy latency exposed), and one barrier per tile separates them.
@@ -62,6 +62,9 @@ constexpr int kDt = kLatent / 32;                            // 32-d output tile
 constexpr int kBlockBytes = kWidth * kBS * 2;                // 18 KiB
 constexpr int kBlockVec = kBlockBytes / 16;
 constexpr int kCopySlots = 2 * kBlockBytes / 1024;           // 1 KiB copy instructions per tile
+// Fourth word of a raw buffer resource on this GPU family (byte offsets,
+// 32-bit data format; out-of-range offsets read zero).
+constexpr int kRsrcWord3 = 0x00020000;
 
 // Operand reads issued one group ahead of the products: S steps per group
 // (dividing 36) and value-product tiles per group (dividing 16).
@@ -404,14 +407,22 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
   // Takes the staging cursor's tile for buffer B: records its descriptor,
   // sets its physical blocks (p1 = p0 when it has one block) and advances the
   // cursor; false when the share has no tile left.
+  //
+  // The table entries of the cursor's tile are read one step ahead (np0,
+  // np1), so that their latency passes under a step's work instead of
+  // holding up its copies.
+  unsigned np0 = 0, np1 = 0;
+  auto fetch = [&]() {
+    const int64_t e = (int64_t)sseq * d.max_blocks_per_seq + 2 * st;
+    np0 = (unsigned)ld_uniform(d.block_tables, e);
+    np1 = (unsigned)ld_uniform(d.block_tables, e + (2 * st + 1 < blocks_of<kBS>(L) ? 1 : 0));
+  };
+  fetch();
   auto take = [&](auto bsel, unsigned& p0, unsigned& p1) -> bool {
     constexpr int B = decltype(bsel)::value;
     if (sdone) return false;
-    const int64_t e = (int64_t)sseq * d.max_blocks_per_seq + 2 * st;
-    p0 = (unsigned)ld_uniform(d.block_tables, e);
-    p1 = (unsigned)ld_uniform(d.block_tables, e + (2 * st + 1 < blocks_of<kBS>(L) ? 1 : 0));
-    p0 = p0 < top ? p0 : top;
-    p1 = p1 < top ? p1 : top;
+    p0 = np0 < top ? np0 : top;
+    p1 = np1 < top ? np1 : top;
     dseq[B] = sseq;
     dinf[B] = min(kTileTok, L - st * kTileTok);
     if (st + 1 < st1) {
@@ -446,15 +457,26 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
     constexpr int B = decltype(bsel)::value;
     return tile_buf<B>() + (s / (kCopySlots / 2)) * kBlockVec + (s % (kCopySlots / 2)) * 64;
   };
-  // Copies the next tile into buffer B straight from HBM to LDS.
+  // Copies the next tile into buffer B straight from HBM to LDS, with the
+  // buffer form of the LDS copy (one resource per cache block, offsets within
+  // its 18 KiB). The global form is a flat-encoded instruction that may touch
+  // LDS, and while one is outstanding the compiler cannot count LDS reads
+  // separately: every wait for an operand read would wait for all of them,
+  // and the reads issued ahead of the products would buy nothing.
   auto stage = [&](auto bsel) -> bool {
     unsigned p0, p1;
     if (!take(bsel, p0, p1)) return false;
+    const __amdgpu_buffer_rsrc_t r0 =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (int64_t)p0 * kBlockBytes), 0, kBlockBytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t r1 =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (int64_t)p1 * kBlockBytes), 0, kBlockBytes, kRsrcWord3);
+    const int lane_off = src_granule(lane) * 16;
 #pragma unroll
-    for (int s = kS0; s < kS1; ++s)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)slot_src(s, p0, p1),
-                                       (__attribute__((address_space(3))) void*)slot_dst(bsel, s), 16, 0,
-                                       2 /* nt */);
+    for (int s = kS0; s < kS1; ++s) {
+      const int blk = s / (kCopySlots / 2), part = s % (kCopySlots / 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(blk ? r1 : r0, (__attribute__((address_space(3))) void*)slot_dst(bsel, s),
+                                               16, part * 1024 + lane_off, 0, 0, 2 /* nt */);
+    }
     return true;
   };
   // The same through registers, for the two tiles copied before the loop: the
@@ -474,7 +496,9 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
   // with nothing outstanding, as it is left at a segment end, and the
   // compiler's count of outstanding loads stays exact inside it.
   stage_through_registers(std::integral_constant<int, 0>{});
+  fetch();
   bool ahead = stage_through_registers(std::integral_constant<int, 1>{});   // the tile after the current one is staged
+  fetch();
   wv.load_q(a, seq, hg);
   wv.reset();
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -497,6 +521,10 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
       wv.template compute<B, true>(nvalid);
     else
       wv.template compute<B, false>(kTileTok);
+    // The cursor always points at a tile of the share (the last one once it
+    // is done); its entries are read here, after the tile's LDS reads, so that
+    // no scalar load is outstanding while they are waited for.
+    fetch();
     if (!(inf & kLast)) return true;
     // The segment ends with this tile: the next segment's queries are loaded
     // while this one's rows are written.
