@@ -44,4 +44,4 @@ from .decode_fp8_compute import (  # noqa: F401,E402
     round_to_e4m3fn,
 )
 from .mla_decode import PINS as MLA_PINS  # noqa: F401,E402
-from .mla_decode import gather_latent, mla_decode  # noqa: F401,E402
+from .mla_decode import append_latent, gather_latent, mla_decode  # noqa: F401,E402

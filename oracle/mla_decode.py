@@ -21,6 +21,11 @@ Readings of points the pages leave open (each also listed in the design notes):
     [num_blocks, (d_c + d_r)/x, block_size, x]; block-table indexing as in §1.
   * Tail slots t >= L and table entries past ceil(L / bs) are never read;
     seq_len == 0 gives an all-zero output row.
+  * Appending latent rows follows the K/V append (kv_append.py): the row of
+    new token j of sequence s goes to logical position positions[s] + j,
+    stored unchanged (the cache holds the input's bf16 patterns); a negative
+    position skips the sequence, and positions past the table or table
+    entries outside the pool are not written.
 
 PINS maps each function to what pins it (tests/test_oracle_mla.py).
 """
@@ -40,6 +45,10 @@ PINS = {
                   "SDPA on K_h = [W_UK_h c, k_rope], V_h = W_UV_h c; physical "
                   "permutation invariance (bitwise); seq_len=1; constant c_kv; "
                   "q=0 mean; rope-only logits",
+    "append_latent": "read-back through gather_latent returns the new rows at their "
+                     "positions and the old rows unchanged; every slot not named by a "
+                     "position is bitwise unchanged; brute-force element scatter; "
+                     "skip rules; decode after append vs dense SDPA on the grown rows",
 }
 
 
@@ -91,3 +100,34 @@ def mla_decode(query: np.ndarray, latent_cache: np.ndarray, block_tables: np.nda
             w = w / np.sum(w)
             out[s, h] = w @ c_kv
     return out
+
+
+def append_latent(latent_cache: np.ndarray, rows: np.ndarray, block_tables: np.ndarray,
+                  positions: np.ndarray) -> np.ndarray:
+    """Copy of latent_cache with the new tokens' latent rows stored.
+
+    rows [S, T, d_c + d_r] in the cache's stored form; token j of sequence s
+    lands at logical position p = positions[s] + j, physical block
+    block_tables[s, p // bs], slot p % bs (10100.com article, §1), element e
+    of the row at [b, e // x, p % bs, e % x] (the pages' K layout, §2, with
+    one kv head). Skip rules as in the module docstring.
+    """
+    cache = latent_cache.copy()
+    num_blocks, dx, bs, x = cache.shape
+    s_count, t_count, width = rows.shape
+    if width != dx * x:
+        raise ValueError("rows must be [num_seqs, T, row width of the cache]")
+    max_pos = block_tables.shape[1] * bs
+    for s in range(s_count):
+        p0 = int(positions[s])
+        if p0 < 0:
+            continue
+        for j in range(t_count):
+            p = p0 + j
+            if p >= max_pos:
+                continue
+            b = int(block_tables[s, p // bs])
+            if b < 0 or b >= num_blocks:
+                continue
+            cache[b, :, p % bs, :] = rows[s, j].reshape(dx, x)
+    return cache

@@ -265,3 +265,119 @@ def test_pin_catches_swapped_slot_and_chunk(monkeypatch):
             return orig(np.ascontiguousarray(bad), row, n)
         mp.setattr(omla, "gather_latent", swapped)
     assert _mutant_outputs(monkeypatch, plant) > 1e-3
+
+
+# --- appending latent rows ---------------------------------------------------
+
+def _grown_problem(rng, lens, new, bs=16, x=4, extra=3):
+    """Pool holding `lens` old rows per sequence (scattered element by element)
+    with table room for `new` more tokens; returns the old rows, pool, table
+    (blocks for the new tokens drawn from the free part of the pool) and new
+    rows [S, new, W]."""
+    width = D_C + D_R
+    old = [rng.standard_normal((n, width)).astype(np.float32) for n in lens]
+    need = [-(-(n + new) // bs) for n in lens]
+    pool_blocks = sum(need) + extra
+    pool = rng.standard_normal((pool_blocks, width // x, bs, x)).astype(np.float32)
+    perm = rng.permutation(pool_blocks)
+    table = np.full((len(lens), max(need)), -1, dtype=np.int32)
+    pos = 0
+    for s, n in enumerate(lens):
+        for i in range(need[s]):
+            table[s, i] = perm[pos]
+            pos += 1
+        for t in range(n):
+            b, o = table[s, t // bs], t % bs
+            for e in range(width):
+                pool[b, e // x, o, e % x] = old[s][t, e]
+    rows = rng.standard_normal((len(lens), new, width)).astype(np.float32)
+    return old, pool, table, rows
+
+
+@pytest.mark.parametrize("x", [4, 8])
+def test_append_latent_read_back_through_the_gather(x):
+    rng = np.random.default_rng(41)
+    lens, new = [0, 5, 16, 31], 19
+    old, pool, table, rows = _grown_problem(rng, lens, new, x=x)
+    grown = oracle.append_latent(pool, rows, table, np.asarray(lens, np.int32))
+    for s, n in enumerate(lens):
+        got = oracle.gather_latent(grown, table[s], n + new)
+        np.testing.assert_array_equal(got[:n], old[s])
+        np.testing.assert_array_equal(got[n:], rows[s])
+
+
+def test_append_latent_leaves_other_slots_bitwise_unchanged():
+    rng = np.random.default_rng(42)
+    lens, new, bs = [3, 17], 6, 16
+    _, pool, table, rows = _grown_problem(rng, lens, new)
+    grown = oracle.append_latent(pool, rows, table, np.asarray(lens, np.int32))
+    named = set()
+    for s, n in enumerate(lens):
+        for p in range(n, n + new):
+            named.add((int(table[s, p // bs]), p % bs))
+    for b in range(pool.shape[0]):
+        for o in range(bs):
+            if (b, o) not in named:
+                np.testing.assert_array_equal(grown[b, :, o, :], pool[b, :, o, :])
+
+
+def test_append_latent_brute_force_element_scatter():
+    rng = np.random.default_rng(43)
+    lens, new, bs, x = [7, 30], 4, 16, 4
+    _, pool, table, rows = _grown_problem(rng, lens, new, bs=bs, x=x)
+    want = pool.copy()
+    for s, p0 in enumerate(lens):
+        for j in range(new):
+            p = p0 + j
+            b, o = table[s, p // bs], p % bs
+            for e in range(rows.shape[2]):
+                want[b, e // x, o, e % x] = rows[s, j, e]
+    got = oracle.append_latent(pool, rows, table, np.asarray(lens, np.int32))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_append_latent_skip_rules():
+    rng = np.random.default_rng(44)
+    lens, new, bs = [10, 20, 5], 8, 16
+    _, pool, table, rows = _grown_problem(rng, lens, new)
+    table = table.copy()
+    table[1, 1] = pool.shape[0]            # entry outside the pool: positions 20..27 go nowhere
+    table[2, 1] = next(b for b in range(pool.shape[0]) if b not in table)   # room for 28..31
+    positions = np.array([-1, 20, 28], np.int32)   # sequence 0 skipped; sequence 2 runs past its table
+    grown = oracle.append_latent(pool, rows, table, positions)
+    changed = np.argwhere(np.any(grown != pool, axis=(1, 3)))
+    slots = {(int(b), int(o)) for b, o in changed}
+    max_pos = table.shape[1] * bs
+    assert max_pos == 32
+    want = {(int(table[2, p // bs]), p % bs) for p in range(28, max_pos)}
+    assert slots == want
+
+
+def test_decode_after_append_matches_dense_attention():
+    rng = np.random.default_rng(45)
+    lens, new, h = [9, 33], 1, 3
+    old, pool, table, rows = _grown_problem(rng, lens, new)
+    grown = oracle.append_latent(pool, rows, table, np.asarray(lens, np.int32))
+    new_lens = [n + new for n in lens]
+    q = rng.standard_normal((len(lens), h, D_C + D_R)).astype(np.float32)
+    got = run(q, grown, table, new_lens, 0.25)
+    for s in range(len(lens)):
+        full = np.concatenate([old[s], rows[s]])
+        np.testing.assert_allclose(got[s], sdpa(q[s], full, full[:, :D_C], 0.25), rtol=1e-12, atol=1e-12)
+
+
+def test_append_pins_catch_swapped_chunk_and_slot(monkeypatch):
+    rng = np.random.default_rng(46)
+    lens, new = [4, 18], 5
+    old, pool, table, rows = _grown_problem(rng, lens, new)
+    orig = omla.append_latent
+
+    def swapped(cache, r, tab, pos):   # writes [b, o, c, i] instead of [b, c, o, i]
+        nb, dx, bs, x = cache.shape
+        view = np.ascontiguousarray(cache.reshape(nb, bs, dx, x).transpose(0, 2, 1, 3))
+        out = orig(view, r, tab, pos)
+        return np.ascontiguousarray(out.transpose(0, 2, 1, 3)).reshape(cache.shape)
+    monkeypatch.setattr(oracle, "append_latent", swapped)
+    grown = oracle.append_latent(pool, rows, table, np.asarray(lens, np.int32))
+    got = oracle.gather_latent(grown, table[1], lens[1] + new)
+    assert not np.array_equal(got[lens[1]:], rows[1])
