@@ -30,6 +30,7 @@ CSRC = os.path.join(ROOT, "decode_attention_paged_07_amd", "csrc")
 KERNEL_SRC = {"pa_streamk_kernel": ("pa_kernels.hip", "pa_sched.h", "pa_wave.h", "pa_kernels.h"),
               "pa_split_kernel": ("pa_kernels.hip", "pa_sched.h", "pa_wave.h", "pa_kernels.h"),
               "pa_append_kernel": ("pa_append.hip", "pa_kernels.h"),
+              "pa_latent_append_kernel": ("pa_append.hip", "pa_kernels.h"),
               "pa_mla_streamk_kernel": ("pa_mla.hip", "pa_sched.h", "pa_wave.h", "pa_kernels.h"),
               "pa_mla_wide_kernel": ("pa_mla_wide.hip", "pa_sched.h", "pa_wave.h", "pa_kernels.h")}
 # Head counts from which the latent-cache call runs its 32-heads-per-wave kernel.
@@ -550,6 +551,59 @@ def bench_append(case, tokens, steps, warmup):
     }
 
 
+def bench_mla_append(name, tokens, steps, warmup, dev):
+    """Time the latent-row append on an MLA workload's shapes: `tokens` new
+    rows per sequence written over each sequence's last `tokens` positions,
+    inputs resident in HBM; timed like bench_append (one graph replay)."""
+    import numpy as np
+    import torch
+
+    import decode_attention_paged_07_amd as pa
+    import workloads
+
+    cfg = workloads.MLA_CONFIGS[name]
+    print(f"[bench] building {name} inputs", file=sys.stderr, flush=True)
+    case = workloads.make_mla_case(cfg, device=dev)
+    S, width = cfg.num_seqs, 576
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed + 100)
+    rows = torch.randn((S, tokens, width), generator=g, device=dev).to(torch.bfloat16)
+    pos = torch.from_numpy(np.maximum(case.meta.seq_lens.astype(np.int64) - tokens, 0).astype(np.int32)).to(dev)
+
+    def step():
+        pa.mla_cache_append(case.latent_cache, rows, case.block_tables, pos)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            step()
+    for _ in range(2):
+        graph.replay()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = S * tokens * width * 2 * 2
+    return {
+        "metric": "paged latent-cache append: tokens/s + algorithmic GB/s (rows read + cache slots written)",
+        "value": round(S * tokens / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic", "config": {"workload": WORKLOAD_TEXT[name] + f"; {tokens} new row(s) per sequence",
+                                        "num_seqs": S, "tokens_per_seq": tokens, "row_width": width},
+        "algorithmic_bytes": nbytes, "kernel": "pa_latent_append_kernel",
+        "kernel_avg_ms": round(ms, 5), "kernel_gbps": round(nbytes / (ms / 1e3) / 1e9, 1),
+        "note": "ms_per_step and kernel_avg_ms: one HIP-graph replay of `steps` captured appends, "
+                "bracketed by events, divided by steps (back-to-back kernels, launch gaps included)",
+        "kernel_sha": kernel_sha("pa_latent_append_kernel"),
+    }
+
+
 def bench_shared(case, steps, warmup):
     """Time the shared-prefix decode and the plain decode on the same batch.
     Logical bytes count every sequence's K/V; unique bytes count each shared
@@ -851,7 +905,10 @@ def main():
     import workloads
 
     if args.config in workloads.MLA_CONFIGS:
-        print(json.dumps(bench_mla(args.config, args, dev)), flush=True)
+        if args.append:
+            print(json.dumps(bench_mla_append(args.config, args.append, args.steps, args.warmup, dev)), flush=True)
+        else:
+            print(json.dumps(bench_mla(args.config, args, dev)), flush=True)
         return
     cfg = {**workloads.CONFIGS, **workloads.EXTRA_CONFIGS}[args.config]
     if cfg.prefix_groups or args.append:

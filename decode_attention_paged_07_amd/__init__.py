@@ -38,7 +38,8 @@ __all__ = [
     "pa_paged_attention_decode_shared", "PrefixGroups", "prefix_groups", "find_prefix_groups",
     "paged_attention_decode_shared", "kv_cache_shapes", "LIB_PATH",
     "PagedAttentionError", "PA_MLA_LATENT_DIM", "PA_MLA_ROPE_DIM", "PA_MLA_MAX_HEADS",
-    "pa_mla_workspace_bytes", "pa_mla_decode", "mla_decode", "mla_cache_shape",
+    "pa_mla_workspace_bytes", "pa_mla_decode", "mla_decode", "mla_cache_shape", "pa_mla_cache_append",
+    "mla_cache_append",
 ]
 
 PA_OK = 0
@@ -145,6 +146,8 @@ _lib.pa_mla_workspace_bytes.restype = _c_int
 _lib.pa_mla_decode.argtypes = [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_float, _vp, _c_int, _vp, _c_int,
                                _c_int, _vp, _c_size, _vp]
 _lib.pa_mla_decode.restype = _c_int
+_lib.pa_mla_cache_append.argtypes = [_vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _c_int, _vp]
+_lib.pa_mla_cache_append.restype = _c_int
 
 
 class PagedAttentionError(RuntimeError):
@@ -579,6 +582,12 @@ def pa_mla_decode(out, query, latent_cache, num_seqs, num_heads, num_blocks, sca
                               workspace_bytes, stream)
 
 
+def pa_mla_cache_append(latent_cache, rows, num_seqs, tokens_per_seq, num_blocks, block_tables,
+                        max_blocks_per_seq, positions, block_size, stream) -> int:
+    return _lib.pa_mla_cache_append(latent_cache, rows, num_seqs, tokens_per_seq, num_blocks, block_tables,
+                                    max_blocks_per_seq, positions, block_size, stream)
+
+
 def mla_cache_shape(num_blocks, block_size=16):
     """Shape of the bf16 latent cache: [num_blocks, 576/8, block_size, 8]."""
     return (num_blocks, (PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM) // 8, block_size, 8)
@@ -681,6 +690,41 @@ def kv_cache_append(key_cache, value_cache, key, value, block_tables, positions,
         positions.data_ptr(), int(block_size), _Q_DTYPES[key.dtype], kvd,
         ks.data_ptr() if ks is not None else None, vs.data_ptr() if vs is not None else None, stream)
     _raise_for(rc, "kv_cache_append")
+
+
+def mla_cache_append(latent_cache, rows, block_tables, positions) -> None:
+    """Store new tokens' latent rows [c_kv, k_rope] in the paged latent cache (in place, current stream).
+
+    rows bf16 [num_seqs, 576] (one token per sequence) or [num_seqs, T, 576], contiguous; token j of
+    sequence s is written at logical position positions[s] + j through block_tables (int32
+    [num_seqs, max_blocks]); positions int32 [num_seqs], negative = skip. latent_cache bf16
+    ``mla_cache_shape(num_blocks)``.
+    """
+    width = PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM
+    dev = rows.device
+    _need(dev.type == "cuda", "rows must be on a GPU")
+    for name, t in (("latent_cache", latent_cache), ("rows", rows), ("block_tables", block_tables),
+                    ("positions", positions)):
+        _need(t.device == dev, f"{name} is not on the rows' device")
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+    if rows.dtype != torch.bfloat16 or latent_cache.dtype != torch.bfloat16:
+        raise TypeError("rows and latent_cache must be bfloat16")
+    _need(rows.dim() in (2, 3) and rows.shape[-1] == width, f"rows must be [S, {width}] or [S, T, {width}]")
+    num_seqs = rows.shape[0]
+    tokens = 1 if rows.dim() == 2 else rows.shape[1]
+    _need(latent_cache.dim() == 4, "latent_cache must be [num_blocks, 72, 16, 8]")
+    num_blocks = latent_cache.shape[0]
+    _need(tuple(latent_cache.shape) == mla_cache_shape(num_blocks),
+          f"latent_cache shape {tuple(latent_cache.shape)} != {mla_cache_shape(num_blocks)}")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == num_seqs, "block_tables must be int32 [num_seqs, max_blocks]")
+    _need(positions.dtype == torch.int32 and positions.shape == (num_seqs,),
+          "positions must be int32 [num_seqs]")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = _lib.pa_mla_cache_append(latent_cache.data_ptr(), rows.data_ptr(), num_seqs, tokens, num_blocks,
+                                  block_tables.data_ptr(), block_tables.shape[1], positions.data_ptr(), 16,
+                                  stream)
+    _raise_for(rc, "mla_cache_append")
 
 
 class PrefixGroups:

@@ -809,6 +809,48 @@ int pa_kv_cache_append(void* key_cache, void* value_cache, const void* key, cons
   return ok();
 }
 
+int pa_mla_cache_append(void* latent_cache, const void* rows, int num_seqs, int tokens_per_seq, int num_blocks,
+                        const int32_t* block_tables, int max_blocks_per_seq, const int32_t* positions,
+                        int block_size, void* stream) {
+  if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
+  if (tokens_per_seq < 1) return fail(PA_ERR_SHAPE, "tokens_per_seq %d must be positive", tokens_per_seq);
+  if (block_size != 16) return fail(PA_ERR_SHAPE, "block_size %d is not 16", block_size);
+  if (num_blocks <= 0) return fail(PA_ERR_SHAPE, "num_blocks %d must be positive", num_blocks);
+  if (max_blocks_per_seq <= 0) return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d must be positive", max_blocks_per_seq);
+  if ((int64_t)num_seqs * tokens_per_seq >= ((int64_t)1 << 31))
+    return fail(PA_ERR_SHAPE, "num_seqs * tokens_per_seq must be below 2^31");
+  if (num_seqs == 0) return ok();
+  if (!latent_cache || !rows || !block_tables || !positions)
+    return fail(PA_ERR_NULL, "latent_cache, rows, block_tables and positions must be non-NULL");
+  if (!aligned(latent_cache, 16) || !aligned(rows, 16))
+    return fail(PA_ERR_ALIGN, "latent_cache and rows must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(positions, 4))
+    return fail(PA_ERR_ALIGN, "block_tables and positions must be 4-byte aligned");
+  const uint64_t width = PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM;
+  const uint64_t cache_bytes = (uint64_t)num_blocks * width * block_size * 2;
+  const uint64_t rows_bytes = (uint64_t)num_seqs * tokens_per_seq * width * 2;
+  const uintptr_t c0 = reinterpret_cast<uintptr_t>(latent_cache), r0 = reinterpret_cast<uintptr_t>(rows);
+  if (c0 < r0 + rows_bytes && r0 < c0 + cache_bytes) return fail(PA_ERR_SHAPE, "rows overlap latent_cache");
+  pa::LatentAppendArgs a{};
+  a.latent_cache = latent_cache;
+  a.rows = rows;
+  a.block_tables = block_tables;
+  a.positions = positions;
+  a.num_seqs = num_seqs;
+  a.tokens_per_seq = tokens_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::unique_lock<std::mutex> lock(g_timing.mu);
+  const bool timed = g_timing.on;
+  if (!timed) lock.unlock();
+  if (timed) record_begin(st);
+  hipError_t err = pa::launch_latent_append(a, st);
+  if (timed) record_end_into(g_timing.app, st);
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "latent append launch failed: %s", hipGetErrorString(err));
+  return ok();
+}
+
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
 int pa_version(void) { return 100; }

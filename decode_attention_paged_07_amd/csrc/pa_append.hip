@@ -183,6 +183,36 @@ hipError_t launch_append_t(const AppendArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Latent rows (one compressed row [c_kv 512, k_rope 64] per token, bf16):
+// one wave per (sequence, physical block touched). Chunk c (8 elements, 16
+// bytes) of slot o sits at byte (16*c + o)*16 of the 18 KiB block, so with
+// the slot index fastest a run of n tokens is 72 contiguous stores of 16*n
+// bytes; the loads then take 16 bytes of each row per lane, n rows side by
+// side. The decode step (n = 1) reads its row contiguously and writes 72
+// pieces 256 bytes apart, which the layout fixes.
+__global__ void __launch_bounds__(64) pa_latent_append_kernel(const LatentAppendArgs a, int runs_per_seq) {
+  constexpr int kBs = 16, kChunks = 72, kRow = 1152, kBlock = kChunks * kBs * 16;
+  const int r = (int)(blockIdx.x % (unsigned)runs_per_seq);
+  const int s = (int)(blockIdx.x / (unsigned)runs_per_seq);
+  const int p0 = a.positions[s];
+  if (p0 < 0) return;
+  const int64_t blk = (int64_t)(p0 / kBs) + r;
+  const int64_t t_lo = blk * kBs > p0 ? blk * kBs : (int64_t)p0;
+  const int64_t p_end = (int64_t)p0 + a.tokens_per_seq;
+  const int64_t t_hi = (blk + 1) * kBs < p_end ? (blk + 1) * kBs : p_end;
+  if (t_lo >= t_hi || blk >= a.max_blocks_per_seq) return;
+  const int b = a.block_tables[(int64_t)s * a.max_blocks_per_seq + blk];
+  if (b < 0 || b >= a.num_blocks) return;
+  const int o0 = (int)(t_lo - blk * kBs);
+  const int n = (int)(t_hi - t_lo);
+  const char* src = reinterpret_cast<const char*>(a.rows) + ((int64_t)s * a.tokens_per_seq + (t_lo - p0)) * kRow;
+  char* dst = reinterpret_cast<char*>(a.latent_cache) + (int64_t)b * kBlock + o0 * 16;
+  for (int i = threadIdx.x; i < kChunks * n; i += 64) {
+    const int c = i / n, t = i - c * n;
+    *reinterpret_cast<u32x4a*>(dst + (c * kBs + t) * 16) = *reinterpret_cast<const u32x4a*>(src + t * kRow + c * 16);
+  }
+}
+
 // Copy-on-write support: pair blockIdx.x copies physical block src -> dst in
 // both caches, 16 bytes per lane, workgroups along y splitting the block.
 __global__ void __launch_bounds__(256) pa_copy_blocks_kernel(char* key_cache, char* value_cache,
@@ -208,6 +238,14 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t*
   hipLaunchKernelGGL(pa_copy_blocks_kernel, dim3(num_pairs, gy), dim3(256), 0, stream,
                      static_cast<char*>(key_cache), static_cast<char*>(value_cache), src, dst, num_blocks,
                      (int64_t)block_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_latent_append(const LatentAppendArgs& a, hipStream_t stream) {
+  // As for the K/V append: T tokens touch at most floor((14 + T) / 16) + 1 blocks.
+  const int runs = (14 + a.tokens_per_seq) / 16 + 1;
+  const int64_t items = (int64_t)a.num_seqs * runs;
+  hipLaunchKernelGGL(pa_latent_append_kernel, dim3((unsigned)items), dim3(64), 0, stream, a, runs);
   return hipGetLastError();
 }
 

@@ -155,6 +155,21 @@ struct AppendArgs {
 
 hipError_t launch_append(const AppendArgs& a, int in_kind, int cache_kind, hipStream_t stream);
 
+// Arguments of the latent-row append kernel (pa_append.hip): bf16 rows of
+// 576 elements into the latent cache [num_blocks][72][16][8].
+struct LatentAppendArgs {
+  void* latent_cache;
+  const void* rows;            // [num_seqs][tokens_per_seq][576]
+  const int32_t* block_tables; // [num_seqs][max_blocks_per_seq]
+  const int32_t* positions;    // [num_seqs]
+  int num_seqs;
+  int tokens_per_seq;
+  int num_blocks;
+  int max_blocks_per_seq;
+};
+
+hipError_t launch_latent_append(const LatentAppendArgs& a, hipStream_t stream);
+
 // Whole-block copies src[i] -> dst[i] in both caches (pa_append.hip).
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* src, const int32_t* dst,
                               int num_pairs, int num_blocks, size_t block_bytes, hipStream_t stream);

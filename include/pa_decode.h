@@ -376,6 +376,35 @@ int pa_mla_decode(void* out, const void* query, const void* latent_cache, int nu
                   const int32_t* seq_lens, int block_size, int max_seq_len, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/*
+ * Latent-cache append: store the latent rows [c_kv, k_rope] of new tokens in
+ * the paged latent cache, the step before pa_mla_decode in every decode
+ * iteration (the cache grows one token per step; "vLLM 0.25.0 解读" §1; one
+ * compressed row per token, 10100.com retirement article, §2). Token j
+ * (0 <= j < tokens_per_seq) of sequence s goes to logical position
+ * p = positions[s] + j, i.e. physical block block_tables[s, p / 16], slot
+ * p % 16 (same article, §1): element e of its row is stored at
+ * latent_cache[b][e / 8][p % 16][e % 8].
+ *   latent_cache device, bf16 [num_blocks][576/8][16][8] as for
+ *                pa_mla_decode, 16-B aligned; written only at the slots
+ *                named by the positions, the rows copied unchanged.
+ *   rows         device, bf16 [num_seqs][tokens_per_seq][576], contiguous,
+ *                16-B aligned, not overlapping latent_cache.
+ *   num_seqs >= 0 (0 is a no-op); tokens_per_seq >= 1; num_blocks > 0;
+ *   max_blocks_per_seq > 0 (table stride); block_size 16;
+ *   num_seqs * tokens_per_seq < 2^31.
+ *   block_tables device int32 [num_seqs][max_blocks_per_seq]; positions device
+ *   int32 [num_seqs]. A negative position skips the sequence; positions past
+ *   max_blocks_per_seq*16 and table entries outside [0, num_blocks) are not
+ *   written.
+ * Two tokens naming the same slot leave either one. Asynchronous on `stream`;
+ * no allocation; host-side validation and errors as for pa_kv_cache_append;
+ * timed with it by pa_timing_read_append.
+ */
+int pa_mla_cache_append(void* latent_cache, const void* rows, int num_seqs, int tokens_per_seq, int num_blocks,
+                        const int32_t* block_tables, int max_blocks_per_seq, const int32_t* positions,
+                        int block_size, void* stream);
+
 /* Text describing the last error returned on the calling thread ("" if none). */
 const char* pa_last_error(void);
 
@@ -393,7 +422,8 @@ int pa_version(void);
 int pa_timing_enable(int on);
 int pa_timing_read(double* partition_ms, int* partition_launches, double* reduce_ms,
                    int* reduce_launches);
-/* The same for the KV-append kernel launched by pa_kv_cache_append. */
+/* The same for the append kernels launched by pa_kv_cache_append and
+ * pa_mla_cache_append (one sum over both). */
 int pa_timing_read_append(double* append_ms, int* append_launches);
 
 #ifdef __cplusplus

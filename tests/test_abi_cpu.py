@@ -41,7 +41,8 @@ def test_header_declares_the_boundary():
                      "pa_timing_enable", "pa_timing_read", "pa_hbm_read_probe",
                      "pa_hbm_gather_probe", "pa_kv_cache_append", "pa_timing_read_append",
                      "pa_pool_create", "pa_pool_destroy", "pa_pool_num_free", "pa_pool_refcount",
-                     "pa_pool_append", "pa_pool_fork", "pa_pool_release", "pa_copy_blocks"):
+                     "pa_pool_append", "pa_pool_fork", "pa_pool_release", "pa_copy_blocks",
+                     "pa_mla_decode", "pa_mla_workspace_bytes", "pa_mla_cache_append"):
         assert required in names
 
 

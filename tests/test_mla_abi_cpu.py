@@ -57,3 +57,37 @@ def test_tensor_call_refuses_cpu_and_wrong_shapes(pa):  # noqa: F811
     with pytest.raises(ValueError):
         pa.mla_decode(out, q, cache, 0.1, tbl, lens, 16)
     assert pa.mla_cache_shape(4) == (4, 72, 16, 8)
+
+
+APPEND = dict(latent=A, rows=2 * A, S=4, T=1, nb=64, table=3 * A, mb=8, pos=4 * A, bs=16, stream=None)
+
+
+def call_append(pa, **over):
+    a = dict(APPEND)
+    a.update(over)
+    return pa.pa_mla_cache_append(a["latent"], a["rows"], a["S"], a["T"], a["nb"], a["table"], a["mb"],
+                                  a["pos"], a["bs"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(S=-1), -2), (dict(T=0), -2), (dict(bs=32), -2), (dict(nb=0), -2), (dict(mb=0), -2),
+    (dict(S=1 << 20, T=1 << 11), -2), (dict(latent=None), -1), (dict(rows=None), -1),
+    (dict(table=None), -1), (dict(pos=None), -1), (dict(latent=A + 8), -5), (dict(rows=2 * A + 4), -5),
+    (dict(table=3 * A + 2), -5), (dict(pos=4 * A + 1), -5),
+    (dict(rows=A + 64 * 18432 - 16), -2),   # rows start inside the cache
+    (dict(rows=A - 1152 * 4 + 16), -2),     # rows end inside the cache
+])
+def test_append_validation_rejects(pa, over, code):  # noqa: F811
+    assert call_append(pa, **over) == code
+    assert pa.pa_last_error()
+
+
+def test_append_zero_sequences_is_a_noop(pa):  # noqa: F811
+    assert call_append(pa, S=0, latent=None, rows=None, table=None, pos=None) == 0
+
+
+def test_tensor_append_refuses_cpu_tensors(pa):  # noqa: F811
+    cache = torch.zeros(pa.mla_cache_shape(4), dtype=torch.bfloat16)
+    rows = torch.zeros(2, 576, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        pa.mla_cache_append(cache, rows, torch.zeros(2, 1, dtype=torch.int32), torch.zeros(2, dtype=torch.int32))
