@@ -26,6 +26,11 @@ Readings of points the pages leave open (each also listed in the design notes):
     stored unchanged (the cache holds the input's bf16 patterns); a negative
     position skips the sequence, and positions past the table or table
     entries outside the pool are not written.
+  * An fp8 latent cache follows the pages' scaled fp8 storage (§4) with one
+    per-tensor scale for the whole row, since the row is both key and value:
+    the stored E4M3FN code times kv_scale stands for the element, and the
+    append stores the code nearest to element / kv_scale (quantise_e4m3fn).
+    The layout is the same K layout with x = 16.
 
 PINS maps each function to what pins it (tests/test_oracle_mla.py).
 """
@@ -34,7 +39,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .decode_fp64 import decode_cache_values
+from .decode_fp64 import bf16_bits_to_f64, decode_cache_values
+from .kv_append import quantise_e4m3fn
 
 PINS = {
     "gather_latent": "brute force vs contiguous latent rows scattered element "
@@ -48,7 +54,8 @@ PINS = {
     "append_latent": "read-back through gather_latent returns the new rows at their "
                      "positions and the old rows unchanged; every slot not named by a "
                      "position is bitwise unchanged; brute-force element scatter; "
-                     "skip rules; decode after append vs dense SDPA on the grown rows",
+                     "skip rules; decode after append vs dense SDPA on the grown rows; "
+                     "fp8 codes vs torch.float8_e4m3fn conversion of the clamped quotient",
 }
 
 
@@ -72,11 +79,12 @@ def gather_latent(latent_cache: np.ndarray, table_row: np.ndarray, seq_len: int)
 
 def mla_decode(query: np.ndarray, latent_cache: np.ndarray, block_tables: np.ndarray,
                seq_lens: np.ndarray, scale: float, latent_dim: int, *,
-               q_kind: str, kv_kind: str) -> np.ndarray:
+               q_kind: str, kv_kind: str, kv_scale: float = 1.0) -> np.ndarray:
     """out[s, h, :] = sum_t softmax_t(scale * q[s,h] . row_t) * row_t[:latent_dim].
 
     query [S, H, d_c + d_r] (stored form ``q_kind``), latent cache
-    [num_blocks, (d_c + d_r)/x, bs, x] (stored form ``kv_kind``), block_tables
+    [num_blocks, (d_c + d_r)/x, bs, x] (stored form ``kv_kind``; for
+    "e4m3fn" the rows are the codes' values times ``kv_scale``), block_tables
     int32 [S, max_blocks], seq_lens [S], latent_dim = d_c. Returns float64
     [S, H, d_c].
     """
@@ -92,7 +100,7 @@ def mla_decode(query: np.ndarray, latent_cache: np.ndarray, block_tables: np.nda
         seq_len = int(seq_lens[s])
         if seq_len == 0:
             continue
-        rows = decode_cache_values(gather_latent(latent_cache, block_tables[s], seq_len), kv_kind)
+        rows = decode_cache_values(gather_latent(latent_cache, block_tables[s], seq_len), kv_kind, kv_scale)
         c_kv = rows[:, :latent_dim]
         for h in range(h_count):
             logits = np.float64(scale) * (rows @ q[s, h])
@@ -103,15 +111,22 @@ def mla_decode(query: np.ndarray, latent_cache: np.ndarray, block_tables: np.nda
 
 
 def append_latent(latent_cache: np.ndarray, rows: np.ndarray, block_tables: np.ndarray,
-                  positions: np.ndarray) -> np.ndarray:
+                  positions: np.ndarray, *, kv_kind: str | None = None,
+                  kv_scale: float = 1.0) -> np.ndarray:
     """Copy of latent_cache with the new tokens' latent rows stored.
 
-    rows [S, T, d_c + d_r] in the cache's stored form; token j of sequence s
-    lands at logical position p = positions[s] + j, physical block
-    block_tables[s, p // bs], slot p % bs (10100.com article, §1), element e
-    of the row at [b, e // x, p % bs, e % x] (the pages' K layout, §2, with
-    one kv head). Skip rules as in the module docstring.
+    rows [S, T, d_c + d_r]; token j of sequence s lands at logical position
+    p = positions[s] + j, physical block block_tables[s, p // bs], slot
+    p % bs (10100.com article, §1), element e of the row at
+    [b, e // x, p % bs, e % x] (the pages' K layout, §2, with one kv head).
+    kv_kind None stores the rows as given (the cache's own stored form);
+    "e4m3fn" takes bf16 rows (uint16 bit patterns) and stores the uint8 codes
+    of element / kv_scale (§4). Skip rules as in the module docstring.
     """
+    if kv_kind == "e4m3fn":
+        rows = quantise_e4m3fn(bf16_bits_to_f64(rows).astype(np.float32), kv_scale)
+    elif kv_kind is not None:
+        raise ValueError(f"unknown cache kind {kv_kind!r}")
     cache = latent_cache.copy()
     num_blocks, dx, bs, x = cache.shape
     s_count, t_count, width = rows.shape

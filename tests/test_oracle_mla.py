@@ -381,3 +381,85 @@ def test_append_pins_catch_swapped_chunk_and_slot(monkeypatch):
     grown = oracle.append_latent(pool, rows, table, np.asarray(lens, np.int32))
     got = oracle.gather_latent(grown, table[1], lens[1] + new)
     assert not np.array_equal(got[lens[1]:], rows[1])
+
+
+# --- fp8 (e4m3fn) latent cache ---------------------------------------------
+
+def _fp8_problem(rng, lens, h, d_c=32, d_r=16, bs=16, x=16):
+    """Random e4m3fn code rows (NaN codes excluded) per sequence, scattered
+    element by element into a pool of codes through a random table."""
+    width = d_c + d_r
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    rows = [finite[rng.integers(0, finite.size, (n, width))] for n in lens]
+    pool_blocks = sum(-(-n // bs) for n in lens) + 2
+    pool = finite[rng.integers(0, finite.size, (pool_blocks, width // x, bs, x))]
+    perm = rng.permutation(pool_blocks)
+    table = np.zeros((len(lens), max(1, max(-(-n // bs) for n in lens))), np.int32)
+    pos = 0
+    for s, n in enumerate(lens):
+        for i in range(-(-n // bs)):
+            table[s, i] = perm[pos]
+            pos += 1
+        for t in range(n):
+            for e in range(width):
+                pool[table[s, t // bs], e // x, t % bs, e % x] = rows[s][t, e]
+    q = rng.standard_normal((len(lens), h, width)).astype(np.float32)
+    return q, rows, pool, table
+
+
+def _torch_e4m3(codes, scale):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy() * scale
+
+
+@pytest.mark.parametrize("kv_scale", [1.0, 0.0123, 3.5])
+def test_fp8_cache_matches_sdpa_on_library_decoded_rows(kv_scale):
+    rng = np.random.default_rng(51)
+    lens, h, d_c = [1, 17, 40], 3, 32
+    q, rows, pool, table = _fp8_problem(rng, lens, h, d_c=d_c)
+    got = oracle.mla_decode(q, pool, table, np.asarray(lens, np.int32), 0.05, d_c, q_kind="f32",
+                            kv_kind="e4m3fn", kv_scale=kv_scale)
+    for s in range(len(lens)):
+        full = _torch_e4m3(rows[s], kv_scale)
+        np.testing.assert_allclose(got[s], sdpa(q[s], full, full[:, :d_c], 0.05), rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_pin_catches_dropped_scale(monkeypatch):
+    rng = np.random.default_rng(52)
+    lens, h, d_c = [9, 30], 2, 32
+    q, rows, pool, table = _fp8_problem(rng, lens, h, d_c=d_c)
+    orig = omla.decode_cache_values
+    monkeypatch.setattr(omla, "decode_cache_values", lambda raw, kind, scale=1.0: orig(raw, kind))
+    bad = oracle.mla_decode(q, pool, table, np.asarray(lens, np.int32), 0.05, d_c, q_kind="f32",
+                            kv_kind="e4m3fn", kv_scale=0.25)
+    full = _torch_e4m3(rows[1], 0.25)
+    assert np.max(np.abs(bad[1] - sdpa(q[1], full, full[:, :d_c], 0.05))) > 1e-3
+
+
+@pytest.mark.parametrize("kv_scale", [1.0, 0.02, 7.0])
+def test_fp8_append_codes_match_library_conversion(kv_scale):
+    """Codes read back through the gather equal torch's float8_e4m3fn
+    conversion of the clamped float32 quotient; other slots unchanged."""
+    rng = np.random.default_rng(53)
+    lens, new, bs, x, width = [3, 16, 29], 5, 16, 16, 48
+    pool_blocks = sum(-(-(n + new) // bs) for n in lens) + 2
+    pool = rng.integers(0, 256, (pool_blocks, width // x, bs, x)).astype(np.uint8)
+    perm = rng.permutation(pool_blocks)
+    need = [-(-(n + new) // bs) for n in lens]
+    table = np.full((len(lens), max(need)), -1, np.int32)
+    pos = 0
+    for s in range(len(lens)):
+        for i in range(need[s]):
+            table[s, i] = perm[pos]
+            pos += 1
+    vals = (rng.standard_normal((len(lens), new, width)) * 4).astype(np.float32)
+    vals[0, 0, :4] = [1e6, -1e6, 0.0, -0.0]          # saturation and signed zeros
+    bits = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    grown = oracle.append_latent(pool, bits, table, np.asarray(lens, np.int32), kv_kind="e4m3fn",
+                                 kv_scale=kv_scale)
+    f32 = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float32)
+    quot = (f32 / torch.tensor(kv_scale, dtype=torch.float32)).clamp(-448.0, 448.0)
+    want = quot.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for s, n in enumerate(lens):
+        got = oracle.gather_latent(grown, table[s], n + new)
+        np.testing.assert_array_equal(got[n:], want[s])
+        np.testing.assert_array_equal(got[:n], oracle.gather_latent(pool, table[s], n))
