@@ -55,6 +55,12 @@ WORKLOAD_TEXT = {
            "128 over 8), one latent head of [c_kv 512, k_rope 64], bf16, bs=16, 131072-block pool",
     "mla128": "latent-cache (MLA) decode: 256 seqs, lens U[1,8192] (seed 7), 128 query heads, one latent head "
               "of [c_kv 512, k_rope 64], bf16, bs=16, 131072-block pool",
+    "mla_fp8": "latent-cache (MLA) decode, fp8 e4m3 latent cache (one scale = amax/448): 256 seqs, lens U[1,8192] "
+               "(seed 8), 16 query heads, one latent head of [c_kv 512, k_rope 64], bf16 q, bs=16, "
+               "131072-block pool",
+    "mla128_fp8": "latent-cache (MLA) decode, fp8 e4m3 latent cache (one scale = amax/448): 256 seqs, lens "
+                  "U[1,8192] (seed 9), 128 query heads, one latent head of [c_kv 512, k_rope 64], bf16 q, bs=16, "
+                  "131072-block pool",
 }
 
 
@@ -569,9 +575,11 @@ def bench_mla_append(name, tokens, steps, warmup, dev):
     g.manual_seed(cfg.seed + 100)
     rows = torch.randn((S, tokens, width), generator=g, device=dev).to(torch.bfloat16)
     pos = torch.from_numpy(np.maximum(case.meta.seq_lens.astype(np.int64) - tokens, 0).astype(np.int32)).to(dev)
+    fp8 = cfg.kv_dtype == "fp8_e4m3"
+    kv_scale = torch.tensor([case.kv_scale], dtype=torch.float32, device=dev)
 
     def step():
-        pa.mla_cache_append(case.latent_cache, rows, case.block_tables, pos)
+        pa.mla_cache_append(case.latent_cache, rows, case.block_tables, pos, kv_scale=kv_scale)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -589,11 +597,12 @@ def bench_mla_append(name, tokens, steps, warmup, dev):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    nbytes = S * tokens * width * 2 * 2
+    nbytes = S * tokens * width * (2 + (1 if fp8 else 2))
     return {
         "metric": "paged latent-cache append: tokens/s + algorithmic GB/s (rows read + cache slots written)",
         "value": round(S * tokens / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
-        "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "dtype": "bf16",
+        "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "dtype": "bf16 in -> fp8 e4m3 cache" if fp8 else "bf16",
         "data": "synthetic", "config": {"workload": WORKLOAD_TEXT[name] + f"; {tokens} new row(s) per sequence",
                                         "num_seqs": S, "tokens_per_seq": tokens, "row_width": width},
         "algorithmic_bytes": nbytes, "kernel": "pa_latent_append_kernel",
@@ -714,15 +723,16 @@ def mla_cpu_baseline(case, out, budget_s: float):
             h = workloads.mla_host_arrays(case, seqs)     # host copy, not timed
             t0 = time.perf_counter()
             ref = oracle.mla_decode(h["query"], h["latent_cache"], h["block_tables"], h["seq_lens"], h["scale"],
-                                    512, q_kind="bf16", kv_kind="bf16")
+                                    512, q_kind="bf16", kv_kind=h["kv_kind"], kv_scale=h["kv_scale"])
             wall += time.perf_counter() - t0
             worst = tuple(max(a, b) for a, b in zip(worst, _run.compare(out, ref, "bf16", seqs=seqs)))
             i += len(seqs)
             per_seq = wall / i
     tokens = int(case.meta.seq_lens[:i].astype("int64").sum())
+    elem = 1 if case.cfg.kv_dtype == "fp8_e4m3" else 2
     return {
         "value": i / wall, "unit": "seqs/s", "cores": cores, "kind": "oracle",
-        "kv_gbps": round(tokens * 576 * 2 / wall / 1e9, 3),
+        "kv_gbps": round(tokens * 576 * elem / wall / 1e9, 3),
         "sample": f"first {i} of {n} sequences ({tokens} tokens), fp64 numpy MLA oracle, host copy untimed, "
                   f"{wall:.1f} s wall",
     }, {"max_abs": float(f"{worst[0]:.3e}"), "max_rel": float(f"{worst[1]:.3e}")}
@@ -739,22 +749,26 @@ def bench_mla(config, args, dev):
     case = workloads.make_mla_case(cfg, device=dev)
     out = torch.empty(cfg.num_seqs, cfg.num_heads, 512, dtype=torch.bfloat16, device=dev)
 
+    fp8 = cfg.kv_dtype == "fp8_e4m3"
+    kv_scale = torch.tensor([case.kv_scale], dtype=torch.float32, device=dev)
+
     def step():
         pa.mla_decode(out, case.query, case.latent_cache, case.scale, case.block_tables, case.seq_lens,
-                      case.max_seq_len)
+                      case.max_seq_len, kv_scale=kv_scale)
 
     ms, (part_ms, part_n), (red_ms, red_n), ms_ev = time_steps(step, args.steps, args.warmup, dev)
     tokens = int(case.meta.seq_lens.astype("int64").sum())
-    nbytes = tokens * 576 * 2
+    nbytes = tokens * 576 * (1 if fp8 else 2)
     flops = tokens * cfg.num_heads * 2 * (576 + 512)
     part_avg = part_ms / max(part_n, 1)
     achieved = nbytes / (part_avg / 1e3) / 1e9
     tflops = flops / (part_avg / 1e3) / 1e12
-    kernel = "pa_mla_wide_kernel" if cfg.num_heads >= MLA_WIDE_MIN_HEADS else "pa_mla_streamk_kernel"
+    kernel = "pa_mla_wide_kernel" if cfg.num_heads >= MLA_WIDE_MIN_HEADS and not fp8 else "pa_mla_streamk_kernel"
     rec = {
         "metric": METRIC, "value": round(cfg.num_seqs / (ms / 1e3), 1), "unit": "seqs/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 e4m3 latent cache -> bf16 MFMA" if fp8 else "bf16",
         "data": "synthetic (seeded N(0,1) values, seeded lengths and block tables)",
         "config": {"workload": WORKLOAD_TEXT[config], "num_seqs": cfg.num_seqs, "num_heads": cfg.num_heads,
                    "latent_dim": 512, "rope_dim": 64, "block_size": cfg.block_size, "pool_blocks": cfg.pool_blocks,

@@ -39,7 +39,7 @@ __all__ = [
     "paged_attention_decode_shared", "kv_cache_shapes", "LIB_PATH",
     "PagedAttentionError", "PA_MLA_LATENT_DIM", "PA_MLA_ROPE_DIM", "PA_MLA_MAX_HEADS",
     "pa_mla_workspace_bytes", "pa_mla_decode", "mla_decode", "mla_cache_shape", "pa_mla_cache_append",
-    "mla_cache_append",
+    "mla_cache_append", "pa_mla_decode_fp8", "pa_mla_cache_append_fp8",
 ]
 
 PA_OK = 0
@@ -148,6 +148,11 @@ _lib.pa_mla_decode.argtypes = [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_float, 
 _lib.pa_mla_decode.restype = _c_int
 _lib.pa_mla_cache_append.argtypes = [_vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _c_int, _vp]
 _lib.pa_mla_cache_append.restype = _c_int
+_lib.pa_mla_decode_fp8.argtypes = [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_float, _vp, _c_int, _vp, _c_int,
+                                   _c_int, _vp, _vp, _c_size, _vp]
+_lib.pa_mla_decode_fp8.restype = _c_int
+_lib.pa_mla_cache_append_fp8.argtypes = [_vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _c_int, _vp, _vp]
+_lib.pa_mla_cache_append_fp8.restype = _c_int
 
 
 class PagedAttentionError(RuntimeError):
@@ -588,18 +593,39 @@ def pa_mla_cache_append(latent_cache, rows, num_seqs, tokens_per_seq, num_blocks
                                     max_blocks_per_seq, positions, block_size, stream)
 
 
-def mla_cache_shape(num_blocks, block_size=16):
-    """Shape of the bf16 latent cache: [num_blocks, 576/8, block_size, 8]."""
-    return (num_blocks, (PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM) // 8, block_size, 8)
+def pa_mla_decode_fp8(out, query, latent_cache, num_seqs, num_heads, num_blocks, scale, block_tables,
+                      max_blocks_per_seq, seq_lens, block_size, max_seq_len, kv_scale, workspace,
+                      workspace_bytes, stream) -> int:
+    return _lib.pa_mla_decode_fp8(out, query, latent_cache, num_seqs, num_heads, num_blocks, scale, block_tables,
+                                  max_blocks_per_seq, seq_lens, block_size, max_seq_len, kv_scale, workspace,
+                                  workspace_bytes, stream)
+
+
+def pa_mla_cache_append_fp8(latent_cache, rows, num_seqs, tokens_per_seq, num_blocks, block_tables,
+                            max_blocks_per_seq, positions, block_size, kv_scale, stream) -> int:
+    return _lib.pa_mla_cache_append_fp8(latent_cache, rows, num_seqs, tokens_per_seq, num_blocks, block_tables,
+                                        max_blocks_per_seq, positions, block_size, kv_scale, stream)
+
+
+def mla_cache_shape(num_blocks, block_size=16, fp8=False):
+    """Shape of the latent cache: bf16 [num_blocks, 576/8, block_size, 8], or
+    with fp8=True uint8 e4m3fn codes [num_blocks, 576/16, block_size, 16]."""
+    x = 16 if fp8 else 8
+    return (num_blocks, (PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM) // x, block_size, x)
+
+
+_FP8_CODES = (torch.uint8, torch.float8_e4m3fn)
 
 
 def mla_decode(out, query, latent_cache, scale, block_tables, seq_lens, max_seq_len, *,
-               workspace=None) -> None:
+               workspace=None, kv_scale=1.0) -> None:
     """Latent-cache (MLA) decode: out[s,h] = sum_t softmax_t(scale*q[s,h].row_t) * row_t[:512].
 
     query bf16 [num_seqs, num_heads, 576] (absorbed query and rope query), out bf16
-    [num_seqs, num_heads, 512], latent_cache bf16 ``mla_cache_shape(num_blocks)``; block_tables
-    int32 [num_seqs, max_blocks]; seq_lens int32 [num_seqs]. Runs on the current stream.
+    [num_seqs, num_heads, 512], latent_cache bf16 ``mla_cache_shape(num_blocks)``, or uint8 /
+    float8_e4m3fn codes ``mla_cache_shape(num_blocks, fp8=True)`` whose values are code * kv_scale
+    (float or one-element float32 device tensor); block_tables int32 [num_seqs, max_blocks];
+    seq_lens int32 [num_seqs]. Runs on the current stream.
     """
     dev = query.device
     _need(dev.type == "cuda", "query must be on a GPU")
@@ -608,16 +634,17 @@ def mla_decode(out, query, latent_cache, scale, block_tables, seq_lens, max_seq_
         _need(t.device == dev, f"{name} is not on the query's device")
         _need(t.is_contiguous(), f"{name} must be contiguous")
     width = PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM
-    if query.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or latent_cache.dtype != torch.bfloat16:
-        raise TypeError("query, out and latent_cache must be bfloat16")
+    fp8 = latent_cache.dtype in _FP8_CODES
+    if query.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or not (fp8 or latent_cache.dtype == torch.bfloat16):
+        raise TypeError("query and out must be bfloat16, latent_cache bfloat16 or e4m3fn codes")
     _need(query.dim() == 3 and query.shape[2] == width, f"query must be [num_seqs, num_heads, {width}]")
     num_seqs, num_heads, _ = query.shape
     _need(tuple(out.shape) == (num_seqs, num_heads, PA_MLA_LATENT_DIM),
           f"out must be [num_seqs, num_heads, {PA_MLA_LATENT_DIM}]")
-    _need(latent_cache.dim() == 4, "latent_cache must be [num_blocks, 72, block_size, 8]")
+    _need(latent_cache.dim() == 4, "latent_cache must be [num_blocks, 576/x, block_size, x]")
     num_blocks, block_size = latent_cache.shape[0], latent_cache.shape[2]
-    _need(tuple(latent_cache.shape) == mla_cache_shape(num_blocks, block_size),
-          f"latent_cache shape {tuple(latent_cache.shape)} != {mla_cache_shape(num_blocks, block_size)}")
+    want = mla_cache_shape(num_blocks, block_size, fp8)
+    _need(tuple(latent_cache.shape) == want, f"latent_cache shape {tuple(latent_cache.shape)} != {want}")
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
           and block_tables.shape[0] == num_seqs, "block_tables must be int32 [num_seqs, max_blocks]")
     _need(seq_lens.dtype == torch.int32 and seq_lens.shape == (num_seqs,), "seq_lens must be int32 [num_seqs]")
@@ -626,9 +653,16 @@ def mla_decode(out, query, latent_cache, scale, block_tables, seq_lens, max_seq_
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = _lib.pa_mla_decode(out.data_ptr(), query.data_ptr(), latent_cache.data_ptr(), num_seqs, num_heads,
-                            num_blocks, float(scale), block_tables.data_ptr(), block_tables.shape[1],
-                            seq_lens.data_ptr(), block_size, int(max_seq_len), ws_ptr, ws_bytes, stream)
+    if fp8:
+        ks = _device_scalar(kv_scale, dev)
+        rc = _lib.pa_mla_decode_fp8(out.data_ptr(), query.data_ptr(), latent_cache.data_ptr(), num_seqs,
+                                    num_heads, num_blocks, float(scale), block_tables.data_ptr(),
+                                    block_tables.shape[1], seq_lens.data_ptr(), block_size, int(max_seq_len),
+                                    ks.data_ptr(), ws_ptr, ws_bytes, stream)
+    else:
+        rc = _lib.pa_mla_decode(out.data_ptr(), query.data_ptr(), latent_cache.data_ptr(), num_seqs, num_heads,
+                                num_blocks, float(scale), block_tables.data_ptr(), block_tables.shape[1],
+                                seq_lens.data_ptr(), block_size, int(max_seq_len), ws_ptr, ws_bytes, stream)
     _raise_for(rc, "mla_decode")
 
 
@@ -692,13 +726,14 @@ def kv_cache_append(key_cache, value_cache, key, value, block_tables, positions,
     _raise_for(rc, "kv_cache_append")
 
 
-def mla_cache_append(latent_cache, rows, block_tables, positions) -> None:
+def mla_cache_append(latent_cache, rows, block_tables, positions, kv_scale=1.0) -> None:
     """Store new tokens' latent rows [c_kv, k_rope] in the paged latent cache (in place, current stream).
 
     rows bf16 [num_seqs, 576] (one token per sequence) or [num_seqs, T, 576], contiguous; token j of
     sequence s is written at logical position positions[s] + j through block_tables (int32
     [num_seqs, max_blocks]); positions int32 [num_seqs], negative = skip. latent_cache bf16
-    ``mla_cache_shape(num_blocks)``.
+    ``mla_cache_shape(num_blocks)``, or uint8 / float8_e4m3fn ``mla_cache_shape(num_blocks, fp8=True)``
+    receiving the e4m3fn codes of row / kv_scale.
     """
     width = PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM
     dev = rows.device
@@ -707,23 +742,30 @@ def mla_cache_append(latent_cache, rows, block_tables, positions) -> None:
                     ("positions", positions)):
         _need(t.device == dev, f"{name} is not on the rows' device")
         _need(t.is_contiguous(), f"{name} must be contiguous")
-    if rows.dtype != torch.bfloat16 or latent_cache.dtype != torch.bfloat16:
-        raise TypeError("rows and latent_cache must be bfloat16")
+    fp8 = latent_cache.dtype in _FP8_CODES
+    if rows.dtype != torch.bfloat16 or not (fp8 or latent_cache.dtype == torch.bfloat16):
+        raise TypeError("rows must be bfloat16, latent_cache bfloat16 or e4m3fn codes")
     _need(rows.dim() in (2, 3) and rows.shape[-1] == width, f"rows must be [S, {width}] or [S, T, {width}]")
     num_seqs = rows.shape[0]
     tokens = 1 if rows.dim() == 2 else rows.shape[1]
-    _need(latent_cache.dim() == 4, "latent_cache must be [num_blocks, 72, 16, 8]")
+    _need(latent_cache.dim() == 4, "latent_cache must be [num_blocks, 576/x, 16, x]")
     num_blocks = latent_cache.shape[0]
-    _need(tuple(latent_cache.shape) == mla_cache_shape(num_blocks),
-          f"latent_cache shape {tuple(latent_cache.shape)} != {mla_cache_shape(num_blocks)}")
+    want = mla_cache_shape(num_blocks, 16, fp8)
+    _need(tuple(latent_cache.shape) == want, f"latent_cache shape {tuple(latent_cache.shape)} != {want}")
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
           and block_tables.shape[0] == num_seqs, "block_tables must be int32 [num_seqs, max_blocks]")
     _need(positions.dtype == torch.int32 and positions.shape == (num_seqs,),
           "positions must be int32 [num_seqs]")
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = _lib.pa_mla_cache_append(latent_cache.data_ptr(), rows.data_ptr(), num_seqs, tokens, num_blocks,
-                                  block_tables.data_ptr(), block_tables.shape[1], positions.data_ptr(), 16,
-                                  stream)
+    if fp8:
+        ks = _device_scalar(kv_scale, dev)
+        rc = _lib.pa_mla_cache_append_fp8(latent_cache.data_ptr(), rows.data_ptr(), num_seqs, tokens, num_blocks,
+                                          block_tables.data_ptr(), block_tables.shape[1], positions.data_ptr(),
+                                          16, ks.data_ptr(), stream)
+    else:
+        rc = _lib.pa_mla_cache_append(latent_cache.data_ptr(), rows.data_ptr(), num_seqs, tokens, num_blocks,
+                                      block_tables.data_ptr(), block_tables.shape[1], positions.data_ptr(), 16,
+                                      stream)
     _raise_for(rc, "mla_cache_append")
 
 

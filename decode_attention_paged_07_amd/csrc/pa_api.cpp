@@ -454,6 +454,11 @@ SharedPlan make_shared_plan(int num_seqs, int num_heads, int num_kv_heads, int h
 #ifndef PA_MLA_WAVES_PER_CU_ONE_GROUP
 #define PA_MLA_WAVES_PER_CU_ONE_GROUP 2
 #endif
+// The same for an fp8 latent cache: each wave has one 9 KiB tile in flight
+// instead of 18 KiB, so more waves keep as many bytes in flight.
+#ifndef PA_MLA_FP8_WAVES_PER_CU_ONE_GROUP
+#define PA_MLA_FP8_WAVES_PER_CU_ONE_GROUP 4
+#endif
 // Head counts from which the 32-heads-per-wave kernel (pa_mla_wide.hip) runs:
 // three or four of its waves fill a compute unit's SIMDs (its 124 KiB of LDS
 // admit one workgroup per compute unit); fewer heads fit the 16-heads-per-wave
@@ -469,7 +474,8 @@ SharedPlan make_shared_plan(int num_seqs, int num_heads, int num_kv_heads, int h
 //    one pair of 18 KiB LDS tile buffers, more groups in `chunks` workgroups
 //    per share.
 //  * 32 heads per wave (pa_mla_wide.hip): one workgroup of ceil(H / 32) waves
-//    (one per SIMD) per share and compute unit.
+//    (one per SIMD) per share and compute unit; bf16 cache only (an fp8
+//    cache runs the 16-heads-per-wave kernel at every head count).
 // Workspace: seg_out [slots][hpad][512] | seg_max [slots][hpad] |
 // seg_sum [slots][hpad] | seg_meta [S][2], slots = S + shares.
 struct MlaPlan {
@@ -479,9 +485,9 @@ struct MlaPlan {
   size_t bytes;
 };
 
-MlaPlan make_mla_plan(int num_seqs, int num_heads) {
+MlaPlan make_mla_plan(int num_seqs, int num_heads, bool fp8) {
   MlaPlan p{};
-  p.wide = num_heads >= PA_MLA_WIDE_MIN_HEADS;
+  p.wide = !fp8 && num_heads >= PA_MLA_WIDE_MIN_HEADS;
   const int cus = device_cus();
   if (p.wide) {
     p.head_groups = (num_heads + 31) / 32;
@@ -495,7 +501,8 @@ MlaPlan make_mla_plan(int num_seqs, int num_heads) {
     p.chunks = (p.head_groups + p.waves_per_wg - 1) / p.waves_per_wg;
     // Shares: the waves per compute unit of the knobs in all, a multiple of 8
     // so that the head groups of a share land on one XCD.
-    const int waves = cus * (p.head_groups == 1 ? PA_MLA_WAVES_PER_CU_ONE_GROUP : PA_MLA_WAVES_PER_CU);
+    const int one = fp8 ? PA_MLA_FP8_WAVES_PER_CU_ONE_GROUP : PA_MLA_WAVES_PER_CU_ONE_GROUP;
+    const int waves = cus * (p.head_groups == 1 ? one : PA_MLA_WAVES_PER_CU);
     const int shares = std::max(8, waves / (p.waves_per_wg * p.chunks) / 8 * 8);
     p.shares = std::min(shares, PA_MLA_MAX_WAVES / (p.waves_per_wg * p.chunks));
     p.hpad = 16 * p.head_groups;
@@ -809,9 +816,11 @@ int pa_kv_cache_append(void* key_cache, void* value_cache, const void* key, cons
   return ok();
 }
 
-int pa_mla_cache_append(void* latent_cache, const void* rows, int num_seqs, int tokens_per_seq, int num_blocks,
-                        const int32_t* block_tables, int max_blocks_per_seq, const int32_t* positions,
-                        int block_size, void* stream) {
+namespace {
+
+int mla_cache_append(void* latent_cache, const void* rows, int num_seqs, int tokens_per_seq, int num_blocks,
+                     const int32_t* block_tables, int max_blocks_per_seq, const int32_t* positions, int block_size,
+                     bool fp8, const float* kv_scale, void* stream) {
   if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
   if (tokens_per_seq < 1) return fail(PA_ERR_SHAPE, "tokens_per_seq %d must be positive", tokens_per_seq);
   if (block_size != 16) return fail(PA_ERR_SHAPE, "block_size %d is not 16", block_size);
@@ -824,10 +833,10 @@ int pa_mla_cache_append(void* latent_cache, const void* rows, int num_seqs, int 
     return fail(PA_ERR_NULL, "latent_cache, rows, block_tables and positions must be non-NULL");
   if (!aligned(latent_cache, 16) || !aligned(rows, 16))
     return fail(PA_ERR_ALIGN, "latent_cache and rows must be 16-byte aligned");
-  if (!aligned(block_tables, 4) || !aligned(positions, 4))
-    return fail(PA_ERR_ALIGN, "block_tables and positions must be 4-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(positions, 4) || (kv_scale && !aligned(kv_scale, 4)))
+    return fail(PA_ERR_ALIGN, "block_tables, positions and kv_scale must be 4-byte aligned");
   const uint64_t width = PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM;
-  const uint64_t cache_bytes = (uint64_t)num_blocks * width * block_size * 2;
+  const uint64_t cache_bytes = (uint64_t)num_blocks * width * block_size * (fp8 ? 1 : 2);
   const uint64_t rows_bytes = (uint64_t)num_seqs * tokens_per_seq * width * 2;
   const uintptr_t c0 = reinterpret_cast<uintptr_t>(latent_cache), r0 = reinterpret_cast<uintptr_t>(rows);
   if (c0 < r0 + rows_bytes && r0 < c0 + cache_bytes) return fail(PA_ERR_SHAPE, "rows overlap latent_cache");
@@ -840,6 +849,8 @@ int pa_mla_cache_append(void* latent_cache, const void* rows, int num_seqs, int 
   a.tokens_per_seq = tokens_per_seq;
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
+  a.kv_scale = fp8 ? kv_scale : nullptr;
+  a.fp8 = fp8 ? 1 : 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   std::unique_lock<std::mutex> lock(g_timing.mu);
   const bool timed = g_timing.on;
@@ -851,6 +862,22 @@ int pa_mla_cache_append(void* latent_cache, const void* rows, int num_seqs, int 
   return ok();
 }
 
+}  // namespace
+
+int pa_mla_cache_append(void* latent_cache, const void* rows, int num_seqs, int tokens_per_seq, int num_blocks,
+                        const int32_t* block_tables, int max_blocks_per_seq, const int32_t* positions,
+                        int block_size, void* stream) {
+  return mla_cache_append(latent_cache, rows, num_seqs, tokens_per_seq, num_blocks, block_tables,
+                          max_blocks_per_seq, positions, block_size, false, nullptr, stream);
+}
+
+int pa_mla_cache_append_fp8(void* latent_cache, const void* rows, int num_seqs, int tokens_per_seq,
+                            int num_blocks, const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* positions, int block_size, const float* kv_scale, void* stream) {
+  return mla_cache_append(latent_cache, rows, num_seqs, tokens_per_seq, num_blocks, block_tables,
+                          max_blocks_per_seq, positions, block_size, true, kv_scale, stream);
+}
+
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
 int pa_version(void) { return 100; }
@@ -859,14 +886,19 @@ int pa_mla_workspace_bytes(int num_seqs, int num_heads, size_t* bytes) {
   if (!bytes) return fail(PA_ERR_NULL, "bytes is NULL");
   const int rc = check_mla_plan_args(num_seqs, num_heads);
   if (rc) return rc;
-  *bytes = num_seqs == 0 ? 0 : make_mla_plan(num_seqs, num_heads).bytes;
+  // One size serves both cache types.
+  *bytes = num_seqs == 0 ? 0
+                         : std::max(make_mla_plan(num_seqs, num_heads, false).bytes,
+                                    make_mla_plan(num_seqs, num_heads, true).bytes);
   return ok();
 }
 
-int pa_mla_decode(void* out, const void* query, const void* latent_cache, int num_seqs, int num_heads,
-                  int num_blocks, float scale, const int32_t* block_tables, int max_blocks_per_seq,
-                  const int32_t* seq_lens, int block_size, int max_seq_len, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+namespace {
+
+int mla_decode(void* out, const void* query, const void* latent_cache, int num_seqs, int num_heads, int num_blocks,
+               float scale, const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_lens,
+               int block_size, int max_seq_len, bool fp8, const float* kv_scale, void* workspace,
+               size_t workspace_bytes, void* stream) {
   int rc = check_mla_plan_args(num_seqs, num_heads);
   if (rc) return rc;
   if (block_size != 16) return fail(PA_ERR_SHAPE, "block_size %d is not 16", block_size);
@@ -882,13 +914,13 @@ int pa_mla_decode(void* out, const void* query, const void* latent_cache, int nu
   if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(latent_cache, 16))
     return fail(PA_ERR_ALIGN, "out, query and latent_cache must be 16-byte aligned");
-  if (!aligned(block_tables, 4) || !aligned(seq_lens, 4))
-    return fail(PA_ERR_ALIGN, "block_tables and seq_lens must be 4-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(seq_lens, 4) || (kv_scale && !aligned(kv_scale, 4)))
+    return fail(PA_ERR_ALIGN, "block_tables, seq_lens and kv_scale must be 4-byte aligned");
   const size_t q_bytes = (size_t)num_seqs * num_heads * (PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM) * 2;
   const size_t o_bytes = (size_t)num_seqs * num_heads * PA_MLA_LATENT_DIM * 2;
   const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), q0 = reinterpret_cast<uintptr_t>(query);
   if (o0 < q0 + q_bytes && q0 < o0 + o_bytes) return fail(PA_ERR_SHAPE, "out overlaps query");
-  const MlaPlan plan = make_mla_plan(num_seqs, num_heads);
+  const MlaPlan plan = make_mla_plan(num_seqs, num_heads, fp8);
   if ((rc = check_workspace(workspace, workspace_bytes, plan.bytes))) return rc;
 
   pa::MlaArgs a{};
@@ -904,8 +936,10 @@ int pa_mla_decode(void* out, const void* query, const void* latent_cache, int nu
   d.seg_max = reinterpret_cast<float*>(ws + plan.off[1]);
   d.seg_sum = reinterpret_cast<float*>(ws + plan.off[2]);
   d.seg_meta = reinterpret_cast<int32_t*>(ws + plan.off[3]);
-  d.k_block_stride_bytes = (int64_t)(PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM) * block_size * 2;
+  d.k_block_stride_bytes = (int64_t)(PA_MLA_LATENT_DIM + PA_MLA_ROPE_DIM) * block_size * (fp8 ? 1 : 2);
   d.v_block_stride_bytes = d.k_block_stride_bytes;
+  d.k_scale = fp8 ? kv_scale : nullptr;
+  d.v_scale = d.k_scale;
   d.scale = scale;
   d.num_seqs = num_seqs;
   d.num_heads = num_heads;
@@ -922,6 +956,7 @@ int pa_mla_decode(void* out, const void* query, const void* latent_cache, int nu
   a.shares = plan.shares;
   a.hpad = plan.hpad;
   a.wide = plan.wide ? 1 : 0;
+  a.fp8 = fp8 ? 1 : 0;
   d.streamk_workgroups = a.shares * a.chunks;
 
   pa::LaunchHooks hooks;
@@ -941,6 +976,26 @@ int pa_mla_decode(void* out, const void* query, const void* latent_cache, int nu
   hipError_t err = pa::launch_mla(a, static_cast<hipStream_t>(stream), hooks);
   if (err != hipSuccess) return fail(PA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return ok();
+}
+
+}  // namespace
+
+int pa_mla_decode(void* out, const void* query, const void* latent_cache, int num_seqs, int num_heads,
+                  int num_blocks, float scale, const int32_t* block_tables, int max_blocks_per_seq,
+                  const int32_t* seq_lens, int block_size, int max_seq_len, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  return mla_decode(out, query, latent_cache, num_seqs, num_heads, num_blocks, scale, block_tables,
+                    max_blocks_per_seq, seq_lens, block_size, max_seq_len, false, nullptr, workspace,
+                    workspace_bytes, stream);
+}
+
+int pa_mla_decode_fp8(void* out, const void* query, const void* latent_cache, int num_seqs, int num_heads,
+                      int num_blocks, float scale, const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* seq_lens, int block_size, int max_seq_len, const float* kv_scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return mla_decode(out, query, latent_cache, num_seqs, num_heads, num_blocks, scale, block_tables,
+                    max_blocks_per_seq, seq_lens, block_size, max_seq_len, true, kv_scale, workspace,
+                    workspace_bytes, stream);
 }
 
 int pa_timing_enable(int on) {

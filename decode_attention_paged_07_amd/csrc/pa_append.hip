@@ -184,14 +184,17 @@ hipError_t launch_append_t(const AppendArgs& a, hipStream_t stream) {
 }
 
 // Latent rows (one compressed row [c_kv 512, k_rope 64] per token, bf16):
-// one wave per (sequence, physical block touched). Chunk c (8 elements, 16
-// bytes) of slot o sits at byte (16*c + o)*16 of the 18 KiB block, so with
-// the slot index fastest a run of n tokens is 72 contiguous stores of 16*n
-// bytes; the loads then take 16 bytes of each row per lane, n rows side by
-// side. The decode step (n = 1) reads its row contiguously and writes 72
-// pieces 256 bytes apart, which the layout fixes.
+// one wave per (sequence, physical block touched). Chunk c (8 bf16 or 16
+// fp8 codes, 16 bytes) of slot o sits at byte (16*c + o)*16 of the block
+// (18 or 9 KiB), so with the slot index fastest a run of n tokens is 72 (36)
+// contiguous stores of 16*n bytes; the loads then take one chunk's elements
+// of each row per lane, n rows side by side. The decode step (n = 1) reads
+// its row contiguously and writes pieces 256 bytes apart, which the layout
+// fixes. fp8 codes are those of the K/V append (quant_e4m3).
+template <bool FP8>
 __global__ void __launch_bounds__(64) pa_latent_append_kernel(const LatentAppendArgs a, int runs_per_seq) {
-  constexpr int kBs = 16, kChunks = 72, kRow = 1152, kBlock = kChunks * kBs * 16;
+  constexpr int kBs = 16, kRow = 1152;
+  constexpr int kChunks = FP8 ? 36 : 72, kBlock = kChunks * kBs * 16;
   const int r = (int)(blockIdx.x % (unsigned)runs_per_seq);
   const int s = (int)(blockIdx.x / (unsigned)runs_per_seq);
   const int p0 = a.positions[s];
@@ -207,9 +210,16 @@ __global__ void __launch_bounds__(64) pa_latent_append_kernel(const LatentAppend
   const int n = (int)(t_hi - t_lo);
   const char* src = reinterpret_cast<const char*>(a.rows) + ((int64_t)s * a.tokens_per_seq + (t_lo - p0)) * kRow;
   char* dst = reinterpret_cast<char*>(a.latent_cache) + (int64_t)b * kBlock + o0 * 16;
+  const float vs = (FP8 && a.kv_scale) ? *a.kv_scale : 1.f;
   for (int i = threadIdx.x; i < kChunks * n; i += 64) {
     const int c = i / n, t = i - c * n;
-    *reinterpret_cast<u32x4a*>(dst + (c * kBs + t) * 16) = *reinterpret_cast<const u32x4a*>(src + t * kRow + c * 16);
+    if constexpr (FP8) {
+      QuantPolicy<unsigned short>::k_chunk(reinterpret_cast<const unsigned short*>(src + t * kRow + c * 32),
+                                           dst + (c * kBs + t) * 16, vs);
+    } else {
+      *reinterpret_cast<u32x4a*>(dst + (c * kBs + t) * 16) =
+          *reinterpret_cast<const u32x4a*>(src + t * kRow + c * 16);
+    }
   }
 }
 
@@ -245,7 +255,10 @@ hipError_t launch_latent_append(const LatentAppendArgs& a, hipStream_t stream) {
   // As for the K/V append: T tokens touch at most floor((14 + T) / 16) + 1 blocks.
   const int runs = (14 + a.tokens_per_seq) / 16 + 1;
   const int64_t items = (int64_t)a.num_seqs * runs;
-  hipLaunchKernelGGL(pa_latent_append_kernel, dim3((unsigned)items), dim3(64), 0, stream, a, runs);
+  if (a.fp8)
+    hipLaunchKernelGGL((pa_latent_append_kernel<true>), dim3((unsigned)items), dim3(64), 0, stream, a, runs);
+  else
+    hipLaunchKernelGGL((pa_latent_append_kernel<false>), dim3((unsigned)items), dim3(64), 0, stream, a, runs);
   return hipGetLastError();
 }
 

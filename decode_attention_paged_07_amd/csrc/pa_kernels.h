@@ -156,12 +156,15 @@ struct AppendArgs {
 hipError_t launch_append(const AppendArgs& a, int in_kind, int cache_kind, hipStream_t stream);
 
 // Arguments of the latent-row append kernel (pa_append.hip): bf16 rows of
-// 576 elements into the latent cache [num_blocks][72][16][8].
+// 576 elements into the latent cache [num_blocks][72][16][8], or as e4m3fn
+// codes of row / *kv_scale into [num_blocks][36][16][16].
 struct LatentAppendArgs {
   void* latent_cache;
   const void* rows;            // [num_seqs][tokens_per_seq][576]
   const int32_t* block_tables; // [num_seqs][max_blocks_per_seq]
   const int32_t* positions;    // [num_seqs]
+  const float* kv_scale;       // fp8 only, nullable (1.0)
+  int fp8;
   int num_seqs;
   int tokens_per_seq;
   int num_blocks;
@@ -195,6 +198,7 @@ struct MlaArgs {
   int shares;         // stream-K shares (a multiple of 8 when chunks > 1)
   int hpad;           // rows per slot in the segment partials (head groups x heads per group)
   int wide;           // 1: pa_mla_wide_kernel (32 heads per wave, one workgroup per share)
+  int fp8;            // 1: e4m3fn latent cache [num_blocks][36][16][16], scale *d.k_scale (nullable: 1)
 };
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream, const LaunchHooks& hooks);

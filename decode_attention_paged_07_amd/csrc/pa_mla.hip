@@ -36,6 +36,14 @@
 // Scheduling is stream-K over (sequence, block) tiles, as for the decode
 // kernels: every share has the same number of blocks; a sequence cut by a
 // share boundary writes partials that a merge kernel combines.
+//
+// fp8 latent cache (the pages' scaled fp8 storage, §4, one scale for the
+// row): x = 16 codes per chunk, [num_blocks, 36, 16, 16], 9 KiB per block.
+// A lane's 16-byte LDS slot then holds 16 consecutive d of one token, which
+// become the A operands of two consecutive S steps after an exact e4m3 ->
+// bf16 conversion: step s covers d = 64*(s/2) + 16*q4 + 8*(s%2) + u. The
+// query is loaded in that d order, and everything after the conversion is
+// the bf16 path; the scale multiplies the logits and the output.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -57,6 +65,19 @@ constexpr int64_t kMlaBlockBytes = (int64_t)kMlaWidth * kMlaBS * 2;
 
 constexpr int kMlaTileVec = kMlaSteps * 64;            // 16-byte slots per tile (18 KiB)
 
+// 1 KiB copies per tile: 18 for bf16, 9 for fp8 codes.
+template <bool FP8>
+constexpr int kMlaSlots = FP8 ? kMlaSteps / 2 : kMlaSteps;
+template <bool FP8>
+constexpr int64_t kMlaTileBytes = (int64_t)kMlaSlots<FP8> * 1024;
+
+// d offset of element u of this lane's S step s (lane quad q4), and of the
+// first of the four rows r of output tile 2s + hf.
+template <bool FP8>
+__device__ __forceinline__ int mla_d(int s, int q4) {
+  return FP8 ? 64 * (s >> 1) + 16 * q4 + 8 * (s & 1) : 32 * s + 8 * q4;
+}
+
 // s_waitcnt immediate (gfx9 encoding) of lgkmcnt(0) alone.
 constexpr int kWaitLgkm0 = 0xC07F;
 
@@ -69,13 +90,15 @@ __device__ __forceinline__ s16x4 pack_bf16x4_pairs(f32x4 v) {
 
 // One wave's attention state for 16 query heads. The latent tiles are staged
 // in LDS by direct global->LDS loads (global_load_lds_dwordx4) in the cache
-// layout, so slot s*64 + lane holds chunk 4s + q4 of token (lane & 15), the A
-// operand of S step s for this lane.
+// layout, so slot s*64 + lane holds chunk 4s + q4 of token (lane & 15): the A
+// operand of S step s for this lane (bf16), or of steps 2s and 2s + 1 (fp8).
+template <bool FP8>
 struct MlaWave {
   bf16x8 q[kMlaSteps];
   f32x4 o[kMlaDt];
   s16x4 ident;          // B operand of the transposing product
   float m, lsum, c;
+  float vs;             // output multiplier: the fp8 scale, or 1
   int lane, q4;
   bool active;          // this lane's column is a real query head
 
@@ -84,7 +107,8 @@ struct MlaWave {
     q4 = lane >> 4;
     const int j = lane & 15;
     active = hg * 16 + j < a.d.num_heads;
-    c = a.d.scale * kLog2e;
+    vs = (FP8 && a.d.k_scale) ? *a.d.k_scale : 1.f;
+    c = a.d.scale * kLog2e * vs;
     // lane (j + 16*q4) holds I[4*q4 + u][j], u = 0..3.
     short e[4];
 #pragma unroll
@@ -93,14 +117,14 @@ struct MlaWave {
   }
 
   // q rows of heads hg*16 + column, in the d-order of the tile: step s, lane
-  // quad q4 -> d = 8*(4s + q4) + u.
+  // quad q4 -> d = mla_d(s, q4) + u.
   __device__ void load_q(const MlaArgs& a, int seq, int hg) {
     const int h = hg * 16 + (active ? (lane & 15) : 0);
     const __bf16* qh = reinterpret_cast<const __bf16*>(a.d.query) + ((int64_t)seq * a.d.num_heads + h) * kMlaWidth;
 #pragma unroll
     for (int s = 0; s < kMlaSteps; ++s) {
       u32x4 w = {0, 0, 0, 0};
-      if (active) w = *reinterpret_cast<const u32x4*>(qh + 8 * (4 * s + q4));
+      if (active) w = *reinterpret_cast<const u32x4*>(qh + mla_d<FP8>(s, q4));
       q[s] = __builtin_bit_cast(bf16x8, w);
     }
   }
@@ -164,14 +188,53 @@ struct MlaWave {
         : "memory");
   }
 
+  // The same for a tile of fp8 codes: nine slots.
+  template <int PENDING>
+  __device__ static void read_tile_fp8(const u32x4* buf, u32x4 (&k)[kMlaSteps / 2]) {
+    const uint32_t addr = (uint32_t)(uintptr_t)buf;
+    asm volatile(
+        "s_waitcnt vmcnt(%9)\n\t"
+        "ds_read_b128 %0, %10 offset:0\n\t"
+        "ds_read_b128 %1, %10 offset:1024\n\t"
+        "ds_read_b128 %2, %10 offset:2048\n\t"
+        "ds_read_b128 %3, %10 offset:3072\n\t"
+        "ds_read_b128 %4, %10 offset:4096\n\t"
+        "ds_read_b128 %5, %10 offset:5120\n\t"
+        "ds_read_b128 %6, %10 offset:6144\n\t"
+        "ds_read_b128 %7, %10 offset:7168\n\t"
+        "ds_read_b128 %8, %10 offset:8192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]),
+          "=&v"(k[7]), "=&v"(k[8])
+        : "n"(PENDING), "v"(addr + 16u * (threadIdx.x & 63))
+        : "memory");
+  }
+
   template <int PENDING>
   __device__ void consume(u32x4* buf, int nvalid) {
     const bool partial = nvalid < kMlaBS;
     u32x4 k[kMlaSteps];
-    read_tile<PENDING>(buf, k);
-    if (partial && (lane & 15) >= nvalid) {
+    if constexpr (FP8) {
+      // 16 codes (d .. d + 15 of one token) per slot -> steps 2i and 2i + 1.
+      u32x4 raw[kMlaSteps / 2];
+      read_tile_fp8<PENDING>(buf, raw);
+      if (partial && (lane & 15) >= nvalid) {
 #pragma unroll
-      for (int s = 0; s < kMlaSteps; ++s) k[s] = u32x4{0, 0, 0, 0};
+        for (int i = 0; i < kMlaSteps / 2; ++i) raw[i] = u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int i = 0; i < kMlaSteps / 2; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          k[2 * i + h] = u32x4{fp8x2_to_bf16x2<false>(raw[i][2 * h]), fp8x2_to_bf16x2<true>(raw[i][2 * h]),
+                               fp8x2_to_bf16x2<false>(raw[i][2 * h + 1]), fp8x2_to_bf16x2<true>(raw[i][2 * h + 1])};
+      }
+    } else {
+      read_tile<PENDING>(buf, k);
+      if (partial && (lane & 15) >= nvalid) {
+#pragma unroll
+        for (int s = 0; s < kMlaSteps; ++s) k[s] = u32x4{0, 0, 0, 0};
+      }
     }
     f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};   // two chains in flight
 #pragma unroll
@@ -218,17 +281,17 @@ struct MlaWave {
 
   __device__ void finish() { lsum = quad_sum(lsum); }
 
-  // o / lsum for this lane's head. Tile 2s + hf row 4*q4 + r is
-  // d = 32s + 8*q4 + 4*hf + r: four consecutive d per tile.
+  // o * vs / lsum for this lane's head. Tile 2s + hf row 4*q4 + r is
+  // d = mla_d(s, q4) + 4*hf + r: four consecutive d per tile.
   template <typename T>
   __device__ void store_rows(T* row_base, int64_t row_stride) const {
     if (!active) return;
-    T* dst = row_base + (int64_t)(lane & 15) * row_stride + 8 * q4;
-    const float f = 1.f / lsum;
+    T* dst = row_base + (int64_t)(lane & 15) * row_stride;
+    const float f = vs / lsum;
 #pragma unroll
     for (int s = 0; s < kMlaVSteps; ++s)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) store4(dst + 32 * s + 4 * hf, o[2 * s + hf] * f);
+      for (int hf = 0; hf < 2; ++hf) store4(dst + mla_d<FP8>(s, q4) + 4 * hf, o[2 * s + hf] * f);
   }
 };
 
@@ -240,10 +303,11 @@ struct MlaWave {
 // With W > 1 each block starts with a barrier: each wave first waits for its
 // own copies, so after it the tile is complete in LDS, and every wave is
 // past the previous block, whose buffer the next copy overwrites.
-template <int W, int WAVE>
+template <int W, int WAVE, bool FP8>
 __device__ __forceinline__ void mla_share(const MlaArgs& a, int share, int hg, int seq, int blk, int64_t units,
                                           u32x4* __restrict__ buf0, u32x4* __restrict__ buf1) {
-  constexpr int kS0 = kMlaSteps * WAVE / W, kS1 = kMlaSteps * (WAVE + 1) / W;
+  constexpr int kSlots = kMlaSlots<FP8>;
+  constexpr int kS0 = kSlots * WAVE / W, kS1 = kSlots * (WAVE + 1) / W;
   const DecodeArgs& d = a.d;
   const int S = d.num_seqs;
   const unsigned top = (unsigned)(d.num_blocks - 1);
@@ -260,7 +324,7 @@ __device__ __forceinline__ void mla_share(const MlaArgs& a, int share, int hg, i
     return g;
   };
 
-  MlaWave wv;
+  MlaWave<FP8> wv;
   wv.init(a, hg);
   const int lane = wv.lane;
   Seg cur = make_seg(seq, blk, units);
@@ -293,7 +357,7 @@ __device__ __forceinline__ void mla_share(const MlaArgs& a, int share, int hg, i
   auto stage_block = [&](unsigned phys, u32x4* buf) {
     phys = phys < top ? phys : top;
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // earlier LDS reads of buf are complete
-    wv.template stage<kS0, kS1>(base + (int64_t)phys * kMlaBlockBytes, buf);
+    wv.template stage<kS0, kS1>(base + (int64_t)phys * kMlaTileBytes<FP8>, buf);
   };
   auto stage_cur = [&](int g, u32x4* buf) {
     if (g - chunk >= 64) {
@@ -369,9 +433,10 @@ __device__ __forceinline__ void mla_share(const MlaArgs& a, int share, int hg, i
 // apart: the same XCD under the round-robin dispatch of workgroups to the
 // eight XCDs. A wave past the last head group runs with no active lane (it
 // still copies its slots and meets the barriers).
-template <int W>
+template <int W, bool FP8>
 __global__ void __launch_bounds__(64 * W) pa_mla_streamk_kernel(const MlaArgs a) {
-  __shared__ u32x4 tiles0[kMlaTileVec], tiles1[kMlaTileVec];   // two 18 KiB tile buffers
+  // two tile buffers: 18 KiB each (bf16), 9 KiB (fp8)
+  __shared__ u32x4 tiles0[kMlaSlots<FP8> * 64], tiles1[kMlaSlots<FP8> * 64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = blockIdx.x;
@@ -391,10 +456,10 @@ __global__ void __launch_bounds__(64 * W) pa_mla_streamk_kernel(const MlaArgs a)
   locate_block<kMlaBS>(a.d, lane, (int)u0, bsum, seq, blk);
   // Each wave runs its own instantiation (its copy slots); all meet the same barriers.
   switch (wave) {
-    case 0: mla_share<W, 0>(a, share, hg, seq, blk, u1 - u0, tiles0, tiles1); break;
-    case 1: if constexpr (W > 1) mla_share<W, 1 % W>(a, share, hg, seq, blk, u1 - u0, tiles0, tiles1); break;
-    case 2: if constexpr (W > 2) mla_share<W, 2 % W>(a, share, hg, seq, blk, u1 - u0, tiles0, tiles1); break;
-    default: if constexpr (W > 3) mla_share<W, 3 % W>(a, share, hg, seq, blk, u1 - u0, tiles0, tiles1); break;
+    case 0: mla_share<W, 0, FP8>(a, share, hg, seq, blk, u1 - u0, tiles0, tiles1); break;
+    case 1: if constexpr (W > 1) mla_share<W, 1 % W, FP8>(a, share, hg, seq, blk, u1 - u0, tiles0, tiles1); break;
+    case 2: if constexpr (W > 2) mla_share<W, 2 % W, FP8>(a, share, hg, seq, blk, u1 - u0, tiles0, tiles1); break;
+    default: if constexpr (W > 3) mla_share<W, 3 % W, FP8>(a, share, hg, seq, blk, u1 - u0, tiles0, tiles1); break;
   }
 }
 
@@ -480,14 +545,20 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t stream, const LaunchHooks& h
   if (hooks.before_partition) hooks.before_partition(stream);
   hipError_t err = hipSuccess;
   if (a.wide) {
+    if (a.fp8) return hipErrorInvalidValue;   // the wide kernel reads bf16 tiles only
     err = launch_mla_wide(a, stream);
   } else {
     const dim3 grid(a.shares * a.chunks);
-    switch (a.waves_per_wg) {
-      case 1: hipLaunchKernelGGL(pa_mla_streamk_kernel<1>, grid, dim3(64), 0, stream, a); break;
-      case 2: hipLaunchKernelGGL(pa_mla_streamk_kernel<2>, grid, dim3(128), 0, stream, a); break;
-      case 3: hipLaunchKernelGGL(pa_mla_streamk_kernel<3>, grid, dim3(192), 0, stream, a); break;
-      case 4: hipLaunchKernelGGL(pa_mla_streamk_kernel<4>, grid, dim3(256), 0, stream, a); break;
+    const int key = a.waves_per_wg * 2 + (a.fp8 ? 1 : 0);
+    switch (key) {
+      case 2: hipLaunchKernelGGL((pa_mla_streamk_kernel<1, false>), grid, dim3(64), 0, stream, a); break;
+      case 4: hipLaunchKernelGGL((pa_mla_streamk_kernel<2, false>), grid, dim3(128), 0, stream, a); break;
+      case 6: hipLaunchKernelGGL((pa_mla_streamk_kernel<3, false>), grid, dim3(192), 0, stream, a); break;
+      case 8: hipLaunchKernelGGL((pa_mla_streamk_kernel<4, false>), grid, dim3(256), 0, stream, a); break;
+      case 3: hipLaunchKernelGGL((pa_mla_streamk_kernel<1, true>), grid, dim3(64), 0, stream, a); break;
+      case 5: hipLaunchKernelGGL((pa_mla_streamk_kernel<2, true>), grid, dim3(128), 0, stream, a); break;
+      case 7: hipLaunchKernelGGL((pa_mla_streamk_kernel<3, true>), grid, dim3(192), 0, stream, a); break;
+      case 9: hipLaunchKernelGGL((pa_mla_streamk_kernel<4, true>), grid, dim3(256), 0, stream, a); break;
       default: return hipErrorInvalidValue;
     }
     err = hipGetLastError();

@@ -377,6 +377,25 @@ int pa_mla_decode(void* out, const void* query, const void* latent_cache, int nu
                   size_t workspace_bytes, void* stream);
 
 /*
+ * pa_mla_decode over an fp8 latent cache: the pages' scaled fp8 storage
+ * (10100.com retirement article, §4) applied to the latent row, with one
+ * per-tensor scale because the row is both key and value. Element e of a
+ * token's row stands for e4m3fn(code) * *kv_scale, and the call computes
+ * pa_mla_decode's formula over those values.
+ *   latent_cache device, uint8 E4M3FN codes [num_blocks][576/16][16][16]
+ *                (the pages' K layout with one kv head and x = 16), 16-B
+ *                aligned.
+ *   kv_scale     device fp32 scalar (NULL = 1.0), 4-B aligned.
+ * Every other argument, the workspace size (pa_mla_workspace_bytes serves
+ * both calls) and the errors as for pa_mla_decode. Every head count runs
+ * the 16-heads-per-wave kernel (several workgroups per share from 65 heads).
+ */
+int pa_mla_decode_fp8(void* out, const void* query, const void* latent_cache, int num_seqs, int num_heads,
+                      int num_blocks, float scale, const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* seq_lens, int block_size, int max_seq_len, const float* kv_scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Latent-cache append: store the latent rows [c_kv, k_rope] of new tokens in
  * the paged latent cache, the step before pa_mla_decode in every decode
  * iteration (the cache grows one token per step; "vLLM 0.25.0 解读" §1; one
@@ -404,6 +423,19 @@ int pa_mla_decode(void* out, const void* query, const void* latent_cache, int nu
 int pa_mla_cache_append(void* latent_cache, const void* rows, int num_seqs, int tokens_per_seq, int num_blocks,
                         const int32_t* block_tables, int max_blocks_per_seq, const int32_t* positions,
                         int block_size, void* stream);
+
+/*
+ * pa_mla_cache_append into an fp8 latent cache (pa_mla_decode_fp8's layout,
+ * uint8 [num_blocks][36][16][16]): each element of the bf16 rows is stored
+ * as the E4M3FN code nearest to value / *kv_scale (float32 quotient, ties to
+ * even, magnitude saturated at 448, NaN -> 0x7F, sign kept), the inverse of
+ * the decode's dequantisation (10100.com article, §4). kv_scale: device fp32
+ * scalar, NULL = 1.0, 4-B aligned. Everything else as for
+ * pa_mla_cache_append.
+ */
+int pa_mla_cache_append_fp8(void* latent_cache, const void* rows, int num_seqs, int tokens_per_seq,
+                            int num_blocks, const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* positions, int block_size, const float* kv_scale, void* stream);
 
 /* Text describing the last error returned on the calling thread ("" if none). */
 const char* pa_last_error(void);

@@ -91,3 +91,44 @@ def test_tensor_append_refuses_cpu_tensors(pa):  # noqa: F811
     rows = torch.zeros(2, 576, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         pa.mla_cache_append(cache, rows, torch.zeros(2, 1, dtype=torch.int32), torch.zeros(2, dtype=torch.int32))
+
+
+def call_fp8(pa, **over):
+    args = dict(out=A, query=2 * A, latent=3 * A, S=4, H=16, nb=64, scale=0.1, table=4 * A, mb=8,
+                lens=5 * A, bs=16, msl=128, ks=7 * A, ws=6 * A, wsb=1 << 40, stream=None)
+    args.update(over)
+    return pa.pa_mla_decode_fp8(args["out"], args["query"], args["latent"], args["S"], args["H"], args["nb"],
+                                args["scale"], args["table"], args["mb"], args["lens"], args["bs"], args["msl"],
+                                args["ks"], args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(H=0), -2), (dict(H=129), -2), (dict(bs=32), -2), (dict(msl=129), -2), (dict(latent=None), -1),
+    (dict(latent=A + 8), -5), (dict(ks=7 * A + 2), -5), (dict(ws=None), -4), (dict(out=2 * A + 64), -2),
+])
+def test_fp8_decode_validation_rejects(pa, over, code):  # noqa: F811
+    assert call_fp8(pa, **over) == code
+    assert pa.pa_last_error()
+
+
+def test_fp8_decode_zero_sequences_is_a_noop(pa):  # noqa: F811
+    assert call_fp8(pa, S=0, out=None, query=None, latent=None, table=None, lens=None, ws=None, wsb=0) == 0
+
+
+def test_fp8_append_validation(pa):  # noqa: F811
+    a = dict(APPEND)
+    f = pa.pa_mla_cache_append_fp8
+    args = [a["latent"], a["rows"], a["S"], a["T"], a["nb"], a["table"], a["mb"], a["pos"], a["bs"], 8 * A, None]
+    bad = list(args)
+    bad[9] = 8 * A + 2
+    assert f(*bad) == -5
+    bad = list(args)
+    bad[8] = 32
+    assert f(*bad) == -2
+    bad = list(args)
+    bad[1] = A + 64 * 9216 - 16          # rows start inside the (9 KiB-block) cache
+    assert f(*bad) == -2
+    bad = list(args)
+    bad[1] = A + 64 * 9216               # just past it: accepted by the overlap check, rejected nowhere else
+    bad[0] = None
+    assert f(*bad) == -1

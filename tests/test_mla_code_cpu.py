@@ -84,8 +84,10 @@ def read_groups(asm, op):
 @pytest.mark.skipif(not os.path.exists(OBJDUMP), reason="llvm-objdump not installed")
 @pytest.mark.parametrize("op", ["ds_read_b128"])
 def test_tile_reads_never_overwrite_their_address(lib_path, op):
-    groups = [g for g in read_groups(mla_kernel_asm(lib_path), op) if len(g) >= 16]
-    assert groups, f"expected asm groups of 16 or more {op}"
+    # 18 reads per bf16 tile, 9 per fp8 tile
+    groups = [g for g in read_groups(mla_kernel_asm(lib_path), op) if len(g) >= 9]
+    assert sum(len(g) >= 16 for g in groups) and sum(len(g) == 9 for g in groups), \
+        f"expected asm groups of 18 and of 9 {op}"
     for g in groups:
         for i, (lo, hi, _) in enumerate(g):
             later = {a for _, _, a in g[i + 1:]}
@@ -94,7 +96,7 @@ def test_tile_reads_never_overwrite_their_address(lib_path, op):
 
 def test_persistent_grid_is_resident(lib_path):
     k = {name: r for name, r in bench.code_object_kernels(lib_path).items() if "pa_mla_streamk_kernel" in name}
-    assert len(k) == 4                  # one to four head-group waves per workgroup
+    assert len(k) == 8                  # one to four head-group waves per workgroup, bf16 and fp8 cache
     for res in k.values():
         check_resident(res)
 
@@ -123,7 +125,7 @@ def check_resident(res):
     # worst case: one-wave workgroups, each with its own tile buffers
     csrc = os.path.join(ROOT, "decode_attention_paged_07_amd", "csrc")
     knobs = open(os.path.join(csrc, "pa_kernels.h")).read() + open(os.path.join(csrc, "pa_api.cpp")).read()
-    waves_per_cu = max(int(x) for x in re.findall(r"#define PA_MLA_WAVES_PER_CU\w* (\d+)", knobs))
+    waves_per_cu = max(int(x) for x in re.findall(r"#define PA_MLA_(?:FP8_)?WAVES_PER_CU\w* (\d+)", knobs))
     assert waves_per_cu * res["lds"] <= LDS_PER_CU
     per_simd = math_ceil_div(waves_per_cu, 4)
     assert per_simd * (res["alloc"] or res["vgpr"]) <= REGISTERS_PER_SIMD_LANE

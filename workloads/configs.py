@@ -85,4 +85,7 @@ EXTRA_CONFIGS = {c.name: c for c in (SHARED, GQA32, FP8C)}
 MLA = DecodeConfig("mla", 256, 16, 1, 576, 16, 128 * 1024, "bf16", "auto",
                    ("uniform", 1, 8192), False, 6)
 MLA128 = MLA.with_(name="mla128", num_heads=128, seed=7)
-MLA_CONFIGS = {c.name: c for c in (MLA, MLA128)}
+# The same with the latent rows stored as fp8 e4m3 codes and one scale.
+MLA_FP8 = MLA.with_(name="mla_fp8", kv_dtype="fp8_e4m3", seed=8)
+MLA128_FP8 = MLA128.with_(name="mla128_fp8", kv_dtype="fp8_e4m3", seed=9)
+MLA_CONFIGS = {c.name: c for c in (MLA, MLA128, MLA_FP8, MLA128_FP8)}

@@ -338,10 +338,11 @@ class MlaCase:
     cfg: DecodeConfig
     meta: Metadata
     query: torch.Tensor           # bf16 [S, H, 576]
-    latent_cache: torch.Tensor    # bf16 [NB, 72, bs, 8]
+    latent_cache: torch.Tensor    # bf16 [NB, 72, bs, 8], or uint8 e4m3fn codes [NB, 36, bs, 16]
     block_tables: torch.Tensor
     seq_lens: torch.Tensor
     scale: float
+    kv_scale: float = 1.0         # fp8 cache: value = code * kv_scale
 
     @property
     def max_seq_len(self) -> int:
@@ -354,7 +355,9 @@ def make_mla_case(cfg: DecodeConfig, seed: int | None = None, device="cpu", *, s
     """One MLA workload instance; poison=True writes NaN into every pool slot
     no valid token uses and points unused table entries at a NaN block.
     share_prefix_blocks > 0 maps the first blocks of every long enough
-    sequence to sequence 0's physical blocks (read-only sharing)."""
+    sequence to sequence 0's physical blocks (read-only sharing). With
+    cfg.kv_dtype "fp8_e4m3" the N(0,1) rows are stored as e4m3fn codes of
+    value / s, s = amax / 448 over the pool (the fp8 workloads' recipe)."""
     seed = cfg.seed if seed is None else seed
     if num_heads is not None:
         cfg = cfg.with_(num_heads=num_heads)
@@ -364,7 +367,15 @@ def make_mla_case(cfg: DecodeConfig, seed: int | None = None, device="cpu", *, s
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
     query = _randn((cfg.num_seqs, cfg.num_heads, width), gen, device).to(torch.bfloat16)
-    pool = _fill_pool((cfg.pool_blocks, width // 8, cfg.block_size, 8), torch.bfloat16, gen, device)
+    fp8 = cfg.kv_dtype == "fp8_e4m3"
+    kv_scale = 1.0
+    if fp8:
+        pool = _fill_pool((cfg.pool_blocks, width // 16, cfg.block_size, 16), torch.float32, gen, device)
+        kv_scale = float(pool.abs().max()) / 448.0
+        pool = _quantise_e4m3(pool, kv_scale)
+    else:
+        pool = _fill_pool((cfg.pool_blocks, width // 8, cfg.block_size, 8), torch.bfloat16, gen, device)
+    nan = FP8_NAN_CODE if fp8 else float("nan")
     table = meta.block_tables.copy()
     if poison:
         used = np.zeros(cfg.pool_blocks, dtype=bool)
@@ -372,18 +383,18 @@ def make_mla_case(cfg: DecodeConfig, seed: int | None = None, device="cpu", *, s
         unused = np.flatnonzero(~used)
         if unused.size == 0:
             raise ValueError("poison needs at least one unused pool block")
-        pool.index_fill_(0, torch.from_numpy(unused).to(pool.device), float("nan"))
+        pool.index_fill_(0, torch.from_numpy(unused).to(pool.device), nan)
         bs = cfg.block_size
         for s in range(cfg.num_seqs):
             n = int(meta.seq_lens[s])
             nblk = -(-n // bs)
             table[s, nblk:] = int(unused[0])
             if nblk and n % bs:
-                pool[int(table[s, nblk - 1]), :, n % bs:, :] = float("nan")
+                pool[int(table[s, nblk - 1]), :, n % bs:, :] = nan
     return MlaCase(cfg=cfg, meta=meta, query=query, latent_cache=pool,
                    block_tables=torch.from_numpy(table).to(device),
                    seq_lens=torch.from_numpy(meta.seq_lens).to(device),
-                   scale=1.0 / math.sqrt(128 + 64))
+                   scale=1.0 / math.sqrt(128 + 64), kv_scale=kv_scale)
 
 
 def mla_host_arrays(case: MlaCase, seqs=None) -> dict:
@@ -411,4 +422,6 @@ def mla_host_arrays(case: MlaCase, seqs=None) -> dict:
         "block_tables": new_table.astype(np.int32),
         "seq_lens": lens.astype(np.int32),
         "scale": case.scale,
+        "kv_kind": "e4m3fn" if case.cfg.kv_dtype == "fp8_e4m3" else "bf16",
+        "kv_scale": case.kv_scale,
     }
