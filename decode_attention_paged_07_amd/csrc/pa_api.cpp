@@ -466,6 +466,7 @@ SharedPlan make_shared_plan(int num_seqs, int num_heads, int num_kv_heads, int h
 #ifndef PA_MLA_WIDE_MIN_HEADS
 #define PA_MLA_WIDE_MIN_HEADS 65
 #endif
+static_assert(PA_MLA_WIDE_MIN_HEADS > 64, "the 32-heads-per-wave kernel is built for three or four waves");
 
 // Stream-K plan of the MLA kernels.
 //  * 16 heads per wave (pa_mla.hip; fewer than PA_MLA_WIDE_MIN_HEADS heads):
@@ -474,8 +475,7 @@ SharedPlan make_shared_plan(int num_seqs, int num_heads, int num_kv_heads, int h
 //    one pair of 18 KiB LDS tile buffers, more groups in `chunks` workgroups
 //    per share.
 //  * 32 heads per wave (pa_mla_wide.hip): one workgroup of ceil(H / 32) waves
-//    (one per SIMD) per share and compute unit; bf16 cache only (an fp8
-//    cache runs the 16-heads-per-wave kernel at every head count).
+//    (one per SIMD) per share and compute unit.
 // Workspace: seg_out [slots][hpad][512] | seg_max [slots][hpad] |
 // seg_sum [slots][hpad] | seg_meta [S][2], slots = S + shares.
 struct MlaPlan {
@@ -487,7 +487,7 @@ struct MlaPlan {
 
 MlaPlan make_mla_plan(int num_seqs, int num_heads, bool fp8) {
   MlaPlan p{};
-  p.wide = !fp8 && num_heads >= PA_MLA_WIDE_MIN_HEADS;
+  p.wide = num_heads >= PA_MLA_WIDE_MIN_HEADS;
   const int cus = device_cus();
   if (p.wide) {
     p.head_groups = (num_heads + 31) / 32;

@@ -545,7 +545,6 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t stream, const LaunchHooks& h
   if (hooks.before_partition) hooks.before_partition(stream);
   hipError_t err = hipSuccess;
   if (a.wide) {
-    if (a.fp8) return hipErrorInvalidValue;   // the wide kernel reads bf16 tiles only
     err = launch_mla_wide(a, stream);
   } else {
     const dim3 grid(a.shares * a.chunks);

@@ -35,6 +35,14 @@
 // Scheduling is the decode kernels' stream-K over (sequence, tile) units: every
 // workgroup takes an equal share; a sequence cut by a share boundary writes
 // partials that pa_mla_reduce_kernel combines.
+//
+// fp8 latent cache (the pages' scaled fp8 storage, §4, one scale for the row;
+// [num_blocks, 36, 16, 16] codes): each wave copies its part of the next tile
+// (18 KiB of codes) into an LDS staging buffer, and once the current tile is
+// computed converts that same part, exactly, into the bf16 tile layout above
+// in the other tile buffer. The barrier that opens the next step then makes
+// the converted tile whole for every wave, and the arithmetic is the bf16
+// path's; the scale multiplies the logits and the output.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -62,6 +70,9 @@ constexpr int kDt = kLatent / 32;                            // 32-d output tile
 constexpr int kBlockBytes = kWidth * kBS * 2;                // 18 KiB
 constexpr int kBlockVec = kBlockBytes / 16;
 constexpr int kCopySlots = 2 * kBlockBytes / 1024;           // 1 KiB copy instructions per tile
+constexpr int kFpBlockBytes = kWidth * kBS;                  // 9 KiB: a block of fp8 codes
+constexpr int kFpBlockVec = kFpBlockBytes / 16;
+constexpr int kFpSlots = 2 * kFpBlockBytes / 1024;           // 1 KiB copies per fp8 tile
 // Fourth word of a raw buffer resource on this GPU family (byte offsets,
 // 32-bit data format; out-of-range offsets read zero).
 constexpr int kRsrcWord3 = 0x00020000;
@@ -92,6 +103,12 @@ __shared__ f32x4 mla_wide_stage[4 * 4 * 64];
 template <int B>
 __device__ __forceinline__ u32x4* tile_buf() {
   return B == 0 ? mla_wide_tile0 : B == 1 ? mla_wide_tile1 : mla_wide_tile2;
+}
+// With an fp8 cache, tile buffers 0 and 1 hold converted tiles and the third
+// holds two 18 KiB staging buffers for the codes.
+template <int F>
+__device__ __forceinline__ u32x4* code_buf() {
+  return mla_wide_tile2 + F * (2 * kFpBlockVec);
 }
 
 // LDS layout of a cache block: chunk c (eight d of 16 tokens, 256 bytes) keeps
@@ -147,10 +164,12 @@ __device__ __forceinline__ float pair_reduce(float v, Op op) {
   return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+template <bool FP8>
 struct WideWave {
   bf16x8 q[kSteps];   // B operand of S: head i, d = 16 s + 8 h + e
   f32x16 o[kDt];      // O[32 dt + 8(v/4) + 4h + v%4][head i]
   float m, lsum, c;
+  float vs;           // fp8: the cache's scale (output multiplier)
   int lane, half, wave;
   bool active;        // this lane's head exists
   uint32_t k_off[2];  // byte offset of this lane's S operand in a tile buffer, even / odd steps (step 0 / 1 less 512 B)
@@ -162,7 +181,8 @@ struct WideWave {
     wave = hg;
     const int i = lane & 31;
     active = hg * 32 + i < a.d.num_heads;
-    c = a.d.scale * kLog2e;
+    vs = (FP8 && a.d.k_scale) ? *a.d.k_scale : 1.f;
+    c = a.d.scale * kLog2e * (FP8 ? vs : 1.f);
     // S operand: token i (block i / 16), chunk 2 s + h, in its swizzled slot.
     const int t = i & 15;
     k_off[0] = (uint32_t)((i >> 4) * kBlockBytes + half * 256 + slot_of(half, t) * 16);
@@ -339,7 +359,7 @@ struct WideWave {
     // (a rare path) rather than hoisted into registers the loop needs.
     asm volatile("" : "+v"(c), "+v"(r));
     const int src = (c >> 1) * 64 + (c & 1) * 32 + r;   // slot of chunk c of head r
-    const float f = 1.f / lsum;
+    const float f = (FP8 ? vs : 1.f) / lsum;
     float fk[4];   // 1 / lsum of head 8 k + r
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -363,63 +383,48 @@ struct WideWave {
   }
 };
 
-// A workgroup's share: tiles [u0, u0 + units) in (sequence, tile) order, one
-// pipeline across the sequences it spans. Wave WAVE of W copies slots
-// [36 WAVE / W, 36 (WAVE + 1) / W) of every tile (slot s: 1 KiB s % 18 of the
-// tile's block s / 18; a tile with one block copies that block twice, so that
-// every tile costs each wave the same number of copy instructions).
-//
-// Two cursors walk the share: the staging cursor, two tiles ahead, and the
-// compute cursor. Step k (tile k of the share, in buffer k % 3) opens with a
-// barrier behind which every wave's copies of tile k have landed and every
-// wave is done with tile k - 1; it then starts the copy of tile k + 2 into
-// tile k - 1's buffer and computes tile k. Two tiles' copies are thus in flight
-// while one is computed.
-template <int W, int WAVE>
-__device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq, int tile, int units) {
-  constexpr int kS0 = kCopySlots * WAVE / W, kS1 = kCopySlots * (WAVE + 1) / W;
-  constexpr int kCopies = kS1 - kS0;   // copy instructions per tile of this wave
-  // Descriptor bits of a staged tile besides its valid-token count (1..32).
-  constexpr int kLast = 64, kFirstOfSeq = 128, kLastOfSeq = 256;
-  const DecodeArgs& d = a.d;
-  const int S = d.num_seqs;
-  const unsigned top = (unsigned)(d.num_blocks - 1);
-  const int hg = WAVE;
-
-  WideWave wv;
-  wv.init(a, hg);
-  const int lane = wv.lane;
-  const char* cache = reinterpret_cast<const char*>(d.key_cache);
-
-  // Staging cursor: tile st of sequence sseq (L tokens) is the next to copy;
-  // its segment of the share ends before tile st1; sleft tiles of the share
-  // follow that segment. Sequence lengths and table entries are read through
-  // the scalar cache (uniform loads; waiting for them never waits for copies).
-  int sseq = seq, st = tile, L = clamp_len(ld_uniform(d.seq_lens, seq), d.max_seq_len);
-  int st1 = min(blocks_of<kTileTok>(L), tile + units);
-  int sleft = units - (st1 - tile);
-  int sflags = (tile == 0 ? kFirstOfSeq : 0) | (st1 == blocks_of<kTileTok>(L) ? kLastOfSeq : 0);
-  bool sdone = false;
-  // Descriptor of the tile in each buffer: its sequence, and its token count
-  // with the kLast / kFirstOfSeq / kLastOfSeq bits.
+// Staging cursor of a share: tile st of sequence sseq (L tokens) is the next
+// to copy; its segment of the share ends before tile st1; sleft tiles of the
+// share follow that segment. Sequence lengths and table entries are read
+// through the scalar cache (uniform loads; waiting for them never waits for
+// copies). Each buffer's tile has a descriptor: its sequence, and its token
+// count (1..32) with the kLast / kFirstOfSeq / kLastOfSeq bits.
+struct ShareCursor {
+  static constexpr int kLast = 64, kFirstOfSeq = 128, kLastOfSeq = 256;
+  const DecodeArgs& d;
+  int S;
+  unsigned top;
+  int sseq, st, L, st1, sleft, sflags;
+  bool sdone;
   int dseq[3], dinf[3];
+  // The table entries of the cursor's tile, read one step ahead (fetch), so
+  // that their latency passes under a step's work instead of holding up its
+  // copies.
+  unsigned np0, np1;
 
-  // Takes the staging cursor's tile for buffer B: records its descriptor,
-  // sets its physical blocks (p1 = p0 when it has one block) and advances the
-  // cursor; false when the share has no tile left.
-  //
-  // The table entries of the cursor's tile are read one step ahead (np0,
-  // np1), so that their latency passes under a step's work instead of
-  // holding up its copies.
-  unsigned np0 = 0, np1 = 0;
-  auto fetch = [&]() {
+  __device__ __forceinline__ ShareCursor(const DecodeArgs& args, int seq, int tile, int units)
+      : d(args), S(args.num_seqs), top((unsigned)(args.num_blocks - 1)) {
+    sseq = seq;
+    st = tile;
+    L = clamp_len(ld_uniform(d.seq_lens, seq), d.max_seq_len);
+    st1 = min(blocks_of<kTileTok>(L), tile + units);
+    sleft = units - (st1 - tile);
+    sflags = (tile == 0 ? kFirstOfSeq : 0) | (st1 == blocks_of<kTileTok>(L) ? kLastOfSeq : 0);
+    sdone = false;
+    np0 = np1 = 0;
+  }
+
+  __device__ __forceinline__ void fetch() {
     const int64_t e = (int64_t)sseq * d.max_blocks_per_seq + 2 * st;
     np0 = (unsigned)ld_uniform(d.block_tables, e);
     np1 = (unsigned)ld_uniform(d.block_tables, e + (2 * st + 1 < blocks_of<kBS>(L) ? 1 : 0));
-  };
-  fetch();
-  auto take = [&](auto bsel, unsigned& p0, unsigned& p1) -> bool {
-    constexpr int B = decltype(bsel)::value;
+  }
+
+  // Takes the cursor's tile for buffer B: records its descriptor, sets its
+  // physical blocks (p1 = p0 when it has one block) and advances the cursor;
+  // false when the share has no tile left.
+  template <int B>
+  __device__ __forceinline__ bool take(unsigned& p0, unsigned& p1) {
     if (sdone) return false;
     p0 = np0 < top ? np0 : top;
     p1 = np1 < top ? np1 : top;
@@ -447,7 +452,37 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
       }
     }
     return true;
-  };
+  }
+};
+
+// A workgroup's share: tiles [u0, u0 + units) in (sequence, tile) order, one
+// pipeline across the sequences it spans. Wave WAVE of W copies slots
+// [36 WAVE / W, 36 (WAVE + 1) / W) of every tile (slot s: 1 KiB s % 18 of the
+// tile's block s / 18; a tile with one block copies that block twice, so that
+// every tile costs each wave the same number of copy instructions).
+//
+// Two cursors walk the share: the staging cursor, two tiles ahead, and the
+// compute cursor. Step k (tile k of the share, in buffer k % 3) opens with a
+// barrier behind which every wave's copies of tile k have landed and every
+// wave is done with tile k - 1; it then starts the copy of tile k + 2 into
+// tile k - 1's buffer and computes tile k. Two tiles' copies are thus in flight
+// while one is computed.
+template <int W, int WAVE>
+__device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq, int tile, int units) {
+  constexpr int kS0 = kCopySlots * WAVE / W, kS1 = kCopySlots * (WAVE + 1) / W;
+  constexpr int kCopies = kS1 - kS0;   // copy instructions per tile of this wave
+  const DecodeArgs& d = a.d;
+  const int hg = WAVE;
+
+  WideWave<false> wv;
+  wv.init(a, hg);
+  const int lane = wv.lane;
+  const char* cache = reinterpret_cast<const char*>(d.key_cache);
+
+  ShareCursor cur(d, seq, tile, units);
+  cur.fetch();
+  constexpr int kLast = ShareCursor::kLast, kFirstOfSeq = ShareCursor::kFirstOfSeq,
+                kLastOfSeq = ShareCursor::kLastOfSeq;
   // Byte address of copy slot s of the tile with blocks p0, p1, and its LDS slot.
   auto slot_src = [&](int s, unsigned p0, unsigned p1) {
     const int blk = s / (kCopySlots / 2), part = s % (kCopySlots / 2);
@@ -465,7 +500,7 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
   // and the reads issued ahead of the products would buy nothing.
   auto stage = [&](auto bsel) -> bool {
     unsigned p0, p1;
-    if (!take(bsel, p0, p1)) return false;
+    if (!cur.template take<decltype(bsel)::value>(p0, p1)) return false;
     const __amdgpu_buffer_rsrc_t r0 =
         __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (int64_t)p0 * kBlockBytes), 0, kBlockBytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t r1 =
@@ -484,7 +519,7 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
   // otherwise make one of the loop's steps wait for every copy in flight.
   auto stage_through_registers = [&](auto bsel) -> bool {
     unsigned p0, p1;
-    if (!take(bsel, p0, p1)) return false;
+    if (!cur.template take<decltype(bsel)::value>(p0, p1)) return false;
 #pragma unroll
     for (int s = kS0; s < kS1; ++s)
       slot_dst(bsel, s)[lane] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(slot_src(s, p0, p1)));
@@ -496,9 +531,9 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
   // with nothing outstanding, as it is left at a segment end, and the
   // compiler's count of outstanding loads stays exact inside it.
   stage_through_registers(std::integral_constant<int, 0>{});
-  fetch();
+  cur.fetch();
   bool ahead = stage_through_registers(std::integral_constant<int, 1>{});   // the tile after the current one is staged
-  fetch();
+  cur.fetch();
   wv.load_q(a, seq, hg);
   wv.reset();
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -515,7 +550,7 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
       tile_barrier<0>();
     const bool has_next = ahead;
     ahead = stage(std::integral_constant<int, (B + 2) % 3>{});
-    const int inf = dinf[B];
+    const int inf = cur.dinf[B];
     const int nvalid = inf & 63;
     if (nvalid < kTileTok)
       wv.template compute<B, true>(nvalid);
@@ -524,14 +559,14 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
     // The cursor always points at a tile of the share (the last one once it
     // is done); its entries are read here, after the tile's LDS reads, so that
     // no scalar load is outstanding while they are waited for.
-    fetch();
+    cur.fetch();
     if (!(inf & kLast)) return true;
     // The segment ends with this tile: the next segment's queries are loaded
     // while this one's rows are written.
     wv.finish();
     const float m_end = wv.m, l_end = wv.lsum;
-    if (has_next) wv.load_q(a, dseq[(B + 1) % 3], hg);
-    const int cseq = dseq[B];
+    if (has_next) wv.load_q(a, cur.dseq[(B + 1) % 3], hg);
+    const int cseq = cur.dseq[B];
     const int nh = min(32, d.num_heads - hg * 32);
     if ((inf & kFirstOfSeq) && (inf & kLastOfSeq)) {
       wv.store_rows(reinterpret_cast<__bf16*>(d.out) + ((int64_t)cseq * d.num_heads + hg * 32) * kLatent, kLatent, nh);
@@ -568,8 +603,167 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// Converts this lane's 16-byte granules of e4m3 codes, slots S0 .. S0 + N - 1
+// of a tile of codes (slot s: granule `lane` of 1 KiB s % 9 of block s / 9,
+// i.e. 16 d of token lane % 16, chunk c16 = 4 (s % 9) + lane / 16), into the
+// bf16 layout of tile buffer T: chunks c = 2 c16 + h (h = 0, 1) of that token
+// in their swizzled slots, byte 2048 (s % 9) + 512 (lane / 16) + 256 h +
+// 16 slot_of(c, token) of the block, where c % 4 = (2 (lane / 16) + h) % 4.
+// Exact: every e4m3 value is a bf16 value. The two lane-dependent offsets are
+// formed here, so that they are not held in registers across the loop.
+template <int T, int S0, int N>
+__device__ __forceinline__ void convert_granules(const u32x4 (&raw)[N], int lane) {
+  int t = lane & 15, q = lane >> 4;
+  asm volatile("" : "+v"(t), "+v"(q));
+  const uint32_t a0 = (uint32_t)(q * 512 + (t ^ (4 * ((2 * q) & 3))) * 16);
+  const uint32_t a1 = (uint32_t)(q * 512 + 256 + (t ^ (4 * ((2 * q + 1) & 3))) * 16);
+  char* const tb = reinterpret_cast<char*>(tile_buf<T>());
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    constexpr int kHalf = kFpSlots / 2;
+    const int off = ((S0 + i) / kHalf) * kBlockBytes + ((S0 + i) % kHalf) * 2048;
+    const u32x4 w0 = {fp8x2_to_bf16x2<false>(raw[i][0]), fp8x2_to_bf16x2<true>(raw[i][0]),
+                      fp8x2_to_bf16x2<false>(raw[i][1]), fp8x2_to_bf16x2<true>(raw[i][1])};
+    const u32x4 w1 = {fp8x2_to_bf16x2<false>(raw[i][2]), fp8x2_to_bf16x2<true>(raw[i][2]),
+                      fp8x2_to_bf16x2<false>(raw[i][3]), fp8x2_to_bf16x2<true>(raw[i][3])};
+    *reinterpret_cast<u32x4*>(tb + off + a0) = w0;
+    *reinterpret_cast<u32x4*>(tb + off + a1) = w1;
+  }
+}
+
+// Slots [S0, S1) of the tile of codes in staging buffer F into tile buffer T,
+// six at a time (reads issued together, then converted).
+template <int F, int T, int S0, int S1>
+__device__ __forceinline__ void convert_staged(int lane) {
+  if constexpr (S0 < S1) {
+    constexpr int kN = S1 - S0 < 6 ? S1 - S0 : 6;
+    constexpr int kHalf = kFpSlots / 2;
+    u32x4 raw[kN];
+#pragma unroll
+    for (int i = 0; i < kN; ++i)
+      raw[i] = code_buf<F>()[((S0 + i) / kHalf) * kFpBlockVec + ((S0 + i) % kHalf) * 64 + lane];
+    convert_granules<T, S0, kN>(raw, lane);
+    convert_staged<F, T, S0 + kN, S1>(lane);
+  }
+}
+
+// The share loop with an fp8 cache. Wave WAVE of W copies slots
+// [18 WAVE / W, 18 (WAVE + 1) / W) of every tile of codes (slot s: 1 KiB s % 9
+// of block s / 9, lane L's 16 bytes at granule L) and converts the same
+// slots, so the codes it reads are its own copies and only the converted
+// tile needs the barrier. Step k (tile k, tile buffer k % 2) opens with the
+// barrier behind which tile k is converted by every wave and every wave is
+// done with tile k - 1; it copies tile k + 1's codes into staging buffer
+// (k + 1) % 2, computes tile k, then waits for its copies and converts them
+// into tile buffer (k + 1) % 2. One tile's codes are in flight while one is
+// computed.
+template <int W, int WAVE>
+__device__ __forceinline__ void wide_share_fp8(const MlaArgs& a, int share, int seq, int tile, int units) {
+  constexpr int kS0 = kFpSlots * WAVE / W, kS1 = kFpSlots * (WAVE + 1) / W;
+  const DecodeArgs& d = a.d;
+  const int hg = WAVE;
+
+  WideWave<true> wv;
+  wv.init(a, hg);
+  const int lane = wv.lane;
+  const char* cache = reinterpret_cast<const char*>(d.key_cache);
+
+  ShareCursor cur(d, seq, tile, units);
+  cur.fetch();
+  constexpr int kLast = ShareCursor::kLast, kFirstOfSeq = ShareCursor::kFirstOfSeq,
+                kLastOfSeq = ShareCursor::kLastOfSeq;
+
+  // Tile 0: codes through registers (then staging buffer 1, not in use yet),
+  // converted into tile buffer 0.
+  {
+    unsigned p0 = 0, p1 = 0;
+    cur.template take<0>(p0, p1);   // a share holds at least one tile
+#pragma unroll
+    for (int s = kS0; s < kS1; ++s) {
+      const int blk = s / (kFpSlots / 2), part = s % (kFpSlots / 2);
+      code_buf<1>()[blk * kFpBlockVec + part * 64 + lane] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(cache + (int64_t)(blk ? p1 : p0) * kFpBlockBytes + part * 1024 + lane * 16));
+    }
+    convert_staged<1, 0, kS0, kS1>(lane);
+  }
+  cur.fetch();
+  wv.load_q(a, seq, hg);
+  wv.reset();
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  // Copies the codes of the cursor's next tile into staging buffer F (its
+  // descriptor in slot F); false when the share has no tile left.
+  auto stage = [&](auto fsel) -> bool {
+    constexpr int F = decltype(fsel)::value;
+    unsigned p0, p1;
+    if (!cur.template take<F>(p0, p1)) return false;
+    const __amdgpu_buffer_rsrc_t r0 =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (int64_t)p0 * kFpBlockBytes), 0, kFpBlockBytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t r1 =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (int64_t)p1 * kFpBlockBytes), 0, kFpBlockBytes, kRsrcWord3);
+#pragma unroll
+    for (int s = kS0; s < kS1; ++s) {
+      const int blk = s / (kFpSlots / 2), part = s % (kFpSlots / 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          blk ? r1 : r0, (__attribute__((address_space(3))) void*)(code_buf<F>() + blk * kFpBlockVec + part * 64), 16,
+          part * 1024 + lane * 16, 0, 0, 2 /* nt */);
+    }
+    return true;
+  };
+
+  // Computes the tile in tile buffer B; false once the share is done.
+  auto step = [&](auto bsel) -> bool {
+    constexpr int B = decltype(bsel)::value, N = 1 - B;
+    tile_barrier<0>();
+    const bool has_next = stage(std::integral_constant<int, N>{});
+    const int inf = cur.dinf[B];
+    const int nvalid = inf & 63;
+    if (nvalid < kTileTok)
+      wv.template compute<B, true>(nvalid);
+    else
+      wv.template compute<B, false>(kTileTok);
+    if (has_next) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of the next tile
+      convert_staged<N, N, kS0, kS1>(lane);
+    }
+    cur.fetch();
+    if (!(inf & kLast)) return true;
+    wv.finish();
+    const float m_end = wv.m, l_end = wv.lsum;
+    if (has_next) wv.load_q(a, cur.dseq[N], hg);
+    const int cseq = cur.dseq[B];
+    const int nh = min(32, d.num_heads - hg * 32);
+    if ((inf & kFirstOfSeq) && (inf & kLastOfSeq)) {
+      wv.store_rows(reinterpret_cast<__bf16*>(d.out) + ((int64_t)cseq * d.num_heads + hg * 32) * kLatent, kLatent, nh);
+    } else {
+      const int64_t row = (int64_t)(cseq + share) * a.hpad + hg * 32;   // slot (seq + share)
+      wv.store_rows(d.seg_out + row * kLatent, kLatent, nh);
+      float* mbase = d.seg_max;
+      float* sbase = d.seg_sum;
+      asm volatile("" : "+s"(mbase), "+s"(sbase));   // kept in scalar registers
+      float* const mrow = mbase + row;
+      float* const srow = sbase + row;
+      if (wv.active && wv.half == 0) {
+        mrow[lane & 31] = m_end;
+        srow[lane & 31] = l_end;
+      }
+    }
+    if (hg == 0 && lane == 0) {
+      if (inf & kFirstOfSeq) d.seg_meta[2 * cseq] = share;
+      if (inf & kLastOfSeq) d.seg_meta[2 * cseq + 1] = share;
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (!has_next) return false;
+    wv.reset();
+    return true;
+  };
+  while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 // Grid: one workgroup of W waves (32 heads each) per stream-K share.
-template <int W>
+template <int W, bool FP8>
 __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(1, 1)))
 pa_mla_wide_kernel(const MlaArgs a) {
   const int lane = threadIdx.x & 63;
@@ -585,11 +779,22 @@ pa_mla_wide_kernel(const MlaArgs a) {
   int seq = 0, tile = 0;
   locate_block<kTileTok>(a.d, lane, (int)u0, bsum, seq, tile);
   // Each wave runs its own instantiation (its copy slots); all meet the same barriers.
-  switch (wave) {
-    case 0: wide_share<W, 0>(a, share, seq, tile, (int)(u1 - u0)); break;
-    case 1: if constexpr (W > 1) wide_share<W, 1 % W>(a, share, seq, tile, (int)(u1 - u0)); break;
-    case 2: if constexpr (W > 2) wide_share<W, 2 % W>(a, share, seq, tile, (int)(u1 - u0)); break;
-    default: if constexpr (W > 3) wide_share<W, 3 % W>(a, share, seq, tile, (int)(u1 - u0)); break;
+  const int n = (int)(u1 - u0);
+  static_assert(W == 3 || W == 4, "three or four 32-head waves");
+  if constexpr (FP8) {
+    switch (wave) {
+      case 0: wide_share_fp8<W, 0>(a, share, seq, tile, n); break;
+      case 1: wide_share_fp8<W, 1>(a, share, seq, tile, n); break;
+      case 2: wide_share_fp8<W, 2>(a, share, seq, tile, n); break;
+      default: if constexpr (W > 3) wide_share_fp8<W, 3 % W>(a, share, seq, tile, n); break;
+    }
+  } else {
+    switch (wave) {
+      case 0: wide_share<W, 0>(a, share, seq, tile, n); break;
+      case 1: wide_share<W, 1>(a, share, seq, tile, n); break;
+      case 2: wide_share<W, 2>(a, share, seq, tile, n); break;
+      default: if constexpr (W > 3) wide_share<W, 3 % W>(a, share, seq, tile, n); break;
+    }
   }
 }
 
@@ -597,11 +802,13 @@ pa_mla_wide_kernel(const MlaArgs a) {
 
 hipError_t launch_mla_wide(const MlaArgs& a, hipStream_t stream) {
   const dim3 grid(a.shares);
-  switch (a.waves_per_wg) {
-    case 1: hipLaunchKernelGGL(pa_mla_wide_kernel<1>, grid, dim3(64), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(pa_mla_wide_kernel<2>, grid, dim3(128), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(pa_mla_wide_kernel<3>, grid, dim3(192), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(pa_mla_wide_kernel<4>, grid, dim3(256), 0, stream, a); break;
+  switch (a.waves_per_wg * 2 + (a.fp8 ? 1 : 0)) {
+    // 65 to 128 heads: three or four waves (the plan runs fewer heads on the
+    // 16-heads-per-wave kernel).
+    case 6: hipLaunchKernelGGL((pa_mla_wide_kernel<3, false>), grid, dim3(192), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((pa_mla_wide_kernel<4, false>), grid, dim3(256), 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((pa_mla_wide_kernel<3, true>), grid, dim3(192), 0, stream, a); break;
+    case 9: hipLaunchKernelGGL((pa_mla_wide_kernel<4, true>), grid, dim3(256), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -387,8 +387,10 @@ int pa_mla_decode(void* out, const void* query, const void* latent_cache, int nu
  *                aligned.
  *   kv_scale     device fp32 scalar (NULL = 1.0), 4-B aligned.
  * Every other argument, the workspace size (pa_mla_workspace_bytes serves
- * both calls) and the errors as for pa_mla_decode. Every head count runs
- * the 16-heads-per-wave kernel (several workgroups per share from 65 heads).
+ * both calls), the kernels by head count and the errors as for
+ * pa_mla_decode; the kernels convert the codes to bf16 exactly (in registers
+ * up to 64 heads, into the LDS tile from 65) and then run the bf16
+ * arithmetic.
  */
 int pa_mla_decode_fp8(void* out, const void* query, const void* latent_cache, int num_seqs, int num_heads,
                       int num_blocks, float scale, const int32_t* block_tables, int max_blocks_per_seq,

@@ -107,7 +107,7 @@ def test_wide_kernel_is_resident(lib_path):
     staging) fits one compute unit's, each wave fits a SIMD's 512 registers
     per lane, and nothing spills to scratch."""
     k = {name: r for name, r in bench.code_object_kernels(lib_path).items() if "pa_mla_wide_kernel" in name}
-    assert len(k) == 4                  # one to four 32-head waves per workgroup
+    assert len(k) == 4                  # three or four 32-head waves per workgroup, bf16 and fp8 cache
     for res in k.values():
         assert res["scratch"] == 0
         assert 108 * 1024 <= res["lds"] <= LDS_PER_CU
