@@ -763,7 +763,7 @@ def bench_mla(config, args, dev):
     part_avg = part_ms / max(part_n, 1)
     achieved = nbytes / (part_avg / 1e3) / 1e9
     tflops = flops / (part_avg / 1e3) / 1e12
-    kernel = "pa_mla_wide_kernel" if cfg.num_heads >= MLA_WIDE_MIN_HEADS and not fp8 else "pa_mla_streamk_kernel"
+    kernel = "pa_mla_wide_kernel" if cfg.num_heads >= MLA_WIDE_MIN_HEADS else "pa_mla_streamk_kernel"
     rec = {
         "metric": METRIC, "value": round(cfg.num_seqs / (ms / 1e3), 1), "unit": "seqs/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
