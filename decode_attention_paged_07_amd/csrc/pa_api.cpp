@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -312,6 +313,66 @@ int check_workspace(const void* workspace, size_t workspace_bytes, size_t need) 
   return PA_OK;
 }
 
+// ---- opt-in check of the device-resident metadata -----------------------------
+
+// With PA_VALIDATE_DEVICE=1 in the environment, the decode calls copy
+// seq_lens and the table entries each sequence uses (the first
+// ceil(seq_len / block_size) of its row) to the host after the stream's
+// earlier work, and reject values outside [0, max_seq_len] and
+// [0, num_blocks) with PA_ERR_SHAPE before anything is launched. Without it
+// the kernels clamp such values (a length into [0, max_seq_len], a block id
+// into the pool), which keeps every access in bounds but gives meaningless
+// output. The check synchronizes the stream and is slow: a debugging aid. It
+// copies through a fixed buffer on the host stack (no allocation), and it is
+// skipped while the stream is being captured into a graph.
+bool validate_device_requested() {
+  const char* v = std::getenv("PA_VALIDATE_DEVICE");
+  return v && v[0] == '1' && v[1] == '\0';
+}
+
+int validate_device_metadata(const int32_t* seq_lens, const int32_t* block_tables, int num_seqs,
+                             int max_blocks_per_seq, int block_size, int max_seq_len, int num_blocks,
+                             hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess)
+    return fail(PA_ERR_HIP, "PA_VALIDATE_DEVICE: hipStreamIsCapturing failed");
+  if (cs != hipStreamCaptureStatusNone) return PA_OK;
+  constexpr int kBuf = 2048;
+  int32_t lens[kBuf], ent[kBuf];
+  auto copy = [&](int32_t* dst, const int32_t* src, int64_t n) -> bool {
+    if (hipMemcpyAsync(dst, src, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess) return false;
+    return hipStreamSynchronize(stream) == hipSuccess;
+  };
+  for (int s0 = 0; s0 < num_seqs; s0 += kBuf) {
+    const int n = std::min(kBuf, num_seqs - s0);
+    if (!copy(lens, seq_lens + s0, n)) return fail(PA_ERR_HIP, "PA_VALIDATE_DEVICE: copy of seq_lens failed");
+    for (int i = 0; i < n; ++i) {
+      const int s = s0 + i, L = lens[i];
+      if (L < 0 || L > max_seq_len)
+        return fail(PA_ERR_SHAPE, "PA_VALIDATE_DEVICE: seq_lens[%d] = %d is outside [0, max_seq_len = %d]", s, L,
+                    max_seq_len);
+      const int used = (L + block_size - 1) / block_size;
+      for (int b0 = 0; b0 < used; b0 += kBuf) {
+        const int m = std::min(kBuf, used - b0);
+        if (!copy(ent, block_tables + (int64_t)s * max_blocks_per_seq + b0, m))
+          return fail(PA_ERR_HIP, "PA_VALIDATE_DEVICE: copy of block_tables failed");
+        for (int j = 0; j < m; ++j)
+          if (ent[j] < 0 || ent[j] >= num_blocks)
+            return fail(PA_ERR_SHAPE, "PA_VALIDATE_DEVICE: block_tables[%d][%d] = %d is outside [0, num_blocks = %d)",
+                        s, b0 + j, ent[j], num_blocks);
+      }
+    }
+  }
+  return PA_OK;
+}
+
+int maybe_validate_device(const int32_t* seq_lens, const int32_t* block_tables, int num_seqs,
+                          int max_blocks_per_seq, int block_size, int max_seq_len, int num_blocks, void* stream) {
+  if (!validate_device_requested()) return PA_OK;
+  return validate_device_metadata(seq_lens, block_tables, num_seqs, max_blocks_per_seq, block_size, max_seq_len,
+                                  num_blocks, static_cast<hipStream_t>(stream));
+}
+
 int decode_impl(void* out, const void* query, const void* key_cache, const void* value_cache,
                 int num_seqs, int num_heads, int num_kv_heads, int head_size, int num_blocks,
                 float scale, const int32_t* block_tables, int max_blocks_per_seq,
@@ -332,6 +393,9 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
   const int sk_waves = split_tokens == 0 ? streamk_waves(kind, block_size) : 0;
   const Plan plan = make_plan(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len, split_tokens, sk_waves);
   if ((rc = check_workspace(workspace, workspace_bytes, plan.bytes))) return rc;
+  if ((rc = maybe_validate_device(seq_lens, block_tables, num_seqs, max_blocks_per_seq, block_size, max_seq_len,
+                                  num_blocks, stream)))
+    return rc;
   char* ws = static_cast<char*>(workspace);
   if (plan.bytes && !plan.streamk) {
     a.tmp_out = reinterpret_cast<float*>(ws + plan.off[0]);
@@ -697,6 +761,9 @@ int pa_paged_attention_decode_shared(void* out, const void* query, const void* k
                                            num_groups, max_group_size, max_prefix_blocks, max_tiles);
   if (plan.max_prefix_splits > 65535) return fail(PA_ERR_SHAPE, "too many prefix splits");
   if ((rc = check_workspace(workspace, workspace_bytes, plan.bytes))) return rc;
+  if ((rc = maybe_validate_device(seq_lens, block_tables, num_seqs, max_blocks_per_seq, block_size, max_seq_len,
+                                  num_blocks, stream)))
+    return rc;
 
   pa::SharedArgs sa{};
   const int kind = fill_decode_args(sa.d, out, query, key_cache, value_cache, num_seqs, num_heads, num_kv_heads,
@@ -922,6 +989,9 @@ int mla_decode(void* out, const void* query, const void* latent_cache, int num_s
   if (o0 < q0 + q_bytes && q0 < o0 + o_bytes) return fail(PA_ERR_SHAPE, "out overlaps query");
   const MlaPlan plan = make_mla_plan(num_seqs, num_heads, fp8);
   if ((rc = check_workspace(workspace, workspace_bytes, plan.bytes))) return rc;
+  if ((rc = maybe_validate_device(seq_lens, block_tables, num_seqs, max_blocks_per_seq, block_size, max_seq_len,
+                                  num_blocks, stream)))
+    return rc;
 
   pa::MlaArgs a{};
   pa::DecodeArgs& d = a.d;

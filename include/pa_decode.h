@@ -34,6 +34,15 @@
  *    blocks a sequence uses in [0, num_blocks). The kernels clamp both into
  *    range, so a violation gives unspecified output values but never an
  *    out-of-bounds access.
+ *  - Debugging aid: with the environment variable PA_VALIDATE_DEVICE=1, the
+ *    decode calls (pa_paged_attention_decode and its _split, _noalloc and
+ *    _shared forms, pa_mla_decode and pa_mla_decode_fp8) first copy seq_lens
+ *    and the table entries each sequence uses to the host, after the
+ *    stream's earlier work, and return PA_ERR_SHAPE, launching nothing, for
+ *    a value outside the ranges above. This synchronises the stream (an
+ *    exception to "never blocks the host"; no allocation: the copies go
+ *    through a fixed buffer), is slow, and is skipped while the stream is
+ *    being captured into a graph.
  *  - Results are deterministic for given inputs and launch plan (no atomics).
  */
 #ifndef PA_DECODE_H
