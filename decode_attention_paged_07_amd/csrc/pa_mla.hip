@@ -61,11 +61,7 @@ constexpr int kMlaBS = 16;
 constexpr int kMlaSteps = kMlaWidth / 32;              // S steps (32 d each)
 constexpr int kMlaVSteps = kMlaLatent / 32;            // steps that hold c_kv
 constexpr int kMlaDt = kMlaLatent / 16;                // 16-row output tiles
-constexpr int64_t kMlaBlockBytes = (int64_t)kMlaWidth * kMlaBS * 2;
-
-constexpr int kMlaTileVec = kMlaSteps * 64;            // 16-byte slots per tile (18 KiB)
-
-// 1 KiB copies per tile: 18 for bf16, 9 for fp8 codes.
+// 1 KiB copies per tile (one cache block): 18 for bf16, 9 for fp8 codes.
 template <bool FP8>
 constexpr int kMlaSlots = FP8 ? kMlaSteps / 2 : kMlaSteps;
 template <bool FP8>
