@@ -66,21 +66,23 @@ def sdpa(q_sh, k, v, scale):
     return o.reshape(h, -1).numpy()
 
 
-def test_gather_latent_brute_force_and_x_invariance():
+@pytest.mark.parametrize("bs", [16, 32])
+def test_gather_latent_brute_force_and_x_invariance(bs):
     rng = np.random.default_rng(11)
-    lens = [5, 33, 16]
+    lens = [5, 33, 16, 70]
     rows = [rng.standard_normal((n, D_C + D_R)).astype(np.float32) for n in lens]
     for x in (1, 4, 8, D_C + D_R):
-        pool, table = scatter_latent(rows, 12, 16, x, np.random.default_rng(x))
+        pool, table = scatter_latent(rows, 12, bs, x, np.random.default_rng(x))
         for s, n in enumerate(lens):
             got = omla.gather_latent(pool, table[s], n)
             assert np.array_equal(got, rows[s])
 
 
-@pytest.mark.parametrize("lens,h", [([1, 17, 40], 4), ([16, 32, 64], 16), ([255, 3], 2)])
-def test_matches_dense_sdpa(lens, h):
+@pytest.mark.parametrize("lens,h,bs", [([1, 17, 40], 4, 16), ([16, 32, 64], 16, 16), ([255, 3], 2, 16),
+                                       ([1, 31, 32, 33, 100], 3, 32)])
+def test_matches_dense_sdpa(lens, h, bs):
     rng = np.random.default_rng(len(lens) * 100 + h)
-    q, rows, pool, table = problem(rng, lens, h)
+    q, rows, pool, table = problem(rng, lens, h, bs=bs)
     scale = 1.0 / np.sqrt(24.0)
     got = run(q, pool, table, lens, scale)
     for s, n in enumerate(lens):
@@ -294,11 +296,11 @@ def _grown_problem(rng, lens, new, bs=16, x=4, extra=3):
     return old, pool, table, rows
 
 
-@pytest.mark.parametrize("x", [4, 8])
-def test_append_latent_read_back_through_the_gather(x):
+@pytest.mark.parametrize("x,bs", [(4, 16), (8, 16), (8, 32)])
+def test_append_latent_read_back_through_the_gather(x, bs):
     rng = np.random.default_rng(41)
-    lens, new = [0, 5, 16, 31], 19
-    old, pool, table, rows = _grown_problem(rng, lens, new, x=x)
+    lens, new = [0, 5, 16, 31, 33], 19
+    old, pool, table, rows = _grown_problem(rng, lens, new, bs=bs, x=x)
     grown = oracle.append_latent(pool, rows, table, np.asarray(lens, np.int32))
     for s, n in enumerate(lens):
         got = oracle.gather_latent(grown, table[s], n + new)
@@ -321,9 +323,10 @@ def test_append_latent_leaves_other_slots_bitwise_unchanged():
                 np.testing.assert_array_equal(grown[b, :, o, :], pool[b, :, o, :])
 
 
-def test_append_latent_brute_force_element_scatter():
+@pytest.mark.parametrize("bs", [16, 32])
+def test_append_latent_brute_force_element_scatter(bs):
     rng = np.random.default_rng(43)
-    lens, new, bs, x = [7, 30], 4, 16, 4
+    lens, new, x = [7, 30, 62], 4, 4
     _, pool, table, rows = _grown_problem(rng, lens, new, bs=bs, x=x)
     want = pool.copy()
     for s, p0 in enumerate(lens):
