@@ -61,6 +61,10 @@ WORKLOAD_TEXT = {
     "mla128_fp8": "latent-cache (MLA) decode, fp8 e4m3 latent cache (one scale = amax/448): 256 seqs, lens "
                   "U[1,8192] (seed 9), 128 query heads, one latent head of [c_kv 512, k_rope 64], bf16 q, bs=16, "
                   "131072-block pool",
+    "mla_bs32": "latent-cache (MLA) decode, 32-token blocks: 256 seqs, lens U[1,8192] (seed 6), 16 query heads, "
+                "one latent head of [c_kv 512, k_rope 64], bf16, bs=32, 65536-block pool",
+    "mla128_bs32": "latent-cache (MLA) decode, 32-token blocks: 256 seqs, lens U[1,8192] (seed 7), 128 query heads, "
+                   "one latent head of [c_kv 512, k_rope 64], bf16, bs=32, 65536-block pool",
 }
 
 

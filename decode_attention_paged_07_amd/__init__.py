@@ -748,9 +748,9 @@ def mla_cache_append(latent_cache, rows, block_tables, positions, kv_scale=1.0) 
     _need(rows.dim() in (2, 3) and rows.shape[-1] == width, f"rows must be [S, {width}] or [S, T, {width}]")
     num_seqs = rows.shape[0]
     tokens = 1 if rows.dim() == 2 else rows.shape[1]
-    _need(latent_cache.dim() == 4, "latent_cache must be [num_blocks, 576/x, 16, x]")
-    num_blocks = latent_cache.shape[0]
-    want = mla_cache_shape(num_blocks, 16, fp8)
+    _need(latent_cache.dim() == 4, "latent_cache must be [num_blocks, 576/x, block_size, x]")
+    num_blocks, block_size = latent_cache.shape[0], latent_cache.shape[2]
+    want = mla_cache_shape(num_blocks, block_size, fp8)
     _need(tuple(latent_cache.shape) == want, f"latent_cache shape {tuple(latent_cache.shape)} != {want}")
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
           and block_tables.shape[0] == num_seqs, "block_tables must be int32 [num_seqs, max_blocks]")
@@ -761,11 +761,11 @@ def mla_cache_append(latent_cache, rows, block_tables, positions, kv_scale=1.0) 
         ks = _device_scalar(kv_scale, dev)
         rc = _lib.pa_mla_cache_append_fp8(latent_cache.data_ptr(), rows.data_ptr(), num_seqs, tokens, num_blocks,
                                           block_tables.data_ptr(), block_tables.shape[1], positions.data_ptr(),
-                                          16, ks.data_ptr(), stream)
+                                          block_size, ks.data_ptr(), stream)
     else:
         rc = _lib.pa_mla_cache_append(latent_cache.data_ptr(), rows.data_ptr(), num_seqs, tokens, num_blocks,
-                                      block_tables.data_ptr(), block_tables.shape[1], positions.data_ptr(), 16,
-                                      stream)
+                                      block_tables.data_ptr(), block_tables.shape[1], positions.data_ptr(),
+                                      block_size, stream)
     _raise_for(rc, "mla_cache_append")
 
 

@@ -890,7 +890,7 @@ int mla_cache_append(void* latent_cache, const void* rows, int num_seqs, int tok
                      bool fp8, const float* kv_scale, void* stream) {
   if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
   if (tokens_per_seq < 1) return fail(PA_ERR_SHAPE, "tokens_per_seq %d must be positive", tokens_per_seq);
-  if (block_size != 16) return fail(PA_ERR_SHAPE, "block_size %d is not 16", block_size);
+  if (block_size != 16 && block_size != 32) return fail(PA_ERR_SHAPE, "block_size %d is not 16 or 32", block_size);
   if (num_blocks <= 0) return fail(PA_ERR_SHAPE, "num_blocks %d must be positive", num_blocks);
   if (max_blocks_per_seq <= 0) return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d must be positive", max_blocks_per_seq);
   if ((int64_t)num_seqs * tokens_per_seq >= ((int64_t)1 << 31))
@@ -916,6 +916,7 @@ int mla_cache_append(void* latent_cache, const void* rows, int num_seqs, int tok
   a.tokens_per_seq = tokens_per_seq;
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
+  a.block_size = block_size;
   a.kv_scale = fp8 ? kv_scale : nullptr;
   a.fp8 = fp8 ? 1 : 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -968,7 +969,7 @@ int mla_decode(void* out, const void* query, const void* latent_cache, int num_s
                size_t workspace_bytes, void* stream) {
   int rc = check_mla_plan_args(num_seqs, num_heads);
   if (rc) return rc;
-  if (block_size != 16) return fail(PA_ERR_SHAPE, "block_size %d is not 16", block_size);
+  if (block_size != 16 && block_size != 32) return fail(PA_ERR_SHAPE, "block_size %d is not 16 or 32", block_size);
   if (max_seq_len < 0) return fail(PA_ERR_SHAPE, "max_seq_len %d < 0", max_seq_len);
   if (num_seqs == 0) return ok();
   if (!out || !query || !latent_cache || !block_tables || !seq_lens)

@@ -185,39 +185,41 @@ hipError_t launch_append_t(const AppendArgs& a, hipStream_t stream) {
 
 // Latent rows (one compressed row [c_kv 512, k_rope 64] per token, bf16):
 // one wave per (sequence, physical block touched). Chunk c (8 bf16 or 16
-// fp8 codes, 16 bytes) of slot o sits at byte (16*c + o)*16 of the block
-// (18 or 9 KiB), so with the slot index fastest a run of n tokens is 72 (36)
+// fp8 codes, 16 bytes) of slot o sits at byte (B*c + o)*16 of a block of B
+// tokens, so with the slot index fastest a run of n tokens is 72 (36)
 // contiguous stores of 16*n bytes; the loads then take one chunk's elements
 // of each row per lane, n rows side by side. The decode step (n = 1) reads
-// its row contiguously and writes pieces 256 bytes apart, which the layout
+// its row contiguously and writes pieces 16 B bytes apart, which the layout
 // fixes. fp8 codes are those of the K/V append (quant_e4m3).
 template <bool FP8>
 __global__ void __launch_bounds__(64) pa_latent_append_kernel(const LatentAppendArgs a, int runs_per_seq) {
-  constexpr int kBs = 16, kRow = 1152;
-  constexpr int kChunks = FP8 ? 36 : 72, kBlock = kChunks * kBs * 16;
+  constexpr int kRow = 1152;
+  constexpr int kChunks = FP8 ? 36 : 72;
+  const int bs = a.block_size;                             // 16 or 32 tokens
+  const int64_t block_bytes = (int64_t)kChunks * bs * 16;
   const int r = (int)(blockIdx.x % (unsigned)runs_per_seq);
   const int s = (int)(blockIdx.x / (unsigned)runs_per_seq);
   const int p0 = a.positions[s];
   if (p0 < 0) return;
-  const int64_t blk = (int64_t)(p0 / kBs) + r;
-  const int64_t t_lo = blk * kBs > p0 ? blk * kBs : (int64_t)p0;
+  const int64_t blk = (int64_t)(p0 / bs) + r;
+  const int64_t t_lo = blk * bs > p0 ? blk * bs : (int64_t)p0;
   const int64_t p_end = (int64_t)p0 + a.tokens_per_seq;
-  const int64_t t_hi = (blk + 1) * kBs < p_end ? (blk + 1) * kBs : p_end;
+  const int64_t t_hi = (blk + 1) * bs < p_end ? (blk + 1) * bs : p_end;
   if (t_lo >= t_hi || blk >= a.max_blocks_per_seq) return;
   const int b = a.block_tables[(int64_t)s * a.max_blocks_per_seq + blk];
   if (b < 0 || b >= a.num_blocks) return;
-  const int o0 = (int)(t_lo - blk * kBs);
+  const int o0 = (int)(t_lo - blk * bs);
   const int n = (int)(t_hi - t_lo);
   const char* src = reinterpret_cast<const char*>(a.rows) + ((int64_t)s * a.tokens_per_seq + (t_lo - p0)) * kRow;
-  char* dst = reinterpret_cast<char*>(a.latent_cache) + (int64_t)b * kBlock + o0 * 16;
+  char* dst = reinterpret_cast<char*>(a.latent_cache) + (int64_t)b * block_bytes + o0 * 16;
   const float vs = (FP8 && a.kv_scale) ? *a.kv_scale : 1.f;
   for (int i = threadIdx.x; i < kChunks * n; i += 64) {
     const int c = i / n, t = i - c * n;
     if constexpr (FP8) {
       QuantPolicy<unsigned short>::k_chunk(reinterpret_cast<const unsigned short*>(src + t * kRow + c * 32),
-                                           dst + (c * kBs + t) * 16, vs);
+                                           dst + (c * bs + t) * 16, vs);
     } else {
-      *reinterpret_cast<u32x4a*>(dst + (c * kBs + t) * 16) =
+      *reinterpret_cast<u32x4a*>(dst + (c * bs + t) * 16) =
           *reinterpret_cast<const u32x4a*>(src + t * kRow + c * 16);
     }
   }
@@ -252,8 +254,10 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t*
 }
 
 hipError_t launch_latent_append(const LatentAppendArgs& a, hipStream_t stream) {
-  // As for the K/V append: T tokens touch at most floor((14 + T) / 16) + 1 blocks.
-  const int runs = (14 + a.tokens_per_seq) / 16 + 1;
+  // As for the K/V append: T tokens touch at most floor((B - 2 + T) / B) + 1
+  // blocks of B tokens.
+  const int bs = a.block_size;
+  const int runs = (bs - 2 + a.tokens_per_seq) / bs + 1;
   const int64_t items = (int64_t)a.num_seqs * runs;
   if (a.fp8)
     hipLaunchKernelGGL((pa_latent_append_kernel<true>), dim3((unsigned)items), dim3(64), 0, stream, a, runs);

@@ -156,8 +156,8 @@ struct AppendArgs {
 hipError_t launch_append(const AppendArgs& a, int in_kind, int cache_kind, hipStream_t stream);
 
 // Arguments of the latent-row append kernel (pa_append.hip): bf16 rows of
-// 576 elements into the latent cache [num_blocks][72][16][8], or as e4m3fn
-// codes of row / *kv_scale into [num_blocks][36][16][16].
+// 576 elements into the latent cache [num_blocks][72][block_size][8], or as
+// e4m3fn codes of row / *kv_scale into [num_blocks][36][block_size][16].
 struct LatentAppendArgs {
   void* latent_cache;
   const void* rows;            // [num_seqs][tokens_per_seq][576]
@@ -169,6 +169,7 @@ struct LatentAppendArgs {
   int tokens_per_seq;
   int num_blocks;
   int max_blocks_per_seq;
+  int block_size;              // 16 or 32 tokens
 };
 
 hipError_t launch_latent_append(const LatentAppendArgs& a, hipStream_t stream);

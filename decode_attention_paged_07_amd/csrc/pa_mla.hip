@@ -10,7 +10,9 @@
 //
 // Cache layout: the pages' K layout (§2) with one kv head and x = 8 bf16,
 // [num_blocks, 576/8, 16, 8]: 16 tokens of one 16-byte chunk are 256 bytes
-// contiguous, and a block is one 18 KiB run.
+// contiguous, and a block is one 18 KiB run. With 32-token blocks
+// ([num_blocks, 72, 32, 8], 36 KiB) each block is two 16-token tiles, chunk c
+// of tile h at 512 c + 256 h; the kernels work on 16-token tiles either way.
 //
 // One wave owns 16 query heads (the MFMA column count) of a run of blocks:
 //   S[t][g] = sum_d row_t[d] q[g][d]: A = the latent tile (rows = tokens),
@@ -96,6 +98,7 @@ struct MlaWave {
   float m, lsum, c;
   float vs;             // output multiplier: the fp8 scale, or 1
   int lane, q4;
+  int sh;               // 16-token tiles per cache block: 1 << sh
   bool active;          // this lane's column is a real query head
 
   __device__ void init(const MlaArgs& a, int hg) {
@@ -105,6 +108,7 @@ struct MlaWave {
     active = hg * 16 + j < a.d.num_heads;
     vs = (FP8 && a.d.k_scale) ? *a.d.k_scale : 1.f;
     c = a.d.scale * kLog2e * vs;
+    sh = a.d.block_size == 32 ? 1 : 0;
     // lane (j + 16*q4) holds I[4*q4 + u][j], u = 0..3.
     short e[4];
 #pragma unroll
@@ -132,14 +136,18 @@ struct MlaWave {
     for (int dt = 0; dt < kMlaDt; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Copy slots [S0, S1) of one 18 KiB tile into buf: instruction s moves
-  // bytes [1024 s, 1024 s + 1024) of the tile, 16 per lane, to buf + 64 s.
+  // Copy slots [S0, S1) of 16-token tile `half` of a cache block into buf:
+  // instruction s moves chunks 4s .. 4s + 3 of the tile's tokens, lane L's
+  // 16 bytes being chunk 4s + L / 16 of token L % 16, to buf + 64 s. A chunk
+  // of a block spans 256 << sh bytes, so with 16-token blocks instruction s
+  // reads bytes [1024 s, 1024 s + 1024) of the block.
   template <int S0, int S1>
-  __device__ void stage(const char* tile, u32x4* buf) const {
+  __device__ void stage(const char* block, int half, u32x4* buf) const {
+    const char* src = block + (lane >> 4) * (256 << sh) + half * 256 + (lane & 15) * 16;
 #pragma unroll
     for (int s = S0; s < S1; ++s)
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(tile + s * 1024 + lane * 16),
+          (const __attribute__((address_space(1))) void*)(src + s * (1024 << sh)),
           (__attribute__((address_space(3))) void*)(buf + s * 64), 16, 0, 2 /* nt */);
   }
 
@@ -327,9 +335,12 @@ __device__ __forceinline__ void mla_share(const MlaArgs& a, int share, int hg, i
   int64_t left = units - (cur.b1 - cur.b0);
   wv.load_q(a, cur.seq, hg);
   wv.reset();
+  // Lane i of tbl holds the table entry of tile chunk + i (tile g is in
+  // block g >> sh).
+  const int sh = wv.sh;
   const int32_t* trow = d.block_tables + (int64_t)cur.seq * d.max_blocks_per_seq;
   int chunk = cur.b0;
-  int tbl = trow[min(chunk + lane, cur.b1 - 1)];
+  int tbl = trow[min((chunk + lane) >> sh, (cur.b1 - 1) >> sh)];
 
   // The share's next sequence (seq_len and first 64 table entries).
   Seg nx{};
@@ -345,22 +356,22 @@ __device__ __forceinline__ void mla_share(const MlaArgs& a, int share, int hg, i
     if (s >= S) return;   // only with inconsistent inputs
     nx = make_seg(s, 0, left);
     has_nx = true;
-    tbl_n = d.block_tables[(int64_t)nx.seq * d.max_blocks_per_seq + min(lane, nx.b1 - 1)];
+    tbl_n = d.block_tables[(int64_t)nx.seq * d.max_blocks_per_seq + min(lane >> sh, (nx.b1 - 1) >> sh)];
   };
   prefetch();
 
   const char* base = reinterpret_cast<const char*>(d.key_cache);
-  auto stage_block = [&](unsigned phys, u32x4* buf) {
+  auto stage_block = [&](unsigned phys, int half, u32x4* buf) {
     phys = phys < top ? phys : top;
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // earlier LDS reads of buf are complete
-    wv.template stage<kS0, kS1>(base + (int64_t)phys * kMlaTileBytes<FP8>, buf);
+    wv.template stage<kS0, kS1>(base + (int64_t)phys * (kMlaTileBytes<FP8> << sh), half, buf);
   };
   auto stage_cur = [&](int g, u32x4* buf) {
     if (g - chunk >= 64) {
       chunk += 64;
-      tbl = trow[min(chunk + lane, cur.b1 - 1)];
+      tbl = trow[min((chunk + lane) >> sh, (cur.b1 - 1) >> sh)];
     }
-    stage_block((unsigned)__builtin_amdgcn_readlane(tbl, g - chunk), buf);
+    stage_block((unsigned)__builtin_amdgcn_readlane(tbl, g - chunk), g & sh, buf);
   };
 
   int g = cur.b0;
@@ -380,7 +391,7 @@ __device__ __forceinline__ void mla_share(const MlaArgs& a, int share, int hg, i
       stage_cur(g + 1, bn);
       wv.template consume<kPending>(bc, nvalid);
     } else if (has_nx) {
-      stage_block((unsigned)__builtin_amdgcn_readlane(tbl_n, 0), bn);
+      stage_block((unsigned)__builtin_amdgcn_readlane(tbl_n, 0), 0, bn);
       wv.template consume<kPending>(bc, nvalid);
     } else {
       wv.template consume<W == 1 ? 0 : 63>(bc, nvalid);

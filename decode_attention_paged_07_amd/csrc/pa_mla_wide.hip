@@ -36,6 +36,11 @@
 // workgroup takes an equal share; a sequence cut by a share boundary writes
 // partials that pa_mla_reduce_kernel combines.
 //
+// With 32-token cache blocks ([num_blocks, 72, 32, 8]) a tile is one block:
+// chunk c of its tokens 16 h .. 16 h + 15 is 256 bytes at 512 c + 256 h, and
+// goes to the LDS rows of tile half h as above (the copy addresses differ,
+// the LDS layout does not).
+//
 // fp8 latent cache (the pages' scaled fp8 storage, §4, one scale for the row;
 // [num_blocks, 36, 16, 16] codes): each wave copies its part of the next tile
 // (18 KiB of codes) into an LDS staging buffer, and once the current tile is
@@ -394,6 +399,7 @@ struct ShareCursor {
   const DecodeArgs& d;
   int S;
   unsigned top;
+  int one;            // 1: 32-token cache blocks, a tile is one block
   int sseq, st, L, st1, sleft, sflags;
   bool sdone;
   int dseq[3], dinf[3];
@@ -403,7 +409,7 @@ struct ShareCursor {
   unsigned np0, np1;
 
   __device__ __forceinline__ ShareCursor(const DecodeArgs& args, int seq, int tile, int units)
-      : d(args), S(args.num_seqs), top((unsigned)(args.num_blocks - 1)) {
+      : d(args), S(args.num_seqs), top((unsigned)(args.num_blocks - 1)), one(args.block_size == 32 ? 1 : 0) {
     sseq = seq;
     st = tile;
     L = clamp_len(ld_uniform(d.seq_lens, seq), d.max_seq_len);
@@ -415,6 +421,10 @@ struct ShareCursor {
   }
 
   __device__ __forceinline__ void fetch() {
+    if (one) {
+      np0 = np1 = (unsigned)ld_uniform(d.block_tables, (int64_t)sseq * d.max_blocks_per_seq + st);
+      return;
+    }
     const int64_t e = (int64_t)sseq * d.max_blocks_per_seq + 2 * st;
     np0 = (unsigned)ld_uniform(d.block_tables, e);
     np1 = (unsigned)ld_uniform(d.block_tables, e + (2 * st + 1 < blocks_of<kBS>(L) ? 1 : 0));
@@ -483,10 +493,20 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
   cur.fetch();
   constexpr int kLast = ShareCursor::kLast, kFirstOfSeq = ShareCursor::kFirstOfSeq,
                 kLastOfSeq = ShareCursor::kLastOfSeq;
-  // Byte address of copy slot s of the tile with blocks p0, p1, and its LDS slot.
-  auto slot_src = [&](int s, unsigned p0, unsigned p1) {
+  // Copy slot s of a tile: LDS tile half blk = s / 18, piece part = s % 18.
+  // Lane L fills LDS slot L of the piece with granule g = src_granule(L):
+  // chunk 4 part + g / 16 of token g % 16 of the half. In the cache that is
+  // byte voff(s) of block p_blk (16-token blocks) or of the tile's one block
+  // (32-token blocks: chunks 512 bytes apart, the half 256 bytes in).
+  const int one = cur.one;
+  const int blk_bytes = kBlockBytes << one;
+  const int lane_off = (src_granule(lane) >> 4) * (256 << one) + (src_granule(lane) & 15) * 16;
+  auto voff = [&](int s) {
     const int blk = s / (kCopySlots / 2), part = s % (kCopySlots / 2);
-    return cache + (int64_t)(blk ? p1 : p0) * kBlockBytes + part * 1024 + src_granule(lane) * 16;
+    return part * (1024 << one) + blk * 256 * one + lane_off;
+  };
+  auto slot_src = [&](int s, unsigned p0, unsigned p1) {
+    return cache + (int64_t)(s / (kCopySlots / 2) ? p1 : p0) * blk_bytes + voff(s);
   };
   auto slot_dst = [&](auto bsel, int s) {
     constexpr int B = decltype(bsel)::value;
@@ -502,15 +522,14 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
     unsigned p0, p1;
     if (!cur.template take<decltype(bsel)::value>(p0, p1)) return false;
     const __amdgpu_buffer_rsrc_t r0 =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (int64_t)p0 * kBlockBytes), 0, kBlockBytes, kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (int64_t)p0 * blk_bytes), 0, blk_bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t r1 =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (int64_t)p1 * kBlockBytes), 0, kBlockBytes, kRsrcWord3);
-    const int lane_off = src_granule(lane) * 16;
+        __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (int64_t)p1 * blk_bytes), 0, blk_bytes, kRsrcWord3);
 #pragma unroll
     for (int s = kS0; s < kS1; ++s) {
-      const int blk = s / (kCopySlots / 2), part = s % (kCopySlots / 2);
+      const int blk = s / (kCopySlots / 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(blk ? r1 : r0, (__attribute__((address_space(3))) void*)slot_dst(bsel, s),
-                                               16, part * 1024 + lane_off, 0, 0, 2 /* nt */);
+                                               16, voff(s), 0, 0, 2 /* nt */);
     }
     return true;
   };
@@ -673,6 +692,17 @@ __device__ __forceinline__ void wide_share_fp8(const MlaArgs& a, int share, int 
   constexpr int kLast = ShareCursor::kLast, kFirstOfSeq = ShareCursor::kFirstOfSeq,
                 kLastOfSeq = ShareCursor::kLastOfSeq;
 
+  // Copy slot s: lane L's 16 bytes are chunk 4 (s % 9) + L / 16 of token
+  // L % 16 of tile half s / 9, at byte voff(s) of its cache block (as for
+  // the bf16 copies, with 16-byte chunks and no swizzle).
+  const int one = cur.one;
+  const int blk_bytes = kFpBlockBytes << one;
+  const int lane_off = (lane >> 4) * (256 << one) + (lane & 15) * 16;
+  auto voff = [&](int s) {
+    const int blk = s / (kFpSlots / 2), part = s % (kFpSlots / 2);
+    return part * (1024 << one) + blk * 256 * one + lane_off;
+  };
+
   // Tile 0: codes through registers (then staging buffer 1, not in use yet),
   // converted into tile buffer 0.
   {
@@ -682,7 +712,7 @@ __device__ __forceinline__ void wide_share_fp8(const MlaArgs& a, int share, int 
     for (int s = kS0; s < kS1; ++s) {
       const int blk = s / (kFpSlots / 2), part = s % (kFpSlots / 2);
       code_buf<1>()[blk * kFpBlockVec + part * 64 + lane] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(cache + (int64_t)(blk ? p1 : p0) * kFpBlockBytes + part * 1024 + lane * 16));
+          reinterpret_cast<const u32x4*>(cache + (int64_t)(blk ? p1 : p0) * blk_bytes + voff(s)));
     }
     convert_staged<1, 0, kS0, kS1>(lane);
   }
@@ -698,15 +728,15 @@ __device__ __forceinline__ void wide_share_fp8(const MlaArgs& a, int share, int 
     unsigned p0, p1;
     if (!cur.template take<F>(p0, p1)) return false;
     const __amdgpu_buffer_rsrc_t r0 =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (int64_t)p0 * kFpBlockBytes), 0, kFpBlockBytes, kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (int64_t)p0 * blk_bytes), 0, blk_bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t r1 =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (int64_t)p1 * kFpBlockBytes), 0, kFpBlockBytes, kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (int64_t)p1 * blk_bytes), 0, blk_bytes, kRsrcWord3);
 #pragma unroll
     for (int s = kS0; s < kS1; ++s) {
       const int blk = s / (kFpSlots / 2), part = s % (kFpSlots / 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           blk ? r1 : r0, (__attribute__((address_space(3))) void*)(code_buf<F>() + blk * kFpBlockVec + part * 64), 16,
-          part * 1024 + lane * 16, 0, 0, 2 /* nt */);
+          voff(s), 0, 0, 2 /* nt */);
     }
     return true;
   };

@@ -359,7 +359,7 @@ int pa_paged_attention_decode_shared(void* out, const void* query, const void* k
  *   out          device, bf16 [num_seqs][num_heads][512], 16-byte aligned,
  *                not overlapping query
  *   block_tables, seq_lens, max_seq_len: as for pa_paged_attention_decode
- *   block_size   16; num_heads in [1, PA_MLA_MAX_HEADS]
+ *   block_size   16 or 32; num_heads in [1, PA_MLA_MAX_HEADS]
  *   workspace    device, at least pa_mla_workspace_bytes(num_seqs,
  *                num_heads) bytes, 16-byte aligned (NULL allowed when that
  *                size is 0); contents on entry do not matter, and on return
@@ -391,7 +391,7 @@ int pa_mla_decode(void* out, const void* query, const void* latent_cache, int nu
  * per-tensor scale because the row is both key and value. Element e of a
  * token's row stands for e4m3fn(code) * *kv_scale, and the call computes
  * pa_mla_decode's formula over those values.
- *   latent_cache device, uint8 E4M3FN codes [num_blocks][576/16][16][16]
+ *   latent_cache device, uint8 E4M3FN codes [num_blocks][576/16][block_size][16]
  *                (the pages' K layout with one kv head and x = 16), 16-B
  *                aligned.
  *   kv_scale     device fp32 scalar (NULL = 1.0), 4-B aligned.
@@ -412,21 +412,21 @@ int pa_mla_decode_fp8(void* out, const void* query, const void* latent_cache, in
  * iteration (the cache grows one token per step; "vLLM 0.25.0 解读" §1; one
  * compressed row per token, 10100.com retirement article, §2). Token j
  * (0 <= j < tokens_per_seq) of sequence s goes to logical position
- * p = positions[s] + j, i.e. physical block block_tables[s, p / 16], slot
- * p % 16 (same article, §1): element e of its row is stored at
- * latent_cache[b][e / 8][p % 16][e % 8].
- *   latent_cache device, bf16 [num_blocks][576/8][16][8] as for
+ * p = positions[s] + j, i.e. physical block block_tables[s, p / block_size],
+ * slot p % block_size (same article, §1): element e of its row is stored at
+ * latent_cache[b][e / 8][p % block_size][e % 8].
+ *   latent_cache device, bf16 [num_blocks][576/8][block_size][8] as for
  *                pa_mla_decode, 16-B aligned; written only at the slots
  *                named by the positions, the rows copied unchanged.
  *   rows         device, bf16 [num_seqs][tokens_per_seq][576], contiguous,
  *                16-B aligned, not overlapping latent_cache.
  *   num_seqs >= 0 (0 is a no-op); tokens_per_seq >= 1; num_blocks > 0;
- *   max_blocks_per_seq > 0 (table stride); block_size 16;
+ *   max_blocks_per_seq > 0 (table stride); block_size 16 or 32;
  *   num_seqs * tokens_per_seq < 2^31.
  *   block_tables device int32 [num_seqs][max_blocks_per_seq]; positions device
  *   int32 [num_seqs]. A negative position skips the sequence; positions past
- *   max_blocks_per_seq*16 and table entries outside [0, num_blocks) are not
- *   written.
+ *   max_blocks_per_seq*block_size and table entries outside [0, num_blocks)
+ *   are not written.
  * Two tokens naming the same slot leave either one. Asynchronous on `stream`;
  * no allocation; host-side validation and errors as for pa_kv_cache_append;
  * timed with it by pa_timing_read_append.
@@ -437,7 +437,7 @@ int pa_mla_cache_append(void* latent_cache, const void* rows, int num_seqs, int 
 
 /*
  * pa_mla_cache_append into an fp8 latent cache (pa_mla_decode_fp8's layout,
- * uint8 [num_blocks][36][16][16]): each element of the bf16 rows is stored
+ * uint8 [num_blocks][36][block_size][16]): each element of the bf16 rows is stored
  * as the E4M3FN code nearest to value / *kv_scale (float32 quotient, ties to
  * even, magnitude saturated at 448, NaN -> 0x7F, sign kept), the inverse of
  * the decode's dequantisation (10100.com article, §4). kv_scale: device fp32

@@ -21,7 +21,7 @@ def call(pa, **over):
 
 @pytest.mark.parametrize("over,code", [
     (dict(H=0), -2), (dict(H=129), -2), (dict(S=-1), -2), (dict(S=65536), -2),
-    (dict(bs=32), -2), (dict(msl=-1), -2), (dict(msl=129), -2), (dict(nb=0), -2), (dict(mb=0), -2),
+    (dict(bs=64), -2), (dict(msl=-1), -2), (dict(msl=129), -2), (dict(nb=0), -2), (dict(mb=0), -2),
     (dict(scale=float("nan")), -2), (dict(out=None), -1), (dict(query=None), -1), (dict(latent=None), -1),
     (dict(table=None), -1), (dict(lens=None), -1), (dict(out=A + 8), -5), (dict(latent=A + 4), -5),
     (dict(lens=5 * A + 2), -5), (dict(ws=None), -4), (dict(wsb=16), -4), (dict(ws=6 * A + 8), -5),
@@ -70,7 +70,7 @@ def call_append(pa, **over):
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(S=-1), -2), (dict(T=0), -2), (dict(bs=32), -2), (dict(nb=0), -2), (dict(mb=0), -2),
+    (dict(S=-1), -2), (dict(T=0), -2), (dict(bs=64), -2), (dict(nb=0), -2), (dict(mb=0), -2),
     (dict(S=1 << 20, T=1 << 11), -2), (dict(latent=None), -1), (dict(rows=None), -1),
     (dict(table=None), -1), (dict(pos=None), -1), (dict(latent=A + 8), -5), (dict(rows=2 * A + 4), -5),
     (dict(table=3 * A + 2), -5), (dict(pos=4 * A + 1), -5),
@@ -103,7 +103,7 @@ def call_fp8(pa, **over):
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(H=0), -2), (dict(H=129), -2), (dict(bs=32), -2), (dict(msl=129), -2), (dict(latent=None), -1),
+    (dict(H=0), -2), (dict(H=129), -2), (dict(bs=64), -2), (dict(msl=129), -2), (dict(latent=None), -1),
     (dict(latent=A + 8), -5), (dict(ks=7 * A + 2), -5), (dict(ws=None), -4), (dict(out=2 * A + 64), -2),
 ])
 def test_fp8_decode_validation_rejects(pa, over, code):  # noqa: F811
@@ -123,7 +123,7 @@ def test_fp8_append_validation(pa):  # noqa: F811
     bad[9] = 8 * A + 2
     assert f(*bad) == -5
     bad = list(args)
-    bad[8] = 32
+    bad[8] = 64
     assert f(*bad) == -2
     bad = list(args)
     bad[1] = A + 64 * 9216 - 16          # rows start inside the (9 KiB-block) cache

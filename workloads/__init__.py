@@ -1,7 +1,7 @@
 """Seeded synthetic decode workloads (no attention arithmetic lives here)."""
 
 from .configs import (  # noqa: F401
-    CONFIGS, EXTRA_CONFIGS, FP8, FP8C, GQA, GQA32, LONG, MHA, MLA, MLA128, MLA128_FP8, MLA_CONFIGS, MLA_FP8, SHARED, TINY, DecodeConfig,
+    CONFIGS, EXTRA_CONFIGS, FP8, FP8C, GQA, GQA32, LONG, MHA, MLA, MLA128, MLA128_BS32, MLA128_FP8, MLA_BS32, MLA_CONFIGS, MLA_FP8, SHARED, TINY, DecodeConfig,
 )
 from .generate import (  # noqa: F401
     Case,

@@ -88,4 +88,7 @@ MLA128 = MLA.with_(name="mla128", num_heads=128, seed=7)
 # The same with the latent rows stored as fp8 e4m3 codes and one scale.
 MLA_FP8 = MLA.with_(name="mla_fp8", kv_dtype="fp8_e4m3", seed=8)
 MLA128_FP8 = MLA128.with_(name="mla128_fp8", kv_dtype="fp8_e4m3", seed=9)
-MLA_CONFIGS = {c.name: c for c in (MLA, MLA128, MLA_FP8, MLA128_FP8)}
+# 32-token cache blocks (the same 2.4 GB pool in half as many blocks).
+MLA_BS32 = MLA.with_(name="mla_bs32", block_size=32, pool_blocks=64 * 1024)
+MLA128_BS32 = MLA128.with_(name="mla128_bs32", block_size=32, pool_blocks=64 * 1024)
+MLA_CONFIGS = {c.name: c for c in (MLA, MLA128, MLA_FP8, MLA128_FP8, MLA_BS32, MLA128_BS32)}
