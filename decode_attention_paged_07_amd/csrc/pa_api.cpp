@@ -540,7 +540,7 @@ static_assert(PA_MLA_WIDE_MIN_HEADS > 64, "the 32-heads-per-wave kernel is built
 //    per share.
 //  * 32 heads per wave (pa_mla_wide.hip): one workgroup of ceil(H / 32) waves
 //    (one per SIMD) per share and compute unit.
-// Workspace: seg_out [slots][hpad][512] | seg_max [slots][hpad] |
+// Workspace: seg_out [slots][hpad][512] bf16 | seg_max [slots][hpad] |
 // seg_sum [slots][hpad] | seg_meta [S][2], slots = S + shares.
 struct MlaPlan {
   bool wide;
@@ -574,7 +574,7 @@ MlaPlan make_mla_plan(int num_seqs, int num_heads, bool fp8) {
   const size_t hpad = (size_t)p.hpad;
   const size_t slots = (size_t)num_seqs + p.shares;
   p.off[0] = 0;
-  p.off[1] = round_up(slots * hpad * PA_MLA_LATENT_DIM * sizeof(float), 256);
+  p.off[1] = round_up(slots * hpad * PA_MLA_LATENT_DIM * 2, 256);   // bf16 rows
   p.off[2] = p.off[1] + round_up(slots * hpad * sizeof(float), 256);
   p.off[3] = p.off[2] + round_up(slots * hpad * sizeof(float), 256);
   p.bytes = p.off[3] + round_up((size_t)num_seqs * 2 * sizeof(int32_t), 256);

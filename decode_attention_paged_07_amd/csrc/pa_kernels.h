@@ -190,7 +190,8 @@ hipError_t launch_decode(const DecodeArgs& a, int kind, hipStream_t stream, cons
 
 // Latent-cache (MLA) decode (pa_mla.hip). d carries the batch: key_cache is
 // the latent cache, head_size the row width, group 16 (heads per wave),
-// num_kv_heads 1; seg_* as for stream-K with slots [S + shares][head_groups*16].
+// num_kv_heads 1; seg_* as for stream-K with slots [S + shares][hpad], except
+// that seg_out holds bf16 rows.
 struct MlaArgs {
   DecodeArgs d;
   int head_groups;    // head groups: ceil(num_heads / 16), or ceil(num_heads / 32) for the wide kernel

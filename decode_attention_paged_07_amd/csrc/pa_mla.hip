@@ -406,7 +406,7 @@ __device__ __forceinline__ void mla_share(const MlaArgs& a, int share, int hg, i
       wv.store_rows(reinterpret_cast<__bf16*>(d.out) + h0 * kMlaLatent, kMlaLatent);
     } else {
       const int64_t row = (int64_t)(cur.seq + share) * a.hpad + hg * 16;   // slot (seq + share)
-      wv.store_rows(d.seg_out + row * kMlaLatent, kMlaLatent);
+      wv.store_rows(reinterpret_cast<__bf16*>(d.seg_out) + row * kMlaLatent, kMlaLatent);
       if (wv.active && wv.q4 == 0) {
         d.seg_max[row + (lane & 15)] = wv.m;
         d.seg_sum[row + (lane & 15)] = wv.lsum;
@@ -470,7 +470,9 @@ __global__ void __launch_bounds__(64 * W) pa_mla_streamk_kernel(const MlaArgs a)
   }
 }
 
-// Merge of the segments of cut sequences, zero rows of empty ones: grid
+// Merge of the segments of cut sequences, zero rows of empty ones. A
+// segment's row is stored in bf16, the output type, as the pages' partition
+// buffers hold it (its max and sum stay fp32). Grid
 // (num_seqs, ceil(num_heads / 4)), four waves of 64; one (sequence, head) row
 // per wave, eight of its 512 values per lane. The segments' weights are
 // computed one per lane; their rows are read eight segments at a time with
@@ -530,9 +532,12 @@ __global__ void __launch_bounds__(256) pa_mla_reduce_kernel(const MlaArgs a) {
       for (int k = 0; k < kU; ++k) {
         const int idx = min(u + k, n - 1);
         fw[k] = u + k < n ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), idx)) : 0.f;
-        const float* src = d.seg_out + row(c + idx) * kMlaLatent + 8 * lane;
-        v0[k] = *reinterpret_cast<const f32x4*>(src);
-        v1[k] = *reinterpret_cast<const f32x4*>(src + 4);
+        const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(d.seg_out) +
+                                                        row(c + idx) * kMlaLatent + 8 * lane);
+        v0[k] = f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u), __uint_as_float(w[1] << 16),
+                      __uint_as_float(w[1] & 0xFFFF0000u)};
+        v1[k] = f32x4{__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xFFFF0000u), __uint_as_float(w[3] << 16),
+                      __uint_as_float(w[3] & 0xFFFF0000u)};
       }
 #pragma unroll
       for (int k = 0; k < kU; ++k) {

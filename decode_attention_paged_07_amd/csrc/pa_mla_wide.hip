@@ -591,7 +591,7 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
       wv.store_rows(reinterpret_cast<__bf16*>(d.out) + ((int64_t)cseq * d.num_heads + hg * 32) * kLatent, kLatent, nh);
     } else {
       const int64_t row = (int64_t)(cseq + share) * a.hpad + hg * 32;   // slot (seq + share)
-      wv.store_rows(d.seg_out + row * kLatent, kLatent, nh);
+      wv.store_rows(reinterpret_cast<__bf16*>(d.seg_out) + row * kLatent, kLatent, nh);
       float* mbase = d.seg_max;
       float* sbase = d.seg_sum;
       asm volatile("" : "+s"(mbase), "+s"(sbase));   // kept in scalar registers
@@ -767,7 +767,7 @@ __device__ __forceinline__ void wide_share_fp8(const MlaArgs& a, int share, int 
       wv.store_rows(reinterpret_cast<__bf16*>(d.out) + ((int64_t)cseq * d.num_heads + hg * 32) * kLatent, kLatent, nh);
     } else {
       const int64_t row = (int64_t)(cseq + share) * a.hpad + hg * 32;   // slot (seq + share)
-      wv.store_rows(d.seg_out + row * kLatent, kLatent, nh);
+      wv.store_rows(reinterpret_cast<__bf16*>(d.seg_out) + row * kLatent, kLatent, nh);
       float* mbase = d.seg_max;
       float* sbase = d.seg_sum;
       asm volatile("" : "+s"(mbase), "+s"(sbase));   // kept in scalar registers
