@@ -471,8 +471,9 @@ __global__ void __launch_bounds__(64 * W) pa_mla_streamk_kernel(const MlaArgs a)
 }
 
 // Merge of the segments of cut sequences, zero rows of empty ones. A
-// segment's row is stored in bf16, the output type, as the pages' partition
-// buffers hold it (its max and sum stay fp32). Grid
+// segment's row is stored in bf16, the output type (its max and sum stay
+// fp32): half the bytes written and read back, for one more rounding of at
+// most 2^-9 relative per row. Grid
 // (num_seqs, ceil(num_heads / 4)), four waves of 64; one (sequence, head) row
 // per wave, eight of its 512 values per lane. The segments' weights are
 // computed one per lane; their rows are read eight segments at a time with
