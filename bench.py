@@ -708,6 +708,26 @@ def time_steps(step, steps, warmup, dev):
     return ms_per_step, (part_ms, part_n), (red_ms, red_n), e0.elapsed_time(e1) / steps
 
 
+def step_percentiles(step, steps, dev):
+    """p10 / p50 / p90 of the step time in µs over ``steps`` more back-to-back
+    steps: one event before each step and one after the last, on the launch
+    stream, read after a single synchronisation (so the steps still run back
+    to back). Reported beside the mean of the timed loop, not instead of it."""
+    import numpy as np
+    import torch
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i].record(stream)
+        step()
+    ev[steps].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)])
+    return {"p10": round(float(np.percentile(us, 10)), 2), "p50": round(float(np.percentile(us, 50)), 2),
+            "p90": round(float(np.percentile(us, 90)), 2), "steps": steps}
+
+
 def mla_cpu_baseline(case, out, budget_s: float):
     """The MLA oracle timed on the host over the first sequences (about
     budget_s of work), with the GPU output checked on them."""
@@ -761,6 +781,7 @@ def bench_mla(config, args, dev):
                       case.max_seq_len, kv_scale=kv_scale)
 
     ms, (part_ms, part_n), (red_ms, red_n), ms_ev = time_steps(step, args.steps, args.warmup, dev)
+    pct = step_percentiles(step, args.steps, dev)
     tokens = int(case.meta.seq_lens.astype("int64").sum())
     nbytes = tokens * 576 * (1 if fp8 else 2)
     flops = tokens * cfg.num_heads * 2 * (576 + 512)
@@ -788,6 +809,7 @@ def bench_mla(config, args, dev):
                  "peak_tflops": PEAK_BF16_TFLOPS, "frac": round(tflops / PEAK_BF16_TFLOPS, 4)},
         "reduce_avg_ms": round(red_ms / red_n, 5) if red_n else 0.0,
         "ms_per_step_with_kernel_events": round(ms_ev, 5),
+        "step_us": pct,
         "kernel_sha": kernel_sha(kernel),
         "cpu_baseline": None,
     }
@@ -945,7 +967,7 @@ def main():
         sec = bench_decode("fp8", args, dev, ceiling=False)
         rec["secondary"] = {k: sec[k] for k in ("ms_per_step", "value", "unit", "dtype", "config",
                                                  "effective_kv_gbps", "frac_of_peak_hbm", "roofline",
-                                                 "reduce_avg_ms", "kernel_sha", "cpu_baseline")
+                                                 "reduce_avg_ms", "step_us", "kernel_sha", "cpu_baseline")
                             if k in sec}
         rec["secondary"]["target_frac_of_peak_hbm"] = 0.60
         if "parity_on_sample" in sec:
@@ -1004,6 +1026,7 @@ def bench_decode(name, args, dev, ceiling=True):
     pa.pa_timing_enable(False)
     part_ms, part_n, red_ms, red_n = pa.pa_timing_read()
     ms_with_events = e0.elapsed_time(e1) / args.steps
+    pct = step_percentiles(step, args.steps, dev)
 
     nbytes = kv_bytes(case)
     kernel_name = "pa_streamk_kernel" if split_tokens == 0 else "pa_split_kernel"
@@ -1051,6 +1074,7 @@ def bench_decode(name, args, dev, ceiling=True):
             "avg_launch_ms": round(part_avg, 5),
             "algorithmic_bytes_per_launch": nbytes,
         },
+        "step_us": pct,
         "reduce_avg_ms": round(red_ms / red_n, 5) if red_n else 0.0,
         "ms_per_step_with_kernel_events": round(ms_with_events, 5),
         "kernel_sha": kernel_sha(kernel_name),
