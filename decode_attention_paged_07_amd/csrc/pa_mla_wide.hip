@@ -25,9 +25,10 @@
 // two halves of the head's tokens and meet through v_permlane32_swap.
 //
 // Tiles go from HBM straight to LDS (buffer_load_dwordx4 ... lds, each wave a part
-// of every tile) into three 36 KiB buffers used in turn: while one tile is
-// computed the copies of the next two are in flight (one tile in flight per
-// CU leaves the copy latency exposed), and one barrier per tile separates them.
+// of every tile) into two 36 KiB buffers used in turn: while one tile is
+// computed the copy of the next is in flight, and one barrier per tile
+// separates them. (A third buffer with two tiles in flight was slower: its
+// three-step loop holds six copies of the tile arithmetic instead of four.)
 // The buffers are distinct arrays named at compile time in the code that reads
 // and the code that writes them, so the compiler orders reads of one only
 // after copies into that one.
@@ -94,7 +95,8 @@ static_assert(kSteps % PA_MLA_WIDE_KG == 0 && kDt % PA_MLA_WIDE_KV == 0, "groups
 
 __shared__ u32x4 mla_wide_tile0[2 * kBlockVec];
 __shared__ u32x4 mla_wide_tile1[2 * kBlockVec];
-__shared__ u32x4 mla_wide_tile2[2 * kBlockVec];
+// fp8 cache: two 18 KiB staging buffers for the codes of the next tile.
+__shared__ u32x4 mla_wide_codes[2 * 2 * kFpBlockVec];
 // Per-wave staging of one output tile (16 floats per lane), the only route by
 // which the output accumulators reach ordinary registers. The accumulators
 // (256 registers per lane: 16 tiles of 32 d x 32 heads) fill the
@@ -107,13 +109,13 @@ __shared__ f32x4 mla_wide_stage[4 * 4 * 64];
 
 template <int B>
 __device__ __forceinline__ u32x4* tile_buf() {
-  return B == 0 ? mla_wide_tile0 : B == 1 ? mla_wide_tile1 : mla_wide_tile2;
+  static_assert(B == 0 || B == 1, "two tile buffers");
+  return B == 0 ? mla_wide_tile0 : mla_wide_tile1;
 }
-// With an fp8 cache, tile buffers 0 and 1 hold converted tiles and the third
-// holds two 18 KiB staging buffers for the codes.
 template <int F>
 __device__ __forceinline__ u32x4* code_buf() {
-  return mla_wide_tile2 + F * (2 * kFpBlockVec);
+  static_assert(F == 0 || F == 1, "two staging buffers");
+  return mla_wide_codes + F * (2 * kFpBlockVec);
 }
 
 // LDS layout of a cache block: chunk c (eight d of 16 tokens, 256 bytes) keeps
@@ -471,16 +473,14 @@ struct ShareCursor {
 // tile's block s / 18; a tile with one block copies that block twice, so that
 // every tile costs each wave the same number of copy instructions).
 //
-// Two cursors walk the share: the staging cursor, two tiles ahead, and the
-// compute cursor. Step k (tile k of the share, in buffer k % 3) opens with a
+// Two cursors walk the share: the staging cursor, one tile ahead, and the
+// compute cursor. Step k (tile k of the share, in buffer k % 2) opens with a
 // barrier behind which every wave's copies of tile k have landed and every
-// wave is done with tile k - 1; it then starts the copy of tile k + 2 into
-// tile k - 1's buffer and computes tile k. Two tiles' copies are thus in flight
-// while one is computed.
+// wave is done with tile k - 1; it then starts the copy of tile k + 1 into
+// tile k - 1's buffer and computes tile k.
 template <int W, int WAVE>
 __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq, int tile, int units) {
   constexpr int kS0 = kCopySlots * WAVE / W, kS1 = kCopySlots * (WAVE + 1) / W;
-  constexpr int kCopies = kS1 - kS0;   // copy instructions per tile of this wave
   const DecodeArgs& d = a.d;
   const int hg = WAVE;
 
@@ -533,7 +533,7 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
     }
     return true;
   };
-  // The same through registers, for the two tiles copied before the loop: the
+  // The same through registers, for the tile copied before the loop: the
   // compiler's bookkeeping of copies into LDS, merged at the loop head, would
   // otherwise make one of the loop's steps wait for every copy in flight.
   auto stage_through_registers = [&](auto bsel) -> bool {
@@ -545,13 +545,10 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
     return true;
   };
 
-  // The first two tiles and the queries are waited for before the loop (the
-  // tiles are issued together and land together): the loop is then entered
-  // with nothing outstanding, as it is left at a segment end, and the
-  // compiler's count of outstanding loads stays exact inside it.
+  // The first tile and the queries are waited for before the loop: the loop
+  // is then entered with nothing outstanding, as it is left at a segment end,
+  // and the compiler's count of outstanding loads stays exact inside it.
   stage_through_registers(std::integral_constant<int, 0>{});
-  cur.fetch();
-  bool ahead = stage_through_registers(std::integral_constant<int, 1>{});   // the tile after the current one is staged
   cur.fetch();
   wv.load_q(a, seq, hg);
   wv.reset();
@@ -560,15 +557,9 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
   // Computes the tile in buffer B; false once the share is done.
   auto step = [&](auto bsel) -> bool {
     constexpr int B = decltype(bsel)::value;
-    // This wave's copies of the current tile have landed once no more than
-    // the next tile's copies are outstanding (vector memory reads complete in
-    // issue order).
-    if (ahead)
-      tile_barrier<kCopies>();
-    else
-      tile_barrier<0>();
-    const bool has_next = ahead;
-    ahead = stage(std::integral_constant<int, (B + 2) % 3>{});
+    // Nothing but this wave's copies of the current tile is outstanding here.
+    tile_barrier<0>();
+    const bool has_next = stage(std::integral_constant<int, 1 - B>{});
     const int inf = cur.dinf[B];
     const int nvalid = inf & 63;
     if (nvalid < kTileTok)
@@ -584,7 +575,7 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
     // while this one's rows are written.
     wv.finish();
     const float m_end = wv.m, l_end = wv.lsum;
-    if (has_next) wv.load_q(a, cur.dseq[(B + 1) % 3], hg);
+    if (has_next) wv.load_q(a, cur.dseq[1 - B], hg);
     const int cseq = cur.dseq[B];
     const int nh = min(32, d.num_heads - hg * 32);
     if ((inf & kFirstOfSeq) && (inf & kLastOfSeq)) {
@@ -615,8 +606,7 @@ __device__ __forceinline__ void wide_share(const MlaArgs& a, int share, int seq,
     wv.reset();
     return true;
   };
-  while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{}) &&
-         step(std::integral_constant<int, 2>{})) {
+  while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
   }
   // Nothing may be left in flight into LDS when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(0x0F70);

@@ -103,14 +103,16 @@ def test_persistent_grid_is_resident(lib_path):
 
 def test_wide_kernel_is_resident(lib_path):
     """The 32-heads-per-wave kernel: one workgroup (one wave per SIMD) per
-    compute unit, so its LDS (three 36 KiB tile buffers and the accumulator
-    staging) fits one compute unit's, each wave fits a SIMD's 512 registers
-    per lane, and nothing spills to scratch."""
+    compute unit, so its LDS (two 36 KiB tile buffers and the accumulator
+    staging, plus two 18 KiB code buffers with an fp8 cache) fits one compute
+    unit's, each wave fits a SIMD's 512 registers per lane, and nothing spills
+    to scratch."""
     k = {name: r for name, r in bench.code_object_kernels(lib_path).items() if "pa_mla_wide_kernel" in name}
     assert len(k) == 4                  # three or four 32-head waves per workgroup, bf16 and fp8 cache
-    for res in k.values():
+    for name, res in k.items():
         assert res["scratch"] == 0
-        assert 108 * 1024 <= res["lds"] <= LDS_PER_CU
+        low = (72 + 36 if "true>" in name else 72) * 1024
+        assert low <= res["lds"] <= LDS_PER_CU, (name, res["lds"])
         assert (res["alloc"] or res["vgpr"]) <= REGISTERS_PER_SIMD_LANE
 
 
