@@ -524,9 +524,9 @@ SharedPlan make_shared_plan(int num_seqs, int num_heads, int num_kv_heads, int h
 #define PA_MLA_FP8_WAVES_PER_CU_ONE_GROUP 4
 #endif
 // Head counts from which the 32-heads-per-wave kernel (pa_mla_wide.hip) runs:
-// three or four of its waves fill a compute unit's SIMDs (its 124 KiB of LDS
-// admit one workgroup per compute unit); fewer heads fit the 16-heads-per-wave
-// kernel's single workgroup per share.
+// three or four of its waves fill a compute unit's SIMDs (its 88 KiB of LDS,
+// 124 KiB with an fp8 cache, admit one workgroup per compute unit); fewer
+// heads fit the 16-heads-per-wave kernel's single workgroup per share.
 #ifndef PA_MLA_WIDE_MIN_HEADS
 #define PA_MLA_WIDE_MIN_HEADS 65
 #endif
