@@ -916,7 +916,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the decode path has no multi-GPU mode in this build).", file=sys.stderr)
+              "(the decode path runs on one GPU; how it would shard is described in the design notes).", file=sys.stderr)
         sys.exit(2)
 
     import torch
