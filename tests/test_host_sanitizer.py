@@ -4,7 +4,7 @@ UndefinedBehaviorSanitizer (no GPU needed).
 A copy of the library is built with the sanitizers on its host code only
 (each -fsanitize behind -Xarch_host; the gfx950 device code is unchanged) into
 _build/sanitize/, rebuilt when a source changes, and the CPU tests of the C
-ABI, the block pool and the latent-cache ABI run against it in a child
+ABI, the block pool, the latent-cache ABI and the threaded calls run against it in a child
 process that preloads the ASan runtime. Any report aborts the child.
 """
 
@@ -18,7 +18,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OUT_DIR = os.path.join(ROOT, "_build", "sanitize")
-TESTS = ["tests/test_abi_cpu.py", "tests/test_block_pool.py", "tests/test_mla_abi_cpu.py"]
+TESTS = ["tests/test_abi_cpu.py", "tests/test_block_pool.py", "tests/test_mla_abi_cpu.py", "tests/test_threads_cpu.py"]
 HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
               "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
               "-shared-libasan"]
