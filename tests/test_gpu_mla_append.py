@@ -155,3 +155,38 @@ def test_full_size_decode_step_append():
     where = torch.nonzero(changed).cpu().numpy()
     written = {(b, o) for b, o in zip(blocks, slots)}
     assert {(int(b), int(o)) for b, o in where} <= written
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_appends(seed):
+    """Seeded random appends: bf16 or fp8 cache, 16- or 32-token blocks, 1-69
+    tokens per sequence, distinct table blocks with some entries outside the
+    pool, positions from negative to past the table, several value ranges and
+    scales; the whole cache compared bit for bit with the oracle."""
+    import decode_attention_paged_07_amd as pa
+    rng = np.random.default_rng(70000 + seed)
+    fp8 = bool(rng.random() < 0.5)
+    bs = 32 if rng.random() < 0.5 else 16
+    S, T, mb = int(rng.integers(1, 20)), int(rng.integers(1, 70)), int(rng.integers(1, 12))
+    pool = S * mb + int(rng.integers(0, 10))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    shape = pa.mla_cache_shape(pool, bs, fp8)
+    if fp8:
+        cache = torch.randint(0, 256, shape, generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
+    else:
+        cache = torch.randn(shape, generator=g, device=DEV).to(torch.bfloat16)
+    table = rng.permutation(pool)[:S * mb].reshape(S, mb).astype(np.int32)
+    off = rng.random((S, mb)) < 0.1
+    table[off] = rng.choice([-2, -1, pool, pool + 1], int(off.sum()))
+    pos = rng.integers(-3, mb * bs + 5, S).astype(np.int32)
+    rows = (torch.randn((S, T, WIDTH), generator=g, device=DEV) * float(rng.choice([0.5, 3.0, 40.0])))
+    rows = rows.to(torch.bfloat16)
+    scale = float(np.float32(rng.choice([1.0, 0.02, 0.3])))
+    print(f"[case] random append {seed}: fp8={fp8} bs={bs} S={S} T={T} mb={mb} pool={pool}", flush=True)
+    before = host(cache)
+    pa.mla_cache_append(cache, rows, torch.from_numpy(table).to(DEV), torch.from_numpy(pos).to(DEV), kv_scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.append_latent(before, host(rows), table, pos, kv_kind="e4m3fn" if fp8 else None, kv_scale=scale)
+    bad = np.argwhere(host(cache) != ref)
+    assert bad.size == 0, f"cache differs in {len(bad)} elements, first {bad[:4].tolist()}"
