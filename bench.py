@@ -32,7 +32,8 @@ KERNEL_SRC = {"pa_streamk_kernel": ("pa_kernels.hip", "pa_sched.h", "pa_wave.h",
               "pa_append_kernel": ("pa_append.hip", "pa_kernels.h"),
               "pa_latent_append_kernel": ("pa_append.hip", "pa_kernels.h"),
               "pa_mla_streamk_kernel": ("pa_mla.hip", "pa_sched.h", "pa_wave.h", "pa_kernels.h"),
-              "pa_mla_wide_kernel": ("pa_mla_wide.hip", "pa_sched.h", "pa_wave.h", "pa_kernels.h")}
+              "pa_mla_wide_kernel": ("pa_mla_wide.hip", "pa_sched.h", "pa_wave.h", "pa_kernels.h"),
+              "pa_shared_kernel": ("pa_shared.hip", "pa_wave.h", "pa_kernels.h")}
 # Head counts from which the latent-cache call runs its 32-heads-per-wave kernel.
 MLA_WIDE_MIN_HEADS = 65
 PEAK_BF16_TFLOPS = 2500.0
@@ -311,6 +312,7 @@ def summarise_shared(stats_dir):
     lines = [
         "# rocprofv3 summary: shared-prefix decode (pa_shared_kernel + pa_shared_merge_kernel)", "",
         f"Workload: {WORKLOAD_TEXT['shared']}", "",
+        f"kernel source sha256[:16]: {rec['kernel_sha']}", "",
         "Command (run from the repository root, TMPDIR=/tmp):",
         f"  rocprofv3 --kernel-trace --stats --output-format csv -d {rel} -o run -- "
         "python3 bench.py --config shared --steps 20 --warmup 5", "",
@@ -672,6 +674,7 @@ def bench_shared(case, steps, warmup):
         "plain_decode_ms": round(ms_plain, 5),
         "plain_decode_logical_gbps": round(logical / (ms_plain / 1e3) / 1e9, 1),
         "speedup_vs_plain": round(ms_plain / ms_shared, 3),
+        "kernel_sha": kernel_sha("pa_shared_kernel"),
     }
 
 
@@ -881,7 +884,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps before the timed ones; enough for the clocks to settle (after "
+                         "10, the latent-cache kernels, bound by their arithmetic, time about 5%% slow)")
     ap.add_argument("--config", default="gqa", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--split", type=int, default=0, help="split tokens (0 = library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
