@@ -465,28 +465,41 @@ def _device_scalar(v, device):
     return t
 
 
-_retired: list = []   # replaced workspaces: kept alive, kernels still queued on their stream may write them
+# Outgrown workspaces, each with an event recorded on its stream after its
+# last use: kept until that event has completed (kernels queued before it may
+# still write the buffer), then dropped.
+_retired: list = []
 
 
 def _workspace_for(device, nbytes):
     """A workspace of at least nbytes for a call on the current stream.
 
     Eager calls share one cached buffer per (device, stream), so calls on
-    different streams never share one; a buffer outgrown by a larger call is
-    kept alive, since kernels still queued may write it. Under graph capture the
-    call gets a buffer of its own from torch's allocator (the graph's memory
-    pool, like any temporary of a captured op) that is never cached: the graph's
-    replays use it alone, and later eager calls cannot replace it."""
+    different streams never share one. A buffer outgrown by a larger call is
+    replaced by one half as large again as it (or the request, if larger), so
+    a slowly growing batch replaces it a logarithmic number of times; the old
+    one stays alive until the work queued on its stream so far has finished.
+    Under graph capture the call gets a buffer of its own from torch's
+    allocator (the graph's memory pool, like any temporary of a captured op)
+    that is never cached: the graph's replays use it alone, and later eager
+    calls cannot replace it."""
     if nbytes == 0:
         return None
     if _capturing():
         return torch.empty(nbytes, dtype=torch.uint8, device=device)
-    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    if _retired:
+        _retired[:] = [(b, e) for b, e in _retired if not e.query()]
+    stream = torch.cuda.current_stream(device)
+    key = (device, stream.cuda_stream)
     t = _workspaces.get(key)
     if t is None or t.numel() < nbytes:
+        size = nbytes
         if t is not None:
-            _retired.append(t)
-        t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            done = torch.cuda.Event()
+            done.record(stream)
+            _retired.append((t, done))
+            size = max(nbytes, t.numel() + t.numel() // 2)
+        t = torch.empty(size, dtype=torch.uint8, device=device)
         _workspaces[key] = t
     return t
 
