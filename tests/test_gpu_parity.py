@@ -134,7 +134,7 @@ def test_zero_length_sequences():
 @pytest.mark.parametrize("num_seqs", [129, 1100])
 def test_many_sequences(num_seqs):
     # More than 128 sequences take the stream-K start-up scan in batches of
-    # 8 x 64 sequences; 1100 spans three batches, the last one partial, and
+    # 16 x 64 sequences; 1100 spans two batches, the second one partial, and
     # about a fifth of the sequences are empty, some at chunk boundaries.
     rng = np.random.default_rng(num_seqs)
     lens = rng.integers(1, 41, num_seqs)
