@@ -269,7 +269,7 @@ def summarise_counters(config, pmc_dir, kernel, label):
         f"kernel source sha256[:16]: {rec['kernel_sha']}", "",
         "Command (run from the repository root, TMPDIR=/tmp):",
         f"  rocprofv3 --pmc {' '.join(counters)} --output-format csv -d {rel} -o run -- "
-        f"python3 bench.py --config {config} --steps 3 --warmup 1 {bench_mode_flags(config)}", "",
+        f"python3 bench.py --config {config} {_run_args(rec, 3, 1)} {bench_mode_flags(config)}", "",
         f"Per dispatch of {kernel} (median over {len(next(iter(vals.values())))} dispatches), summed over the device:",
     ]
     for k in counters:
@@ -298,6 +298,12 @@ def summarise_counters(config, pmc_dir, kernel, label):
     print(f"wrote {path}")
 
 
+def _run_args(rec, steps, warmup):
+    """--steps/--warmup of the bench run whose JSON line is rec (the given
+    defaults for a line that does not record them)."""
+    return f"--steps {rec.get('steps', steps)} --warmup {rec.get('warmup', warmup)}"
+
+
 def summarise_shared(stats_dir):
     """Write the committed summary of a --kernel-trace --stats run of
     ``bench.py --config shared`` (its log, <dir>.log, beside the directory)."""
@@ -315,7 +321,7 @@ def summarise_shared(stats_dir):
         f"kernel source sha256[:16]: {rec['kernel_sha']}", "",
         "Command (run from the repository root, TMPDIR=/tmp):",
         f"  rocprofv3 --kernel-trace --stats --output-format csv -d {rel} -o run -- "
-        "python3 bench.py --config shared --steps 20 --warmup 5", "",
+        f"python3 bench.py --config shared {_run_args(rec, 20, 5)}", "",
         "The bench times the shared-prefix call and then the plain decode call on the same batch, so both "
         "appear below", "(pa_streamk_kernel + pa_streamk_reduce_kernel are the plain call).", "",
         "Kernel stats (ns): name | calls | average | min | max",
@@ -376,11 +382,13 @@ def summarise_profiles(config, stats_dir, fetch_dir, write_dir, cal_fetch_dir, c
     label = f"{config}_append{append}" if append else config
     cmds = {
         "stats": f"rocprofv3 --kernel-trace --stats --output-format csv -d {rel(stats_dir)} -o run -- "
-                 f"python3 bench.py --config {config} --steps 20 --warmup 5 {mode}",
+                 f"python3 bench.py --config {config} {_run_args(rec, 20, 5)} {mode}",
         "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {rel(fetch_dir)} -o run -- "
-                 f"python3 bench.py --config {config} --steps 3 --warmup 1 {mode}",
+                 f"python3 bench.py --config {config} {_run_args(_last_json(fetch_dir.rstrip('/') + '.log'), 3, 1)} "
+                 f"{mode}",
         "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {rel(write_dir)} -o run -- "
-                 f"python3 bench.py --config {config} --steps 3 --warmup 1 {mode}",
+                 f"python3 bench.py --config {config} {_run_args(_last_json(write_dir.rstrip('/') + '.log'), 3, 1)} "
+                 f"{mode}",
         "calibration": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run -- "
                        "python3 bench.py --copy-calibration --steps 3",
     }
