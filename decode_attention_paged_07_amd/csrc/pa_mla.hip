@@ -473,141 +473,85 @@ __global__ void __launch_bounds__(64 * W) pa_mla_streamk_kernel(const MlaArgs a)
 // Merge of the segments of cut sequences, zero rows of empty ones. A
 // segment's row is stored in bf16, the output type (its max and sum stay
 // fp32): half the bytes written and read back, for one more rounding of at
-// most 2^-9 relative per row. Grid (num_seqs, ceil(num_heads / (4 HPW))),
-// four waves of 64; each wave merges the rows of HPW heads of one sequence,
-// eight of a row's 512 values per lane. The merge is bound by the latency of
-// its dependent reads (segment bounds, then maxima and sums, then rows), so a
-// wave issues each round for all its heads at once: the segments' weights one
-// per lane, then every head's rows kMergeSegs segments at a time, added in
-// segment order. Four heads per wave from 64 heads on; with fewer, one, so
-// that the grid still has several waves per SIMD.
-constexpr int kMergeSegs = 2;
-constexpr int kMergeWideHeads = 64;
-
-__device__ __forceinline__ float merge_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
-}
-__device__ __forceinline__ float merge_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-// One head's merge over any number of segments (64 or more: rare), the
-// maxima gathered first and the sums read per chunk of 64.
-__device__ __forceinline__ void merge_head_many(const MlaArgs& a, int seq, int h, int w0, int w1, int lane) {
-  const DecodeArgs& d = a.d;
-  auto row = [&](int w) { return (int64_t)(seq + w) * a.hpad + h; };
-  float big_m = kNegInf;
-  for (int w = w0 + lane; w <= w1; w += 64) big_m = fmaxf(big_m, d.seg_max[row(w)]);
-  big_m = merge_max(big_m);
-  float tot = 0.f;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int c = w0; c <= w1; c += 64) {
-    const int n = min(64, w1 - c + 1);
-    float f = 0.f;
-    if (lane < n) f = fast_exp2(d.seg_max[row(c + lane)] - big_m) * d.seg_sum[row(c + lane)];
-    tot += f;
-    for (int u = 0; u < n; ++u) {
-      const float fw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), u));
-      const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(d.seg_out) +
-                                                      row(c + u) * kMlaLatent + 8 * lane);
-      acc0 += fw * f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
-                         __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
-      acc1 += fw * f32x4{__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xFFFF0000u),
-                         __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xFFFF0000u)};
-    }
-  }
-  const float inv = 1.f / merge_sum(tot);
-  __bf16* out = reinterpret_cast<__bf16*>(d.out) + ((int64_t)seq * d.num_heads + h) * kMlaLatent + 8 * lane;
-  store4(out, acc0 * inv);
-  store4(out + 4, acc1 * inv);
-}
-
-template <int HPW>
+// most 2^-9 relative per row. Grid
+// (num_seqs, ceil(num_heads / 4)), four waves of 64; one (sequence, head) row
+// per wave, eight of its 512 values per lane. The segments' weights are
+// computed one per lane; their rows are read eight segments at a time with
+// the loads in flight together, and added in segment order.
 __global__ void __launch_bounds__(256) pa_mla_reduce_kernel(const MlaArgs a) {
-  constexpr int kMergeHeads = HPW;
   const DecodeArgs& d = a.d;
   const int seq = blockIdx.x;
-  const int h0 = (blockIdx.y * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kMergeHeads;
+  const int h = blockIdx.y * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (h0 >= d.num_heads) return;
-  const int nh = min(kMergeHeads, d.num_heads - h0);
+  if (h >= d.num_heads) return;
+  const int64_t hpad = a.hpad;
   // The length and the segment bounds are read together (the bounds are
   // only used when the length is non-zero).
   const int len = d.seq_lens[seq];
   const int m0 = d.seg_meta[2 * seq], m1 = d.seg_meta[2 * seq + 1];
   const int L = clamp_len(len, d.max_seq_len);
-  __bf16* out = reinterpret_cast<__bf16*>(d.out) + ((int64_t)seq * d.num_heads + h0) * kMlaLatent + 8 * lane;
+  __bf16* out = reinterpret_cast<__bf16*>(d.out) + ((int64_t)seq * d.num_heads + h) * kMlaLatent + 8 * lane;
   if (L == 0) {
-    for (int i = 0; i < nh; ++i) {
-      store4(out + i * kMlaLatent, f32x4{0.f, 0.f, 0.f, 0.f});
-      store4(out + i * kMlaLatent + 4, f32x4{0.f, 0.f, 0.f, 0.f});
-    }
+    store4(out, f32x4{0.f, 0.f, 0.f, 0.f});
+    store4(out + 4, f32x4{0.f, 0.f, 0.f, 0.f});
     return;
   }
   const int w0 = max(0, m0);
   const int w1 = min(a.shares - 1, m1);
   if (w0 >= w1) return;   // one segment: written directly
-  if (w1 - w0 >= 64) {
-    for (int i = 0; i < nh; ++i) merge_head_many(a, seq, h0 + i, w0, w1, lane);
-    return;
+  auto row = [&](int w) { return (int64_t)(seq + w) * hpad + h; };
+  // Up to 64 segments: lane i keeps segment w0 + i's max and sum from one
+  // read. More: the maxima are gathered first, the sums read per chunk.
+  const bool one_chunk = w1 - w0 < 64;
+  float sm = kNegInf, ss = 0.f;
+  if (one_chunk && w0 + lane <= w1) {
+    sm = d.seg_max[row(w0 + lane)];
+    ss = d.seg_sum[row(w0 + lane)];
   }
-  // Up to 64 segments: lane i keeps segment w0 + i's max and sum of each head
-  // (heads past num_heads repeat the last one; they are not stored).
-  const int n = w1 - w0 + 1;
-  auto row = [&](int w, int i) { return (int64_t)(seq + w) * a.hpad + h0 + min(i, nh - 1); };
-  float f[kMergeHeads], tot[kMergeHeads];
+  float big_m = sm;
+  if (!one_chunk)
+    for (int w = w0 + lane; w <= w1; w += 64) big_m = fmaxf(big_m, d.seg_max[row(w)]);
 #pragma unroll
-  for (int i = 0; i < kMergeHeads; ++i) {
-    float sm = kNegInf, ss = 0.f;
+  for (int off = 32; off >= 1; off >>= 1) big_m = fmaxf(big_m, __shfl_xor(big_m, off, 64));
+  float tot = 0.f;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int c = w0; c <= w1; c += 64) {
+    const int n = min(64, w1 - c + 1);
+    float f = 0.f;
     if (lane < n) {
-      sm = d.seg_max[row(w0 + lane, i)];
-      ss = d.seg_sum[row(w0 + lane, i)];
+      if (one_chunk)
+        f = fast_exp2(sm - big_m) * ss;
+      else
+        f = fast_exp2(d.seg_max[row(c + lane)] - big_m) * d.seg_sum[row(c + lane)];
     }
-    f[i] = ss;
-    tot[i] = sm;   // the maximum, until the weights are formed below
-  }
+    tot += f;
+    constexpr int kU = 8;
+    for (int u = 0; u < n; u += kU) {
+      f32x4 v0[kU], v1[kU];
+      float fw[kU];
 #pragma unroll
-  for (int i = 0; i < kMergeHeads; ++i) {
-    const float big_m = merge_max(tot[i]);
-    f[i] = lane < n ? fast_exp2(tot[i] - big_m) * f[i] : 0.f;
-    tot[i] = merge_sum(f[i]);
-  }
-  f32x4 acc0[kMergeHeads], acc1[kMergeHeads];
+      for (int k = 0; k < kU; ++k) {
+        const int idx = min(u + k, n - 1);
+        fw[k] = u + k < n ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), idx)) : 0.f;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(d.seg_out) +
+                                                        row(c + idx) * kMlaLatent + 8 * lane);
+        v0[k] = f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u), __uint_as_float(w[1] << 16),
+                      __uint_as_float(w[1] & 0xFFFF0000u)};
+        v1[k] = f32x4{__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xFFFF0000u), __uint_as_float(w[3] << 16),
+                      __uint_as_float(w[3] & 0xFFFF0000u)};
+      }
 #pragma unroll
-  for (int i = 0; i < kMergeHeads; ++i) acc0[i] = acc1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int u = 0; u < n; u += kMergeSegs) {
-    u32x4 v[kMergeSegs][kMergeHeads];
-#pragma unroll
-    for (int k = 0; k < kMergeSegs; ++k)
-#pragma unroll
-      for (int i = 0; i < kMergeHeads; ++i)
-        v[k][i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(d.seg_out) +
-                                                  row(w0 + min(u + k, n - 1), i) * kMlaLatent + 8 * lane);
-#pragma unroll
-    for (int k = 0; k < kMergeSegs; ++k) {
-      if (u + k >= n) break;
-#pragma unroll
-      for (int i = 0; i < kMergeHeads; ++i) {
-        const float fw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f[i]), u + k));
-        const u32x4 w = v[k][i];
-        acc0[i] += fw * f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
-                              __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
-        acc1[i] += fw * f32x4{__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xFFFF0000u),
-                              __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xFFFF0000u)};
+      for (int k = 0; k < kU; ++k) {
+        acc0 += fw[k] * v0[k];
+        acc1 += fw[k] * v1[k];
       }
     }
   }
 #pragma unroll
-  for (int i = 0; i < kMergeHeads; ++i) {
-    if (i >= nh) break;
-    const float inv = 1.f / tot[i];
-    store4(out + i * kMlaLatent, acc0[i] * inv);
-    store4(out + i * kMlaLatent + 4, acc1[i] * inv);
-  }
+  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+  const float inv = 1.f / tot;
+  store4(out, acc0 * inv);
+  store4(out + 4, acc1 * inv);
 }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream, const LaunchHooks& hooks) {
@@ -634,10 +578,7 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t stream, const LaunchHooks& h
   if (hooks.after_partition) hooks.after_partition(stream);
   if (err != hipSuccess) return err;
   if (hooks.before_reduce) hooks.before_reduce(stream);
-  if (a.d.num_heads >= kMergeWideHeads)
-    hipLaunchKernelGGL(pa_mla_reduce_kernel<4>, dim3(a.d.num_seqs, (a.d.num_heads + 15) / 16), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(pa_mla_reduce_kernel<1>, dim3(a.d.num_seqs, (a.d.num_heads + 3) / 4), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(pa_mla_reduce_kernel, dim3(a.d.num_seqs, (a.d.num_heads + 3) / 4), dim3(256), 0, stream, a);
   err = hipGetLastError();
   if (hooks.after_reduce) hooks.after_reduce(stream);
   return err;
